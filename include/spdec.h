@@ -1,0 +1,206 @@
+/*
+ * spdec.h - query-aware page-sparse decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of block-sparse (page) attention over a paged KV cache, the
+ * dense attention it is checked against, and the per-token sparse-vs-dense
+ * acceptance measure. Sources (web pages, cited by title and section):
+ *   - Sparrow project page ("Sparrow: Sparse Rollout for Stable and Efficient
+ *     Long-context RL of Large Language Models"): "Insights" (block-sparse
+ *     attention; per-token mismatch against the dense model; lower 5th
+ *     percentile), "Control Study 1" (budget grows with generation length),
+ *     "Control Study 2" (cost model: KV budget B, page size, Top-k page
+ *     selection; page size 16).
+ *   - S3R page ("S3R: Fast and Faithful RL Rollouts via Self-Sparse
+ *     Speculative Decoding"): abstract (dense verification needs the complete
+ *     KV cache), Table 3 (KV capacity fixed per rollout; graph replay).
+ *   - Sparrow citation-map page: Quest (query-aware page bound) and
+ *     StreamingLLM (attention sinks) cited by title only.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Ownership: every pointer is a device pointer owned by the caller, unless a
+ *   parameter says "host". The library never allocates, frees or synchronises;
+ *   scratch memory is a caller-provided workspace whose size comes from the
+ *   matching *_workspace_bytes query. Workspaces must be zero-filled once
+ *   after allocation; every call leaves the parts it relies on zeroed again.
+ * Streams: `stream` is a hipStream_t (NULL = the default stream). All work is
+ *   enqueued on it in order; calls return before the GPU finishes. No call
+ *   syncs the host, so every call can be captured into a HIP graph.
+ * Errors: host-side arguments are checked before anything is launched; a
+ *   failed check returns a negative status and launches nothing. A launch
+ *   failure reported by the HIP runtime returns SPDEC_ERR_HIP.
+ * Device-data preconditions (not checked on the host, which cannot read device
+ *   memory without a sync): 0 <= seq_lens[b] <= max_pages_per_seq*page_size;
+ *   page-table entries of pages in use are in [0, num_phys_pages); inputs are
+ *   finite. Kernels never dereference an out-of-range physical page or page
+ *   index: such a page is treated as holding no token.
+ * Threading: calls keep no global state; concurrent calls on different
+ *   streams must not share a workspace.
+ */
+#ifndef SPDEC_H
+#define SPDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spdec_status {
+  SPDEC_OK = 0,
+  SPDEC_ERR_INVALID = -1,     /* null pointer, bad shape or out-of-range scalar            */
+  SPDEC_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, page_size, group size, ... */
+  SPDEC_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query returned      */
+  SPDEC_ERR_HIP = -4          /* the HIP runtime reported a launch error                   */
+} spdec_status;
+
+/* Element type of queries, keys, values and the key min/max summaries. */
+typedef enum spdec_dtype { SPDEC_F32 = 0, SPDEC_BF16 = 1 } spdec_dtype;
+
+/*
+ * Paged KV cache descriptor (plain data, read by every call; host memory).
+ *
+ *  batch                sequences (>= 1)
+ *  num_q_heads (Hq)     query heads; query head h reads KV head h / G, G = Hq/Hkv
+ *  num_kv_heads (Hkv)   KV heads; Hq % Hkv == 0 and G in {1, 2, 4, 8}
+ *  head_dim (D)         64 or 128
+ *  page_size (ps)       tokens per page: 8, 16, 32 or 64
+ *  max_pages_per_seq    row length of page_table (1 .. 32768)
+ *  num_phys_pages       physical pages in each pool
+ *  dtype                spdec_dtype of k_pool, v_pool, kminmax and all queries
+ *  k_pool, v_pool       [num_phys_pages][Hkv][ps][D]: one (page, KV head) is a
+ *                       contiguous ps*D block
+ *  kminmax              [num_phys_pages][Hkv][2][D]: per-channel minimum (row 0)
+ *                       and maximum (row 1) of the page's valid keys
+ *  page_table           int32 [batch][max_pages_per_seq]: logical page -> physical
+ *  seq_lens             int32 [batch]: tokens in the cache, the current one included
+ */
+typedef struct spdec_cache {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int64_t num_phys_pages;
+  int32_t dtype;
+  int32_t reserved;
+  void* k_pool;
+  void* v_pool;
+  void* kminmax;
+  const int32_t* page_table;
+  int32_t* seq_lens;
+} spdec_cache;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* spdec_status_string(int status);
+
+/* Version of this ABI: major*10000 + minor*100 + patch. */
+int spdec_version(void);
+
+/*
+ * spdec_append_kv - write the new token's key and value into the paged cache
+ * and keep its page's key summary current.
+ *
+ * Definition: the budgeted pages are chosen from per-page key summaries that
+ * must cover every token in the cache (page scoring as in Quest, cited on the
+ * Sparrow citation-map page; pages of `page_size` tokens per the Sparrow
+ * project page, "Control Study 2"). For each sequence b and KV head g, with
+ * t = seq_lens[b]: slot t % ps of logical page t / ps receives k_new[b][g] and
+ * v_new[b][g]; if the slot is the page's first, the page's minimum and maximum
+ * become that key, otherwise they widen to include it (elementwise). Then
+ * seq_lens[b] becomes t + 1.
+ *
+ * k_new, v_new: [batch][Hkv][D] in the cache dtype. A sequence whose next slot
+ * falls outside its page table or maps to an out-of-range physical page is
+ * left unchanged (no write, no increment).
+ */
+spdec_status spdec_append_kv(const spdec_cache* cache, const void* k_new, const void* v_new, void* stream);
+
+/*
+ * spdec_build_meta - recompute every in-use page's key minimum and maximum
+ * from the keys in the cache (bulk form of the upkeep in spdec_append_kv, for
+ * a prefilled cache). Only the page's valid tokens t < seq_lens[b] count.
+ */
+spdec_status spdec_build_meta(const spdec_cache* cache, void* stream);
+
+/*
+ * spdec_select_pages - score every page of every (sequence, KV head) and keep
+ * the budgeted Top-k (Sparrow project page, "Control Study 2": a KV budget of
+ * B tokens in pages of `page_size`, chosen by Top-k; budget schedule per
+ * sequence, "Control Study 1").
+ *
+ * Score of page p for KV head g (Quest-style bound, computed in fp32):
+ *   s_p = sum over the G query heads h of g, sum over channels d, of
+ *         max(q_hd * kmax_pd, q_hd * kmin_pd)
+ * Selection with P = ceil(seq_lens[b]/ps) pages and
+ * K = min(max(budget_pages[b], 2), max_budget_pages, P):
+ *   K >= P -> all pages; otherwise page 0 (sink) and page P-1 (local, holds
+ *   the current token) plus the K-2 highest-scoring pages of 1..P-2, equal
+ *   scores going to the lower page index.
+ *
+ * q:            [batch][Hq][D], cache dtype
+ * budget_pages: int32 [batch], budget in pages (sink and local included)
+ * sel_idx:      int32 [batch][Hkv][max_budget_pages] out: logical page indices,
+ *               ascending; entries past sel_cnt are left untouched
+ * sel_cnt:      int32 [batch][Hkv] out: K
+ * scores_out:   nullable fp32 [batch][Hkv][max_pages_per_seq] out: s_p for p < P
+ * max_budget_pages >= 2. Workspace: spdec_select_workspace_bytes().
+ */
+size_t spdec_select_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
+spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
+                                int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spdec_sparse_decode - block-sparse decode attention over the selected pages
+ * (Sparrow project page, "Insights": block-sparse attention; "Control Study
+ * 2": reads only the budgeted KV).
+ *
+ * For query head h of sequence b with group g = h / G, over the tokens t of the
+ * pages sel_idx[b][g][0 .. sel_cnt[b][g]) with t < seq_lens[b]:
+ *   z_t = scale * q_h . k_t,  out_h = sum_t e^{z_t} v_t / sum_t e^{z_t},
+ *   lse_h = ln sum_t e^{z_t}
+ * computed in fp32 as split-KV partials with an online softmax, merged by
+ * log-sum-exp in a fixed order (deterministic, no float atomics).
+ *
+ * q: [batch][Hq][D] cache dtype; out: fp32 [batch][Hq][D]; lse: nullable fp32
+ * [batch][Hq]. sel_idx/sel_cnt as written by spdec_select_pages with the same
+ * max_budget_pages. Workspace: spdec_decode_workspace_bytes(cache, max_budget_pages).
+ */
+size_t spdec_decode_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
+spdec_status spdec_sparse_decode(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
+                                 const int32_t* sel_cnt, int max_budget_pages, float scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spdec_dense_decode - the same attention over every page of the cache: the
+ * dense verifier over the complete KV (S3R abstract: dense verification needs
+ * the complete historical KV cache). Workspace: spdec_decode_workspace_bytes(cache, 0).
+ */
+spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spdec_acceptance - per-token sparse-vs-dense acceptance (Sparrow project
+ * page, "Insights": per-token mismatch against the dense model; wispaper blog:
+ * "acceptance rate"):
+ *   alpha_r = sum_v min(softmax(a_r / T)_v, softmax(b_r / T)_v) = 1 - TV,
+ * computed in fp32 with a fixed reduction order and clamped to [0, 1].
+ *
+ * logits_a, logits_b: fp32 rows of `vocab` entries, row r at r*row_stride
+ * (elements); alpha: fp32 [rows] out. temperature > 0. rows >= 1,
+ * 1 <= vocab <= 2^28. Workspace: spdec_acceptance_workspace_bytes(rows, vocab).
+ * The mean and lower 5th percentile of alpha are host-side statistics.
+ */
+size_t spdec_acceptance_workspace_bytes(int rows, int vocab);
+spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab,
+                              int64_t row_stride, float temperature, float* alpha, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPDEC_H */

@@ -1,0 +1,167 @@
+// C ABI of libspdec: argument checks, workspace queries and stream-ordered launches.
+//
+// Every entry point validates its host-side arguments before touching the HIP
+// runtime, so a rejected call launches nothing and needs no GPU.
+#include <math.h>
+
+#include "launch.h"
+#include "spdec.h"
+
+using spdec::CacheView;
+
+namespace {
+
+constexpr int kMaxPagesPerSeq = 32768;
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return (1 << s) == v ? s : -1;
+}
+
+// Checks the descriptor's shape fields; fills `v` on success.
+spdec_status view_of(const spdec_cache* c, CacheView* v) {
+  if (c == nullptr) return SPDEC_ERR_INVALID;
+  if (c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 || c->max_pages_per_seq < 1 ||
+      c->num_phys_pages < 1 || c->head_dim < 1 || c->page_size < 1)
+    return SPDEC_ERR_INVALID;
+  if (c->num_q_heads % c->num_kv_heads != 0) return SPDEC_ERR_INVALID;
+  if ((int64_t)c->batch * c->num_kv_heads > 65535) return SPDEC_ERR_UNSUPPORTED;  // grid.y limit
+  if (c->max_pages_per_seq > kMaxPagesPerSeq) return SPDEC_ERR_UNSUPPORTED;
+  const int group = c->num_q_heads / c->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return SPDEC_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return SPDEC_ERR_UNSUPPORTED;
+  if (c->page_size != 8 && c->page_size != 16 && c->page_size != 32 && c->page_size != 64) return SPDEC_ERR_UNSUPPORTED;
+  if (c->dtype != SPDEC_F32 && c->dtype != SPDEC_BF16) return SPDEC_ERR_UNSUPPORTED;
+  if (c->page_table == nullptr || c->seq_lens == nullptr) return SPDEC_ERR_INVALID;
+  v->batch = c->batch;
+  v->hq = c->num_q_heads;
+  v->hkv = c->num_kv_heads;
+  v->group = group;
+  v->head_dim = c->head_dim;
+  v->page_size = c->page_size;
+  v->ps_log2 = log2_exact(c->page_size);
+  v->max_pages = c->max_pages_per_seq;
+  v->num_phys = c->num_phys_pages;
+  v->dtype = c->dtype;
+  v->k_pool = c->k_pool;
+  v->v_pool = c->v_pool;
+  v->kminmax = c->kminmax;
+  v->page_table = c->page_table;
+  v->seq_lens = c->seq_lens;
+  return SPDEC_OK;
+}
+
+spdec_status from_hip(hipError_t e) { return e == hipSuccess ? SPDEC_OK : SPDEC_ERR_HIP; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* spdec_status_string(int status) {
+  switch (status) {
+    case SPDEC_OK: return "SPDEC_OK";
+    case SPDEC_ERR_INVALID: return "SPDEC_ERR_INVALID: invalid argument";
+    case SPDEC_ERR_UNSUPPORTED: return "SPDEC_ERR_UNSUPPORTED: shape or dtype not supported";
+    case SPDEC_ERR_WORKSPACE: return "SPDEC_ERR_WORKSPACE: workspace missing or too small";
+    case SPDEC_ERR_HIP: return "SPDEC_ERR_HIP: HIP runtime error";
+    default: return "unknown spdec status";
+  }
+}
+
+int spdec_version(void) { return 100; }
+
+spdec_status spdec_append_kv(const spdec_cache* cache, const void* k_new, const void* v_new, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.k_pool || !v.v_pool || !v.kminmax || !k_new || !v_new) return SPDEC_ERR_INVALID;
+  if (!aligned16(v.k_pool) || !aligned16(v.v_pool) || !aligned16(v.kminmax) || !aligned16(k_new) || !aligned16(v_new))
+    return SPDEC_ERR_INVALID;
+  return from_hip(spdec::launch_append_kv(v, k_new, v_new, static_cast<hipStream_t>(stream)));
+}
+
+spdec_status spdec_build_meta(const spdec_cache* cache, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.k_pool || !v.kminmax || !aligned16(v.k_pool) || !aligned16(v.kminmax)) return SPDEC_ERR_INVALID;
+  return from_hip(spdec::launch_build_meta(v, static_cast<hipStream_t>(stream)));
+}
+
+size_t spdec_select_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK || max_budget_pages < 2) return 0;
+  return spdec::select_workspace_bytes(v);
+}
+
+spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
+                                int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.kminmax || !q || !budget_pages || !sel_idx || !sel_cnt) return SPDEC_ERR_INVALID;
+  if (!aligned16(v.kminmax) || !aligned16(q)) return SPDEC_ERR_INVALID;
+  if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
+  if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
+    return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_select(v, q, budget_pages, max_budget_pages, sel_idx, sel_cnt, scores_out, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t spdec_decode_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK || max_budget_pages < 0) return 0;
+  return spdec::decode_workspace_bytes(v, spdec::decode_plan(v, max_budget_pages));
+}
+
+static spdec_status decode_common(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
+                                  const int32_t* sel_cnt, int max_budget_pages, float scale, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.k_pool || !v.v_pool || !q || !out) return SPDEC_ERR_INVALID;
+  if (!aligned16(v.k_pool) || !aligned16(v.v_pool) || !aligned16(q)) return SPDEC_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return SPDEC_ERR_INVALID;
+  const spdec::DecodePlan plan = spdec::decode_plan(v, max_budget_pages);
+  if (workspace == nullptr || workspace_bytes < spdec::decode_workspace_bytes(v, plan)) return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_decode(v, plan, q, sel_idx, sel_cnt, scale, out, lse, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+spdec_status spdec_sparse_decode(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
+                                 const int32_t* sel_cnt, int max_budget_pages, float scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sel_idx || !sel_cnt || max_budget_pages < 1) return SPDEC_ERR_INVALID;
+  return decode_common(cache, q, sel_idx, sel_cnt, max_budget_pages, scale, out, lse, workspace, workspace_bytes,
+                       stream);
+}
+
+spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(cache, q, nullptr, nullptr, 0, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t spdec_acceptance_workspace_bytes(int rows, int vocab) {
+  if (rows < 1 || vocab < 1 || vocab > (1 << 28)) return 0;
+  return spdec::acceptance_workspace_bytes(rows, vocab);
+}
+
+spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab, int64_t row_stride,
+                              float temperature, float* alpha, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!logits_a || !logits_b || !alpha) return SPDEC_ERR_INVALID;
+  if (rows < 1 || vocab < 1 || vocab > (1 << 28) || row_stride < vocab) return SPDEC_ERR_INVALID;
+  if (rows > 65535) return SPDEC_ERR_UNSUPPORTED;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return SPDEC_ERR_INVALID;
+  if (workspace == nullptr || workspace_bytes < spdec::acceptance_workspace_bytes(rows, vocab))
+    return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_acceptance(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Per-token sparse-vs-dense acceptance over the vocabulary.
+//
+// alpha_r = sum_v min(softmax(a_r/T)_v, softmax(b_r/T)_v) = 1 - TV(p, q)
+// (Sparrow project page, "Insights": the per-token mismatch of the sparse
+// actor against the dense policy; the wispaper blog calls it the acceptance
+// rate). Each row is split into 4096-entry chunks so a few rows still fill the
+// GPU:
+//   pass 1: per chunk, the max and sum of 2^(x - max) of both rows (x = logit*log2e/T);
+//   pass 2: per chunk, the row's global normalisers from the pass-1 partials
+//           (fixed order), then sum_v min(p_v, q_v) over the chunk;
+//   pass 3: per row, the chunk sums in index order, clamped to [0, 1].
+// The second read of the logits in pass 2 comes from the L2 / last-level cache
+// right after pass 1. No float atomics: results are run-to-run identical.
+#include "common.h"
+#include "launch.h"
+
+namespace spdec {
+
+namespace {
+
+constexpr int kAccThreads = 256;
+constexpr int kAccPer = 16;  // entries per thread per row
+constexpr int kAccChunk = kAccThreads * kAccPer;
+
+struct AccArgs {
+  const float* a;
+  const float* b;
+  int rows, vocab, nchunk;
+  int64_t stride;
+  float c;        // log2(e) / T
+  float* part;    // [rows][nchunk][4]: max_a, sum_a, max_b, sum_b
+  float* csum;    // [rows][nchunk]
+  float* alpha;   // [rows]
+};
+
+// Thread t loads entries base + 4t + 1024j .. +3, j = 0..3 (16-byte loads).
+template <bool ALIGNED>
+__device__ __forceinline__ void load_row(const float* row, int vocab, int base, float c, float* x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = base + 4 * (int)threadIdx.x + 1024 * j;
+    if (ALIGNED && idx + 3 < vocab) {
+      const float4 v = *reinterpret_cast<const float4*>(row + idx);
+      x[4 * j + 0] = v.x * c;
+      x[4 * j + 1] = v.y * c;
+      x[4 * j + 2] = v.z * c;
+      x[4 * j + 3] = v.w * c;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[4 * j + u] = (idx + u < vocab) ? row[idx + u] * c : -INFINITY;
+    }
+  }
+}
+
+// Fixed-order block reductions (wave butterfly, then waves in index order).
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  v = group_max<kWave>(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kAccThreads / kWave; ++i) r = fmaxf(r, sh[i]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = group_sum<kWave>(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kAccThreads / kWave; ++i) r += sh[i];
+  return r;
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kAccThreads) void acc_stats_kernel(AccArgs x) {
+  __shared__ float sh[kAccThreads / kWave];
+  const int r = blockIdx.y, ch = blockIdx.x;
+  const int base = ch * kAccChunk;
+  float va[kAccPer], vb[kAccPer];
+  load_row<ALIGNED>(x.a + (int64_t)r * x.stride, x.vocab, base, x.c, va);
+  load_row<ALIGNED>(x.b + (int64_t)r * x.stride, x.vocab, base, x.c, vb);
+  float ma = va[0], mb = vb[0];
+#pragma unroll
+  for (int i = 1; i < kAccPer; ++i) { ma = fmaxf(ma, va[i]); mb = fmaxf(mb, vb[i]); }
+  ma = block_max(ma, sh);
+  mb = block_max(mb, sh);
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) { sa += exp2f(va[i] - ma); sb += exp2f(vb[i] - mb); }
+  sa = block_sum(sa, sh);
+  sb = block_sum(sb, sh);
+  if (threadIdx.x == 0) {
+    float* p = x.part + ((int64_t)r * x.nchunk + ch) * 4;
+    p[0] = ma; p[1] = sa; p[2] = mb; p[3] = sb;
+  }
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kAccThreads) void acc_min_kernel(AccArgs x) {
+  __shared__ float sh[kAccThreads / kWave];
+  __shared__ float s_norm[4];
+  const int r = blockIdx.y, ch = blockIdx.x;
+  if (threadIdx.x < kWave) {
+    // Row normalisers from the chunk partials: lane i folds chunks i, i+64, ...
+    const float* p = x.part + (int64_t)r * x.nchunk * 4;
+    float ma = kNegBig, mb = kNegBig;
+    for (int j = threadIdx.x; j < x.nchunk; j += kWave) { ma = fmaxf(ma, p[4 * j]); mb = fmaxf(mb, p[4 * j + 2]); }
+    ma = group_max<kWave>(ma);
+    mb = group_max<kWave>(mb);
+    float sa = 0.f, sb = 0.f;
+    for (int j = threadIdx.x; j < x.nchunk; j += kWave) {
+      sa += exp2f(p[4 * j] - ma) * p[4 * j + 1];
+      sb += exp2f(p[4 * j + 2] - mb) * p[4 * j + 3];
+    }
+    sa = group_sum<kWave>(sa);
+    sb = group_sum<kWave>(sb);
+    if (threadIdx.x == 0) { s_norm[0] = ma; s_norm[1] = 1.f / sa; s_norm[2] = mb; s_norm[3] = 1.f / sb; }
+  }
+  __syncthreads();
+  const float ma = s_norm[0], ia = s_norm[1], mb = s_norm[2], ib = s_norm[3];
+  float va[kAccPer], vb[kAccPer];
+  const int base = ch * kAccChunk;
+  load_row<ALIGNED>(x.a + (int64_t)r * x.stride, x.vocab, base, x.c, va);
+  load_row<ALIGNED>(x.b + (int64_t)r * x.stride, x.vocab, base, x.c, vb);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) s += fminf(exp2f(va[i] - ma) * ia, exp2f(vb[i] - mb) * ib);
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) x.csum[(int64_t)r * x.nchunk + ch] = s;
+}
+
+__global__ __launch_bounds__(kWave) void acc_final_kernel(AccArgs x) {
+  const int r = blockIdx.x;
+  float s = 0.f;
+  for (int j = threadIdx.x; j < x.nchunk; j += kWave) s += x.csum[(int64_t)r * x.nchunk + j];
+  s = group_sum<kWave>(s);
+  if (threadIdx.x == 0) x.alpha[r] = fminf(1.f, fmaxf(0.f, s));
+}
+
+int nchunks(int vocab) { return (vocab + kAccChunk - 1) / kAccChunk; }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t acceptance_workspace_bytes(int rows, int vocab) {
+  const size_t n = (size_t)rows * nchunks(vocab);
+  return align256(n * 4 * sizeof(float)) + align256(n * sizeof(float));
+}
+
+hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
+                             float* alpha, void* ws, hipStream_t s) {
+  AccArgs x;
+  x.a = a;
+  x.b = b;
+  x.rows = rows;
+  x.vocab = vocab;
+  x.nchunk = nchunks(vocab);
+  x.stride = stride;
+  x.c = kLog2e / temperature;
+  const size_t n = (size_t)rows * x.nchunk;
+  x.part = reinterpret_cast<float*>(ws);
+  x.csum = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(n * 4 * sizeof(float)));
+  x.alpha = alpha;
+  const bool aligned = (reinterpret_cast<uintptr_t>(a) % 16 == 0) && (reinterpret_cast<uintptr_t>(b) % 16 == 0) &&
+                       (stride % 4 == 0);
+  dim3 grid(x.nchunk, rows);
+  if (aligned) {
+    hipLaunchKernelGGL((acc_stats_kernel<true>), grid, dim3(kAccThreads), 0, s, x);
+    hipLaunchKernelGGL((acc_min_kernel<true>), grid, dim3(kAccThreads), 0, s, x);
+  } else {
+    hipLaunchKernelGGL((acc_stats_kernel<false>), grid, dim3(kAccThreads), 0, s, x);
+    hipLaunchKernelGGL((acc_min_kernel<false>), grid, dim3(kAccThreads), 0, s, x);
+  }
+  hipLaunchKernelGGL(acc_final_kernel, dim3(rows), dim3(kWave), 0, s, x);
+  return hipGetLastError();
+}
+
+}  // namespace spdec

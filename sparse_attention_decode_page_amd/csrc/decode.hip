@@ -1,0 +1,330 @@
+// Split-KV decode attention over a page list (sparse) or over every page (dense).
+//
+// Block-sparse decode attention reads only the budgeted pages (Sparrow project
+// page, "Insights" and the "Control Study 2" cost model, whose memory term is
+// the KV budget read per generated token); the dense verifier reads the
+// complete KV (S3R abstract). Both run the same kernel; only the page-list
+// iterator differs.
+//
+// Work decomposition: one workgroup per (split, sequence, KV head). A split is
+// a run of `pages_per_split` entries of the page list, so ragged lengths and
+// budgets become equal-sized work items. All G query heads of the KV head are
+// served by the same workgroup, so every K/V byte is read from HBM once.
+//
+// Lane layout: a token row of D channels is spread over LPT = D/VEC lanes
+// that each hold one 16-byte chunk; one wave load instruction covers TPI =
+// 64/LPT tokens (1 KiB for bf16 D=128). Scores are LPT-lane butterfly sums.
+// Each group of LPT lanes keeps its own fp32 online softmax (running max m,
+// sum l, accumulator acc[G][VEC]) in the log2 domain; the groups, then the
+// four waves, are merged by log-sum-exp at the end of the split, and the
+// per-split partials are merged by a second kernel in a fixed order, so the
+// result is deterministic.
+#include <limits.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace spdec {
+
+namespace {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / kWave;
+constexpr int kChunk = 4;           // load instructions per wave per step
+constexpr int kMaxPagesPerSplit = 256;
+
+struct DecodeArgs {
+  CacheView c;
+  const void* q;
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  int list_cap;         // row stride of sel_idx
+  int pages_per_split;
+  int nsplit;
+  float qk_scale;       // softmax scale * log2(e)
+  float* part_acc;      // [B][Hq][nsplit][D]
+  float* part_ml;       // [B][Hq][nsplit][2]  (running max in log2 units, sum)
+  float* out;           // [B][Hq][D]
+  float* lse;           // [B][Hq] or null
+};
+
+template <bool SPARSE>
+__device__ __forceinline__ int list_length(const DecodeArgs& a, int unit, int P) {
+  if constexpr (SPARSE) return min(max(a.sel_cnt[unit], 0), a.list_cap);
+  return P;
+}
+
+template <typename T, int D, int G, bool SPARSE>
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs a) {
+  constexpr int VEC = T::VEC;
+  constexpr int LPT = D / VEC;
+  constexpr int TPI = kWave / LPT;
+  using S = typename T::storage;
+  const CacheView& c = a.c;
+  const int unit = blockIdx.y;
+  const int b = unit / c.hkv;
+  const int g = unit % c.hkv;
+  const int L = max(c.seq_lens[b], 0);
+  const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  const int n = list_length<SPARSE>(a, unit, P);
+  const int e0 = blockIdx.x * a.pages_per_split;
+  if (e0 >= n) return;
+  const int ne = min(a.pages_per_split, n - e0);
+
+  __shared__ int s_phys[kMaxPagesPerSplit];
+  __shared__ int s_valid[kMaxPagesPerSplit];  // tokens of the page present in the cache
+  for (int i = threadIdx.x; i < ne; i += kDecodeThreads) {
+    int logical = SPARSE ? a.sel_idx[(int64_t)unit * a.list_cap + e0 + i] : e0 + i;
+    int phys = -1;
+    if (logical >= 0 && logical < P) phys = c.page_table[(int64_t)b * c.max_pages + logical];
+    const bool ok = phys >= 0 && phys < c.num_phys;
+    s_phys[i] = ok ? phys : 0;
+    s_valid[i] = ok ? min(c.page_size, L - logical * c.page_size) : 0;
+  }
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int sub = lane % LPT;
+  const int tslot = lane / LPT;
+  const int d0 = sub * VEC;
+
+  float qf[G][VEC];
+  const S* q = reinterpret_cast<const S*>(a.q);
+#pragma unroll
+  for (int h = 0; h < G; ++h) unpack<T>(load16(q + ((int64_t)b * c.hq + g * G + h) * D + d0), qf[h]);
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegBig;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+  }
+  __syncthreads();
+
+  const S* kp = reinterpret_cast<const S*>(c.k_pool);
+  const S* vp = reinterpret_cast<const S*>(c.v_pool);
+  const int ninstr = (ne << c.ps_log2) / TPI;  // TPI divides every supported page size
+  const int nchunks = (ninstr + kChunk - 1) / kChunk;
+
+  auto load_chunk = [&](int chunk, u32x4* kr, u32x4* vr, bool* ok) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int ins = chunk * kChunk + i;
+      const int s = ins * TPI + tslot;
+      const int e = min(s >> c.ps_log2, ne - 1);
+      const int slot = s & (c.page_size - 1);
+      ok[i] = ins < ninstr && slot < s_valid[e];
+      const int64_t off = ((((int64_t)s_phys[e] * c.hkv + g) << c.ps_log2) + (ok[i] ? slot : 0)) * D + d0;
+      kr[i] = load16(kp + off);
+      vr[i] = load16(vp + off);
+    }
+  };
+
+  u32x4 kA[kChunk], vA[kChunk], kB[kChunk], vB[kChunk];
+  bool okA[kChunk], okB[kChunk];
+  int chunk = wave;
+  if (chunk < nchunks) load_chunk(chunk, kA, vA, okA);
+  for (; chunk < nchunks; chunk += kDecodeWaves) {
+    const int next = chunk + kDecodeWaves;
+    if (next < nchunks) load_chunk(next, kB, vB, okB);
+
+    float sc[kChunk][G];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      float kf[VEC];
+      unpack<T>(kA[i], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d = fmaf(qf[h][e], kf[e], d);
+        d = group_sum<LPT>(d);
+        sc[i][h] = okA[i] ? d * a.qk_scale : -INFINITY;
+      }
+    }
+    float p[kChunk][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = sc[0][h];
+#pragma unroll
+      for (int i = 1; i < kChunk; ++i) mx = fmaxf(mx, sc[i][h]);
+      const float mn = fmaxf(m[h], mx);
+      const float alpha = exp2f(m[h] - mn);
+      m[h] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        p[i][h] = exp2f(sc[i][h] - mn);
+        ps += p[i][h];
+      }
+      l[h] = l[h] * alpha + ps;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      float vf[VEC];
+      unpack<T>(vA[i], vf);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) vf[e] = okA[i] ? vf[e] : 0.f;  // never multiply unread slots
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p[i][h], vf[e], acc[h][e]);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) { kA[i] = kB[i]; vA[i] = vB[i]; okA[i] = okB[i]; }
+  }
+
+  // Merge the TPI token groups of the wave (butterfly over lanes LPT apart).
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float M = fmaxf(m[h], mo);
+      const float f1 = exp2f(m[h] - M), f2 = exp2f(mo - M);
+      l[h] = l[h] * f1 + lo * f2;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * f1 + ao * f2;
+      }
+      m[h] = M;
+    }
+  }
+
+  // Merge the waves through LDS and write this split's partial.
+  __shared__ float s_acc[kDecodeWaves][G][D];
+  __shared__ float s_m[kDecodeWaves][G], s_l[kDecodeWaves][G];
+  if (tslot == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s_acc[wave][h][d0 + e] = acc[h][e];
+      if (sub == 0) { s_m[wave][h] = m[h]; s_l[wave][h] = l[h]; }
+    }
+  }
+  __syncthreads();
+  const int64_t row0 = ((int64_t)b * c.hq + g * G) * a.nsplit + blockIdx.x;  // head g*G, this split
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+    const int h = idx / D, d = idx % D;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) o += exp2f(s_m[w][h] - M) * s_acc[w][h][d];
+    a.part_acc[(row0 + (int64_t)h * a.nsplit) * D + d] = o;
+    if (d == 0) {
+      float Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) Ls += exp2f(s_m[w][h] - M) * s_l[w][h];
+      a.part_ml[(row0 + (int64_t)h * a.nsplit) * 2 + 0] = M;
+      a.part_ml[(row0 + (int64_t)h * a.nsplit) * 2 + 1] = Ls;
+    }
+  }
+}
+
+// out_h = sum_j 2^{m_j-M} acc_j / sum_j 2^{m_j-M} l_j, lse_h = ln2 (M + log2 sum_j 2^{m_j-M} l_j),
+// splits taken in index order.
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  const CacheView& c = a.c;
+  const int bh = blockIdx.x;
+  const int b = bh / c.hq;
+  const int h = bh % c.hq;
+  const int unit = b * c.hkv + h / c.group;
+  const int L = max(c.seq_lens[b], 0);
+  const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  const int n = list_length<SPARSE>(a, unit, P);
+  const int ns = (n + a.pages_per_split - 1) / a.pages_per_split;
+  const int d = threadIdx.x;
+  const float* ml = a.part_ml + (int64_t)bh * a.nsplit * 2;
+  const float* pa = a.part_acc + (int64_t)bh * a.nsplit * D;
+  float M = kNegBig;
+  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[2 * j]);
+  float Ls = 0.f, o = 0.f;
+  for (int j = 0; j < ns; ++j) {
+    const float w = exp2f(ml[2 * j] - M);
+    Ls += w * ml[2 * j + 1];
+    o += w * pa[(int64_t)j * D + d];
+  }
+  a.out[(int64_t)bh * D + d] = Ls > 0.f ? o / Ls : 0.f;
+  if (a.lse != nullptr && d == 0) a.lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int D, int G, bool SPARSE>
+hipError_t decode_impl(const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.nsplit, a.c.batch * a.c.hkv);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, SPARSE>), grid, dim3(kDecodeThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D, SPARSE>), dim3(a.c.batch * a.c.hq), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool SPARSE>
+hipError_t decode_g(const DecodeArgs& a, hipStream_t s) {
+  switch (a.c.group) {
+    case 1: return decode_impl<T, D, 1, SPARSE>(a, s);
+    case 2: return decode_impl<T, D, 2, SPARSE>(a, s);
+    case 4: return decode_impl<T, D, 4, SPARSE>(a, s);
+    default: return decode_impl<T, D, 8, SPARSE>(a, s);
+  }
+}
+
+template <bool SPARSE>
+hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
+  if (a.c.dtype == SPDEC_BF16)
+    return a.c.head_dim == 64 ? decode_g<BF16, 64, SPARSE>(a, s) : decode_g<BF16, 128, SPARSE>(a, s);
+  return a.c.head_dim == 64 ? decode_g<F32, 64, SPARSE>(a, s) : decode_g<F32, 128, SPARSE>(a, s);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+DecodePlan decode_plan(const CacheView& c, int max_budget_pages) {
+  DecodePlan p;
+  p.list_pages = max_budget_pages > 0 ? max_budget_pages : c.max_pages;
+  // About 512 tokens per split, fewer when the grid would otherwise leave the
+  // 256 compute units idle. The plan depends only on the list capacity, so a
+  // sparse call whose capacity is every page splits exactly like the dense one.
+  constexpr int kTargetTokens = 512;
+  int pps = max(1, kTargetTokens / c.page_size);
+  const int64_t units = (int64_t)c.batch * c.hkv;
+  while (pps > 1 && units * ((p.list_pages + pps - 1) / pps) < 2048) pps >>= 1;
+  p.pages_per_split = min(pps, kMaxPagesPerSplit);
+  p.nsplit = (p.list_pages + p.pages_per_split - 1) / p.pages_per_split;
+  return p;
+}
+
+size_t decode_workspace_bytes(const CacheView& c, const DecodePlan& p) {
+  const size_t rows = (size_t)c.batch * c.hq * p.nsplit;
+  return align256(rows * c.head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q, const int32_t* sel_idx,
+                         const int32_t* sel_cnt, float scale, float* out, float* lse, void* ws, hipStream_t s) {
+  DecodeArgs a;
+  a.c = c;
+  a.q = q;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.list_cap = p.list_pages;
+  a.pages_per_split = p.pages_per_split;
+  a.nsplit = p.nsplit;
+  a.qk_scale = scale * kLog2e;
+  const size_t rows = (size_t)c.batch * c.hq * p.nsplit;
+  a.part_acc = reinterpret_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(rows * c.head_dim * sizeof(float)));
+  a.out = out;
+  a.lse = lse;
+  return sel_idx != nullptr ? decode_dispatch<true>(a, s) : decode_dispatch<false>(a, s);
+}
+
+}  // namespace spdec

@@ -1,0 +1,254 @@
+// Page scoring and top-B page selection.
+//
+// Score (Quest-style bound; Quest is cited by title on the Sparrow citation-map
+// page): s_p = sum_h sum_d max(q_hd*kmax_pd, q_hd*kmin_pd) over the G query
+// heads of a KV head. Because kmax >= kmin, the maximum picks kmax exactly when
+// q_hd > 0, so s_p = sum_d (kmax_pd*Qpos_d + kmin_pd*Qneg_d) with
+// Qpos_d = sum_h max(q_hd,0) and Qneg_d = sum_h min(q_hd,0): two fp32 FMAs per
+// channel and page instead of 2G. Scoring is a GEMV over 2*D values per page,
+// so it streams the page summaries with 16-byte loads and reduces across lanes.
+//
+// Selection (Top-k pages under a KV budget, Sparrow project page "Control
+// Study 2"; sink/local pages always kept): K = min(max(budget,2), cap, P);
+// pages 0 and P-1 are forced, the other K-2 are the largest scores of 1..P-2
+// with ties to the lower index. A 4-pass MSB-first radix select on
+// order-preserving uint32 keys in LDS finds the cut key T and how many keys
+// equal to T are taken; one ordered compaction then emits the kept pages
+// already ascending, and equal keys are taken in index order, which is the
+// tie rule.
+#include "common.h"
+#include "launch.h"
+
+namespace spdec {
+
+namespace {
+
+constexpr int kScorePages = 256;   // pages per scoring workgroup
+constexpr int kSelectThreads = 256;
+constexpr size_t kSelectLdsKeyBytes = 60 * 1024;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const void* __restrict__ qv,
+                                                          float* __restrict__ scores) {
+  constexpr int VEC = T::VEC;
+  constexpr int LPT = D / VEC;      // lanes per page summary row
+  constexpr int PPI = kWave / LPT;  // pages per load instruction
+  constexpr int ITERS = kScorePages / 4 / PPI;
+  using S = typename T::storage;
+  const int unit = blockIdx.y;
+  const int b = unit / c.hkv;
+  const int g = unit % c.hkv;
+  const int L = c.seq_lens[b];
+  const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  const int p_begin = blockIdx.x * kScorePages;
+  if (p_begin >= P) return;
+
+  __shared__ int s_phys[kScorePages];
+  {
+    const int p = p_begin + threadIdx.x;
+    int phys = -1;
+    if (p < P) phys = c.page_table[(int64_t)b * c.max_pages + p];
+    s_phys[threadIdx.x] = (phys >= 0 && phys < c.num_phys) ? phys : -1;
+  }
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int sub = lane % LPT;
+  const int d0 = sub * VEC;
+  float qpos[VEC], qneg[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) { qpos[e] = 0.f; qneg[e] = 0.f; }
+  const S* q = reinterpret_cast<const S*>(qv);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float f[VEC];
+    unpack<T>(load16(q + ((int64_t)b * c.hq + g * G + h) * D + d0), f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      qpos[e] += fmaxf(f[e], 0.f);
+      qneg[e] += fminf(f[e], 0.f);
+    }
+  }
+  __syncthreads();
+
+  const S* mm = reinterpret_cast<const S*>(c.kminmax);
+  float* srow = scores + (int64_t)unit * c.max_pages;
+#pragma unroll 4
+  for (int it = 0; it < ITERS; ++it) {
+    const int pl = wave * (kScorePages / 4) + it * PPI + lane / LPT;
+    const int phys = s_phys[pl];
+    const int64_t row = ((int64_t)(phys < 0 ? 0 : phys) * c.hkv + g) * 2 * D + d0;
+    const u32x4 lo = load16(mm + row);
+    const u32x4 hi = load16(mm + row + D);
+    float fl[VEC], fh[VEC];
+    unpack<T>(lo, fl);
+    unpack<T>(hi, fh);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      s = fmaf(fh[e], qpos[e], s);
+      s = fmaf(fl[e], qneg[e], s);
+    }
+    s = group_sum<LPT>(s);
+    const int p = p_begin + pl;
+    if (sub == 0 && phys >= 0 && p < P) srow[p] = s;
+  }
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Keys live in LDS when the page count allows it (KEYS_IN_LDS), otherwise
+// every pass re-reads the fp32 scores (L2-resident after the first pass).
+template <int NT, bool KEYS_IN_LDS>
+__global__ __launch_bounds__(NT) void select_topk_kernel(CacheView c, const int32_t* __restrict__ budget,
+                                                         int cap, const float* __restrict__ scores,
+                                                         int32_t* __restrict__ sel_idx,
+                                                         int32_t* __restrict__ sel_cnt) {
+  extern __shared__ uint32_t keys[];
+  __shared__ uint32_t hist[256];
+  __shared__ int s_digit, s_above;
+  __shared__ int s_wave[NT / kWave][2];
+  const int unit = blockIdx.x;
+  const int b = unit / c.hkv;
+  const int tid = threadIdx.x;
+  const int L = c.seq_lens[b];
+  const int P = min((max(L, 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  int32_t* out = sel_idx + (int64_t)unit * cap;
+  const int K = min(min(max(budget[b], 2), cap), P);
+  if (K >= P) {
+    for (int i = tid; i < P; i += NT) out[i] = i;
+    if (tid == 0) sel_cnt[unit] = P;
+    return;
+  }
+  // Here 2 <= K < P, so P >= 3.
+  const int M = P - 2;
+  const int need = K - 2;
+  if (tid == 0) {
+    out[0] = 0;
+    out[K - 1] = P - 1;
+    sel_cnt[unit] = K;
+  }
+  if (need == 0) return;
+  const float* srow = scores + (int64_t)unit * c.max_pages + 1;
+  if constexpr (KEYS_IN_LDS) {
+    for (int i = tid; i < M; i += NT) keys[i] = score_key(srow[i]);
+    __syncthreads();
+  }
+  auto key = [&](int i) -> uint32_t {
+    if constexpr (KEYS_IN_LDS) return keys[i];
+    return score_key(srow[i]);
+  };
+
+  uint32_t prefix = 0, mask = 0;
+  int remaining = need;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < M; i += NT) {
+      const uint32_t k = key(i);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // Lane l owns bins 255-4l .. 252-4l, scanned from the top.
+      const int top = 255 - 4 * tid;
+      const int c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+      const int tot = c0 + c1 + c2 + c3;
+      const int incl = wave_incl_scan(tot);
+      const int excl = incl - tot;
+      if (excl < remaining && remaining <= incl) {
+        const int r = remaining - excl;
+        int digit, above;
+        if (r <= c0) { digit = top; above = excl; }
+        else if (r <= c0 + c1) { digit = top - 1; above = excl + c0; }
+        else if (r <= c0 + c1 + c2) { digit = top - 2; above = excl + c0 + c1; }
+        else { digit = top - 3; above = excl + c0 + c1 + c2; }
+        s_digit = digit;
+        s_above = above;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_digit << shift;
+    mask |= 0xFFu << shift;
+    remaining -= s_above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const int eq_take = remaining;  // keys equal to T still to take, in index order
+
+  // Ordered compaction: thread t owns a contiguous run of the middle pages.
+  const int per = (M + NT - 1) / NT;
+  const int i0 = min(tid * per, M);
+  const int i1 = min(i0 + per, M);
+  int gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = key(i);
+    gt += k > T;
+    eq += k == T;
+  }
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int gt_incl = wave_incl_scan(gt);
+  const int eq_incl = wave_incl_scan(eq);
+  if (lane == kWave - 1) { s_wave[wave][0] = gt_incl; s_wave[wave][1] = eq_incl; }
+  __syncthreads();
+  int gt_before = gt_incl - gt, eq_before = eq_incl - eq;
+  for (int w = 0; w < wave; ++w) { gt_before += s_wave[w][0]; eq_before += s_wave[w][1]; }
+  int pos = 1 + gt_before + min(eq_before, eq_take);
+  int eq_seen = eq_before;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = key(i);
+    bool take = k > T;
+    if (k == T) { take = eq_seen < eq_take; ++eq_seen; }
+    if (take && pos < K - 1) out[pos++] = i + 1;  // pos never passes the local page's slot
+  }
+}
+
+template <typename T, int D>
+hipError_t score_impl(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+  dim3 grid((c.max_pages + kScorePages - 1) / kScorePages, c.batch * c.hkv);
+  switch (c.group) {
+    case 1: hipLaunchKernelGGL((score_pages_kernel<T, D, 1>), grid, dim3(256), 0, s, c, q, scores); break;
+    case 2: hipLaunchKernelGGL((score_pages_kernel<T, D, 2>), grid, dim3(256), 0, s, c, q, scores); break;
+    case 4: hipLaunchKernelGGL((score_pages_kernel<T, D, 4>), grid, dim3(256), 0, s, c, q, scores); break;
+    default: hipLaunchKernelGGL((score_pages_kernel<T, D, 8>), grid, dim3(256), 0, s, c, q, scores); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t select_workspace_bytes(const CacheView& c) {
+  return (size_t)c.batch * c.hkv * c.max_pages * sizeof(float);
+}
+
+hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budget, int max_budget, int32_t* sel_idx,
+                         int32_t* sel_cnt, float* scores_out, void* ws, hipStream_t s) {
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
+  hipError_t e;
+  if (c.dtype == SPDEC_BF16) {
+    e = c.head_dim == 64 ? score_impl<BF16, 64>(c, q, scores, s) : score_impl<BF16, 128>(c, q, scores, s);
+  } else {
+    e = c.head_dim == 64 ? score_impl<F32, 64>(c, q, scores, s) : score_impl<F32, 128>(c, q, scores, s);
+  }
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)c.max_pages * sizeof(uint32_t);
+  if (lds <= kSelectLdsKeyBytes) {
+    hipLaunchKernelGGL((select_topk_kernel<kSelectThreads, true>), dim3(c.batch * c.hkv), dim3(kSelectThreads), lds,
+                       s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+  } else {
+    hipLaunchKernelGGL((select_topk_kernel<kSelectThreads, false>), dim3(c.batch * c.hkv), dim3(kSelectThreads), 0,
+                       s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace spdec

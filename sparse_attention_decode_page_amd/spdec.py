@@ -1,0 +1,245 @@
+"""Python binding of libspdec (ctypes): argument marshalling only.
+
+Every step runs in the HIP kernels behind the C ABI declared in
+``include/spdec.h``; this module only turns torch device tensors into raw
+pointers, passes torch's current HIP stream, and raises on a non-OK status.
+PyTorch provides device memory and streams. There is no fallback: if the
+shared library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspdec.so")
+
+SPDEC_OK, SPDEC_ERR_INVALID, SPDEC_ERR_UNSUPPORTED, SPDEC_ERR_WORKSPACE, SPDEC_ERR_HIP = 0, -1, -2, -3, -4
+SPDEC_F32, SPDEC_BF16 = 0, 1
+
+ABI_FUNCTIONS = (
+    "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
+    "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_decode_workspace_bytes",
+    "spdec_sparse_decode", "spdec_dense_decode", "spdec_acceptance_workspace_bytes", "spdec_acceptance",
+)
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of ``struct spdec_cache``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("kminmax", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspdec.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run sparse_attention_decode_page_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    D = ctypes.POINTER(CacheDesc)
+    sig = {
+        "spdec_status_string": (ctypes.c_char_p, [I]),
+        "spdec_version": (I, []),
+        "spdec_append_kv": (I, [D, P, P, P]),
+        "spdec_build_meta": (I, [D, P]),
+        "spdec_select_workspace_bytes": (SZ, [D, I]),
+        "spdec_select_pages": (I, [D, P, P, I, P, P, P, P, SZ, P]),
+        "spdec_decode_workspace_bytes": (SZ, [D, I]),
+        "spdec_sparse_decode": (I, [D, P, P, P, I, F, P, P, P, SZ, P]),
+        "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
+        "spdec_acceptance_workspace_bytes": (SZ, [I, I]),
+        "spdec_acceptance": (I, [P, P, I, I, I64, F, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().spdec_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != SPDEC_OK:
+        raise RuntimeError(f"{what} failed: {status_string(status)}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> torch.Tensor:
+    if given is not None:
+        return given
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class PagedCache:
+    """Paged KV cache: torch device tensors plus the ``spdec_cache`` descriptor over them.
+
+    k_pool, v_pool: [num_phys_pages][Hkv][page_size][D] (bfloat16 or float32);
+    kminmax: [num_phys_pages][Hkv][2][D] same dtype; page_table: int32
+    [batch][max_pages]; seq_lens: int32 [batch].
+    """
+
+    def __init__(self, k_pool, v_pool, kminmax, page_table, seq_lens, num_q_heads: int):
+        for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (kminmax, "kminmax")):
+            _need(t, n)
+        _need(page_table, "page_table", torch.int32)
+        _need(seq_lens, "seq_lens", torch.int32)
+        if k_pool.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("cache dtype must be bfloat16 or float32")
+        if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype or kminmax.dtype != k_pool.dtype:
+            raise ValueError("k_pool, v_pool and kminmax must share dtype and pool shape")
+        nphys, hkv, ps, d = k_pool.shape
+        if tuple(kminmax.shape) != (nphys, hkv, 2, d):
+            raise ValueError("kminmax must be [num_phys_pages][Hkv][2][D]")
+        batch, max_pages = page_table.shape
+        if tuple(seq_lens.shape) != (batch,):
+            raise ValueError("seq_lens must be [batch]")
+        self.k_pool, self.v_pool, self.kminmax = k_pool, v_pool, kminmax
+        self.page_table, self.seq_lens = page_table, seq_lens
+        self.batch, self.num_q_heads, self.num_kv_heads = batch, int(num_q_heads), hkv
+        self.head_dim, self.page_size, self.max_pages, self.num_phys = d, ps, max_pages, nphys
+        self.dtype = k_pool.dtype
+        self.desc = CacheDesc(batch, self.num_q_heads, hkv, d, ps, max_pages, nphys,
+                              SPDEC_BF16 if k_pool.dtype == torch.bfloat16 else SPDEC_F32, 0,
+                              k_pool.data_ptr(), v_pool.data_ptr(), kminmax.data_ptr(),
+                              page_table.data_ptr(), seq_lens.data_ptr())
+
+    @property
+    def device(self):
+        return self.k_pool.device
+
+
+def append_kv(cache: PagedCache, k_new: torch.Tensor, v_new: torch.Tensor):
+    shape = (cache.batch, cache.num_kv_heads, cache.head_dim)
+    _need(k_new, "k_new", cache.dtype, shape)
+    _need(v_new, "v_new", cache.dtype, shape)
+    _check(lib().spdec_append_kv(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _stream()), "spdec_append_kv")
+
+
+def build_meta(cache: PagedCache):
+    _check(lib().spdec_build_meta(ctypes.byref(cache.desc), _stream()), "spdec_build_meta")
+
+
+def select_workspace_bytes(cache: PagedCache, max_budget_pages: int) -> int:
+    return int(lib().spdec_select_workspace_bytes(ctypes.byref(cache.desc), int(max_budget_pages)))
+
+
+def select_pages(cache: PagedCache, q, budget_pages, max_budget_pages: int, sel_idx=None, sel_cnt=None,
+                 scores_out=None, workspace=None):
+    _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    _need(budget_pages, "budget_pages", torch.int32, (cache.batch,))
+    dev = cache.device
+    if sel_idx is None:
+        sel_idx = torch.zeros((cache.batch, cache.num_kv_heads, max_budget_pages), dtype=torch.int32, device=dev)
+    if sel_cnt is None:
+        sel_cnt = torch.zeros((cache.batch, cache.num_kv_heads), dtype=torch.int32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, (cache.batch, cache.num_kv_heads, max_budget_pages))
+    _need(sel_cnt, "sel_cnt", torch.int32, (cache.batch, cache.num_kv_heads))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.float32, (cache.batch, cache.num_kv_heads, cache.max_pages))
+        ws_ptr, ws_bytes = _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size()
+    else:
+        workspace = _workspace(select_workspace_bytes(cache, max_budget_pages), dev, workspace)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check(lib().spdec_select_pages(ctypes.byref(cache.desc), _ptr(q), _ptr(budget_pages), int(max_budget_pages),
+                                    _ptr(sel_idx), _ptr(sel_cnt), _ptr(scores_out), ws_ptr, ws_bytes, _stream()),
+           "spdec_select_pages")
+    return sel_idx, sel_cnt
+
+
+def decode_workspace_bytes(cache: PagedCache, max_budget_pages: int) -> int:
+    return int(lib().spdec_decode_workspace_bytes(ctypes.byref(cache.desc), int(max_budget_pages)))
+
+
+def _outs(cache, out, lse):
+    dev = cache.device
+    if out is None:
+        out = torch.empty((cache.batch, cache.num_q_heads, cache.head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((cache.batch, cache.num_q_heads), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (cache.batch, cache.num_q_heads, cache.head_dim))
+    _need(lse, "lse", torch.float32, (cache.batch, cache.num_q_heads))
+    return out, lse
+
+
+def sparse_decode(cache: PagedCache, q, sel_idx, sel_cnt, max_budget_pages: int, scale: Optional[float] = None,
+                  out=None, lse=None, workspace=None):
+    _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    _need(sel_idx, "sel_idx", torch.int32, (cache.batch, cache.num_kv_heads, max_budget_pages))
+    _need(sel_cnt, "sel_cnt", torch.int32, (cache.batch, cache.num_kv_heads))
+    out, lse = _outs(cache, out, lse)
+    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    ws = _workspace(decode_workspace_bytes(cache, max_budget_pages), cache.device, workspace)
+    _check(lib().spdec_sparse_decode(ctypes.byref(cache.desc), _ptr(q), _ptr(sel_idx), _ptr(sel_cnt),
+                                     int(max_budget_pages), scale, _ptr(out), _ptr(lse), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream()), "spdec_sparse_decode")
+    return out, lse
+
+
+def dense_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None, lse=None, workspace=None):
+    _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    out, lse = _outs(cache, out, lse)
+    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    ws = _workspace(decode_workspace_bytes(cache, 0), cache.device, workspace)
+    _check(lib().spdec_dense_decode(ctypes.byref(cache.desc), _ptr(q), scale, _ptr(out), _ptr(lse), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream()), "spdec_dense_decode")
+    return out, lse
+
+
+def acceptance_workspace_bytes(rows: int, vocab: int) -> int:
+    return int(lib().spdec_acceptance_workspace_bytes(int(rows), int(vocab)))
+
+
+def acceptance(logits_a, logits_b, temperature: float = 1.0, alpha=None, workspace=None):
+    """Per-row acceptance sum_v min(softmax(a/T), softmax(b/T)) of two [rows][vocab] fp32 tensors."""
+    for t, n in ((logits_a, "logits_a"), (logits_b, "logits_b")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or t.dim() != 2:
+            raise ValueError(f"{n} must be a 2-D float32 GPU tensor")
+        if t.stride(1) != 1:
+            raise ValueError(f"{n} rows must be contiguous")
+    if logits_a.shape != logits_b.shape or logits_a.stride(0) != logits_b.stride(0):
+        raise ValueError("logits_a and logits_b must share shape and row stride")
+    rows, vocab = logits_a.shape
+    if alpha is None:
+        alpha = torch.empty(rows, dtype=torch.float32, device=logits_a.device)
+    _need(alpha, "alpha", torch.float32, (rows,))
+    ws = _workspace(acceptance_workspace_bytes(rows, vocab), logits_a.device, workspace)
+    _check(lib().spdec_acceptance(_ptr(logits_a), _ptr(logits_b), rows, vocab, logits_a.stride(0),
+                                  float(temperature), _ptr(alpha), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream()), "spdec_acceptance")
+    return alpha

@@ -1,0 +1,116 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad
+arguments before launching anything (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_decode_page_amd import spdec as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(S.LIB_PATH):
+        from sparse_attention_decode_page_amd import build
+        build.build()
+    return S.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "spdec.h")).read()
+    return sorted(set(re.findall(r"\b(spdec_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = _declared()
+    assert len(names) == len(S.ABI_FUNCTIONS) == 11
+    assert set(names) == set(S.ABI_FUNCTIONS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    for code in (0, -1, -2, -3, -4):
+        assert S.status_string(code).startswith("SPDEC_")
+    assert "unknown" in S.status_string(7)
+    assert L.spdec_version() == 100
+
+
+FAKE = 0x7F0000000000  # 4 KiB-aligned address that is never dereferenced by a rejected call
+
+
+def _desc(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, max_pages_per_seq=64,
+                num_phys_pages=128, dtype=S.SPDEC_BF16, reserved=0, k_pool=FAKE, v_pool=FAKE + 0x100000,
+                kminmax=FAKE + 0x200000, page_table=FAKE + 0x300000, seq_lens=FAKE + 0x400000)
+    base.update(kw)
+    return S.CacheDesc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), S.SPDEC_ERR_UNSUPPORTED),
+    (dict(page_size=12), S.SPDEC_ERR_UNSUPPORTED),
+    (dict(page_size=128), S.SPDEC_ERR_UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=2), S.SPDEC_ERR_UNSUPPORTED),    # group 3
+    (dict(num_q_heads=32, num_kv_heads=2), S.SPDEC_ERR_UNSUPPORTED),   # group 16
+    (dict(num_q_heads=7, num_kv_heads=2), S.SPDEC_ERR_INVALID),        # not a multiple
+    (dict(dtype=5), S.SPDEC_ERR_UNSUPPORTED),
+    (dict(batch=0), S.SPDEC_ERR_INVALID),
+    (dict(max_pages_per_seq=40000), S.SPDEC_ERR_UNSUPPORTED),
+    (dict(page_table=None), S.SPDEC_ERR_INVALID),
+    (dict(seq_lens=None), S.SPDEC_ERR_INVALID),
+    (dict(k_pool=FAKE + 8), S.SPDEC_ERR_INVALID),                      # misaligned pool
+])
+def test_descriptor_validation(L, kw, code):
+    d = _desc(**kw)
+    assert L.spdec_append_kv(ctypes.byref(d), FAKE, FAKE, None) == code
+    if "k_pool" not in kw:
+        assert L.spdec_select_pages(ctypes.byref(d), FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 0, None) == code
+
+
+def test_null_descriptor_and_pointers(L):
+    assert L.spdec_append_kv(None, FAKE, FAKE, None) == S.SPDEC_ERR_INVALID
+    d = _desc()
+    assert L.spdec_append_kv(ctypes.byref(d), None, FAKE, None) == S.SPDEC_ERR_INVALID
+    assert L.spdec_select_pages(ctypes.byref(d), None, FAKE, 16, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert L.spdec_sparse_decode(ctypes.byref(d), FAKE, None, FAKE, 16, 0.1, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert L.spdec_dense_decode(ctypes.byref(d), FAKE, 0.1, None, None, FAKE, 1 << 30, None) == -1
+
+
+def test_budget_scale_and_workspace_checks(L):
+    d = _desc()
+    # max_budget_pages below 2
+    assert L.spdec_select_pages(ctypes.byref(d), FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1 << 30, None) == -1
+    # select workspace: needed unless scores_out is given
+    need = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
+    assert need == 2 * 2 * 64 * 4
+    assert L.spdec_select_pages(ctypes.byref(d), FAKE, FAKE, 16, FAKE, FAKE, None, FAKE, need - 1, None) == -3
+    assert L.spdec_select_pages(ctypes.byref(d), FAKE, FAKE, 16, FAKE, FAKE, None, None, 0, None) == -3
+    # decode: bad scale, then short workspace
+    dw = L.spdec_decode_workspace_bytes(ctypes.byref(d), 0)
+    sw = L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
+    assert dw > 0 and sw > 0
+    assert L.spdec_dense_decode(ctypes.byref(d), FAKE, 0.0, FAKE, None, FAKE, dw, None) == -1
+    assert L.spdec_dense_decode(ctypes.byref(d), FAKE, float("nan"), FAKE, None, FAKE, dw, None) == -1
+    assert L.spdec_dense_decode(ctypes.byref(d), FAKE, 0.1, FAKE, None, FAKE, dw - 1, None) == -3
+    assert L.spdec_sparse_decode(ctypes.byref(d), FAKE, FAKE, FAKE, 16, 0.1, FAKE, None, FAKE, sw - 1, None) == -3
+    assert L.spdec_sparse_decode(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 0.1, FAKE, None, FAKE, sw, None) == -1
+
+
+def test_acceptance_checks(L):
+    ws = L.spdec_acceptance_workspace_bytes(64, 151936)
+    assert ws >= 64 * 38 * 5 * 4
+    assert L.spdec_acceptance_workspace_bytes(0, 10) == 0
+    assert L.spdec_acceptance(FAKE, FAKE, 64, 151936, 151936, 0.0, FAKE, FAKE, ws, None) == -1   # T = 0
+    assert L.spdec_acceptance(FAKE, FAKE, 64, 151936, 100, 1.0, FAKE, FAKE, ws, None) == -1      # stride < vocab
+    assert L.spdec_acceptance(FAKE, FAKE, 0, 151936, 151936, 1.0, FAKE, FAKE, ws, None) == -1
+    assert L.spdec_acceptance(FAKE, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws - 1, None) == -3
+    assert L.spdec_acceptance(None, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws, None) == -1
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(S.CacheDesc) == 80
+    assert S.CacheDesc.num_phys_pages.offset == 24 and S.CacheDesc.k_pool.offset == 40

@@ -1,0 +1,367 @@
+"""GPU parity: every ABI call against the CPU oracle, element by element.
+
+Small and edge-case shapes are checked on every (sequence, KV head); the
+full-size workloads on sampled units (the oracle computes them one by one)
+plus properties checked on every unit. Bars: metadata bit-exact; page sets
+exact outside the 1e-6 score band around the cut; outputs within 1e-5 (fp32)
+or 1e-2 (bf16) max-abs; acceptance within 1e-5.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_decode_page_amd import spdec
+from sparse_attention_decode_page_amd import synth as S
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import gpu_support as GS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(spdec.LIB_PATH):
+        from sparse_attention_decode_page_amd import build
+        build.build()
+    spdec.lib()
+    assert torch.cuda.is_available()
+
+
+def _check_path(wl, units, full_units_props=True):
+    """Run build_meta -> select -> sparse -> dense on the GPU and check against the oracle."""
+    spec = wl.spec
+    dw = GS.DeviceWorkload(wl)
+    c = dw.cache
+    spdec.build_meta(c)
+    sel_idx, sel_cnt, scores = GS.run_select(dw)
+    out_s, lse_s = spdec.sparse_decode(c, dw.q, sel_idx, sel_cnt, dw.max_budget)
+    out_d, lse_d = spdec.dense_decode(c, dw.q)
+    torch.cuda.synchronize()
+    meta = GS.from_device_storage(dw.kminmax, spec.dtype)
+    sel_idx_h, sel_cnt_h = sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
+    scores_h = scores.cpu().numpy()
+    out_s_h, lse_s_h = out_s.cpu().numpy(), lse_s.cpu().numpy()
+    out_d_h, lse_d_h = out_d.cpu().numpy(), lse_d.cpu().numpy()
+    assert np.all(np.isfinite(out_s_h)) and np.all(np.isfinite(out_d_h))
+    assert np.all(np.isfinite(lse_s_h)) and np.all(np.isfinite(lse_d_h))
+    ps, G = spec.page_size, spec.group
+    if full_units_props:
+        for b in range(spec.batch):
+            P = wl.pages(b)
+            for g in range(spec.num_kv_heads):
+                K = GS.expected_count(P, int(wl.budget_pages[b]), dw.max_budget)
+                assert sel_cnt_h[b, g] == K
+                row = sel_idx_h[b, g, :K]
+                assert np.all(np.diff(row) > 0) and row[0] == 0 and row[-1] == P - 1
+    tol = GS.TOL_OUT[spec.dtype]
+    scale = GS.default_scale(wl)
+    worst = {"meta": 0, "score": 0.0, "sparse": 0.0, "dense": 0.0, "lse": 0.0}
+    for (b, g) in units:
+        K64, V64 = GS.unit_kv_f64(wl, b, g)
+        L, P = int(wl.lens[b]), wl.pages(b)
+        # metadata: bit-exact (compared as decoded values)
+        kmin, kmax = O.page_minmax(K64, ps)
+        phys = wl.page_table[b, :P]
+        gmin = O.to_f64(meta[phys, g, 0], spec.dtype)
+        gmax = O.to_f64(meta[phys, g, 1], spec.dtype)
+        assert np.array_equal(gmin, kmin) and np.array_equal(gmax, kmax), (b, g)
+        # scores within the fp32 band, page set valid under the tie rule
+        s64 = O.page_scores(GS.q_group_f64(wl, b, g), kmin, kmax)
+        err = np.abs(scores_h[b, g, :P] - s64).max() / max(np.abs(s64).max(), 1e-30)
+        worst["score"] = max(worst["score"], err)
+        assert err <= GS.SCORE_BAND, (b, g, err)
+        cnt = int(sel_cnt_h[b, g])
+        GS.check_selection(sel_idx_h[b, g], cnt, s64, int(wl.budget_pages[b]), dw.max_budget)
+        # attention over the GPU's page set, and over all pages
+        qg = GS.q_group_f64(wl, b, g)
+        o, lse = O.decode_unit(qg, K64, V64, sel_idx_h[b, g, :cnt], ps, scale)
+        e = np.abs(out_s_h[b, g * G:(g + 1) * G] - o).max()
+        el = np.abs(lse_s_h[b, g * G:(g + 1) * G] - lse).max()
+        worst["sparse"] = max(worst["sparse"], e)
+        worst["lse"] = max(worst["lse"], el)
+        assert e <= tol and el <= tol, (b, g, e, el)
+        o, lse = O.dense_decode_unit(qg, K64, V64, ps, scale)
+        e = np.abs(out_d_h[b, g * G:(g + 1) * G] - o).max()
+        el = np.abs(lse_d_h[b, g * G:(g + 1) * G] - lse).max()
+        worst["dense"] = max(worst["dense"], e)
+        worst["lse"] = max(worst["lse"], el)
+        assert e <= tol and el <= tol, (b, g, e, el)
+    say(f"  {spec.name}: {len(units)} units checked, worst {worst}")
+    return dw, sel_idx_h, sel_cnt_h
+
+
+# ------------------------------------------------------------- small cases ---
+
+def test_tiny_all_units():
+    say("case tiny (fp32, D64, G2, L1024, ps16, budget 16 pages)")
+    wl = S.make_workload("tiny", seed=0)
+    _check_path(wl, GS.sample_units(wl, 10 ** 9))
+
+
+EDGE = [
+    # dtype, D, Hq, Hkv, ps, lens, budget pages
+    ("f32", 64, 2, 2, 16, [1, 2, 15, 16, 17, 33], [16, 16, 16, 2, 3, 2]),
+    ("f32", 128, 8, 1, 8, [100, 257, 64], [5, 9, 8]),
+    ("bf16", 128, 4, 4, 16, [1, 16, 17, 300, 511, 1000], [2, 2, 2, 7, 12, 40]),
+    ("bf16", 64, 16, 2, 32, [33, 64, 65, 2000], [2, 3, 4, 20]),
+    ("bf16", 128, 16, 2, 64, [64, 65, 129, 4100], [2, 2, 3, 30]),
+    ("bf16", 128, 8, 1, 8, [9, 800, 4095], [2, 50, 300]),
+    ("bf16", 128, 32, 8, 16, [5000, 7777], [1, 600]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_edge_shapes_all_units(case, seed):
+    dt, D, Hq, Hkv, ps, lens, bud = EDGE[case]
+    say(f"case edge {case} seed {seed}: {dt} D{D} Hq{Hq}/Hkv{Hkv} ps{ps} lens {lens} budget {bud}")
+    spec = S.custom_spec(f"edge{case}", batch=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                         page_size=ps, dtype=dt, lens=("list", lens), budget=("pages", bud),
+                         outlier_channels=4 if dt == "bf16" else 0)
+    wl = S.make_workload(spec, seed=seed, headroom=ps)
+    _check_path(wl, GS.sample_units(wl, 10 ** 9))
+
+
+def test_exact_ties_go_to_lower_index():
+    """Pages with identical keys tie exactly in fp32 and fp64; the lower index must win."""
+    say("case exact ties")
+    spec = S.custom_spec("ties", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, dtype="bf16",
+                         lens=("list", [16 * 40, 16 * 33 + 5]), budget=("pages", [10, 7]))
+    wl = S.make_workload(spec, seed=3, headroom=0)
+    ps = 16
+    rng = np.random.default_rng(9)
+    for b in range(2):
+        P = wl.pages(b)
+        templ = rng.integers(0, 4, size=P)  # page p copies template page templ[p]
+        for g in range(2):
+            for p in range(1, P - 1):
+                src = wl.page_table[b, 1 + templ[p]]
+                dst = wl.page_table[b, p]
+                if dst != src:
+                    wl.k_pool[dst, g] = wl.k_pool[src, g]
+    dw, sel_idx_h, sel_cnt_h = _check_path(wl, GS.sample_units(wl, 10 ** 9))
+    for b in range(2):
+        for g in range(2):
+            K64, _ = GS.unit_kv_f64(wl, b, g)
+            s64 = GS.oracle_scores(wl, b, g, K64)
+            want = O.select_pages(s64, int(wl.budget_pages[b]))
+            got = sel_idx_h[b, g, :sel_cnt_h[b, g]]
+            assert got.tolist() == want.tolist(), (b, g)
+
+
+def test_full_budget_sparse_equals_dense_bitwise():
+    say("case full budget == dense")
+    spec = S.custom_spec("full", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, dtype="bf16",
+                         lens=("list", [1000, 1024, 37]), budget=("pages", [64, 64, 64]))
+    wl = S.make_workload(spec, seed=1)
+    dw = GS.DeviceWorkload(wl)
+    c = dw.cache
+    spdec.build_meta(c)
+    cap = c.max_pages
+    sel_idx, sel_cnt = spdec.select_pages(c, dw.q, dw.budget, cap)
+    o_s, l_s = spdec.sparse_decode(c, dw.q, sel_idx, sel_cnt, cap)
+    o_d, l_d = spdec.dense_decode(c, dw.q)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d) and torch.equal(l_s, l_d)
+
+
+def test_determinism_bitwise():
+    say("case determinism")
+    wl = S.make_workload(S.custom_spec("det", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                                       dtype="bf16", lens=("list", [3000, 9000, 17, 12345]),
+                                       budget=("pages", [64, 100, 4, 256]), outlier_channels=4), seed=2)
+    dw = GS.DeviceWorkload(wl)
+    c = dw.cache
+    spdec.build_meta(c)
+    runs = []
+    for _ in range(3):
+        si, sc, scores = GS.run_select(dw)
+        o, l = spdec.sparse_decode(c, dw.q, si, sc, dw.max_budget)
+        od, ld = spdec.dense_decode(c, dw.q)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in (si, sc, scores, o, l, od, ld)])
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
+
+
+def test_physical_placement_invariance():
+    say("case physical permutation")
+    spec = S.custom_spec("perm", batch=3, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16, dtype="bf16",
+                         lens=("list", [500, 2048, 1111]), budget=("pages", [8, 30, 20]))
+    wl = S.make_workload(spec, seed=4)
+    outs = []
+    for variant in range(2):
+        if variant == 1:
+            perm = np.random.default_rng(77).permutation(wl.num_phys)
+            kp, vp = np.empty_like(wl.k_pool), np.empty_like(wl.v_pool)
+            kp[perm] = wl.k_pool
+            vp[perm] = wl.v_pool
+            pt = np.where(wl.page_table >= 0, perm[np.maximum(wl.page_table, 0)], -1).astype(np.int32)
+            wl.k_pool, wl.v_pool, wl.page_table = kp, vp, pt
+        dw = GS.DeviceWorkload(wl)
+        spdec.build_meta(dw.cache)
+        si, sc, scores = GS.run_select(dw)
+        o, l = spdec.sparse_decode(dw.cache, dw.q, si, sc, dw.max_budget)
+        od, ld = spdec.dense_decode(dw.cache, dw.q)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (si, sc, o, l, od, ld)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ append ---
+
+@pytest.mark.parametrize("dt,D,ps", [("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 8), ("bf16", 64, 64)])
+def test_append_kv_matches_oracle_and_bulk_build(dt, D, ps):
+    say(f"case append {dt} D{D} ps{ps}")
+    spec = S.custom_spec("append", batch=3, num_q_heads=4, num_kv_heads=2, head_dim=D, page_size=ps, dtype=dt,
+                         lens=("list", [ps - 3, 2 * ps, 5 * ps + 1]), budget=("pages", [3, 3, 4]))
+    steps = 2 * ps + 5
+    wl = S.make_workload(spec, seed=5, headroom=steps)
+    dw = GS.DeviceWorkload(wl)
+    c = dw.cache
+    spdec.build_meta(c)
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    lens = wl.lens.copy()
+    for step in range(steps):
+        kn, vn = S.append_tokens(wl, step)
+        spdec.append_kv(c, GS.to_device_storage(kn, dt), GS.to_device_storage(vn, dt))
+        for b in range(spec.batch):
+            t = int(lens[b])
+            phys = wl.page_table[b, t // ps]
+            kp[phys, :, t % ps] = kn[b]
+            vp[phys, :, t % ps] = vn[b]
+            lens[b] += 1
+    torch.cuda.synchronize()
+    assert np.array_equal(dw.seq_lens.cpu().numpy(), lens)
+    assert np.array_equal(GS.from_device_storage(dw.k_pool, dt), kp)
+    assert np.array_equal(GS.from_device_storage(dw.v_pool, dt), vp)
+    meta_inc = dw.kminmax.clone()
+    spdec.build_meta(c)
+    torch.cuda.synchronize()
+    # incremental upkeep == bulk rebuild on the GPU, both == oracle
+    assert torch.equal(meta_inc.view(torch.int16) if dt == "bf16" else meta_inc,
+                       dw.kminmax.view(torch.int16) if dt == "bf16" else dw.kminmax)
+    meta = GS.from_device_storage(dw.kminmax, dt)
+    for b in range(spec.batch):
+        P = (int(lens[b]) + ps - 1) // ps
+        for g in range(spec.num_kv_heads):
+            K64 = O.to_f64(O.gather_tokens(kp, wl.page_table[b], int(lens[b]), g, ps), dt)
+            kmin, kmax = O.page_minmax(K64, ps)
+            phys = wl.page_table[b, :P]
+            assert np.array_equal(O.to_f64(meta[phys, g, 0], dt), kmin)
+            assert np.array_equal(O.to_f64(meta[phys, g, 1], dt), kmax)
+
+
+def test_append_skips_full_sequences():
+    say("case append past capacity")
+    spec = S.custom_spec("cap", batch=2, num_q_heads=2, num_kv_heads=1, head_dim=64, page_size=8, dtype="bf16",
+                         lens=("list", [16, 10]), budget=("pages", [2, 2]))
+    wl = S.make_workload(spec, seed=0, headroom=0)  # sequence 0 is exactly full
+    dw = GS.DeviceWorkload(wl)
+    kn, vn = S.append_tokens(wl, 0)
+    before = dw.k_pool.clone()
+    spdec.append_kv(dw.cache, GS.to_device_storage(kn, "bf16"), GS.to_device_storage(vn, "bf16"))
+    torch.cuda.synchronize()
+    assert dw.seq_lens.cpu().tolist() == [16, 11]
+    changed = (before.view(torch.int16) != dw.k_pool.view(torch.int16)).any(dim=(1, 2, 3)).cpu().numpy()
+    assert changed.sum() == 1 and changed[wl.page_table[1, 1]]
+
+
+# -------------------------------------------------------------- acceptance ---
+
+def _acc_check(a, b, T, tol=GS.TOL_ALPHA, stride=None):
+    dev = "cuda"
+    R, V = a.shape
+    if stride is None:
+        ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    else:
+        ba = torch.zeros((R, stride), dtype=torch.float32, device=dev)
+        bb = torch.zeros((R, stride), dtype=torch.float32, device=dev)
+        ba[:, :V] = torch.from_numpy(a)
+        bb[:, :V] = torch.from_numpy(b)
+        ta, tb = ba[:, :V], bb[:, :V]
+    alpha = spdec.acceptance(ta, tb, T).cpu().numpy()
+    want = np.array([O.acceptance(a[r], b[r], T) for r in range(R)])
+    err = np.abs(alpha - want).max()
+    assert err <= tol, err
+    return alpha, want
+
+
+def test_acceptance_tiny():
+    say("case acceptance tiny")
+    spec = S.SPECS["tiny"]
+    a, b, _ = S.make_logits(spec, 0)
+    _acc_check(a, b, spec.temperature)
+    _acc_check(a, b, 0.7)
+    alpha, _ = _acc_check(a, a.copy(), 1.0)
+    assert np.all(np.abs(alpha - 1.0) <= 1e-6)
+
+
+@pytest.mark.parametrize("V", [1, 3, 4095, 4097, 10000])
+def test_acceptance_ragged_vocab_and_unaligned_rows(V):
+    say(f"case acceptance V={V}")
+    r = np.random.default_rng(V)
+    a = (2 * r.standard_normal((5, V))).astype(np.float32)
+    b = (a + r.standard_normal((5, V))).astype(np.float32)
+    _acc_check(a, b, 1.0)
+    _acc_check(a, b, 2.5, stride=V + 1)
+
+
+def test_acceptance_full_size():
+    say("case acceptance 64 x 151936")
+    spec = S.SPECS["qwen3-8b-L32k-acceptance"]
+    a, b, heavy = S.make_logits(spec, 0)
+    alpha, want = _acc_check(a, b, spec.temperature)
+    mean, p5 = O.tail_stats(alpha)
+    wmean, wp5 = O.tail_stats(want)
+    say(f"  mean {mean:.6f} (oracle {wmean:.6f}), p5 {p5:.6f} (oracle {wp5:.6f}), heavy rows {heavy.tolist()}")
+    assert abs(mean - wmean) <= 1e-5 and abs(p5 - wp5) <= 1e-5
+    assert np.all(alpha[heavy] < np.delete(alpha, heavy).min())
+
+
+# --------------------------------------------------------------- full size ---
+
+FULL = ["qwen3-1.7b-L16k", "qwen3-8b-ragged", "long-131k-ps8", "long-131k-ps16", "long-131k-ps32",
+        "long-131k-ps64", "qwen3-8b-L32k-acceptance"]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    say(f"case full-size {name}: generating")
+    wl = S.make_workload(name, seed=0, build_pool=True)
+    units = GS.sample_units(wl, 8, seed=1)
+    say(f"  generated; checking units {units}")
+    dw, sel_idx_h, sel_cnt_h = _check_path(wl, units)
+    if wl.spec.planted_block:
+        ps = wl.spec.page_size
+        for (b, g) in units:
+            s0 = int(wl.plant_start[b, g])
+            pages = set(range(s0 // ps, (s0 + wl.spec.planted_block - 1) // ps + 1))
+            got = set(sel_idx_h[b, g, :sel_cnt_h[b, g]].tolist())
+            assert pages <= got, (b, g, sorted(pages - got))
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_binding_rejects_bad_arguments():
+    wl = S.make_workload("tiny", seed=0)
+    dw = GS.DeviceWorkload(wl)
+    with pytest.raises(ValueError):
+        spdec.dense_decode(dw.cache, dw.q[:, :2])
+    with pytest.raises(ValueError):
+        spdec.select_pages(dw.cache, dw.q, dw.budget.to(torch.int64), 16)
+    with pytest.raises(RuntimeError):
+        spdec.dense_decode(dw.cache, dw.q, scale=-1.0)
