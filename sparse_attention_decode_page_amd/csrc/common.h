@@ -73,6 +73,25 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+template <int N>
+__device__ __forceinline__ double group_sum(double x) {
+  if constexpr (N >= 2) x += dpp<kQuadSwap1>(x);
+  if constexpr (N >= 4) x += dpp<kQuadSwap2>(x);
+  if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 2) x = fmaxf(x, dpp<kQuadSwap1>(x));

@@ -4,9 +4,12 @@
 // page): s_p = sum_h sum_d max(q_hd*kmax_pd, q_hd*kmin_pd) over the G query
 // heads of a KV head. Because kmax >= kmin, the maximum picks kmax exactly when
 // q_hd > 0, so s_p = sum_d (kmax_pd*Qpos_d + kmin_pd*Qneg_d) with
-// Qpos_d = sum_h max(q_hd,0) and Qneg_d = sum_h min(q_hd,0): two fp32 FMAs per
+// Qpos_d = sum_h max(q_hd,0) and Qneg_d = sum_h min(q_hd,0): two FMAs per
 // channel and page instead of 2G. Scoring is a GEMV over 2*D values per page,
 // so it streams the page summaries with 16-byte loads and reduces across lanes.
+// The sum is accumulated in fp64 and rounded once, so each fp32 score is the
+// correctly rounded bound even when products cancel (fp64 FMA issues at the
+// fp32 rate on this chip and the kernel is bound by HBM, not ALU).
 //
 // Selection (Top-k pages under a KV budget, Sparrow project page "Control
 // Study 2"; sink/local pages always kept): K = min(max(budget,2), cap, P);
@@ -55,9 +58,9 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
   const int wave = threadIdx.x / kWave;
   const int sub = lane % LPT;
   const int d0 = sub * VEC;
-  float qpos[VEC], qneg[VEC];
+  double qpos[VEC], qneg[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) { qpos[e] = 0.f; qneg[e] = 0.f; }
+  for (int e = 0; e < VEC; ++e) { qpos[e] = 0.0; qneg[e] = 0.0; }
   const S* q = reinterpret_cast<const S*>(qv);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -65,8 +68,8 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
     unpack<T>(load16(q + ((int64_t)b * c.hq + g * G + h) * D + d0), f);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      qpos[e] += fmaxf(f[e], 0.f);
-      qneg[e] += fminf(f[e], 0.f);
+      qpos[e] += (double)fmaxf(f[e], 0.f);
+      qneg[e] += (double)fminf(f[e], 0.f);
     }
   }
   __syncthreads();
@@ -83,15 +86,15 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
     float fl[VEC], fh[VEC];
     unpack<T>(lo, fl);
     unpack<T>(hi, fh);
-    float s = 0.f;
+    double s = 0.0;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      s = fmaf(fh[e], qpos[e], s);
-      s = fmaf(fl[e], qneg[e], s);
+      s = fma((double)fh[e], qpos[e], s);
+      s = fma((double)fl[e], qneg[e], s);
     }
     s = group_sum<LPT>(s);
     const int p = p_begin + pl;
-    if (sub == 0 && phys >= 0 && p < P) srow[p] = s;
+    if (sub == 0 && phys >= 0 && p < P) srow[p] = (float)s;
   }
 }
 

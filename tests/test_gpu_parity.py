@@ -76,9 +76,10 @@ def _check_path(wl, units, full_units_props=True):
         assert np.array_equal(gmin, kmin) and np.array_equal(gmax, kmax), (b, g)
         # scores within the fp32 band, page set valid under the tie rule
         s64 = O.page_scores(GS.q_group_f64(wl, b, g), kmin, kmax)
-        err = np.abs(scores_h[b, g, :P] - s64).max() / max(np.abs(s64).max(), 1e-30)
+        # fp32 scores are the fp64-accumulated bound rounded once: within 2^-23 of each page's own score
+        err = (np.abs(scores_h[b, g, :P] - s64) / np.maximum(np.abs(s64), 1e-30)).max()
         worst["score"] = max(worst["score"], err)
-        assert err <= GS.SCORE_BAND, (b, g, err)
+        assert err <= 1.2e-7, (b, g, err)
         cnt = int(sel_cnt_h[b, g])
         GS.check_selection(sel_idx_h[b, g], cnt, s64, int(wl.budget_pages[b]), dw.max_budget)
         # attention over the GPU's page set, and over all pages
