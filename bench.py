@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of query-aware page-sparse attention with its dense
+verifier and the acceptance measure, on one GPU.
+
+A step is one pass of the whole hot path over one batch: append_kv (new token
+into the paged cache + page key summaries) -> select_pages (Quest-style page
+bounds, top-B with sink/local pages) -> sparse_decode (split-KV attention over
+the kept pages) -> dense_decode (the same attention over every page) ->
+acceptance (sum_v min(p, q) over 64 x 151936 logit rows). Inputs are seeded
+synthetic data shaped like a Qwen3-8B decode layer with ragged 8K-32K contexts;
+everything is resident in HBM before timing starts.
+
+Prints ONE JSON line. `value` is decode tokens/s of the full step (batch / step
+time). Per-row times come from HIP events recorded on the stream the kernels
+run on; `roofline` is for the dominant kernel (dense decode), `sparse` reports
+the sparse path (select + sparse decode) against HBM peak, and `cpu_baseline`
+times the CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode attn tokens/s + effective KV GB/s (% HBM peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "qwen3-8b-ragged"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(spec, lens, budget_pages, cap, rows, vocab):
+    """Bytes each row must move per step (valid tokens / pages only)."""
+    ps, D, Hkv = spec.page_size, spec.head_dim, spec.num_kv_heads
+    elt = 2 if spec.dtype == "bf16" else 4
+    L = lens.astype(np.int64)
+    P = (L + ps - 1) // ps
+    K = np.minimum(np.minimum(np.maximum(budget_pages.astype(np.int64), 2), cap), P)
+    last = L - (P - 1) * ps
+    sel_tokens = np.where(K >= P, L, (K - 1) * ps + last)
+    kv_tok = 2 * D * elt                      # K + V row of one token, one KV head
+    meta_page = 2 * D * elt                   # kmin + kmax of one page, one KV head
+    return {
+        "append_kv": int(spec.batch * Hkv * (kv_tok + 2 * meta_page)),
+        "select_pages": int(Hkv * (P * meta_page).sum()),
+        "sparse_decode": int(Hkv * (sel_tokens * kv_tok).sum()),
+        "dense_decode": int(Hkv * (L * kv_tok).sum()),
+        "acceptance": int(2 * rows * vocab * 4),
+    }
+
+
+def cpu_baseline(wl, steps_tokens, seconds: float):
+    """Time the CPU oracle on the same step for as many sequences as fit in `seconds`."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(O, wl, steps_tokens, seconds)
+
+
+def _cpu_baseline(O, wl, steps_tokens, seconds):
+    spec = wl.spec
+    ps, G, D = spec.page_size, spec.group, spec.head_dim
+    scale = 1.0 / math.sqrt(D)
+    kn, vn = steps_tokens
+    t_total, n_seq = 0.0, 0
+    for b in range(spec.batch):
+        # untimed: the cache as it stands before the step (gathered, decoded, summarised)
+        state = []
+        for g in range(spec.num_kv_heads):
+            L = int(wl.lens[b])
+            K = O.to_f64(O.gather_tokens(wl.k_pool, wl.page_table[b], L, g, ps), spec.dtype)
+            V = O.to_f64(O.gather_tokens(wl.v_pool, wl.page_table[b], L, g, ps), spec.dtype)
+            kmin, kmax = O.page_minmax(K, ps)
+            state.append((K, V, kmin, kmax))
+        t0 = time.perf_counter()
+        for g, (K, V, kmin, kmax) in enumerate(state):
+            k_new = O.to_f64(kn[b, g], spec.dtype)
+            v_new = O.to_f64(vn[b, g], spec.dtype)
+            L = K.shape[0]
+            K = np.concatenate([K, k_new[None]])
+            V = np.concatenate([V, v_new[None]])
+            p, slot = divmod(L, ps)
+            if p == kmin.shape[0]:
+                kmin = np.concatenate([kmin, k_new[None]])
+                kmax = np.concatenate([kmax, k_new[None]])
+            kmin[p], kmax[p] = O.append_minmax(kmin[p], kmax[p], k_new, slot)
+            qg = O.to_f64(wl.q[b, g * G:(g + 1) * G], spec.dtype)
+            pages = O.select_pages(O.page_scores(qg, kmin, kmax), int(wl.budget_pages[b]))
+            O.decode_unit(qg, K, V, pages, ps, scale)
+            O.dense_decode_unit(qg, K, V, ps, scale)
+        O.acceptance(wl.logits_a[b], wl.logits_b[b], spec.temperature)
+        t_total += time.perf_counter() - t0
+        n_seq += 1
+        if t_total >= seconds:
+            break
+    return {"value": n_seq / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"full step (append, select, sparse, dense, acceptance) for {n_seq} of {spec.batch} "
+                      f"sequences x {spec.num_kv_heads} KV heads, fp64 NumPy, 1 thread; "
+                      f"{t_total:.1f} s of CPU time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              "(the per-(sequence, KV head) work shards without any exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_attention_decode_page_amd import spdec
+    from sparse_attention_decode_page_amd import synth as S
+
+    if not os.path.exists(spdec.LIB_PATH):
+        from sparse_attention_decode_page_amd import build
+        build.build()
+    spdec.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K_steps, W = args.steps, args.warmup
+    t_setup = time.perf_counter()
+    wl = S.make_workload(args.workload, seed=args.seed, headroom=K_steps + W + 1)
+    spec = wl.spec
+    assert spec.logits is not None, "the step needs logit rows for the acceptance row"
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+
+    def up(x):
+        if spec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    k_pool, v_pool = up(wl.k_pool), up(wl.v_pool)
+    kminmax = torch.zeros((wl.num_phys, spec.num_kv_heads, 2, spec.head_dim), dtype=tdt, device=dev)
+    page_table = torch.from_numpy(wl.page_table).to(dev)
+    seq_lens = torch.from_numpy(wl.lens.astype(np.int32)).to(dev)
+    cache = spdec.PagedCache(k_pool, v_pool, kminmax, page_table, seq_lens, spec.num_q_heads)
+    q = up(wl.q)
+    budget = torch.from_numpy(wl.budget_pages.astype(np.int32)).to(dev)
+    cap = int(wl.budget_pages.max())
+    new_tokens = [S.append_tokens(wl, s) for s in range(K_steps + W)]
+    k_new = [up(t[0]) for t in new_tokens]
+    v_new = [up(t[1]) for t in new_tokens]
+    la = torch.from_numpy(wl.logits_a).to(dev)
+    lb = torch.from_numpy(wl.logits_b).to(dev)
+    R, V = wl.logits_a.shape
+    # preallocated outputs and workspaces: the timed loop allocates nothing
+    sel_idx = torch.zeros((spec.batch, spec.num_kv_heads, cap), dtype=torch.int32, device=dev)
+    sel_cnt = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
+    ws_sel = torch.zeros(spdec.select_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
+    ws_sp = torch.zeros(spdec.decode_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
+    ws_de = torch.zeros(spdec.decode_workspace_bytes(cache, 0), dtype=torch.uint8, device=dev)
+    ws_acc = torch.zeros(spdec.acceptance_workspace_bytes(R, V), dtype=torch.uint8, device=dev)
+    o_s = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+    l_s = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
+    o_d, l_d = torch.empty_like(o_s), torch.empty_like(l_s)
+    alpha = torch.empty(R, dtype=torch.float32, device=dev)
+    spdec.build_meta(cache)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    rows = ["append_kv", "select_pages", "sparse_decode", "dense_decode", "acceptance"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)] for _ in range(K_steps)]
+
+    def step(i, events=None):
+        rec = (lambda j: events[j].record()) if events is not None else (lambda j: None)
+        rec(0)
+        spdec.append_kv(cache, k_new[i], v_new[i])
+        rec(1)
+        spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
+        rec(2)
+        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
+        rec(3)
+        spdec.dense_decode(cache, q, out=o_d, lse=l_d, workspace=ws_de)
+        rec(4)
+        spdec.acceptance(la, lb, spec.temperature, alpha=alpha, workspace=ws_acc)
+        rec(5)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    lens_before = wl.lens.astype(np.int64) + W
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        step(W + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_row = {r: [] for r in rows}
+    for i in range(K_steps):
+        for j, r in enumerate(rows):
+            per_row[r].append(ev[i][j].elapsed_time(ev[i][j + 1]) * 1e-3)
+    step_s = [ev[i][0].elapsed_time(ev[i][len(rows)]) * 1e-3 for i in range(K_steps)]
+    gpu_total = ev[0][0].elapsed_time(ev[-1][len(rows)]) * 1e-3
+
+    # algorithmic bytes averaged over the timed steps (lengths grow by one per step)
+    byt = {r: 0.0 for r in rows}
+    for i in range(K_steps):
+        b_i = algorithmic_bytes(spec, lens_before + i + 1, wl.budget_pages, cap, R, V)
+        for r in rows:
+            byt[r] += b_i[r] / K_steps
+    mean_t = {r: float(np.mean(per_row[r])) for r in rows}
+    med_t = {r: float(np.median(per_row[r])) for r in rows}
+    rows_out = {r: {"us_mean": mean_t[r] * 1e6, "us_median": med_t[r] * 1e6, "bytes": int(byt[r]),
+                    "GBps": byt[r] / mean_t[r] / 1e9, "frac_hbm": byt[r] / mean_t[r] / 1e9 / HBM_PEAK_GBPS}
+                for r in rows}
+    ms_per_step = gpu_total / K_steps * 1e3
+    value = spec.batch / (gpu_total / K_steps)
+    sp_t = mean_t["select_pages"] + mean_t["sparse_decode"]
+    sp_b = byt["select_pages"] + byt["sparse_decode"]
+    dense_gbps = byt["dense_decode"] / mean_t["dense_decode"] / 1e9
+    sparse_gbps = sp_b / sp_t / 1e9
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded draws shaped like a Qwen3-8B decode layer; no weights or datasets)",
+        "config": {"workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads,
+                   "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
+                   "context": "uniform 8192..32768 per sequence", "budget": "1024->4096 tokens, linear in length",
+                   "acceptance_rows": R, "vocab": V, "accumulate": "fp32",
+                   "step": "append_kv + select_pages + sparse_decode + dense_decode + acceptance"},
+        "roofline": {"bound": "hbm", "achieved": dense_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dense_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "dense_decode (decode_split_kernel + decode_merge_kernel)",
+                     "bytes_per_launch": int(byt["dense_decode"])},
+        "sparse": {"tokens_per_s": spec.batch / sp_t, "us": sp_t * 1e6, "bytes": int(sp_b),
+                   "eff_GBps": sparse_gbps, "frac_hbm": sparse_gbps / HBM_PEAK_GBPS},
+        "rows": rows_out,
+        "step_us_median": float(np.median(step_s)) * 1e6,
+        "wall_s_timed": wall,
+        "setup_s": t_setup,
+    }
+    if args.copy_probe:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = int(x.numel() * 4)
+    if not args.no_cpu_baseline:
+        kn = np.stack([t[0] for t in new_tokens[:1]])[0]
+        vn = np.stack([t[1] for t in new_tokens[:1]])[0]
+        result["cpu_baseline"] = cpu_baseline(wl, (kn, vn), args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

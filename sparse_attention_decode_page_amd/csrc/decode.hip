@@ -21,6 +21,8 @@
 // result is deterministic.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -32,6 +34,7 @@ constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr int kChunk = 4;           // load instructions per wave per step
 constexpr int kMaxPagesPerSplit = 256;
+constexpr int kMaxSplits = 2048;     // per (sequence, KV head); bounded by the page-table length
 
 struct DecodeArgs {
   CacheView c;
@@ -229,10 +232,227 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
   }
 }
 
+// bf16 variant with q.K^T on the matrix cores (v_mfma_f32_16x16x32_bf16).
+//
+// A tile is 16 consecutive tokens of the split's page list. One MFMA contracts
+// 32 channels: A = the group's queries (the 16 rows hold query heads h % G, so
+// every row group of the output sees every head), B = 16 tokens x 32 channels
+// of K loaded straight from the page (lane l: token l%16, channels
+// 32j+8(l/16)..+8), D = 16 rows x 16 tokens in four fp32 registers per lane:
+// lane l holds token l%16 and rows 4(l/16)..+3, i.e. heads 0..3 (a second set
+// of MFMAs with rows shifted by 4 supplies heads 4..7 when G = 8). Softmax
+// state is kept per head and is uniform across the wave; the running maximum
+// is only raised when a tile exceeds it by more than 2^8, so the O(G*D)
+// rescale of the accumulator is rare. P.V stays on the VALU with V rows read
+// as 1 KiB contiguous wave loads; each lane fetches its token's probability
+// from the lane that owns that token (ds_bpermute).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr float kLazyRescale = 8.0f;  // log2 units
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int D, int G, bool SPARSE>
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_mfma_kernel(DecodeArgs a) {
+  constexpr int NJ = D / 32;             // MFMAs per head set per tile
+  constexpr int NSET = G > 4 ? 2 : 1;    // MFMA sets (G = 8 needs two)
+  constexpr int HPS = G > 4 ? 4 : G;     // heads delivered per set
+  constexpr int LPT = D / 8;             // lanes per V row
+  constexpr int TPI = kWave / LPT;       // V rows per load instruction
+  constexpr int NV = 16 / TPI;           // V load instructions per tile
+  const CacheView& c = a.c;
+  const int unit = blockIdx.y;
+  const int b = unit / c.hkv;
+  const int g = unit % c.hkv;
+  const int L = max(c.seq_lens[b], 0);
+  const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  const int n = list_length<SPARSE>(a, unit, P);
+  const int e0 = blockIdx.x * a.pages_per_split;
+  if (e0 >= n) return;
+  const int ne = min(a.pages_per_split, n - e0);
+
+  __shared__ int s_phys[kMaxPagesPerSplit];
+  __shared__ int s_valid[kMaxPagesPerSplit];
+  for (int i = threadIdx.x; i < ne; i += kDecodeThreads) {
+    int logical = SPARSE ? a.sel_idx[(int64_t)unit * a.list_cap + e0 + i] : e0 + i;
+    int phys = -1;
+    if (logical >= 0 && logical < P) phys = c.page_table[(int64_t)b * c.max_pages + logical];
+    const bool ok = phys >= 0 && phys < c.num_phys;
+    s_phys[i] = ok ? phys : 0;
+    s_valid[i] = ok ? min(c.page_size, L - logical * c.page_size) : 0;
+  }
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int r16 = lane % 16;   // token of the tile this lane scores
+  const int q4 = lane / 16;    // row group
+  const int vsub = lane % LPT; // V channel chunk
+  const int vtok = lane / LPT; // V row within a load instruction
+
+  // A operands: row r16 holds query head (r16 + 4*set) % G.
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
+  u32x4 qa[NSET][NJ];
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const int h = (r16 + 4 * st) % G;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) qa[st][j] = load16(qp + ((int64_t)b * c.hq + g * G + h) * D + 32 * j + 8 * q4);
+  }
+  // Which head each output register of each set carries for this lane.
+  float m[G], lsum[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegBig;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  __syncthreads();
+
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(c.k_pool);
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(c.v_pool);
+  const int ntok = ne << c.ps_log2;
+  const int ntiles = (ntok + 15) >> 4;
+
+  // Address of token tau of the split's stream (row start), and whether it is in the cache.
+  auto token_row = [&](int tau, bool& ok) -> int64_t {
+    const int e = min(tau >> c.ps_log2, ne - 1);
+    const int slot = tau & (c.page_size - 1);
+    ok = tau < ntok && slot < s_valid[e];
+    return ((((int64_t)s_phys[e] * c.hkv + g) << c.ps_log2) + (ok ? slot : 0)) * D;
+  };
+  auto load_tile = [&](int tile, u32x4* kr, u32x4* vr, bool& kok, bool* vok) {
+    const int64_t krow = token_row(tile * 16 + r16, kok);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) kr[j] = load16(kp + krow + 32 * j + 8 * q4);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t vrow = token_row(tile * 16 + i * TPI + vtok, vok[i]);
+      vr[i] = load16(vp + vrow + 8 * vsub);
+    }
+  };
+
+  u32x4 kA[NJ], vA[NV], kB[NJ], vB[NV];
+  bool kokA, vokA[NV], kokB, vokB[NV];
+  int tile = wave;
+  if (tile < ntiles) load_tile(tile, kA, vA, kokA, vokA);
+  for (; tile < ntiles; tile += kDecodeWaves) {
+    const int next = tile + kDecodeWaves;
+    if (next < ntiles) load_tile(next, kB, vB, kokB, vokB);
+
+    // scores of the 16 tokens for every head (log2 units)
+    float sc[G];
+#pragma unroll
+    for (int st = 0; st < NSET; ++st) {
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[st][j]), as_bf16x8(kA[j]), d, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < HPS; ++r) {
+        // set st, register r carries head (4*q4 + r + 4*st) % G
+        if constexpr (G <= 4) {
+          sc[r] = d[r];
+        } else {
+          const int h = (4 * q4 + r + 4 * st) % G;   // 0..3 or 4..7 depending on the row group
+          if (h < 4) sc[r] = d[r]; else sc[4 + r] = d[r];
+        }
+      }
+    }
+    float p[G], mnew[G];
+    bool grow = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      p[h] = kokA ? sc[h] * a.qk_scale : -INFINITY;
+      const float tmax = group_max<16>(p[h]);
+      const bool up = tmax > m[h] + kLazyRescale;
+      mnew[h] = up ? tmax : m[h];
+      grow |= up;
+    }
+    if (grow) {  // uniform across the wave: every lane sees the same tile maxima
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float alpha = exp2f(m[h] - mnew[h]);
+        lsum[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+        m[h] = mnew[h];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) p[h] = exp2f(p[h] - m[h]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) lsum[h] += p[h];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float vf[8];
+      unpack<BF16>(vA[i], vf);
+      if (!vokA[i]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = 0.f;  // never multiply unread slots
+      }
+      const int src = (i * TPI + vtok) * 4;       // byte address of the lane owning this token
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ph = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(p[h])));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) kA[j] = kB[j];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) { vA[i] = vB[i]; vokA[i] = vokB[i]; }
+    kokA = kokB;
+  }
+
+  // l: every row group holds the same 16 tokens, sum one row's lanes.
+#pragma unroll
+  for (int h = 0; h < G; ++h) lsum[h] = group_sum<16>(lsum[h]);
+  // acc: lanes LPT apart hold the same channels for different tokens.
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+
+  __shared__ float s_acc[kDecodeWaves][G][D];
+  __shared__ float s_m[kDecodeWaves][G], s_l[kDecodeWaves][G];
+  if (vtok == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * vsub + e] = acc[h][e];
+      if (vsub == 0) { s_m[wave][h] = m[h]; s_l[wave][h] = lsum[h]; }
+    }
+  }
+  __syncthreads();
+  const int64_t row0 = ((int64_t)b * c.hq + g * G) * a.nsplit + blockIdx.x;
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+    const int h = idx / D, d = idx % D;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) o += exp2f(s_m[w][h] - M) * s_acc[w][h][d];
+    a.part_acc[(row0 + (int64_t)h * a.nsplit) * D + d] = o;
+    if (d == 0) {
+      float Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) Ls += exp2f(s_m[w][h] - M) * s_l[w][h];
+      a.part_ml[(row0 + (int64_t)h * a.nsplit) * 2 + 0] = M;
+      a.part_ml[(row0 + (int64_t)h * a.nsplit) * 2 + 1] = Ls;
+    }
+  }
+}
+
 // out_h = sum_j 2^{m_j-M} acc_j / sum_j 2^{m_j-M} l_j, lse_h = ln2 (M + log2 sum_j 2^{m_j-M} l_j),
 // splits taken in index order.
 template <int D, bool SPARSE>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int DPL = D / kWave;  // channels per lane
+  __shared__ float s_w[kMaxSplits];
   const CacheView& c = a.c;
   const int bh = blockIdx.x;
   const int b = bh / c.hq;
@@ -242,28 +462,46 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
   const int n = list_length<SPARSE>(a, unit, P);
   const int ns = (n + a.pages_per_split - 1) / a.pages_per_split;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   const float* ml = a.part_ml + (int64_t)bh * a.nsplit * 2;
   const float* pa = a.part_acc + (int64_t)bh * a.nsplit * D;
   float M = kNegBig;
-  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[2 * j]);
-  float Ls = 0.f, o = 0.f;
-  for (int j = 0; j < ns; ++j) {
+  for (int j = lane; j < ns; j += kWave) M = fmaxf(M, ml[2 * j]);
+  M = group_max<kWave>(M);
+  float Ls = 0.f;
+  for (int j = lane; j < ns; j += kWave) {
     const float w = exp2f(ml[2 * j] - M);
+    s_w[j] = w;
     Ls += w * ml[2 * j + 1];
-    o += w * pa[(int64_t)j * D + d];
   }
-  a.out[(int64_t)bh * D + d] = Ls > 0.f ? o / Ls : 0.f;
-  if (a.lse != nullptr && d == 0) a.lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  Ls = group_sum<kWave>(Ls);
+  __syncthreads();
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < ns; ++j) {
+    const float w = s_w[j];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = fmaf(w, pa[(int64_t)j * D + lane * DPL + e], o[e]);
+  }
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) a.out[(int64_t)bh * D + lane * DPL + e] = o[e] * inv;
+  if (a.lse != nullptr && lane == 0) a.lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D, int G, bool SPARSE>
 hipError_t decode_impl(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.nsplit, a.c.batch * a.c.hkv);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G, SPARSE>), grid, dim3(kDecodeThreads), 0, s, a);
+  if constexpr (std::is_same<T, BF16>::value) {
+    hipLaunchKernelGGL((decode_split_mfma_kernel<D, G, SPARSE>), grid, dim3(kDecodeThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, SPARSE>), grid, dim3(kDecodeThreads), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D, SPARSE>), dim3(a.c.batch * a.c.hq), dim3(D), 0, s, a);
+  hipLaunchKernelGGL((decode_merge_kernel<D, SPARSE>), dim3(a.c.batch * a.c.hq), dim3(kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -298,6 +536,7 @@ DecodePlan decode_plan(const CacheView& c, int max_budget_pages) {
   int pps = max(1, kTargetTokens / c.page_size);
   const int64_t units = (int64_t)c.batch * c.hkv;
   while (pps > 1 && units * ((p.list_pages + pps - 1) / pps) < 2048) pps >>= 1;
+  pps = max(pps, (p.list_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = min(pps, kMaxPagesPerSplit);
   p.nsplit = (p.list_pages + p.pages_per_split - 1) / p.pages_per_split;
   return p;
