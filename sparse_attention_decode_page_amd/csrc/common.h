@@ -109,6 +109,46 @@ constexpr float kNegBig = -1.0e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// In-place exclusive prefix sum of s[0..n) by the whole workgroup; s[n] gets
+// the total. `tmp` needs one int per wave. Ends with a barrier.
+__device__ __forceinline__ void block_exclusive_scan(int* s, int n, int* tmp) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid % kWave, wave = tid / kWave, nw = nt / kWave;
+  const int per = (n + nt - 1) / nt;
+  const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+  int sum = 0;
+  for (int i = i0; i < i1; ++i) sum += s[i];
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) tmp[wave] = incl;
+  __syncthreads();
+  int base = incl - sum;
+  for (int w = 0; w < wave; ++w) base += tmp[w];
+  int total = 0;
+  for (int w = 0; w < nw; ++w) total += tmp[w];
+  for (int i = i0; i < i1; ++i) {
+    const int v = s[i];
+    s[i] = base;
+    base += v;
+  }
+  if (tid == 0) s[n] = total;
+  __syncthreads();
+}
+
+// Largest u in [0, n) with s[u] <= x for a non-decreasing s[0..n] (s[0] <= x).
+__device__ __forceinline__ int find_unit(const int* s, int n, int x) {
+  int lo = 0, hi = n;  // invariant: s[lo] <= x < s[hi] (s[n] > x)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 // Order-preserving map of an fp32 score to uint32 (-0 and +0 share one key).
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);

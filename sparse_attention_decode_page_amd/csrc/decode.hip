@@ -21,6 +21,7 @@
 // result is deterministic.
 #include <limits.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -250,10 +251,44 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
+#ifndef SPDEC_STREAM_ATTR
+#define SPDEC_STREAM_ATTR
+#endif
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+struct StreamArgs {
+  CacheView c;
+  const void* q;
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  int list_cap;      // row stride of sel_idx
+  int jmax;          // partial slots per unit
+  int rmin;          // minimum entries per wave range (bounds the chunks per unit by jmax)
+  float qk_scale;    // softmax scale * log2(e)
+  float* part_acc;   // [units][jmax][G][D]
+  float* part_ml;    // [units][jmax][G][2]
+  int* count;        // [units] chunks written for the unit
+  float* out;
+  float* lse;
+};
+
+template <bool SPARSE>
+__device__ __forceinline__ int unit_entries(const StreamArgs& a, int u) {
+  const CacheView& c = a.c;
+  if constexpr (SPARSE) return min(max(a.sel_cnt[u], 0), a.list_cap);
+  const int L = max(c.seq_lens[u / c.hkv], 0);
+  return min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+}
+
+// Persistent split-KV decode. The (unit, page-list entry) pairs of all
+// sequences and KV heads are laid end to end and every wave owns one
+// contiguous range of R entries: it streams its range once, emitting one
+// partial (m, l, acc) per unit segment it covers, so every wave works until
+// the end and no workgroup is launched for an empty split. The wave that
+// finishes a unit records how many chunks the unit has for the merge.
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_stream_kernel(StreamArgs a) {
   constexpr int NJ = D / 32;             // MFMAs per head set per tile
   constexpr int NSET = G > 4 ? 2 : 1;    // MFMA sets (G = 8 needs two)
   constexpr int HPS = G > 4 ? 4 : G;     // heads delivered per set
@@ -261,190 +296,237 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_mfma_kernel(Decod
   constexpr int TPI = kWave / LPT;       // V rows per load instruction
   constexpr int NV = 16 / TPI;           // V load instructions per tile
   const CacheView& c = a.c;
-  const int unit = blockIdx.y;
-  const int b = unit / c.hkv;
-  const int g = unit % c.hkv;
-  const int L = max(c.seq_lens[b], 0);
-  const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
-  const int n = list_length<SPARSE>(a, unit, P);
-  const int e0 = blockIdx.x * a.pages_per_split;
-  if (e0 >= n) return;
-  const int ne = min(a.pages_per_split, n - e0);
-
-  __shared__ int s_phys[kMaxPagesPerSplit];
-  __shared__ int s_valid[kMaxPagesPerSplit];
-  for (int i = threadIdx.x; i < ne; i += kDecodeThreads) {
-    int logical = SPARSE ? a.sel_idx[(int64_t)unit * a.list_cap + e0 + i] : e0 + i;
-    int phys = -1;
-    if (logical >= 0 && logical < P) phys = c.page_table[(int64_t)b * c.max_pages + logical];
-    const bool ok = phys >= 0 && phys < c.num_phys;
-    s_phys[i] = ok ? phys : 0;
-    s_valid[i] = ok ? min(c.page_size, L - logical * c.page_size) : 0;
-  }
-
+  extern __shared__ int s_pre[];         // units + 1
+  __shared__ int s_tmp[kDecodeWaves];
+  const int units = c.batch * c.hkv;
+  for (int u = threadIdx.x; u < units; u += kDecodeThreads) s_pre[u] = unit_entries<SPARSE>(a, u);
+  __syncthreads();
+  block_exclusive_scan(s_pre, units, s_tmp);
+  const int total = s_pre[units];
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int64_t nw = (int64_t)gridDim.x * kDecodeWaves;
+  const int64_t w = (int64_t)blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
+  const int64_t R = max<int64_t>((total + nw - 1) / nw, a.rmin);
+  if (w * R >= total) return;
+  int pos = (int)(w * R);
+  const int end = (int)min<int64_t>(pos + R, total);
+  int u = find_unit(s_pre, units, pos);
+
   const int r16 = lane % 16;   // token of the tile this lane scores
   const int q4 = lane / 16;    // row group
   const int vsub = lane % LPT; // V channel chunk
   const int vtok = lane / LPT; // V row within a load instruction
-
-  // A operands: row r16 holds query head (r16 + 4*set) % G.
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
-  u32x4 qa[NSET][NJ];
-#pragma unroll
-  for (int st = 0; st < NSET; ++st) {
-    const int h = (r16 + 4 * st) % G;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) qa[st][j] = load16(qp + ((int64_t)b * c.hq + g * G + h) * D + 32 * j + 8 * q4);
-  }
-  // Which head each output register of each set carries for this lane.
-  float m[G], lsum[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    lsum[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
-  __syncthreads();
-
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(c.k_pool);
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(c.v_pool);
-  const int ntok = ne << c.ps_log2;
-  const int ntiles = (ntok + 15) >> 4;
 
-  // Address of token tau of the split's stream (row start), and whether it is in the cache.
-  auto token_row = [&](int tau, bool& ok) -> int64_t {
-    const int e = min(tau >> c.ps_log2, ne - 1);
-    const int slot = tau & (c.page_size - 1);
-    ok = tau < ntok && slot < s_valid[e];
-    return ((((int64_t)s_phys[e] * c.hkv + g) << c.ps_log2) + (ok ? slot : 0)) * D;
-  };
-  auto load_tile = [&](int tile, u32x4* kr, u32x4* vr, bool& kok, bool* vok) {
-    const int64_t krow = token_row(tile * 16 + r16, kok);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) kr[j] = load16(kp + krow + 32 * j + 8 * q4);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int64_t vrow = token_row(tile * 16 + i * TPI + vtok, vok[i]);
-      vr[i] = load16(vp + vrow + 8 * vsub);
-    }
-  };
+  while (pos < end) {
+    const int b = u / c.hkv, g = u % c.hkv;
+    const int ubase = s_pre[u];
+    const int seg_end = min(end, s_pre[u + 1]);
+    const int j = (int)(w - ubase / R);  // this wave's chunk of the unit
+    const int L = max(c.seq_lens[b], 0);
+    const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
 
-  u32x4 kA[NJ], vA[NV], kB[NJ], vB[NV];
-  bool kokA, vokA[NV], kokB, vokB[NV];
-  int tile = wave;
-  if (tile < ntiles) load_tile(tile, kA, vA, kokA, vokA);
-  for (; tile < ntiles; tile += kDecodeWaves) {
-    const int next = tile + kDecodeWaves;
-    if (next < ntiles) load_tile(next, kB, vB, kokB, vokB);
-
-    // scores of the 16 tokens for every head (log2 units)
-    float sc[G];
+    // A operands: row r16 holds query head (r16 + 4*set) % G.
+    u32x4 qa[NSET][NJ];
 #pragma unroll
     for (int st = 0; st < NSET; ++st) {
-      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+      const int h = (r16 + 4 * st) % G;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[st][j]), as_bf16x8(kA[j]), d, 0, 0, 0);
+      for (int jj = 0; jj < NJ; ++jj)
+        qa[st][jj] = load16(qp + ((int64_t)b * c.hq + g * G + h) * D + 32 * jj + 8 * q4);
+    }
+    float m[G], lsum[G], acc[G][8];
 #pragma unroll
-      for (int r = 0; r < HPS; ++r) {
-        // set st, register r carries head (4*q4 + r + 4*st) % G
-        if constexpr (G <= 4) {
-          sc[r] = d[r];
-        } else {
-          const int h = (4 * q4 + r + 4 * st) % G;   // 0..3 or 4..7 depending on the row group
-          if (h < 4) sc[r] = d[r]; else sc[4 + r] = d[r];
+    for (int h = 0; h < G; ++h) {
+      m[h] = kNegBig;
+      lsum[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+
+    for (int wb = pos - ubase; wb < seg_end - ubase; wb += kWave) {
+      // Window of up to 64 entries: lane i holds entry wb+i's physical page and valid tokens.
+      const int nwin = min(kWave, seg_end - ubase - wb);
+      int phys_w = 0, valid_w = 0;
+      if (lane < nwin) {
+        const int logical = SPARSE ? a.sel_idx[(int64_t)u * a.list_cap + wb + lane] : wb + lane;
+        if (logical >= 0 && logical < P) {
+          const int ph = c.page_table[(int64_t)b * c.max_pages + logical];
+          if (ph >= 0 && ph < c.num_phys) {
+            phys_w = ph;
+            valid_w = min(c.page_size, L - logical * c.page_size);
+          }
         }
       }
-    }
-    float p[G], mnew[G];
-    bool grow = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      p[h] = kokA ? sc[h] * a.qk_scale : -INFINITY;
-      const float tmax = group_max<16>(p[h]);
-      const bool up = tmax > m[h] + kLazyRescale;
-      mnew[h] = up ? tmax : m[h];
-      grow |= up;
-    }
-    if (grow) {  // uniform across the wave: every lane sees the same tile maxima
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float alpha = exp2f(m[h] - mnew[h]);
-        lsum[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-        m[h] = mnew[h];
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) p[h] = exp2f(p[h] - m[h]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) lsum[h] += p[h];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float vf[8];
-      unpack<BF16>(vA[i], vf);
-      if (!vokA[i]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = 0.f;  // never multiply unread slots
-      }
-      const int src = (i * TPI + vtok) * 4;       // byte address of the lane owning this token
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ph = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(p[h])));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) kA[j] = kB[j];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) { vA[i] = vB[i]; vokA[i] = vokB[i]; }
-    kokA = kokB;
-  }
+      const int ntok = nwin << c.ps_log2;
+      const int ntiles = (ntok + 15) >> 4;
 
-  // l: every row group holds the same 16 tokens, sum one row's lanes.
+      // Row offset of stream token tau, and whether that token is in the cache.
+      auto token_row = [&](int tau, int e, bool& ok) -> int64_t {
+        const int ph = __shfl(phys_w, e);
+        const int va = __shfl(valid_w, e);
+        const int slot = tau & (c.page_size - 1);
+        ok = tau < ntok && slot < va;
+        return ((((int64_t)ph * c.hkv + g) << c.ps_log2) + (ok ? slot : 0)) * D;
+      };
+      auto load_tile = [&](int t, u32x4* kr, u32x4* vr, bool& kok, bool* vok) {
+        const int tk = t * 16 + r16;
+        const int64_t krow = token_row(tk, min(tk >> c.ps_log2, kWave - 1), kok);
 #pragma unroll
-  for (int h = 0; h < G; ++h) lsum[h] = group_sum<16>(lsum[h]);
-  // acc: lanes LPT apart hold the same channels for different tokens.
+        for (int jj = 0; jj < NJ; ++jj) kr[jj] = load16(kp + krow + 32 * jj + 8 * q4);
 #pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+        for (int i = 0; i < NV; ++i) {
+          const int tv = t * 16 + i * TPI + vtok;
+          const int64_t vrow = token_row(tv, min(tv >> c.ps_log2, kWave - 1), vok[i]);
+          vr[i] = load16(vp + vrow + 8 * vsub);
+        }
+      };
 
-  __shared__ float s_acc[kDecodeWaves][G][D];
-  __shared__ float s_m[kDecodeWaves][G], s_l[kDecodeWaves][G];
-  if (vtok == 0) {
+      u32x4 kA[NJ], vA[NV], kB[NJ], vB[NV];
+      bool kokA, vokA[NV], kokB, vokB[NV];
+      load_tile(0, kA, vA, kokA, vokA);
+      for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_tile(t + 1, kB, vB, kokB, vokB);
+        float sc[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+        for (int st = 0; st < NSET; ++st) {
+          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * vsub + e] = acc[h][e];
-      if (vsub == 0) { s_m[wave][h] = m[h]; s_l[wave][h] = lsum[h]; }
+          for (int jj = 0; jj < NJ; ++jj)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[st][jj]), as_bf16x8(kA[jj]), d, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < HPS; ++r) {
+            if constexpr (G <= 4) {
+              sc[r] = d[r];
+            } else {
+              const int h = (4 * q4 + r + 4 * st) % G;
+              if (h < 4) sc[r] = d[r]; else sc[4 + r] = d[r];
+            }
+          }
+        }
+        float p[G], mnew[G];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          p[h] = kokA ? sc[h] * a.qk_scale : -INFINITY;
+          const float tmax = group_max<16>(p[h]);
+          const bool up = tmax > m[h] + kLazyRescale;
+          mnew[h] = up ? tmax : m[h];
+          grow |= up;
+        }
+        if (grow) {  // uniform across the wave: every lane sees the same tile maxima
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float alpha = exp2f(m[h] - mnew[h]);
+            lsum[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+            m[h] = mnew[h];
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          p[h] = exp2f(p[h] - m[h]);
+          lsum[h] += p[h];
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          float vf[8];
+          unpack<BF16>(vA[i], vf);
+          if (!vokA[i]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vf[e] = 0.f;  // never multiply unread slots
+          }
+          const int src = (i * TPI + vtok) * 4;       // byte address of the lane owning this token
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float ph = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(p[h])));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) kA[jj] = kB[jj];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) { vA[i] = vB[i]; vokA[i] = vokB[i]; }
+        kokA = kokB;
+      }
     }
+
+    // Close the segment: l over the 16 token lanes, acc over the V row groups.
+#pragma unroll
+    for (int h = 0; h < G; ++h) lsum[h] = group_sum<16>(lsum[h]);
+#pragma unroll
+    for (int off = LPT; off < kWave; off <<= 1)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+    if (j < a.jmax) {
+      const int64_t slot0 = ((int64_t)u * a.jmax + j) * G;
+      if (vtok == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float* dst = a.part_acc + (slot0 + h) * D + 8 * vsub;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dst[e] = acc[h][e];
+        }
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          a.part_ml[(slot0 + h) * 2 + 0] = m[h];
+          a.part_ml[(slot0 + h) * 2 + 1] = lsum[h];
+        }
+        if (seg_end == s_pre[u + 1]) a.count[u] = j + 1;
+      }
+    }
+    pos = seg_end;
+    ++u;
   }
+}
+
+// Merge of the stream partials of one (sequence, query head), chunks in order.
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(kWave) void stream_merge_kernel(StreamArgs a) {
+  constexpr int DPL = D / kWave;
+  __shared__ float s_w[kMaxSplits];
+  const CacheView& c = a.c;
+  const int bh = blockIdx.x;
+  const int b = bh / c.hq, h = bh % c.hq;
+  const int u = b * c.hkv + h / c.group;
+  const int hh = h % c.group;
+  const int lane = threadIdx.x;
+  const int n = unit_entries<SPARSE>(a, u);
+  const int J = n > 0 ? min(max(a.count[u], 0), a.jmax) : 0;
+  float M = kNegBig;
+  for (int jj = lane; jj < J; jj += kWave) M = fmaxf(M, a.part_ml[(((int64_t)u * a.jmax + jj) * c.group + hh) * 2]);
+  M = group_max<kWave>(M);
+  float Ls = 0.f;
+  for (int jj = lane; jj < J; jj += kWave) {
+    const float* ml = a.part_ml + (((int64_t)u * a.jmax + jj) * c.group + hh) * 2;
+    const float wgt = exp2f(ml[0] - M);
+    s_w[jj] = wgt;
+    Ls += wgt * ml[1];
+  }
+  Ls = group_sum<kWave>(Ls);
   __syncthreads();
-  const int64_t row0 = ((int64_t)b * c.hq + g * G) * a.nsplit + blockIdx.x;
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = s_m[0][h];
+  float o[DPL];
 #pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float o = 0.f;
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+#pragma unroll 4
+  for (int jj = 0; jj < J; ++jj) {
+    const float wgt = s_w[jj];
+    const float* src = a.part_acc + (((int64_t)u * a.jmax + jj) * c.group + hh) * D + lane * DPL;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) o += exp2f(s_m[w][h] - M) * s_acc[w][h][d];
-    a.part_acc[(row0 + (int64_t)h * a.nsplit) * D + d] = o;
-    if (d == 0) {
-      float Ls = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) Ls += exp2f(s_m[w][h] - M) * s_l[w][h];
-      a.part_ml[(row0 + (int64_t)h * a.nsplit) * 2 + 0] = M;
-      a.part_ml[(row0 + (int64_t)h * a.nsplit) * 2 + 1] = Ls;
-    }
+    for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, src[e], o[e]);
   }
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) a.out[(int64_t)bh * D + lane * DPL + e] = o[e] * inv;
+  if (a.lse != nullptr && lane == 0) a.lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 // out_h = sum_j 2^{m_j-M} acc_j / sum_j 2^{m_j-M} l_j, lse_h = ln2 (M + log2 sum_j 2^{m_j-M} l_j),
@@ -494,11 +576,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int D, int G, bool SPARSE>
 hipError_t decode_impl(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.nsplit, a.c.batch * a.c.hkv);
-  if constexpr (std::is_same<T, BF16>::value) {
-    hipLaunchKernelGGL((decode_split_mfma_kernel<D, G, SPARSE>), grid, dim3(kDecodeThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((decode_split_kernel<T, D, G, SPARSE>), grid, dim3(kDecodeThreads), 0, s, a);
-  }
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, SPARSE>), grid, dim3(kDecodeThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, SPARSE>), dim3(a.c.batch * a.c.hq), dim3(kWave), 0, s, a);
@@ -522,19 +600,58 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
   return a.c.head_dim == 64 ? decode_g<F32, 64, SPARSE>(a, s) : decode_g<F32, 128, SPARSE>(a, s);
 }
 
+template <int D, int G, bool SPARSE>
+hipError_t stream_impl(const StreamArgs& a, hipStream_t s) {
+  const int units = a.c.batch * a.c.hkv;
+  const size_t lds = (size_t)(units + 1) * sizeof(int);
+  int grid = 0;
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&decode_stream_kernel<D, G, SPARSE>), kDecodeThreads,
+                                 lds, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_stream_kernel<D, G, SPARSE>), dim3(grid), dim3(kDecodeThreads), lds, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((stream_merge_kernel<D, SPARSE>), dim3(a.c.batch * a.c.hq), dim3(kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, bool SPARSE>
+hipError_t stream_g(const StreamArgs& a, hipStream_t s) {
+  switch (a.c.group) {
+    case 1: return stream_impl<D, 1, SPARSE>(a, s);
+    case 2: return stream_impl<D, 2, SPARSE>(a, s);
+    case 4: return stream_impl<D, 4, SPARSE>(a, s);
+    default: return stream_impl<D, 8, SPARSE>(a, s);
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Waves the stream plan is sized for (a few per SIMD on a 256-CU part); more
+// resident waves only lengthen each range.
+constexpr int kStreamWaveTarget = 8192;
 
 }  // namespace
 
 DecodePlan decode_plan(const CacheView& c, int max_budget_pages) {
   DecodePlan p;
   p.list_pages = max_budget_pages > 0 ? max_budget_pages : c.max_pages;
-  // About 512 tokens per split, fewer when the grid would otherwise leave the
-  // 256 compute units idle. The plan depends only on the list capacity, so a
-  // sparse call whose capacity is every page splits exactly like the dense one.
-  constexpr int kTargetTokens = 512;
-  int pps = max(1, kTargetTokens / c.page_size);
   const int64_t units = (int64_t)c.batch * c.hkv;
+  p.stream = c.dtype == SPDEC_BF16 && units <= kMaxStreamUnits;
+  // Stream plan: at most jmax partials per unit, so every wave range holds at
+  // least rmin = ceil(cap / (jmax - 1)) entries.
+  p.jmax = (int)std::min<int64_t>(std::max<int64_t>((kStreamWaveTarget + units - 1) / units + 2, 3), 1024);
+  p.rmin = (p.list_pages + p.jmax - 2) / (p.jmax - 1);
+  // Split plan (fp32 caches and very large batches): about 512 tokens per
+  // split, fewer when the grid would leave compute units idle. The plan
+  // depends only on the list capacity, so a sparse call whose capacity is
+  // every page splits exactly like the dense one.
+#ifdef SPDEC_SPLIT_TOKENS
+  constexpr int kTargetTokens = SPDEC_SPLIT_TOKENS;
+#else
+  constexpr int kTargetTokens = 512;
+#endif
+  int pps = max(1, kTargetTokens / c.page_size);
   while (pps > 1 && units * ((p.list_pages + pps - 1) / pps) < 2048) pps >>= 1;
   pps = max(pps, (p.list_pages + kMaxSplits - 1) / kMaxSplits);
   p.pages_per_split = min(pps, kMaxPagesPerSplit);
@@ -543,12 +660,39 @@ DecodePlan decode_plan(const CacheView& c, int max_budget_pages) {
 }
 
 size_t decode_workspace_bytes(const CacheView& c, const DecodePlan& p) {
+  if (p.stream) {
+    const size_t slots = (size_t)c.batch * c.hkv * p.jmax * c.group;
+    return align256(slots * c.head_dim * sizeof(float)) + align256(slots * 2 * sizeof(float)) +
+           align256((size_t)c.batch * c.hkv * sizeof(int));
+  }
   const size_t rows = (size_t)c.batch * c.hq * p.nsplit;
   return align256(rows * c.head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
 hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float scale, float* out, float* lse, void* ws, hipStream_t s) {
+  const bool sparse = sel_idx != nullptr;
+  char* base = reinterpret_cast<char*>(ws);
+  if (p.stream) {
+    StreamArgs a;
+    a.c = c;
+    a.q = q;
+    a.sel_idx = sel_idx;
+    a.sel_cnt = sel_cnt;
+    a.list_cap = p.list_pages;
+    a.jmax = p.jmax;
+    a.rmin = p.rmin;
+    a.qk_scale = scale * kLog2e;
+    const size_t slots = (size_t)c.batch * c.hkv * p.jmax * c.group;
+    a.part_acc = reinterpret_cast<float*>(base);
+    a.part_ml = reinterpret_cast<float*>(base + align256(slots * c.head_dim * sizeof(float)));
+    a.count = reinterpret_cast<int*>(base + align256(slots * c.head_dim * sizeof(float)) +
+                                     align256(slots * 2 * sizeof(float)));
+    a.out = out;
+    a.lse = lse;
+    if (c.head_dim == 64) return sparse ? stream_g<64, true>(a, s) : stream_g<64, false>(a, s);
+    return sparse ? stream_g<128, true>(a, s) : stream_g<128, false>(a, s);
+  }
   DecodeArgs a;
   a.c = c;
   a.q = q;
@@ -559,11 +703,11 @@ hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q,
   a.nsplit = p.nsplit;
   a.qk_scale = scale * kLog2e;
   const size_t rows = (size_t)c.batch * c.hq * p.nsplit;
-  a.part_acc = reinterpret_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(rows * c.head_dim * sizeof(float)));
+  a.part_acc = reinterpret_cast<float*>(base);
+  a.part_ml = reinterpret_cast<float*>(base + align256(rows * c.head_dim * sizeof(float)));
   a.out = out;
   a.lse = lse;
-  return sel_idx != nullptr ? decode_dispatch<true>(a, s) : decode_dispatch<false>(a, s);
+  return sparse ? decode_dispatch<true>(a, s) : decode_dispatch<false>(a, s);
 }
 
 }  // namespace spdec

@@ -23,12 +23,22 @@ struct CacheView {
 
 // Split-KV plan shared by the workspace query and the decode launch.
 struct DecodePlan {
+  bool stream;       // persistent stream-K kernel (bf16) instead of fixed splits
+  int jmax, rmin;    // stream plan: partial slots per unit, minimum entries per wave
   int pages_per_split;
   int nsplit;        // splits per (sequence, KV head) at the list capacity
   int list_pages;    // capacity of the page list (max_budget_pages or max_pages)
 };
 
 DecodePlan decode_plan(const CacheView& c, int max_budget_pages);
+
+// Units (sequence x KV head) up to which the persistent kernels keep the
+// per-unit prefix in LDS.
+constexpr int kMaxStreamUnits = 8192;
+
+// Workgroups that fill the current device once for `kernel` (resident blocks
+// per compute unit x compute units).
+hipError_t persistent_grid(const void* kernel, int block, size_t dyn_lds, int* grid);
 size_t decode_workspace_bytes(const CacheView& c, const DecodePlan& p);
 size_t select_workspace_bytes(const CacheView& c);
 size_t acceptance_workspace_bytes(int rows, int vocab);

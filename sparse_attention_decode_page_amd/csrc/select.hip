@@ -26,7 +26,13 @@ namespace spdec {
 
 namespace {
 
+#ifdef SPDEC_SCORE_PAGES
+constexpr int kScorePages = SPDEC_SCORE_PAGES;
+#else
 constexpr int kScorePages = 256;   // pages per scoring workgroup
+#endif
+// Each of the 4 waves scores kScorePages/4 pages, PPI (>= 1) per load.
+static_assert(kScorePages % 64 == 0 && kScorePages >= 64, "pages per scoring workgroup");
 constexpr int kSelectThreads = 256;
 constexpr size_t kSelectLdsKeyBytes = 60 * 1024;
 
@@ -47,11 +53,11 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
   if (p_begin >= P) return;
 
   __shared__ int s_phys[kScorePages];
-  {
-    const int p = p_begin + threadIdx.x;
+  for (int i = threadIdx.x; i < kScorePages; i += blockDim.x) {
+    const int p = p_begin + i;
     int phys = -1;
     if (p < P) phys = c.page_table[(int64_t)b * c.max_pages + p];
-    s_phys[threadIdx.x] = (phys >= 0 && phys < c.num_phys) ? phys : -1;
+    s_phys[i] = (phys >= 0 && phys < c.num_phys) ? phys : -1;
   }
 
   const int lane = threadIdx.x % kWave;
@@ -95,6 +101,93 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
     s = group_sum<LPT>(s);
     const int p = p_begin + pl;
     if (sub == 0 && phys >= 0 && p < P) srow[p] = (float)s;
+  }
+}
+
+// Persistent form of the scoring pass: the (sequence, KV head, page) triples
+// are laid end to end and every wave scores one contiguous range of R pages,
+// so all waves stream until the end instead of finishing in ragged rounds.
+// A workgroup first builds the prefix of per-unit page counts in LDS; a wave
+// binary-searches its first unit and walks units until its range ends.
+constexpr int kStreamMinPages = 16;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const void* __restrict__ qv,
+                                                           float* __restrict__ scores) {
+  constexpr int VEC = T::VEC;
+  constexpr int LPT = D / VEC;
+  constexpr int PPI = kWave / LPT;
+  using S = typename T::storage;
+  extern __shared__ int s_pre[];  // units + 1
+  __shared__ int s_tmp[256 / kWave];
+  const int units = c.batch * c.hkv;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int L = max(c.seq_lens[u / c.hkv], 0);
+    s_pre[u] = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  }
+  __syncthreads();
+  block_exclusive_scan(s_pre, units, s_tmp);
+  const int total = s_pre[units];
+  const int lane = threadIdx.x % kWave;
+  const int wpb = blockDim.x / kWave;
+  const int64_t nw = (int64_t)gridDim.x * wpb;
+  const int64_t w = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+  const int64_t R = max<int64_t>((total + nw - 1) / nw, kStreamMinPages);
+  if (w * R >= total) return;
+  int pos = (int)(w * R);
+  const int end = (int)min<int64_t>(pos + R, total);
+  int u = find_unit(s_pre, units, pos);
+  const int sub = lane % LPT;
+  const int d0 = sub * VEC;
+  const S* q = reinterpret_cast<const S*>(qv);
+  const S* mm = reinterpret_cast<const S*>(c.kminmax);
+  while (pos < end) {
+    const int b = u / c.hkv, g = u % c.hkv;
+    const int ubase = s_pre[u];
+    const int seg_end = min(end, s_pre[u + 1]);
+    double qpos[VEC], qneg[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) { qpos[e] = 0.0; qneg[e] = 0.0; }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float f[VEC];
+      unpack<T>(load16(q + ((int64_t)b * c.hq + g * G + h) * D + d0), f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        qpos[e] += (double)fmaxf(f[e], 0.f);
+        qneg[e] += (double)fminf(f[e], 0.f);
+      }
+    }
+    float* srow = scores + (int64_t)u * c.max_pages;
+    for (int p0 = pos - ubase; p0 < seg_end - ubase; p0 += kWave) {
+      const int np = min(kWave, seg_end - ubase - p0);
+      int phys_w = -1;
+      if (lane < np) {
+        const int ph = c.page_table[(int64_t)b * c.max_pages + p0 + lane];
+        phys_w = (ph >= 0 && ph < c.num_phys) ? ph : -1;
+      }
+#pragma unroll 4
+      for (int it = 0; it < np; it += PPI) {
+        const int pl = it + lane / LPT;  // < 64: PPI divides 64 and it <= 64 - PPI
+        const int phys = __shfl(phys_w, pl);
+        const int64_t row = ((int64_t)(phys < 0 ? 0 : phys) * c.hkv + g) * 2 * D + d0;
+        const u32x4 lo = load16(mm + row);
+        const u32x4 hi = load16(mm + row + D);
+        float fl[VEC], fh[VEC];
+        unpack<T>(lo, fl);
+        unpack<T>(hi, fh);
+        double sc = 0.0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          sc = fma((double)fh[e], qpos[e], sc);
+          sc = fma((double)fl[e], qneg[e], sc);
+        }
+        sc = group_sum<LPT>(sc);
+        if (sub == 0 && phys >= 0 && pl < np) srow[p0 + pl] = (float)sc;
+      }
+    }
+    pos = seg_end;
+    ++u;
   }
 }
 
@@ -215,16 +308,30 @@ __global__ __launch_bounds__(NT) void select_topk_kernel(CacheView c, const int3
   }
 }
 
-template <typename T, int D>
-hipError_t score_impl(const CacheView& c, const void* q, float* scores, hipStream_t s) {
-  dim3 grid((c.max_pages + kScorePages - 1) / kScorePages, c.batch * c.hkv);
-  switch (c.group) {
-    case 1: hipLaunchKernelGGL((score_pages_kernel<T, D, 1>), grid, dim3(256), 0, s, c, q, scores); break;
-    case 2: hipLaunchKernelGGL((score_pages_kernel<T, D, 2>), grid, dim3(256), 0, s, c, q, scores); break;
-    case 4: hipLaunchKernelGGL((score_pages_kernel<T, D, 4>), grid, dim3(256), 0, s, c, q, scores); break;
-    default: hipLaunchKernelGGL((score_pages_kernel<T, D, 8>), grid, dim3(256), 0, s, c, q, scores); break;
+template <typename T, int D, int G>
+hipError_t score_launch(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+  const int units = c.batch * c.hkv;
+  if (units <= kMaxStreamUnits) {
+    const size_t lds = (size_t)(units + 1) * sizeof(int);
+    int grid = 0;
+    hipError_t e = persistent_grid(reinterpret_cast<const void*>(&score_stream_kernel<T, D, G>), 256, lds, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((score_stream_kernel<T, D, G>), dim3(grid), dim3(256), lds, s, c, q, scores);
+  } else {
+    dim3 grid((c.max_pages + kScorePages - 1) / kScorePages, units);
+    hipLaunchKernelGGL((score_pages_kernel<T, D, G>), grid, dim3(256), 0, s, c, q, scores);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t score_impl(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+  switch (c.group) {
+    case 1: return score_launch<T, D, 1>(c, q, scores, s);
+    case 2: return score_launch<T, D, 2>(c, q, scores, s);
+    case 4: return score_launch<T, D, 4>(c, q, scores, s);
+    default: return score_launch<T, D, 8>(c, q, scores, s);
+  }
 }
 
 }  // namespace
