@@ -117,6 +117,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
   constexpr int VEC = T::VEC;
   constexpr int LPT = D / VEC;
   constexpr int PPI = kWave / LPT;
+  constexpr int BATCH = 4;  // load instructions (pairs) in flight per batch
+  static_assert((BATCH * PPI) <= kWave && kWave % (BATCH * PPI) == 0, "batches tile a page-table window");
   using S = typename T::storage;
   extern __shared__ int s_pre[];  // units + 1
   __shared__ int s_tmp[256 / kWave];
@@ -159,23 +161,50 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
       }
     }
     float* srow = scores + (int64_t)u * c.max_pages;
-    for (int p0 = pos - ubase; p0 < seg_end - ubase; p0 += kWave) {
-      const int np = min(kWave, seg_end - ubase - p0);
-      int phys_w = -1;
-      if (lane < np) {
-        const int ph = c.page_table[(int64_t)b * c.max_pages + p0 + lane];
-        phys_w = (ph >= 0 && ph < c.num_phys) ? ph : -1;
+    // Pages [pb, pe) of this unit, in batches of BATCH load instructions
+    // (PPI pages each). Page-table entries come 64 at a time, one per lane:
+    // win0 holds the current window, win1 the next one (fetched a window ahead).
+    const int pb = pos - ubase, pe = seg_end - ubase;
+    const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
+    auto fetch_window = [&](int wi) -> int {
+      const int pg = pb + wi * kWave + lane;
+      int ph = -1;
+      if (pg < pe) {
+        const int t = c.page_table[(int64_t)b * c.max_pages + pg];
+        ph = (t >= 0 && t < c.num_phys) ? t : -1;
       }
-#pragma unroll 4
-      for (int it = 0; it < np; it += PPI) {
-        const int pl = it + lane / LPT;  // < 64: PPI divides 64 and it <= 64 - PPI
-        const int phys = __shfl(phys_w, pl);
-        const int64_t row = ((int64_t)(phys < 0 ? 0 : phys) * c.hkv + g) * 2 * D + d0;
-        const u32x4 lo = load16(mm + row);
-        const u32x4 hi = load16(mm + row + D);
+      return ph;
+    };
+    int win0 = fetch_window(0), win1 = fetch_window(1);
+    int cur_win = 0;
+    auto issue = [&](int bt, u32x4* lo, u32x4* hi, int* phys) {
+      const int wi = (bt * BATCH * PPI) / kWave;  // a batch never straddles two windows
+      const int wsrc = wi == cur_win ? win0 : win1;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int pl = (bt * BATCH + i) * PPI + lane / LPT;  // page offset in the segment
+        phys[i] = __shfl(wsrc, pl & (kWave - 1));
+        const int64_t row = ((int64_t)(phys[i] < 0 ? 0 : phys[i]) * c.hkv + g) * 2 * D + d0;
+        lo[i] = load16(mm + row);
+        hi[i] = load16(mm + row + D);
+      }
+    };
+    u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];
+    int phA[BATCH], phB[BATCH];
+    issue(0, loA, hiA, phA);
+    for (int bt = 0; bt < nbatch; ++bt) {
+      const int wnext = ((bt + 1) * BATCH * PPI) / kWave;
+      if (wnext != cur_win && bt + 1 < nbatch) {  // next batch opens a new window
+        win0 = win1;
+        cur_win = wnext;
+        win1 = fetch_window(wnext + 1);
+      }
+      if (bt + 1 < nbatch) issue(bt + 1, loB, hiB, phB);
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
         float fl[VEC], fh[VEC];
-        unpack<T>(lo, fl);
-        unpack<T>(hi, fh);
+        unpack<T>(loA[i], fl);
+        unpack<T>(hiA[i], fh);
         double sc = 0.0;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -183,8 +212,11 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
           sc = fma((double)fl[e], qneg[e], sc);
         }
         sc = group_sum<LPT>(sc);
-        if (sub == 0 && phys >= 0 && pl < np) srow[p0 + pl] = (float)sc;
+        const int pl = (bt * BATCH + i) * PPI + lane / LPT;
+        if (sub == 0 && phA[i] >= 0 && pb + pl < pe) srow[pb + pl] = (float)sc;
       }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) { loA[i] = loB[i]; hiA[i] = hiB[i]; phA[i] = phB[i]; }
     }
     pos = seg_end;
     ++u;
@@ -308,6 +340,129 @@ __global__ __launch_bounds__(NT) void select_topk_kernel(CacheView c, const int3
   }
 }
 
+// Register variant of the top-B select for P - 2 <= 256 * KPT middle pages.
+// Thread t holds the keys of middle pages [t*KPT, t*KPT + KPT) (index order,
+// so the compaction emits ascending pages). Radix digits are taken on
+// key - min_key: the span of real scores is a few exponent steps, so the first
+// 8-bit digit already spreads the keys over the histogram and 2-3 passes
+// usually suffice.
+template <int KPT>
+__global__ __launch_bounds__(kSelectThreads) void select_topk_reg_kernel(CacheView c, const int32_t* __restrict__ budget,
+                                                                       int cap, const float* __restrict__ scores,
+                                                                       int32_t* __restrict__ sel_idx,
+                                                                       int32_t* __restrict__ sel_cnt) {
+  constexpr int NT = kSelectThreads;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_red[NT / kWave][2];
+  __shared__ int s_digit, s_above;
+  __shared__ int s_wave[NT / kWave][2];
+  const int unit = blockIdx.x;
+  const int b = unit / c.hkv;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int L = c.seq_lens[b];
+  const int P = min((max(L, 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  int32_t* out = sel_idx + (int64_t)unit * cap;
+  const int K = min(min(max(budget[b], 2), cap), P);
+  if (K >= P) {
+    for (int i = tid; i < P; i += NT) out[i] = i;
+    if (tid == 0) sel_cnt[unit] = P;
+    return;
+  }
+  const int M = P - 2;
+  const int need = K - 2;
+  if (tid == 0) {
+    out[0] = 0;
+    out[K - 1] = P - 1;
+    sel_cnt[unit] = K;
+  }
+  if (need == 0) return;
+  const float* srow = scores + (int64_t)unit * c.max_pages + 1;
+  const int i0 = tid * KPT;
+  uint32_t key[KPT];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const int i = i0 + r;
+    key[r] = i < M ? score_key(srow[i]) : 0u;
+    if (i < M) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
+  }
+  // block min / max of the keys
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) { s_red[wave][0] = kmin; s_red[wave][1] = kmax; }
+  __syncthreads();
+  kmin = s_red[0][0];
+  kmax = s_red[0][1];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) { kmin = min(kmin, s_red[w][0]); kmax = max(kmax, s_red[w][1]); }
+  const uint32_t span = kmax - kmin;
+  const int nbits = span == 0 ? 0 : 32 - __clz((int)span);
+
+  uint32_t prefix = 0, mask = 0;
+  int remaining = need;
+  for (int hi = nbits; hi > 0; hi -= 8) {
+    const int lo = max(hi - 8, 0);
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const uint32_t off = key[r] - kmin;
+      if (i0 + r < M && (off & mask) == prefix) atomicAdd(&hist[(off >> lo) & dmask], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      const int top = 255 - 4 * tid;
+      const int c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+      const int tot = c0 + c1 + c2 + c3;
+      const int incl = wave_incl_scan(tot);
+      const int excl = incl - tot;
+      if (excl < remaining && remaining <= incl) {
+        const int rr = remaining - excl;
+        int digit, above;
+        if (rr <= c0) { digit = top; above = excl; }
+        else if (rr <= c0 + c1) { digit = top - 1; above = excl + c0; }
+        else if (rr <= c0 + c1 + c2) { digit = top - 2; above = excl + c0 + c1; }
+        else { digit = top - 3; above = excl + c0 + c1 + c2; }
+        s_digit = digit;
+        s_above = above;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_digit << lo;
+    mask |= dmask << lo;
+    remaining -= s_above;
+    __syncthreads();
+  }
+  const uint32_t T = kmin + prefix;
+  const int eq_take = remaining;
+
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    if (i0 + r < M) { gt += key[r] > T; eq += key[r] == T; }
+  }
+  const int gt_incl = wave_incl_scan(gt);
+  const int eq_incl = wave_incl_scan(eq);
+  if (lane == kWave - 1) { s_wave[wave][0] = gt_incl; s_wave[wave][1] = eq_incl; }
+  __syncthreads();
+  int gt_before = gt_incl - gt, eq_before = eq_incl - eq;
+  for (int w = 0; w < wave; ++w) { gt_before += s_wave[w][0]; eq_before += s_wave[w][1]; }
+  int pos = 1 + gt_before + min(eq_before, eq_take);
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    if (i0 + r < M) {
+      bool take = key[r] > T;
+      if (key[r] == T) { take = eq_seen < eq_take; ++eq_seen; }
+      if (take && pos < K - 1) out[pos++] = i0 + r + 1;
+    }
+  }
+}
+
 template <typename T, int D, int G>
 hipError_t score_launch(const CacheView& c, const void* q, float* scores, hipStream_t s) {
   const int units = c.batch * c.hkv;
@@ -350,6 +505,20 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
     e = c.head_dim == 64 ? score_impl<F32, 64>(c, q, scores, s) : score_impl<F32, 128>(c, q, scores, s);
   }
   if (e != hipSuccess) return e;
+  const int middle = c.max_pages - 2;
+  const dim3 sgrid(c.batch * c.hkv), sblock(kSelectThreads);
+  if (middle <= kSelectThreads * 8) {
+    hipLaunchKernelGGL((select_topk_reg_kernel<8>), sgrid, sblock, 0, s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+    return hipGetLastError();
+  }
+  if (middle <= kSelectThreads * 32) {
+    hipLaunchKernelGGL((select_topk_reg_kernel<32>), sgrid, sblock, 0, s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+    return hipGetLastError();
+  }
+  if (middle <= kSelectThreads * 64) {
+    hipLaunchKernelGGL((select_topk_reg_kernel<64>), sgrid, sblock, 0, s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)c.max_pages * sizeof(uint32_t);
   if (lds <= kSelectLdsKeyBytes) {
     hipLaunchKernelGGL((select_topk_kernel<kSelectThreads, true>), dim3(c.batch * c.hkv), dim3(kSelectThreads), lds,
