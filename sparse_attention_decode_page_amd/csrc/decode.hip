@@ -121,8 +121,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
       const int slot = s & (c.page_size - 1);
       ok[i] = ins < ninstr && slot < s_valid[e];
       const int64_t off = ((((int64_t)s_phys[e] * c.hkv + g) << c.ps_log2) + (ok[i] ? slot : 0)) * D + d0;
-      kr[i] = load16(kp + off);
-      vr[i] = load16(vp + off);
+      kr[i] = load16_stream(kp + off);
+      vr[i] = load16_stream(vp + off);
     }
   };
 
@@ -360,35 +360,59 @@ __global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_strea
           }
         }
       }
-      const int ntok = nwin << c.ps_log2;
-      const int ntiles = (ntok + 15) >> 4;
+      const int ntiles = ((nwin << c.ps_log2) + 15) >> 4;
 
-      // Row offset of stream token tau, and whether that token is in the cache.
-      auto token_row = [&](int tau, int e, bool& ok) -> int64_t {
-        const int ph = __shfl(phys_w, e);
-        const int va = __shfl(valid_w, e);
-        const int slot = tau & (c.page_size - 1);
-        ok = tau < ntok && slot < va;
-        return ((((int64_t)ph * c.hkv + g) << c.ps_log2) + (ok ? slot : 0)) * D;
+      // Tiles of 16 stream tokens. For every supported page size the entry of
+      // a V load instruction is wave-uniform, and so is a K tile's entry when
+      // ps >= 16 (with ps = 8 a K tile spans entries 2t and 2t+1): physical
+      // page and valid-token count come from the window with v_readlane into
+      // scalar registers, and per-lane addresses are 32-bit offsets from a
+      // scalar page base.
+      auto page_base = [&](int e, int& valid) -> int64_t {
+        const int ee = min(e, kWave - 1);
+        const int ph = __builtin_amdgcn_readlane(phys_w, ee);
+        valid = e < nwin ? __builtin_amdgcn_readlane(valid_w, ee) : 0;
+        return (((int64_t)ph * c.hkv + g) << c.ps_log2) * D;
       };
-      auto load_tile = [&](int t, u32x4* kr, u32x4* vr, bool& kok, bool* vok) {
-        const int tk = t * 16 + r16;
-        const int64_t krow = token_row(tk, min(tk >> c.ps_log2, kWave - 1), kok);
+      // Per tile only wave-uniform valid-token counts are carried (kv0/kv1 for
+      // the K tile's one or two entries, vv[i] for V load i); each lane
+      // re-derives its own validity from its slot when the data is used.
+      struct TileValid { int kv0, kv1, vv[NV]; };
+      auto k_slot = [&](int t) { return (t * 16 + r16) & (c.page_size - 1); };
+      auto v_slot = [&](int t, int i) { return (t * 16 + i * TPI + vtok) & (c.page_size - 1); };
+      auto k_ok = [&](int t, const TileValid& tv) {
+        const int va = (c.page_size < 16 && r16 >= c.page_size) ? tv.kv1 : tv.kv0;
+        return k_slot(t) < va;
+      };
+      auto load_tile = [&](int t, u32x4* kr, u32x4* vr, TileValid& tv) {
+        {
+          const int e0 = (t * 16) >> c.ps_log2;
+          int64_t base = page_base(e0, tv.kv0);
+          tv.kv1 = 0;
+          if (c.page_size < 16) {  // the tile's second half lies on the next entry
+            const int64_t base1 = page_base(e0 + 1, tv.kv1);
+            if (r16 >= c.page_size) base = base1;
+          }
+          const int slot = k_slot(t);
+          const uint16_t* src = kp + base + (k_ok(t, tv) ? slot : 0) * D + 8 * q4;
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) kr[jj] = load16(kp + krow + 32 * jj + 8 * q4);
+          for (int jj = 0; jj < NJ; ++jj) kr[jj] = load16_stream(src + 32 * jj);
+        }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          const int tv = t * 16 + i * TPI + vtok;
-          const int64_t vrow = token_row(tv, min(tv >> c.ps_log2, kWave - 1), vok[i]);
-          vr[i] = load16(vp + vrow + 8 * vsub);
+          const int64_t base = page_base((t * 16 + i * TPI) >> c.ps_log2, tv.vv[i]);
+          const int slot = v_slot(t, i);
+          vr[i] = load16_stream(vp + base + (slot < tv.vv[i] ? slot : 0) * D + 8 * vsub);
         }
       };
 
-      u32x4 kA[NJ], vA[NV], kB[NJ], vB[NV];
-      bool kokA, vokA[NV], kokB, vokB[NV];
-      load_tile(0, kA, vA, kokA, vokA);
+      // Two tiles in flight while one is consumed (ring of three buffers).
+      u32x4 kA[NJ], vA[NV], kB[NJ], vB[NV], kC[NJ], vC[NV];
+      TileValid tA, tB, tC;
+      load_tile(0, kA, vA, tA);
+      if (1 < ntiles) load_tile(1, kB, vB, tB);
       for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_tile(t + 1, kB, vB, kokB, vokB);
+        if (t + 2 < ntiles) load_tile(t + 2, kC, vC, tC);
         float sc[G];
 #pragma unroll
         for (int st = 0; st < NSET; ++st) {
@@ -406,11 +430,12 @@ __global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_strea
             }
           }
         }
+        const bool kok = k_ok(t, tA);
         float p[G], mnew[G];
         bool grow = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          p[h] = kokA ? sc[h] * a.qk_scale : -INFINITY;
+          p[h] = kok ? sc[h] * a.qk_scale : -INFINITY;
           const float tmax = group_max<16>(p[h]);
           const bool up = tmax > m[h] + kLazyRescale;
           mnew[h] = up ? tmax : m[h];
@@ -435,7 +460,7 @@ __global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_strea
         for (int i = 0; i < NV; ++i) {
           float vf[8];
           unpack<BF16>(vA[i], vf);
-          if (!vokA[i]) {
+          if (v_slot(t, i) >= tA.vv[i]) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) vf[e] = 0.f;  // never multiply unread slots
           }
@@ -448,10 +473,11 @@ __global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_strea
           }
         }
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) kA[jj] = kB[jj];
+        for (int jj = 0; jj < NJ; ++jj) { kA[jj] = kB[jj]; kB[jj] = kC[jj]; }
 #pragma unroll
-        for (int i = 0; i < NV; ++i) { vA[i] = vB[i]; vokA[i] = vokB[i]; }
-        kokA = kokB;
+        for (int i = 0; i < NV; ++i) { vA[i] = vB[i]; vB[i] = vC[i]; }
+        tA = tB;
+        tB = tC;
       }
     }
 

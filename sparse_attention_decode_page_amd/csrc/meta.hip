@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void build_meta_kernel(CacheView c) {
     const int valid = min(c.page_size, L - p * c.page_size);
     const S* base = kp + (((int64_t)phys * c.hkv + g) * c.page_size) * D + d0;
     u32x4 lo, hi;
-    for (int s = 0; s < valid; ++s) minmax_chunk<T>(load16(base + (int64_t)s * D), lo, hi, s == 0);
+    for (int s = 0; s < valid; ++s) minmax_chunk<T>(load16_stream(base + (int64_t)s * D), lo, hi, s == 0);
     const int64_t mrow = ((int64_t)phys * c.hkv + g) * 2 * D + d0;
     store16(mm + mrow, lo);
     store16(mm + mrow + D, hi);

@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
     const int pl = wave * (kScorePages / 4) + it * PPI + lane / LPT;
     const int phys = s_phys[pl];
     const int64_t row = ((int64_t)(phys < 0 ? 0 : phys) * c.hkv + g) * 2 * D + d0;
-    const u32x4 lo = load16(mm + row);
-    const u32x4 hi = load16(mm + row + D);
+    const u32x4 lo = load16_stream(mm + row);
+    const u32x4 hi = load16_stream(mm + row + D);
     float fl[VEC], fh[VEC];
     unpack<T>(lo, fl);
     unpack<T>(hi, fh);
@@ -185,8 +185,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
         const int pl = (bt * BATCH + i) * PPI + lane / LPT;  // page offset in the segment
         phys[i] = __shfl(wsrc, pl & (kWave - 1));
         const int64_t row = ((int64_t)(phys[i] < 0 ? 0 : phys[i]) * c.hkv + g) * 2 * D + d0;
-        lo[i] = load16(mm + row);
-        hi[i] = load16(mm + row + D);
+        lo[i] = load16_stream(mm + row);
+        hi[i] = load16_stream(mm + row + D);
       }
     };
     u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];
