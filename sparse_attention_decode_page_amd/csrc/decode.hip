@@ -406,13 +406,11 @@ __global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_strea
         }
       };
 
-      // Two tiles in flight while one is consumed (ring of three buffers).
-      u32x4 kA[NJ], vA[NV], kB[NJ], vB[NV], kC[NJ], vC[NV];
-      TileValid tA, tB, tC;
+      u32x4 kA[NJ], vA[NV], kB[NJ], vB[NV];
+      TileValid tA, tB;
       load_tile(0, kA, vA, tA);
-      if (1 < ntiles) load_tile(1, kB, vB, tB);
       for (int t = 0; t < ntiles; ++t) {
-        if (t + 2 < ntiles) load_tile(t + 2, kC, vC, tC);
+        if (t + 1 < ntiles) load_tile(t + 1, kB, vB, tB);
         float sc[G];
 #pragma unroll
         for (int st = 0; st < NSET; ++st) {
@@ -473,11 +471,10 @@ __global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_strea
           }
         }
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) { kA[jj] = kB[jj]; kB[jj] = kC[jj]; }
+        for (int jj = 0; jj < NJ; ++jj) kA[jj] = kB[jj];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) { vA[i] = vB[i]; vB[i] = vC[i]; }
+        for (int i = 0; i < NV; ++i) vA[i] = vB[i];
         tA = tB;
-        tB = tC;
       }
     }
 
