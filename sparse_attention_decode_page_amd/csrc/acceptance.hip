@@ -3,7 +3,7 @@
 // alpha_r = sum_v min(softmax(a_r/T)_v, softmax(b_r/T)_v) = 1 - TV(p, q)
 // (Sparrow project page, "Insights": the per-token mismatch of the sparse
 // actor against the dense policy; the wispaper blog calls it the acceptance
-// rate). Each row is split into 4096-entry chunks so a few rows still fill the
+// rate). Each row is split into 8192-entry chunks so a few rows still fill the
 // GPU:
 //   pass 1: per chunk, the max and sum of 2^(x - max) of both rows (x = logit*log2e/T);
 //   pass 2: per chunk, the row's global normalisers from the pass-1 partials
@@ -19,8 +19,12 @@ namespace spdec {
 namespace {
 
 constexpr int kAccThreads = 256;
-constexpr int kAccPer = 16;  // entries per thread per row
+constexpr int kAccPer = 32;  // entries per thread per row (8192-entry chunks: one resident round for 64 rows)
 constexpr int kAccChunk = kAccThreads * kAccPer;
+// Pass 1 streams the logits from HBM (non-temporal); pass 2 re-reads them right
+// after and may find them in the last-level cache.
+constexpr bool kPass1Stream = true;
+constexpr bool kPass2Stream = false;
 
 struct AccArgs {
   const float* a;
@@ -33,21 +37,24 @@ struct AccArgs {
   float* alpha;   // [rows]
 };
 
-// Thread t loads entries base + 4t + 1024j .. +3, j = 0..3 (16-byte loads).
-template <bool ALIGNED>
-__device__ __forceinline__ void load_row(const float* row, int vocab, int base, float c, float* x) {
+// Thread t loads entries base + 4t + 1024j .. +3, j = 0..kAccPer/4-1 (16-byte loads).
+// STREAM selects the non-temporal hint (data read once from HBM).
+template <bool ALIGNED, bool STREAM>
+__device__ __forceinline__ void load_row(const float* row, int vocab, int base, float* x) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int idx = base + 4 * (int)threadIdx.x + 1024 * j;
+  for (int j = 0; j < kAccPer / 4; ++j) {
+    const int idx = base + 4 * (int)threadIdx.x + 4 * kAccThreads * j;
     if (ALIGNED && idx + 3 < vocab) {
-      const float4 v = *reinterpret_cast<const float4*>(row + idx);
-      x[4 * j + 0] = v.x * c;
-      x[4 * j + 1] = v.y * c;
-      x[4 * j + 2] = v.z * c;
-      x[4 * j + 3] = v.w * c;
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4* p = reinterpret_cast<const f32x4*>(row + idx);
+      const f32x4 v = STREAM ? __builtin_nontemporal_load(p) : *p;
+      x[4 * j + 0] = v.x;
+      x[4 * j + 1] = v.y;
+      x[4 * j + 2] = v.z;
+      x[4 * j + 3] = v.w;
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[4 * j + u] = (idx + u < vocab) ? row[idx + u] * c : -INFINITY;
+      for (int u = 0; u < 4; ++u) x[4 * j + u] = (idx + u < vocab) ? row[idx + u] : -INFINITY;
     }
   }
 }
@@ -83,8 +90,10 @@ __global__ __launch_bounds__(kAccThreads) void acc_stats_kernel(AccArgs x) {
   const int r = blockIdx.y, ch = blockIdx.x;
   const int base = ch * kAccChunk;
   float va[kAccPer], vb[kAccPer];
-  load_row<ALIGNED>(x.a + (int64_t)r * x.stride, x.vocab, base, x.c, va);
-  load_row<ALIGNED>(x.b + (int64_t)r * x.stride, x.vocab, base, x.c, vb);
+  load_row<ALIGNED, kPass1Stream>(x.a + (int64_t)r * x.stride, x.vocab, base, va);
+  load_row<ALIGNED, kPass1Stream>(x.b + (int64_t)r * x.stride, x.vocab, base, vb);
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) { va[i] *= x.c; vb[i] *= x.c; }
   float ma = va[0], mb = vb[0];
 #pragma unroll
   for (int i = 1; i < kAccPer; ++i) { ma = fmaxf(ma, va[i]); mb = fmaxf(mb, vb[i]); }
@@ -106,6 +115,12 @@ __global__ __launch_bounds__(kAccThreads) void acc_min_kernel(AccArgs x) {
   __shared__ float sh[kAccThreads / kWave];
   __shared__ float s_norm[4];
   const int r = blockIdx.y, ch = blockIdx.x;
+  // The chunk's logits are requested first; the row normalisers are folded
+  // from the pass-1 partials while those loads are in flight.
+  float va[kAccPer], vb[kAccPer];
+  const int base = ch * kAccChunk;
+  load_row<ALIGNED, kPass2Stream>(x.a + (int64_t)r * x.stride, x.vocab, base, va);
+  load_row<ALIGNED, kPass2Stream>(x.b + (int64_t)r * x.stride, x.vocab, base, vb);
   if (threadIdx.x < kWave) {
     // Row normalisers from the chunk partials: lane i folds chunks i, i+64, ...
     const float* p = x.part + (int64_t)r * x.nchunk * 4;
@@ -124,13 +139,9 @@ __global__ __launch_bounds__(kAccThreads) void acc_min_kernel(AccArgs x) {
   }
   __syncthreads();
   const float ma = s_norm[0], ia = s_norm[1], mb = s_norm[2], ib = s_norm[3];
-  float va[kAccPer], vb[kAccPer];
-  const int base = ch * kAccChunk;
-  load_row<ALIGNED>(x.a + (int64_t)r * x.stride, x.vocab, base, x.c, va);
-  load_row<ALIGNED>(x.b + (int64_t)r * x.stride, x.vocab, base, x.c, vb);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kAccPer; ++i) s += fminf(exp2f(va[i] - ma) * ia, exp2f(vb[i] - mb) * ib);
+  for (int i = 0; i < kAccPer; ++i) s += fminf(exp2f(va[i] * x.c - ma) * ia, exp2f(vb[i] * x.c - mb) * ib);
   s = block_sum(s, sh);
   if (threadIdx.x == 0) x.csum[(int64_t)r * x.nchunk + ch] = s;
 }
