@@ -70,6 +70,40 @@ def algorithmic_bytes(spec, lens, budget_pages, cap, rows, vocab):
     }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters_qwen3-8b-ragged.md")
+KERNEL_SOURCES = ("common.h", "launch.h", "decode.hip", "select.hip", "abi.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_attention_decode_page_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """Per-dispatch HBM bytes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
+
+    Returns {kernel: bytes} or None when the summary is missing or the kernel
+    sources changed since the counters were taken.
+    """
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    table, src = {}, None
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] == "source_hash":
+                src = parts[1]
+            elif len(parts) == 3 and parts[0] == "traffic_bytes":
+                table[parts[1]] = int(parts[2])
+    if src != kernel_source_hash():
+        return None
+    return table
+
+
 def cpu_baseline(wl, steps_tokens, seconds: float):
     """Time the CPU oracle on the same step for as many sequences as fit in `seconds`."""
     import oracle as O
@@ -229,6 +263,17 @@ def main():
     sp_b = byt["select_pages"] + byt["sparse_decode"]
     dense_gbps = byt["dense_decode"] / mean_t["dense_decode"] / 1e9
     sparse_gbps = sp_b / sp_t / 1e9
+    # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
+    traffic = counter_traffic() if spec.name == WORKLOAD else None
+    dense_kernels = ["decode_stream_kernel<128,4,false>", "stream_merge_kernel<128,false>"]
+    sparse_kernels = ["score_stream_kernel<BF16,128,4>", "select_topk_reg_kernel<8>",
+                      "decode_stream_kernel<128,4,true>", "stream_merge_kernel<128,true>"]
+
+    def traffic_of(names):
+        if traffic is None or any(n not in traffic for n in names):
+            return None
+        return int(sum(traffic[n] for n in names))
+
     result = {
         "metric": METRIC,
         "value": value,
@@ -248,11 +293,12 @@ def main():
                    "acceptance_rows": R, "vocab": V, "accumulate": "fp32",
                    "step": "append_kv + select_pages + sparse_decode + dense_decode + acceptance"},
         "roofline": {"bound": "hbm", "achieved": dense_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dense_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "dense_decode (decode_split_kernel + decode_merge_kernel)",
+                     "frac": dense_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(dense_kernels),
+                     "kernel": "dense_decode call: " + " + ".join(dense_kernels),
                      "bytes_per_launch": int(byt["dense_decode"])},
         "sparse": {"tokens_per_s": spec.batch / sp_t, "us": sp_t * 1e6, "bytes": int(sp_b),
-                   "eff_GBps": sparse_gbps, "frac_hbm": sparse_gbps / HBM_PEAK_GBPS},
+                   "eff_GBps": sparse_gbps, "frac_hbm": sparse_gbps / HBM_PEAK_GBPS,
+                   "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels)},
         "rows": rows_out,
         "step_us_median": float(np.median(step_s)) * 1e6,
         "wall_s_timed": wall,
