@@ -11,10 +11,13 @@ synthetic data shaped like a Qwen3-8B decode layer with ragged 8K-32K contexts;
 everything is resident in HBM before timing starts.
 
 Prints ONE JSON line. `value` is decode tokens/s of the full step (batch / step
-time). Per-row times come from HIP events recorded on the stream the kernels
-run on; `roofline` is for the dominant kernel (dense decode), `sparse` reports
-the sparse path (select + sparse decode) against HBM peak, and `cpu_baseline`
-times the CPU oracle on a bounded sample of the same step.
+time) over K back-to-back steps timed with one pair of HIP events. Per-row
+times come from K further steps with HIP events recorded between the rows on
+the stream the kernels run on; `roofline` is for the dominant kernel (dense
+decode, its call run K times back to back under one event pair). `sparse`
+reports the sparse path (select + sparse decode, each of K runs after a 1 GiB
+scrub read, the scrubs' own time subtracted) against HBM peak, and
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -174,7 +177,7 @@ def main():
     torch.cuda.set_device(dev)
     K_steps, W = args.steps, args.warmup
     t_setup = time.perf_counter()
-    wl = S.make_workload(args.workload, seed=args.seed, headroom=K_steps + W + 1)
+    wl = S.make_workload(args.workload, seed=args.seed, headroom=2 * K_steps + W + 1)
     spec = wl.spec
     assert spec.logits is not None, "the step needs logit rows for the acceptance row"
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -192,7 +195,7 @@ def main():
     q = up(wl.q)
     budget = torch.from_numpy(wl.budget_pages.astype(np.int32)).to(dev)
     cap = int(wl.budget_pages.max())
-    new_tokens = [S.append_tokens(wl, s) for s in range(K_steps + W)]
+    new_tokens = [S.append_tokens(wl, s) for s in range(2 * K_steps + W)]
     k_new = [up(t[0]) for t in new_tokens]
     v_new = [up(t[1]) for t in new_tokens]
     la = torch.from_numpy(wl.logits_a).to(dev)
@@ -214,7 +217,7 @@ def main():
     t_setup = time.perf_counter() - t_setup
 
     rows = ["append_kv", "select_pages", "sparse_decode", "dense_decode", "acceptance"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)] for _ in range(K_steps)]
+    row_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)] for _ in range(K_steps)]
 
     def step(i, events=None):
         rec = (lambda j: events[j].record()) if events is not None else (lambda j: None)
@@ -234,24 +237,85 @@ def main():
         step(i)
     torch.cuda.synchronize()
     lens_before = wl.lens.astype(np.int64) + W
+    # Timed region: K whole steps back to back, one event pair around them. An
+    # event recorded between two launches holds the next one back by a few
+    # microseconds, so none is recorded inside the steps here.
+    t_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
+    t_ev[0].record()
     for i in range(K_steps):
-        step(W + i, ev[i])
+        step(W + i)
+    t_ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_total = t_ev[0].elapsed_time(t_ev[1]) * 1e-3
+    # Per-row breakdown: K more steps with an event between rows (each row's
+    # time then includes the short hold-up after the event before it).
+    for i in range(K_steps):
+        step(W + K_steps + i, row_ev[i])
+    torch.cuda.synchronize()
     per_row = {r: [] for r in rows}
     for i in range(K_steps):
         for j, r in enumerate(rows):
-            per_row[r].append(ev[i][j].elapsed_time(ev[i][j + 1]) * 1e-3)
-    step_s = [ev[i][0].elapsed_time(ev[i][len(rows)]) * 1e-3 for i in range(K_steps)]
-    gpu_total = ev[0][0].elapsed_time(ev[-1][len(rows)]) * 1e-3
+            per_row[r].append(row_ev[i][j].elapsed_time(row_ev[i][j + 1]) * 1e-3)
+    step_s = [row_ev[i][0].elapsed_time(row_ev[i][len(rows)]) * 1e-3 for i in range(K_steps)]
+    # Sparse path alone: select_pages + sparse_decode K times on the cache as
+    # it stands after the steps above, each time right after a 1 GiB scrub
+    # read (so neither L2 nor the last-level cache holds the previous
+    # iteration's pages), one event pair around all K; the same K scrubs timed
+    # alone are subtracted. The scrub reads (a sum into a preallocated scalar)
+    # rather than writes: a written scrub leaves dirty lines whose write-back
+    # would be charged to the kernels that follow, which the real step never
+    # sees (its previous rows only read the cache).
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    scrub_out = torch.empty((), dtype=torch.float32, device=dev)
 
-    # algorithmic bytes averaged over the timed steps (lengths grow by one per step)
-    byt = {r: 0.0 for r in rows}
+    def timed_loop(body):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for i in range(K_steps):
+            body(i)
+        evs[1].record()
+        torch.cuda.synchronize()
+        return evs[0].elapsed_time(evs[1]) * 1e-3 / K_steps
+
+    def sparse_path():
+        spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
+        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
+
+    def scrub_read():
+        torch.sum(scrub, dim=0, out=scrub_out)
+
+    for _ in range(2):  # untimed: the reduction's first call sets up its workspace
+        scrub_read()
+        sparse_path()
+    t_scrub = timed_loop(lambda i: scrub_read())
+    t_scrub_sparse = timed_loop(lambda i: (scrub_read(), sparse_path()))
+    sp_t = t_scrub_sparse - t_scrub
+    sp_t_warm = timed_loop(lambda i: sparse_path())
+    del scrub, scrub_out
+    # Dense verifier alone, the same way: its average call duration is the
+    # roofline's denominator.
+    de_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    de_ev[0].record()
     for i in range(K_steps):
-        b_i = algorithmic_bytes(spec, lens_before + i + 1, wl.budget_pages, cap, R, V)
-        for r in rows:
-            byt[r] += b_i[r] / K_steps
+        spdec.dense_decode(cache, q, out=o_d, lse=l_d, workspace=ws_de)
+    de_ev[1].record()
+    torch.cuda.synchronize()
+    de_t = de_ev[0].elapsed_time(de_ev[1]) * 1e-3 / K_steps
+
+    # algorithmic bytes averaged over the steps of each region (lengths grow by one per step)
+    def mean_bytes(first_step):
+        acc = {r: 0.0 for r in rows}
+        for i in range(K_steps):
+            b_i = algorithmic_bytes(spec, lens_before + first_step + i + 1, wl.budget_pages, cap, R, V)
+            for r in rows:
+                acc[r] += b_i[r] / K_steps
+        return acc
+
+    byt = mean_bytes(K_steps)
+    final_bytes = algorithmic_bytes(spec, lens_before + 2 * K_steps, wl.budget_pages, cap, R, V)
     mean_t = {r: float(np.mean(per_row[r])) for r in rows}
     med_t = {r: float(np.median(per_row[r])) for r in rows}
     rows_out = {r: {"us_mean": mean_t[r] * 1e6, "us_median": med_t[r] * 1e6, "bytes": int(byt[r]),
@@ -259,9 +323,9 @@ def main():
                 for r in rows}
     ms_per_step = gpu_total / K_steps * 1e3
     value = spec.batch / (gpu_total / K_steps)
-    sp_t = mean_t["select_pages"] + mean_t["sparse_decode"]
-    sp_b = byt["select_pages"] + byt["sparse_decode"]
-    dense_gbps = byt["dense_decode"] / mean_t["dense_decode"] / 1e9
+    sp_b = final_bytes["select_pages"] + final_bytes["sparse_decode"]
+    sp_t_rows = mean_t["select_pages"] + mean_t["sparse_decode"]
+    dense_gbps = final_bytes["dense_decode"] / de_t / 1e9
     sparse_gbps = sp_b / sp_t / 1e9
     # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
     traffic = counter_traffic() if spec.name == WORKLOAD else None
@@ -295,10 +359,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": dense_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dense_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(dense_kernels),
                      "kernel": "dense_decode call: " + " + ".join(dense_kernels),
-                     "bytes_per_launch": int(byt["dense_decode"])},
+                     "bytes_per_launch": int(final_bytes["dense_decode"]), "us_per_launch": de_t * 1e6,
+                     "timing": "dense_decode back to back, K times, one event pair"},
         "sparse": {"tokens_per_s": spec.batch / sp_t, "us": sp_t * 1e6, "bytes": int(sp_b),
                    "eff_GBps": sparse_gbps, "frac_hbm": sparse_gbps / HBM_PEAK_GBPS,
-                   "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels)},
+                   "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels),
+                   "timing": "K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub, one event pair each",
+                   "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6},
         "rows": rows_out,
         "step_us_median": float(np.median(step_s)) * 1e6,
         "wall_s_timed": wall,
