@@ -16,8 +16,9 @@ times come from K further steps with HIP events recorded between the rows on
 the stream the kernels run on; `roofline` is for the dominant kernel (dense
 decode, its call run K times back to back under one event pair). `sparse`
 reports the sparse path (select + sparse decode, each of K runs after a 1 GiB
-scrub read, the scrubs' own time subtracted) against HBM peak, and
-`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+scrub read, the scrubs' own time subtracted) against HBM peak; `graph` times
+the step captured once in a HIP graph and replayed; `cpu_baseline` times the
+CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -177,7 +178,7 @@ def main():
     torch.cuda.set_device(dev)
     K_steps, W = args.steps, args.warmup
     t_setup = time.perf_counter()
-    wl = S.make_workload(args.workload, seed=args.seed, headroom=2 * K_steps + W + 1)
+    wl = S.make_workload(args.workload, seed=args.seed, headroom=3 * K_steps + 2 * W + 2)
     spec = wl.spec
     assert spec.logits is not None, "the step needs logit rows for the acceptance row"
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -304,6 +305,16 @@ def main():
     de_ev[1].record()
     torch.cuda.synchronize()
     de_t = de_ev[0].elapsed_time(de_ev[1]) * 1e-3 / K_steps
+    # The whole step captured once into a HIP graph and replayed K times (the
+    # decode path is replayed from graphs in the pages' rollout engine); each
+    # replay appends the same captured token.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(0)
+    for _ in range(W):
+        graph.replay()
+    gr_t = timed_loop(lambda i: graph.replay())
+    del graph
 
     # algorithmic bytes averaged over the steps of each region (lengths grow by one per step)
     def mean_bytes(first_step):
@@ -366,6 +377,8 @@ def main():
                    "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels),
                    "timing": "K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub, one event pair each",
                    "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6},
+        "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
+                  "timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
         "rows": rows_out,
         "step_us_median": float(np.median(step_s)) * 1e6,
         "wall_s_timed": wall,

@@ -1,0 +1,116 @@
+"""HIP graph capture of the decode step.
+
+Every ABI call is stream-ordered, allocates nothing and never synchronises the
+host, so a whole step (append_kv -> select_pages -> sparse_decode ->
+dense_decode -> acceptance) captured once into a graph must replay to the same
+bits as the same step run eagerly, step after step (the decode path is
+replayed from graphs on the S3R page, Table 3). Each replay is checked against
+an eager twin of the cache, with eager work and host synchronisations between
+the replays.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_decode_page_amd import spdec
+from sparse_attention_decode_page_amd import synth as S
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import gpu_support as GS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(spdec.LIB_PATH):
+        from sparse_attention_decode_page_amd import build
+        build.build()
+    spdec.lib()
+    assert torch.cuda.is_available()
+
+
+class _Step:
+    """Preallocated outputs and workspaces for one cache, and the step itself."""
+
+    def __init__(self, dw, la, lb, temperature):
+        c, dev = dw.cache, dw.q.device
+        spec = dw.wl.spec
+        self.dw, self.la, self.lb, self.t = dw, la, lb, temperature
+        cap = dw.max_budget
+        self.sel_idx = torch.zeros((spec.batch, spec.num_kv_heads, cap), dtype=torch.int32, device=dev)
+        self.sel_cnt = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
+        self.ws_sel = torch.zeros(spdec.select_workspace_bytes(c, cap), dtype=torch.uint8, device=dev)
+        self.ws_sp = torch.zeros(spdec.decode_workspace_bytes(c, cap), dtype=torch.uint8, device=dev)
+        self.ws_de = torch.zeros(spdec.decode_workspace_bytes(c, 0), dtype=torch.uint8, device=dev)
+        self.ws_acc = torch.zeros(spdec.acceptance_workspace_bytes(*la.shape), dtype=torch.uint8, device=dev)
+        shape = (spec.batch, spec.num_q_heads, spec.head_dim)
+        self.o_s = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.o_d = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.l_s = torch.empty(shape[:2], dtype=torch.float32, device=dev)
+        self.l_d = torch.empty(shape[:2], dtype=torch.float32, device=dev)
+        self.alpha = torch.empty(la.shape[0], dtype=torch.float32, device=dev)
+
+    def run(self, k_new, v_new):
+        dw, c = self.dw, self.dw.cache
+        spdec.append_kv(c, k_new, v_new)
+        spdec.select_pages(c, dw.q, dw.budget, dw.max_budget, sel_idx=self.sel_idx, sel_cnt=self.sel_cnt,
+                           workspace=self.ws_sel)
+        spdec.sparse_decode(c, dw.q, self.sel_idx, self.sel_cnt, dw.max_budget, out=self.o_s, lse=self.l_s,
+                            workspace=self.ws_sp)
+        spdec.dense_decode(c, dw.q, out=self.o_d, lse=self.l_d, workspace=self.ws_de)
+        spdec.acceptance(self.la, self.lb, self.t, alpha=self.alpha, workspace=self.ws_acc)
+
+    def snapshot(self):
+        dw = self.dw
+        return {n: t.clone() for n, t in (("seq_lens", dw.seq_lens), ("kminmax", dw.kminmax),
+                                            ("k_pool", dw.k_pool), ("v_pool", dw.v_pool),
+                                            ("sel_idx", self.sel_idx), ("sel_cnt", self.sel_cnt),
+                                            ("o_s", self.o_s), ("l_s", self.l_s), ("o_d", self.o_d),
+                                            ("l_d", self.l_d), ("alpha", self.alpha))}
+
+
+@pytest.mark.parametrize("dtype,D,ps", [("bf16", 128, 16), ("f32", 64, 8)])
+def test_graph_replay_matches_eager(dtype, D, ps):
+    steps = 5
+    spec = S.custom_spec("graph", batch=5, num_q_heads=8, num_kv_heads=2, head_dim=D, page_size=ps, dtype=dtype,
+                         lens=("uniform", 200, 1500), budget=("tokens", 256), outlier_channels=2,
+                         logits=("noisy", 3, 5003, 3.0, 0.3, 0.34, 3.0))
+    wl = S.make_workload(spec, seed=3, headroom=steps + 1)
+    print(f"graph replay: {dtype} D={D} ps={ps}", flush=True)
+    la = torch.from_numpy(wl.logits_a).cuda()
+    lb = torch.from_numpy(wl.logits_b).cuda()
+    eager = _Step(GS.DeviceWorkload(wl), la, lb, spec.temperature)
+    graphed = _Step(GS.DeviceWorkload(wl), la, lb, spec.temperature)
+    spdec.build_meta(eager.dw.cache)
+    spdec.build_meta(graphed.dw.cache)
+    tokens = [S.append_tokens(wl, i) for i in range(steps)]
+    k_static = GS.to_device_storage(tokens[0][0], dtype)
+    v_static = GS.to_device_storage(tokens[0][1], dtype)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run(k_static, v_static)
+    torch.cuda.synchronize()
+
+    for i in range(steps):
+        k_i = GS.to_device_storage(tokens[i][0], dtype)
+        v_i = GS.to_device_storage(tokens[i][1], dtype)
+        eager.run(k_i, v_i)
+        torch.cuda.synchronize()
+        k_static.copy_(k_i)
+        v_static.copy_(v_i)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = eager.snapshot(), graphed.snapshot()
+        for name in a:
+            assert torch.equal(a[name], b[name]), (i, name)
+        # eager work between replays, on the graphed cache's buffers too
+        graphed.o_s.fill_(float("nan"))
+        graphed.alpha.zero_()
+    lens = graphed.dw.seq_lens.cpu().numpy()
+    assert np.array_equal(lens, wl.lens + steps)
