@@ -183,6 +183,30 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spdec_verify_decode - dense verification of a sparse draft: causal
+ * multi-query attention over the complete KV (S3R page, abstract and Tables
+ * 6-7: k tokens drafted with sparse attention are verified by one
+ * full-attention pass over the k + 1 positions).
+ *
+ * The T verified positions of sequence b are the last T tokens of its cache
+ * (append them first): position t sits at L - T + t with L = seq_lens[b] and
+ * attends to tokens 0 .. L - T + t. For query head h (group g = h / G):
+ *   z_s = scale * q_{b,t,h} . k_s,  out = sum_s e^{z_s} v_s / sum_s e^{z_s},
+ *   lse = ln sum_s e^{z_s}
+ * in fp32 (scores and the attention weights pass through bf16 for the matrix
+ * cores), merged by log-sum-exp in a fixed order.
+ *
+ * q: [batch][T][Hq][D] bf16; out: fp32 [batch][T][Hq][D]; lse: nullable fp32
+ * [batch][T][Hq]. Requires a bf16 cache, 1 <= T <= 16 and G * T <= 32
+ * (SPDEC_ERR_UNSUPPORTED otherwise); seq_lens[b] >= T is a device
+ * precondition (a row with no visible token returns zeros and lse = -inf).
+ * Workspace: spdec_verify_workspace_bytes(cache, T), zero-filled once.
+ */
+size_t spdec_verify_workspace_bytes(const spdec_cache* cache, int num_positions);
+spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int num_positions, float scale,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spdec_acceptance - per-token sparse-vs-dense acceptance (Sparrow project
  * page, "Insights": per-token mismatch against the dense model; wispaper blog:
  * "acceptance rate"):

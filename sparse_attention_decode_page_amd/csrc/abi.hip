@@ -160,6 +160,28 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
   return decode_common(cache, q, nullptr, nullptr, 0, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+size_t spdec_verify_workspace_bytes(const spdec_cache* cache, int num_positions) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK || !spdec::verify_supported(v, num_positions)) return 0;
+  return spdec::verify_workspace_bytes(v, num_positions);
+}
+
+spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int num_positions, float scale,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.k_pool || !v.v_pool || !q || !out) return SPDEC_ERR_INVALID;
+  if (!aligned16(v.k_pool) || !aligned16(v.v_pool) || !aligned16(q)) return SPDEC_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return SPDEC_ERR_INVALID;
+  if (num_positions < 1) return SPDEC_ERR_INVALID;
+  if (!spdec::verify_supported(v, num_positions)) return SPDEC_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < spdec::verify_workspace_bytes(v, num_positions))
+    return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_verify(v, q, num_positions, scale, out, lse, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 size_t spdec_acceptance_workspace_bytes(int rows, int vocab) {
   if (rows < 1 || vocab < 1 || vocab > (1 << 28)) return 0;
   return spdec::acceptance_workspace_bytes(rows, vocab);

@@ -49,6 +49,10 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
                          int32_t* sel_idx, int32_t* sel_cnt, float* scores, void* ws, hipStream_t s);
 hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float scale, float* out, float* lse, void* ws, hipStream_t s);
+bool verify_supported(const CacheView& c, int T);
+size_t verify_workspace_bytes(const CacheView& c, int T);
+hipError_t launch_verify(const CacheView& c, const void* q, int T, float scale, float* out, float* lse, void* ws,
+                         hipStream_t s);
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
                              float* alpha, void* ws, hipStream_t s);
 

@@ -23,7 +23,8 @@ SPDEC_F32, SPDEC_BF16 = 0, 1
 ABI_FUNCTIONS = (
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
     "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_decode_workspace_bytes",
-    "spdec_sparse_decode", "spdec_dense_decode", "spdec_acceptance_workspace_bytes", "spdec_acceptance",
+    "spdec_sparse_decode", "spdec_dense_decode", "spdec_verify_workspace_bytes", "spdec_verify_decode",
+    "spdec_acceptance_workspace_bytes", "spdec_acceptance",
 )
 
 
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         "spdec_decode_workspace_bytes": (SZ, [D, I]),
         "spdec_sparse_decode": (I, [D, P, P, P, I, F, P, P, P, SZ, P]),
         "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
+        "spdec_verify_workspace_bytes": (SZ, [D, I]),
+        "spdec_verify_decode": (I, [D, P, I, F, P, P, P, SZ, P]),
         "spdec_acceptance_workspace_bytes": (SZ, [I, I]),
         "spdec_acceptance": (I, [P, P, I, I, I64, F, P, P, SZ, P]),
     }
@@ -218,6 +221,30 @@ def dense_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None, 
     ws = _workspace(decode_workspace_bytes(cache, 0), cache.device, workspace)
     _check(lib().spdec_dense_decode(ctypes.byref(cache.desc), _ptr(q), scale, _ptr(out), _ptr(lse), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream()), "spdec_dense_decode")
+    return out, lse
+
+
+def verify_workspace_bytes(cache: PagedCache, num_positions: int) -> int:
+    return int(lib().spdec_verify_workspace_bytes(ctypes.byref(cache.desc), int(num_positions)))
+
+
+def verify_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None, lse=None, workspace=None):
+    """Causal multi-query attention of the last T cached positions: q [batch][T][Hq][D] (bf16 cache)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [batch][T][Hq][D] tensor")
+    T = int(q.shape[1])
+    _need(q, "q", cache.dtype, (cache.batch, T, cache.num_q_heads, cache.head_dim))
+    dev = cache.device
+    if out is None:
+        out = torch.empty((cache.batch, T, cache.num_q_heads, cache.head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((cache.batch, T, cache.num_q_heads), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (cache.batch, T, cache.num_q_heads, cache.head_dim))
+    _need(lse, "lse", torch.float32, (cache.batch, T, cache.num_q_heads))
+    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    ws = _workspace(verify_workspace_bytes(cache, T), dev, workspace)
+    _check(lib().spdec_verify_decode(ctypes.byref(cache.desc), _ptr(q), T, scale, _ptr(out), _ptr(lse), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream()), "spdec_verify_decode")
     return out, lse
 
 

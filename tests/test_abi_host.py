@@ -26,7 +26,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 11
+    assert len(names) == len(S.ABI_FUNCTIONS) == 13
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -117,3 +117,20 @@ def test_acceptance_checks(L):
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(S.CacheDesc) == 80
     assert S.CacheDesc.num_phys_pages.offset == 24 and S.CacheDesc.k_pool.offset == 40
+
+
+def test_verify_checks(L):
+    d = _desc()  # bf16, G = 4
+    ws = L.spdec_verify_workspace_bytes(ctypes.byref(d), 7)
+    assert ws > 0
+    assert L.spdec_verify_workspace_bytes(ctypes.byref(d), 9) == 0           # G * T = 36 > 32
+    assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 9, 0.1, FAKE, None, FAKE, ws, None) == -2
+    assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 0, 0.1, FAKE, None, FAKE, ws, None) == -1
+    assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 7, 0.0, FAKE, None, FAKE, ws, None) == -1
+    assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 7, 0.1, None, None, FAKE, ws, None) == -1
+    assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 7, 0.1, FAKE, None, FAKE, ws - 1, None) == -3
+    f = _desc(dtype=S.SPDEC_F32)
+    assert L.spdec_verify_workspace_bytes(ctypes.byref(f), 7) == 0
+    assert L.spdec_verify_decode(ctypes.byref(f), FAKE, 7, 0.1, FAKE, None, FAKE, ws, None) == -2
+    # more positions need more workspace
+    assert L.spdec_verify_workspace_bytes(ctypes.byref(d), 8) > L.spdec_verify_workspace_bytes(ctypes.byref(d), 4)
