@@ -207,6 +207,38 @@ spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int nu
                                  float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spdec_spec_accept - exact speculative sampling of the drafted tokens (S3R
+ * page, abstract: drafts proposed with sparse attention are accepted by exact
+ * speculative sampling against the full-attention pass, so the emitted tokens
+ * follow the dense policy; the method is that of the speculative-decoding
+ * papers the citation-map page lists by title).
+ *
+ * For sequence b with k = num_draft drafted tokens x_i = draft[b][i]:
+ *   p_i = softmax(p_logits row (b, i) / T), i = 0..k (the verifier's logits at
+ *         the k + 1 verified positions), q_i = softmax(q_logits row (b, i) / T),
+ *         i = 0..k-1 (the drafter's logits the drafts were sampled from);
+ *   draft i is kept while u_accept[b][i] * q_i(x_i) < p_i(x_i), in order;
+ *   at the first rejection j, next_token[b] is drawn from max(0, p_j - q_j),
+ *   and when all k are kept from p_k. A draw with uniform u = u_sample[b]
+ *   takes the first token whose running weight sum exceeds u times the total.
+ * num_accepted[b] = number of kept drafts. Everything in fp32 with fixed
+ * reduction orders; decisions whose margin is within fp32 rounding may differ
+ * from an exact computation.
+ *
+ * p_logits: fp32, row (b, i) at (b * (k + 1) + i) * row_stride elements;
+ * q_logits: fp32, row (b, i) at (b * k + i) * row_stride (unused when k = 0);
+ * draft: int32 [batch][k]; u_accept: fp32 [batch][k] in [0, 1); u_sample:
+ * fp32 [batch] in [0, 1); num_accepted, next_token: int32 [batch] out.
+ * 0 <= k <= 64, batch * (2k + 1) <= 65535, 1 <= vocab <= 2^28, row_stride >= vocab,
+ * temperature > 0. Workspace: spdec_spec_accept_workspace_bytes(batch, k, vocab).
+ */
+size_t spdec_spec_accept_workspace_bytes(int batch, int num_draft, int vocab);
+spdec_status spdec_spec_accept(const float* p_logits, const float* q_logits, int batch, int num_draft, int vocab,
+                               int64_t row_stride, const int32_t* draft, const float* u_accept,
+                               const float* u_sample, float temperature, int32_t* num_accepted,
+                               int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spdec_acceptance - per-token sparse-vs-dense acceptance (Sparrow project
  * page, "Insights": per-token mismatch against the dense model; wispaper blog:
  * "acceptance rate"):

@@ -182,6 +182,27 @@ spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int nu
                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t spdec_spec_accept_workspace_bytes(int batch, int num_draft, int vocab) {
+  if (batch < 1 || batch > 65535 || num_draft < 0 || num_draft > 64 || vocab < 1 || vocab > (1 << 28)) return 0;
+  return spdec::spec_accept_workspace_bytes(batch, num_draft, vocab);
+}
+
+spdec_status spdec_spec_accept(const float* p_logits, const float* q_logits, int batch, int num_draft, int vocab,
+                               int64_t row_stride, const int32_t* draft, const float* u_accept,
+                               const float* u_sample, float temperature, int32_t* num_accepted,
+                               int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p_logits || !u_sample || !num_accepted || !next_token) return SPDEC_ERR_INVALID;
+  if (num_draft > 0 && (!q_logits || !draft || !u_accept)) return SPDEC_ERR_INVALID;
+  if (batch < 1 || num_draft < 0 || vocab < 1 || vocab > (1 << 28) || row_stride < vocab) return SPDEC_ERR_INVALID;
+  if (batch > 65535 || num_draft > 64 || (int64_t)batch * (2 * num_draft + 1) > 65535) return SPDEC_ERR_UNSUPPORTED;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return SPDEC_ERR_INVALID;
+  if (workspace == nullptr || workspace_bytes < spdec::spec_accept_workspace_bytes(batch, num_draft, vocab))
+    return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_spec_accept(p_logits, num_draft > 0 ? q_logits : p_logits, batch, num_draft, vocab,
+                                            row_stride, draft, u_accept, u_sample, temperature, num_accepted,
+                                            next_token, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t spdec_acceptance_workspace_bytes(int rows, int vocab) {
   if (rows < 1 || vocab < 1 || vocab > (1 << 28)) return 0;
   return spdec::acceptance_workspace_bytes(rows, vocab);

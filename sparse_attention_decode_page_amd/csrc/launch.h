@@ -53,6 +53,10 @@ bool verify_supported(const CacheView& c, int T);
 size_t verify_workspace_bytes(const CacheView& c, int T);
 hipError_t launch_verify(const CacheView& c, const void* q, int T, float scale, float* out, float* lse, void* ws,
                          hipStream_t s);
+size_t spec_accept_workspace_bytes(int batch, int k, int vocab);
+hipError_t launch_spec_accept(const float* p, const float* q, int batch, int k, int vocab, int64_t stride,
+                              const int32_t* draft, const float* u_accept, const float* u_sample, float temperature,
+                              int32_t* n_accepted, int32_t* token, void* ws, hipStream_t s);
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
                              float* alpha, void* ws, hipStream_t s);
 

@@ -24,7 +24,8 @@ ABI_FUNCTIONS = (
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
     "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_decode_workspace_bytes",
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_verify_workspace_bytes", "spdec_verify_decode",
-    "spdec_acceptance_workspace_bytes", "spdec_acceptance",
+    "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
+    "spdec_acceptance",
 )
 
 
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
         "spdec_verify_workspace_bytes": (SZ, [D, I]),
         "spdec_verify_decode": (I, [D, P, I, F, P, P, P, SZ, P]),
+        "spdec_spec_accept_workspace_bytes": (SZ, [I, I, I]),
+        "spdec_spec_accept": (I, [P, P, I, I, I, I64, P, P, P, F, P, P, P, SZ, P]),
         "spdec_acceptance_workspace_bytes": (SZ, [I, I]),
         "spdec_acceptance": (I, [P, P, I, I, I64, F, P, P, SZ, P]),
     }
@@ -246,6 +249,46 @@ def verify_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None,
     _check(lib().spdec_verify_decode(ctypes.byref(cache.desc), _ptr(q), T, scale, _ptr(out), _ptr(lse), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream()), "spdec_verify_decode")
     return out, lse
+
+
+def spec_accept_workspace_bytes(batch: int, num_draft: int, vocab: int) -> int:
+    return int(lib().spdec_spec_accept_workspace_bytes(int(batch), int(num_draft), int(vocab)))
+
+
+def spec_accept(p_logits, q_logits, draft, u_accept, u_sample, temperature: float = 1.0, num_accepted=None,
+                next_token=None, workspace=None):
+    """Exact speculative sampling: p_logits [batch][k+1][vocab], q_logits [batch][k][vocab] fp32,
+    draft [batch][k] int32, u_accept [batch][k] / u_sample [batch] fp32 uniforms.
+    Returns (num_accepted [batch], next_token [batch]) int32."""
+    if not isinstance(p_logits, torch.Tensor) or p_logits.dim() != 3 or p_logits.dtype != torch.float32:
+        raise ValueError("p_logits must be a [batch][k+1][vocab] float32 tensor")
+    batch, k1, vocab = p_logits.shape
+    k = k1 - 1
+    if p_logits.stride(2) != 1 or p_logits.stride(0) != k1 * p_logits.stride(1):
+        raise ValueError("p_logits rows must be contiguous and evenly strided")
+    stride = p_logits.stride(1)
+    dev = p_logits.device
+    if k > 0:
+        if (not isinstance(q_logits, torch.Tensor) or q_logits.dtype != torch.float32
+                or tuple(q_logits.shape) != (batch, k, vocab)):
+            raise ValueError("q_logits must be a [batch][k][vocab] float32 tensor")
+        if q_logits.stride(2) != 1 or q_logits.stride(1) != stride or q_logits.stride(0) != k * stride:
+            raise ValueError("q_logits must share p_logits' row stride")
+        _need(draft, "draft", torch.int32, (batch, k))
+        _need(u_accept, "u_accept", torch.float32, (batch, k))
+    _need(u_sample, "u_sample", torch.float32, (batch,))
+    if num_accepted is None:
+        num_accepted = torch.empty(batch, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(batch, dtype=torch.int32, device=dev)
+    _need(num_accepted, "num_accepted", torch.int32, (batch,))
+    _need(next_token, "next_token", torch.int32, (batch,))
+    ws = _workspace(spec_accept_workspace_bytes(batch, k, vocab), dev, workspace)
+    _check(lib().spdec_spec_accept(_ptr(p_logits), _ptr(q_logits) if k > 0 else None, batch, k, vocab, stride,
+                                   _ptr(draft) if k > 0 else None, _ptr(u_accept) if k > 0 else None,
+                                   _ptr(u_sample), float(temperature), _ptr(num_accepted), _ptr(next_token),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream()), "spdec_spec_accept")
+    return num_accepted, next_token
 
 
 def acceptance_workspace_bytes(rows: int, vocab: int) -> int:

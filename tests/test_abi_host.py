@@ -26,7 +26,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 13
+    assert len(names) == len(S.ABI_FUNCTIONS) == 15
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -134,3 +134,28 @@ def test_verify_checks(L):
     assert L.spdec_verify_decode(ctypes.byref(f), FAKE, 7, 0.1, FAKE, None, FAKE, ws, None) == -2
     # more positions need more workspace
     assert L.spdec_verify_workspace_bytes(ctypes.byref(d), 8) > L.spdec_verify_workspace_bytes(ctypes.byref(d), 4)
+
+
+def test_spec_accept_checks(L):
+    ws = L.spdec_spec_accept_workspace_bytes(64, 6, 151936)
+    assert ws > 0
+    assert L.spdec_spec_accept_workspace_bytes(0, 6, 100) == 0
+    assert L.spdec_spec_accept_workspace_bytes(4, 65, 100) == 0
+    args = dict(p=FAKE, q=FAKE, B=64, k=6, V=151936, stride=151936, d=FAKE, ua=FAKE, us=FAKE, T=1.0,
+                n=FAKE, t=FAKE, ws=FAKE, nbytes=ws)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.spdec_spec_accept(a["p"], a["q"], a["B"], a["k"], a["V"], a["stride"], a["d"], a["ua"], a["us"],
+                                   a["T"], a["n"], a["t"], a["ws"], a["nbytes"], None)
+
+    assert call(T=0.0) == -1
+    assert call(stride=100) == -1
+    assert call(q=None) == -1              # drafts need the drafter's logits
+    # k = 0 needs no drafter inputs; with no workspace it is still rejected before any launch
+    assert call(q=None, d=None, ua=None, k=0, ws=None, nbytes=0) == -3
+    assert call(nbytes=ws - 1) == -3
+    assert call(k=65) == -2
+    assert call(B=70000) == -2
+    assert call(us=None) == -1
