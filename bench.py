@@ -17,8 +17,10 @@ the stream the kernels run on; `roofline` is for the dominant kernel (dense
 decode, its call run K times back to back under one event pair). `sparse`
 reports the sparse path (select + sparse decode, each of K runs after a 1 GiB
 scrub read, the scrubs' own time subtracted) against HBM peak; `graph` times
-the step captured once in a HIP graph and replayed; `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step.
+the step captured once in a HIP graph and replayed; `verify` times the dense
+verification of a 6-token draft (7 positions) and exact speculative sampling
+on the same cache; `cpu_baseline` times the CPU oracle on a bounded sample of
+the same step.
 """
 from __future__ import annotations
 
@@ -49,6 +51,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--no-verify", action="store_true", help="skip the verification / speculative-sampling rows")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -156,6 +159,68 @@ def _cpu_baseline(O, wl, steps_tokens, seconds):
             "sample": f"full step (append, select, sparse, dense, acceptance) for {n_seq} of {spec.batch} "
                       f"sequences x {spec.num_kv_heads} KV heads, fp64 NumPy, 1 thread; "
                       f"{t_total:.1f} s of CPU time"}
+
+
+VERIFY_POSITIONS = 7  # k = 6 drafted tokens plus the bonus position (S3R's measured setting)
+
+
+def speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens):
+    """Dense verification of a k = 6 draft and exact speculative sampling, on the same cache.
+
+    The last 7 cached tokens of every sequence are the verified positions; the
+    logits (64 x 7 verifier rows, 64 x 6 drafter rows of 151936) follow the
+    acceptance workload's recipe (a ~ N(0, 3), drafter = a + N(0, 0.3)), the
+    drafts are drawn from the drafter's softmax, the uniforms are seeded.
+    """
+    import torch
+    from sparse_attention_decode_page_amd import spdec
+    from sparse_attention_decode_page_amd import synth as S
+    T, k = VERIFY_POSITIONS, VERIFY_POSITIONS - 1
+    r = np.random.default_rng(args.seed + 101)
+    B, V = spec.batch, wl.logits_a.shape[1]
+    qv = up(S.f32_to_bf16_bits(r.standard_normal((B, T, spec.num_q_heads, spec.head_dim), dtype=np.float32)))
+    ws_v = torch.zeros(spdec.verify_workspace_bytes(cache, T), dtype=torch.uint8, device=dev)
+    o_v = torch.empty((B, T, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+    l_v = torch.empty((B, T, spec.num_q_heads), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        spdec.verify_decode(cache, qv, out=o_v, lse=l_v, workspace=ws_v)
+    t_v = timed_loop(lambda i: spdec.verify_decode(cache, qv, out=o_v, lse=l_v, workspace=ws_v))
+    kv_bytes = int(2 * spec.num_kv_heads * lens.sum() * spec.head_dim * 2)
+
+    p_log = (3.0 * r.standard_normal((B, T, V), dtype=np.float32))
+    q_log = (p_log[:, :k] + 0.3 * r.standard_normal((B, k, V), dtype=np.float32)).astype(np.float32)
+    draft = np.empty((B, k), dtype=np.int32)
+    for b in range(B):
+        for i in range(k):
+            x = q_log[b, i].astype(np.float64)
+            w = np.exp(x - x.max())
+            draft[b, i] = r.choice(V, p=w / w.sum())
+    ua = torch.from_numpy(r.random((B, k)).astype(np.float32)).to(dev)
+    us = torch.from_numpy(r.random(B).astype(np.float32)).to(dev)
+    pt, qt, dt = torch.from_numpy(p_log).to(dev), torch.from_numpy(q_log).to(dev), torch.from_numpy(draft).to(dev)
+    ws_s = torch.zeros(spdec.spec_accept_workspace_bytes(B, k, V), dtype=torch.uint8, device=dev)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def accept():
+        spdec.spec_accept(pt, qt, dt, ua, us, 1.0, num_accepted=n_acc, next_token=tok, workspace=ws_s)
+
+    for _ in range(3):
+        accept()
+    t_s = timed_loop(lambda i: accept())
+    kept = n_acc.cpu().numpy()
+    # bytes every call must read: all verifier and drafter rows once, plus the draw row(s) of each sequence
+    draw_rows = int(sum(2 if n < k else 1 for n in kept))
+    acc_bytes = int((B * (2 * k + 1) + draw_rows) * V * 4)
+    return {
+        "positions": T,
+        "verify_us": t_v * 1e6, "verify_bytes": kv_bytes, "verify_GBps": kv_bytes / t_v / 1e9,
+        "verify_frac_hbm": kv_bytes / t_v / 1e9 / HBM_PEAK_GBPS,
+        "verified_tokens_per_s": B * T / t_v,
+        "accept_us": t_s * 1e6, "accept_bytes": acc_bytes, "accept_GBps": acc_bytes / t_s / 1e9,
+        "mean_kept_drafts": float(kept.mean()),
+        "timing": "each call K times back to back under one event pair",
+    }
 
 
 def main():
@@ -315,6 +380,8 @@ def main():
         graph.replay()
     gr_t = timed_loop(lambda i: graph.replay())
     del graph
+    verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 2 * K_steps) \
+        if not args.no_verify else None
 
     # algorithmic bytes averaged over the steps of each region (lengths grow by one per step)
     def mean_bytes(first_step):
@@ -377,6 +444,7 @@ def main():
                    "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels),
                    "timing": "K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub, one event pair each",
                    "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6},
+        "verify": verify,
         "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
                   "timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
         "rows": rows_out,
