@@ -183,6 +183,30 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spdec_dense_decode_shared - spdec_dense_decode for groups of sequences that
+ * share their leading pages (a prompt sampled several times; the Sparrow
+ * project page's cost model, "Control Study 2", charges the prompt once per
+ * group rather than once per sample).
+ *
+ * Sequences n*N .. n*N + N - 1 (N = group_size) form group n; their page
+ * tables map logical pages 0 .. shared_pages[n] - 1 to the same physical
+ * pages, all full (device preconditions; the kernel reads those pages through
+ * the first member's page table). The result is the dense decode of every
+ * sequence up to rounding: the shared pages are read once per (group, KV
+ * head) for the group's N * G query rows, each sequence's remaining pages once,
+ * and the two partials are merged by log-sum-exp in a fixed order.
+ *
+ * q: [batch][Hq][D] bf16; shared_pages: int32 [batch / N]; out, lse as for
+ * spdec_dense_decode. Requires a bf16 cache, batch % N == 0 and N * G <= 32
+ * (SPDEC_ERR_UNSUPPORTED otherwise). Workspace:
+ * spdec_shared_workspace_bytes(cache, N), zero-filled once.
+ */
+size_t spdec_shared_workspace_bytes(const spdec_cache* cache, int group_size);
+spdec_status spdec_dense_decode_shared(const spdec_cache* cache, const void* q, int group_size,
+                                       const int32_t* shared_pages, float scale, float* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spdec_verify_decode - dense verification of a sparse draft: causal
  * multi-query attention over the complete KV (S3R page, abstract and Tables
  * 6-7: k tokens drafted with sparse attention are verified by one

@@ -160,6 +160,29 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
   return decode_common(cache, q, nullptr, nullptr, 0, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+size_t spdec_shared_workspace_bytes(const spdec_cache* cache, int group_size) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK || !spdec::shared_supported(v, group_size)) return 0;
+  return spdec::shared_workspace_bytes(v, group_size);
+}
+
+spdec_status spdec_dense_decode_shared(const spdec_cache* cache, const void* q, int group_size,
+                                       const int32_t* shared_pages, float scale, float* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.k_pool || !v.v_pool || !q || !out || !shared_pages) return SPDEC_ERR_INVALID;
+  if (!aligned16(v.k_pool) || !aligned16(v.v_pool) || !aligned16(q)) return SPDEC_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return SPDEC_ERR_INVALID;
+  if (group_size < 1 || v.batch % group_size != 0) return SPDEC_ERR_INVALID;
+  if (!spdec::shared_supported(v, group_size)) return SPDEC_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < spdec::shared_workspace_bytes(v, group_size))
+    return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_dense_shared(v, q, group_size, shared_pages, scale, out, lse, workspace,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 size_t spdec_verify_workspace_bytes(const spdec_cache* cache, int num_positions) {
   CacheView v;
   if (view_of(cache, &v) != SPDEC_OK || !spdec::verify_supported(v, num_positions)) return 0;

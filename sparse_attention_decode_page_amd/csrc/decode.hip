@@ -271,14 +271,27 @@ struct StreamArgs {
   int* count;        // [units] chunks written for the unit
   float* out;
   float* lse;
+  // Dense lists only: sequence b's list starts at logical page
+  // first_page[b / group_size] (the pages before it are attended elsewhere);
+  // null means page 0.
+  const int32_t* first_page;
+  int group_size;
 };
+
+template <bool SPARSE>
+__device__ __forceinline__ int list_first(const StreamArgs& a, int b) {
+  if constexpr (SPARSE) return 0;
+  return a.first_page != nullptr ? max(a.first_page[b / a.group_size], 0) : 0;
+}
 
 template <bool SPARSE>
 __device__ __forceinline__ int unit_entries(const StreamArgs& a, int u) {
   const CacheView& c = a.c;
   if constexpr (SPARSE) return min(max(a.sel_cnt[u], 0), a.list_cap);
-  const int L = max(c.seq_lens[u / c.hkv], 0);
-  return min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  const int b = u / c.hkv;
+  const int L = max(c.seq_lens[b], 0);
+  const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  return max(P - list_first<SPARSE>(a, b), 0);
 }
 
 // Persistent split-KV decode. The (unit, page-list entry) pairs of all
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_strea
       const int nwin = min(kWave, seg_end - ubase - wb);
       int phys_w = 0, valid_w = 0;
       if (lane < nwin) {
-        const int logical = SPARSE ? a.sel_idx[(int64_t)u * a.list_cap + wb + lane] : wb + lane;
+        const int logical = SPARSE ? a.sel_idx[(int64_t)u * a.list_cap + wb + lane] : list_first<SPARSE>(a, b) + wb + lane;
         if (logical >= 0 && logical < P) {
           const int ph = c.page_table[(int64_t)b * c.max_pages + logical];
           if (ph >= 0 && ph < c.num_phys) {
@@ -623,6 +636,19 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
   return a.c.head_dim == 64 ? decode_g<F32, 64, SPARSE>(a, s) : decode_g<F32, 128, SPARSE>(a, s);
 }
 
+// The dense stream kernel alone (partials and per-unit chunk counts, no merge).
+template <int D, int G>
+hipError_t stream_partials_impl(const StreamArgs& a, hipStream_t s) {
+  const int units = a.c.batch * a.c.hkv;
+  const size_t lds = (size_t)(units + 1) * sizeof(int);
+  int grid = 0;
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&decode_stream_kernel<D, G, false>), kDecodeThreads,
+                                 lds, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_stream_kernel<D, G, false>), dim3(grid), dim3(kDecodeThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int G, bool SPARSE>
 hipError_t stream_impl(const StreamArgs& a, hipStream_t s) {
   const int units = a.c.batch * a.c.hkv;
@@ -656,6 +682,11 @@ constexpr int kStreamWaveTarget = 8192;
 
 }  // namespace
 
+void stream_plan(int64_t units, int list_pages, int* jmax, int* rmin) {
+  *jmax = (int)std::min<int64_t>(std::max<int64_t>((kStreamWaveTarget + units - 1) / units + 2, 3), 1024);
+  *rmin = (list_pages + *jmax - 2) / (*jmax - 1);
+}
+
 DecodePlan decode_plan(const CacheView& c, int max_budget_pages) {
   DecodePlan p;
   p.list_pages = max_budget_pages > 0 ? max_budget_pages : c.max_pages;
@@ -663,8 +694,7 @@ DecodePlan decode_plan(const CacheView& c, int max_budget_pages) {
   p.stream = c.dtype == SPDEC_BF16 && units <= kMaxStreamUnits;
   // Stream plan: at most jmax partials per unit, so every wave range holds at
   // least rmin = ceil(cap / (jmax - 1)) entries.
-  p.jmax = (int)std::min<int64_t>(std::max<int64_t>((kStreamWaveTarget + units - 1) / units + 2, 3), 1024);
-  p.rmin = (p.list_pages + p.jmax - 2) / (p.jmax - 1);
+  stream_plan(units, p.list_pages, &p.jmax, &p.rmin);
   // Split plan (fp32 caches and very large batches): about 512 tokens per
   // split, fewer when the grid would leave compute units idle. The plan
   // depends only on the list capacity, so a sparse call whose capacity is
@@ -713,6 +743,8 @@ hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q,
                                      align256(slots * 2 * sizeof(float)));
     a.out = out;
     a.lse = lse;
+    a.first_page = nullptr;
+    a.group_size = 1;
     if (c.head_dim == 64) return sparse ? stream_g<64, true>(a, s) : stream_g<64, false>(a, s);
     return sparse ? stream_g<128, true>(a, s) : stream_g<128, false>(a, s);
   }
@@ -731,6 +763,34 @@ hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q,
   a.out = out;
   a.lse = lse;
   return sparse ? decode_dispatch<true>(a, s) : decode_dispatch<false>(a, s);
+}
+
+hipError_t launch_dense_stream_partials(const CacheView& c, const DecodePlan& p, const void* q,
+                                        const int32_t* first_page, int group_size, float scale, float* part_acc,
+                                        float* part_ml, int* count, hipStream_t s) {
+  StreamArgs a;
+  a.c = c;
+  a.q = q;
+  a.sel_idx = nullptr;
+  a.sel_cnt = nullptr;
+  a.list_cap = p.list_pages;
+  a.jmax = p.jmax;
+  a.rmin = p.rmin;
+  a.qk_scale = scale * kLog2e;
+  a.part_acc = part_acc;
+  a.part_ml = part_ml;
+  a.count = count;
+  a.out = nullptr;
+  a.lse = nullptr;
+  a.first_page = first_page;
+  a.group_size = group_size;
+  const int D = c.head_dim;
+  switch (c.group) {
+    case 1: return D == 64 ? stream_partials_impl<64, 1>(a, s) : stream_partials_impl<128, 1>(a, s);
+    case 2: return D == 64 ? stream_partials_impl<64, 2>(a, s) : stream_partials_impl<128, 2>(a, s);
+    case 4: return D == 64 ? stream_partials_impl<64, 4>(a, s) : stream_partials_impl<128, 4>(a, s);
+    default: return D == 64 ? stream_partials_impl<64, 8>(a, s) : stream_partials_impl<128, 8>(a, s);
+  }
 }
 
 }  // namespace spdec

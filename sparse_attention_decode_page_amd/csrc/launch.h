@@ -32,6 +32,11 @@ struct DecodePlan {
 
 DecodePlan decode_plan(const CacheView& c, int max_budget_pages);
 
+// Stream plan for `units` lists of at most `list_pages` entries: partial slots
+// per unit (jmax) and the minimum entries per wave range (rmin) that bound the
+// chunks of a unit by jmax.
+void stream_plan(int64_t units, int list_pages, int* jmax, int* rmin);
+
 // Units (sequence x KV head) up to which the persistent kernels keep the
 // per-unit prefix in LDS.
 constexpr int kMaxStreamUnits = 8192;
@@ -49,6 +54,21 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
                          int32_t* sel_idx, int32_t* sel_cnt, float* scores, void* ws, hipStream_t s);
 hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float scale, float* out, float* lse, void* ws, hipStream_t s);
+// Dense stream partials over each sequence's pages from first_page[b / group_size]
+// on (the shared-prefix decode's suffix pass); no merge.
+hipError_t launch_dense_stream_partials(const CacheView& c, const DecodePlan& p, const void* q,
+                                        const int32_t* first_page, int group_size, float scale, float* part_acc,
+                                        float* part_ml, int* count, hipStream_t s);
+// Multi-row partials over the pages a group of group_size sequences shares
+// (shared_pages[n] leading pages of group n, read once for the group's
+// group_size * G query rows); no merge.
+hipError_t launch_prefix_partials(const CacheView& c, const void* q, int group_size, const int32_t* shared_pages,
+                                  int jmax, int rmin, float scale, float* part_acc, float* part_ml, int* count,
+                                  hipStream_t s);
+bool shared_supported(const CacheView& c, int group_size);
+size_t shared_workspace_bytes(const CacheView& c, int group_size);
+hipError_t launch_dense_shared(const CacheView& c, const void* q, int group_size, const int32_t* shared_pages,
+                               float scale, float* out, float* lse, void* ws, hipStream_t s);
 bool verify_supported(const CacheView& c, int T);
 size_t verify_workspace_bytes(const CacheView& c, int T);
 hipError_t launch_verify(const CacheView& c, const void* q, int T, float scale, float* out, float* lse, void* ws,

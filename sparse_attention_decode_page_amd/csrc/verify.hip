@@ -23,6 +23,8 @@
 // tile exceeds it by 2^8. The (unit, page) pairs are streamed persistently
 // exactly like the single-query dense decode; partials are merged per output
 // row by a second kernel, chunks in index order.
+#include <limits.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -67,9 +69,10 @@ __device__ __forceinline__ uint32_t vchunk_half(const C& v, int i) {
 
 struct VerifyArgs {
   CacheView c;
-  const void* q;     // [B][T][Hq][D]
-  int T;             // verified positions per sequence
-  int rows;          // G * T query rows per (sequence, KV head)
+  const void* q;     // verify: [B][T][Hq][D]; shared prefix: [B][Hq][D]
+  int T;             // verify: positions per sequence; shared prefix: sequences per group
+  const int32_t* shared;  // shared prefix: leading pages of each group (read once for the group)
+  int rows;          // G * T query rows per unit
   int jmax, rmin;    // stream plan of the dense decode
   float qk_scale;    // softmax scale * log2(e)
   float* part_acc;   // [units][jmax][rows][D]
@@ -81,7 +84,13 @@ struct VerifyArgs {
 
 // Two waves per SIMD: with the query rows parked in LDS the 32-row form fits
 // the 256 registers that occupancy needs.
-template <int D, int NSETS>
+//
+// PREFIX = true is the same stream over the pages a group of T consecutive
+// sequences shares (their prompt): a unit is (group, KV head), its list is the
+// group's shared pages (page table and lengths of the group's first
+// sequence), and its query rows are the G heads of each of the T members,
+// with no causal limit. Each shared page is then read once for the group.
+template <int D, int NSETS, bool PREFIX>
 __global__ __launch_bounds__(kVerifyThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void verify_stream_kernel(VerifyArgs a) {
   constexpr int NJ = D / 32;        // q.K^T MFMA steps (16x16x32)
@@ -92,10 +101,12 @@ void verify_stream_kernel(VerifyArgs a) {
   extern __shared__ int s_pre[];    // units + 1
   __shared__ int s_tmp[kVerifyWaves];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[kVerifyWaves][16 * NSETS * D];  // query rows per wave
-  const int units = c.batch * c.hkv;
+  const int units = (PREFIX ? c.batch / a.T : c.batch) * c.hkv;
   for (int u = threadIdx.x; u < units; u += kVerifyThreads) {
-    const int L = max(c.seq_lens[u / c.hkv], 0);
-    s_pre[u] = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+    const int b = PREFIX ? (u / c.hkv) * a.T : u / c.hkv;
+    const int L = max(c.seq_lens[b], 0);
+    const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+    s_pre[u] = PREFIX ? min(max(a.shared[u / c.hkv], 0), P) : P;
   }
   __syncthreads();
   block_exclusive_scan(s_pre, units, s_tmp);
@@ -119,7 +130,8 @@ void verify_stream_kernel(VerifyArgs a) {
   uint16_t* qs = s_q[wave];
 
   while (pos < end) {
-    const int b = u / c.hkv, g = u % c.hkv;
+    const int b = PREFIX ? (u / c.hkv) * a.T : u / c.hkv;  // sequence whose page table the list follows
+    const int g = u % c.hkv;
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);
     const int j = (int)(w - ubase / R);  // this wave's chunk of the unit
@@ -139,8 +151,13 @@ void verify_stream_kernel(VerifyArgs a) {
       const uint16_t* src = qp;
       if (row < a.rows) {
         const int t = row / G, h = row % G;
-        lim[st] = L - a.T + t;
-        src = qp + (((int64_t)b * a.T + t) * c.hq + g * G + h) * D + 8 * q4;
+        if constexpr (PREFIX) {  // member t of the group; the shared pages precede every query
+          lim[st] = INT_MAX;
+          src = qp + ((int64_t)(b + t) * c.hq + g * G + h) * D + 8 * q4;
+        } else {
+          lim[st] = L - a.T + t;
+          src = qp + (((int64_t)b * a.T + t) * c.hq + g * G + h) * D + 8 * q4;
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
@@ -375,16 +392,21 @@ __global__ __launch_bounds__(kWave) void verify_merge_kernel(VerifyArgs a) {
   if (a.lse != nullptr && lane == 0) a.lse[orow] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
-template <int D, int NSETS>
-hipError_t verify_impl(const VerifyArgs& a, hipStream_t s) {
-  const int units = a.c.batch * a.c.hkv;
+template <int D, int NSETS, bool PREFIX>
+hipError_t stream_launch(const VerifyArgs& a, hipStream_t s) {
+  const int units = (PREFIX ? a.c.batch / a.T : a.c.batch) * a.c.hkv;
   const size_t lds = (size_t)(units + 1) * sizeof(int);
   int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&verify_stream_kernel<D, NSETS>), kVerifyThreads,
-                                 lds, &grid);
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&verify_stream_kernel<D, NSETS, PREFIX>),
+                                 kVerifyThreads, lds, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_stream_kernel<D, NSETS>), dim3(grid), dim3(kVerifyThreads), lds, s, a);
-  e = hipGetLastError();
+  hipLaunchKernelGGL((verify_stream_kernel<D, NSETS, PREFIX>), dim3(grid), dim3(kVerifyThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int NSETS>
+hipError_t verify_impl(const VerifyArgs& a, hipStream_t s) {
+  hipError_t e = stream_launch<D, NSETS, false>(a, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(a.c.batch * a.T * a.c.hq), dim3(kWave), 0, s, a);
   return hipGetLastError();
@@ -413,6 +435,7 @@ hipError_t launch_verify(const CacheView& c, const void* q, int T, float scale, 
   a.c = c;
   a.q = q;
   a.T = T;
+  a.shared = nullptr;
   a.rows = c.group * T;
   a.jmax = p.jmax;
   a.rmin = p.rmin;
@@ -428,6 +451,28 @@ hipError_t launch_verify(const CacheView& c, const void* q, int T, float scale, 
   const bool two = a.rows > 16;
   if (c.head_dim == 64) return two ? verify_impl<64, 2>(a, s) : verify_impl<64, 1>(a, s);
   return two ? verify_impl<128, 2>(a, s) : verify_impl<128, 1>(a, s);
+}
+
+hipError_t launch_prefix_partials(const CacheView& c, const void* q, int group_size, const int32_t* shared_pages,
+                                  int jmax, int rmin, float scale, float* part_acc, float* part_ml, int* count,
+                                  hipStream_t s) {
+  VerifyArgs a;
+  a.c = c;
+  a.q = q;
+  a.T = group_size;
+  a.shared = shared_pages;
+  a.rows = c.group * group_size;
+  a.jmax = jmax;
+  a.rmin = rmin;
+  a.qk_scale = scale * kLog2e;
+  a.part_acc = part_acc;
+  a.part_ml = part_ml;
+  a.count = count;
+  a.out = nullptr;
+  a.lse = nullptr;
+  const bool two = a.rows > 16;
+  if (c.head_dim == 64) return two ? stream_launch<64, 2, true>(a, s) : stream_launch<64, 1, true>(a, s);
+  return two ? stream_launch<128, 2, true>(a, s) : stream_launch<128, 1, true>(a, s);
 }
 
 }  // namespace spdec

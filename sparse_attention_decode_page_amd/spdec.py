@@ -23,7 +23,8 @@ SPDEC_F32, SPDEC_BF16 = 0, 1
 ABI_FUNCTIONS = (
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
     "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_decode_workspace_bytes",
-    "spdec_sparse_decode", "spdec_dense_decode", "spdec_verify_workspace_bytes", "spdec_verify_decode",
+    "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
+    "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
     "spdec_acceptance",
 )
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
         "spdec_decode_workspace_bytes": (SZ, [D, I]),
         "spdec_sparse_decode": (I, [D, P, P, P, I, F, P, P, P, SZ, P]),
         "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
+        "spdec_shared_workspace_bytes": (SZ, [D, I]),
+        "spdec_dense_decode_shared": (I, [D, P, I, P, F, P, P, P, SZ, P]),
         "spdec_verify_workspace_bytes": (SZ, [D, I]),
         "spdec_verify_decode": (I, [D, P, I, F, P, P, P, SZ, P]),
         "spdec_spec_accept_workspace_bytes": (SZ, [I, I, I]),
@@ -224,6 +227,26 @@ def dense_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None, 
     ws = _workspace(decode_workspace_bytes(cache, 0), cache.device, workspace)
     _check(lib().spdec_dense_decode(ctypes.byref(cache.desc), _ptr(q), scale, _ptr(out), _ptr(lse), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream()), "spdec_dense_decode")
+    return out, lse
+
+
+def shared_workspace_bytes(cache: PagedCache, group_size: int) -> int:
+    return int(lib().spdec_shared_workspace_bytes(ctypes.byref(cache.desc), int(group_size)))
+
+
+def dense_decode_shared(cache: PagedCache, q, group_size: int, shared_pages, scale: Optional[float] = None,
+                        out=None, lse=None, workspace=None):
+    """Dense decode where groups of group_size consecutive sequences share shared_pages[n] leading pages."""
+    _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    if cache.batch % int(group_size) != 0:
+        raise ValueError("batch must be a multiple of group_size")
+    _need(shared_pages, "shared_pages", torch.int32, (cache.batch // int(group_size),))
+    out, lse = _outs(cache, out, lse)
+    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    ws = _workspace(shared_workspace_bytes(cache, group_size), cache.device, workspace)
+    _check(lib().spdec_dense_decode_shared(ctypes.byref(cache.desc), _ptr(q), int(group_size), _ptr(shared_pages),
+                                           scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream()), "spdec_dense_decode_shared")
     return out, lse
 
 

@@ -35,6 +35,10 @@ Recipe
 * Physical placement: every sequence owns ``ceil((L+headroom)/ps)`` logical
   pages that map to a seeded random permutation of the physical pages, so
   gathers are never contiguous. Unused page-table entries are -1.
+* Grouped prompts (the shared-prefix workload): 8 consecutive sequences form a
+  group that shares a 16384-token prompt drawn once per (group, KV head) from
+  its own streams; each sample then has 1024-4096 generated tokens of its own.
+  Full prompt pages are the same physical pages in every member's page table.
 * Slots of the pool that hold no token (the tail of a partial last page and
   headroom pages) are filled with a poison value (1000.0) so that a kernel
   that forgets to mask them produces visibly wrong results.
@@ -54,7 +58,7 @@ import numpy as np
 
 # Stream tags (spawn keys); fixed so a stream never depends on another's draws.
 _T_Q, _T_K, _T_V, _T_OUTLIER, _T_PLANT, _T_LENS, _T_PERM = 1, 2, 3, 4, 5, 6, 7
-_T_LOGIT_A, _T_NOISE, _T_HEAVY, _T_APPEND = 8, 9, 10, 11
+_T_LOGIT_A, _T_NOISE, _T_HEAVY, _T_APPEND, _T_PROMPT = 8, 9, 10, 11, 12
 
 POISON = 1000.0
 
@@ -91,6 +95,7 @@ class Spec:
     planted_block: int = 0
     logits: Optional[tuple] = None  # ("independent", rows, vocab, sigma) / ("noisy", rows, vocab, sa, sn, frac_heavy, s_heavy)
     temperature: float = 1.0
+    prompt: Optional[tuple] = None  # ("shared", group_size, prompt_tokens): groups of consecutive sequences share a prompt
 
     @property
     def group(self) -> int:
@@ -109,6 +114,10 @@ def _specs() -> dict:
     for ps in (8, 16, 32, 64):
         s[f"long-131k-ps{ps}"] = Spec(f"long-131k-ps{ps}", 4, 32, 8, 128, ps, "bf16", ("fixed", 131072),
                                       ("tokens", 4096), planted_block=64)
+    # GRPO-style groups: 8 prompts x 8 samples, each sample = the group's 16K-token prompt + its own
+    # 1K-4K generated tokens (shared prompt pages are the same physical pages)
+    s["qwen3-8b-grouped"] = Spec("qwen3-8b-grouped", 64, 32, 8, 128, 16, "bf16", ("uniform", 1024, 4096),
+                                 ("tokens", 2048), outlier_channels=4, prompt=("shared", 8, 16384))
     s["qwen3-8b-L32k-acceptance"] = Spec("qwen3-8b-L32k-acceptance", 64, 32, 8, 128, 16, "bf16",
                                          ("fixed", 32768), ("tokens", 4096), outlier_channels=4,
                                          logits=("noisy", 64, 151936, 3.0, 0.3, 0.05, 3.0))
@@ -143,6 +152,7 @@ class Workload:
     logits_a: Optional[np.ndarray] = None  # float32 [R][V]
     logits_b: Optional[np.ndarray] = None
     heavy_rows: Optional[np.ndarray] = None
+    shared_pages: Optional[np.ndarray] = None  # int32 [batch / group_size]: leading pages a group shares
 
     @property
     def storage_dtype(self):
@@ -192,16 +202,35 @@ def make_workload(spec, seed: int = 0, headroom: int = 0, build_pool: bool = Tru
         spec = SPECS[spec]
     B, Hq, Hkv, D, ps = spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size
     lens = _lens(spec, seed)
+    shared = np.zeros(0, dtype=np.int32)
+    if spec.prompt is not None:  # lens are the generated parts; every sequence starts with its group's prompt
+        _, N, prompt = spec.prompt
+        assert B % N == 0
+        lens = (lens.astype(np.int64) + prompt).astype(np.int32)
+        shared = np.full(B // N, prompt // ps, dtype=np.int32)  # only full pages are shared
     bpages = (budget_tokens(spec, lens) // ps).astype(np.int32)
     caps = (lens.astype(np.int64) + headroom + ps - 1) // ps
     max_pages = int(caps.max())
-    num_phys = int(caps.sum())
+    own = caps.copy()
+    if spec.prompt is not None:
+        own -= np.repeat(shared, spec.prompt[1])
+    num_phys = int(own.sum() + shared.sum())
     perm = _rng(seed, _T_PERM).permutation(num_phys).astype(np.int32)
     page_table = np.full((B, max_pages), -1, dtype=np.int32)
     off = 0
     for b in range(B):
-        page_table[b, :caps[b]] = perm[off:off + caps[b]]
-        off += int(caps[b])
+        first = 0
+        if spec.prompt is not None:
+            N = spec.prompt[1]
+            n = b // N
+            first = int(shared[n])
+            if b % N == 0:  # the group's shared pages, allocated once
+                page_table[b, :first] = perm[off:off + first]
+                off += first
+            else:
+                page_table[b, :first] = page_table[n * N, :first]
+        page_table[b, first:caps[b]] = perm[off:off + int(caps[b]) - first]
+        off += int(caps[b]) - first
     q32 = _rng(seed, _T_Q).standard_normal((B, Hq, D), dtype=np.float32)
     q = _to_storage(q32, spec.dtype)
     if spec.outlier_channels:
@@ -216,6 +245,8 @@ def make_workload(spec, seed: int = 0, headroom: int = 0, build_pool: bool = Tru
             for g in range(Hkv):
                 plant[b, g] = prng.integers(64, int(lens[b]) - 128, endpoint=True)
     wl = Workload(spec, seed, lens, bpages, max_pages, num_phys, page_table, q, outliers, plant)
+    if spec.prompt is not None:
+        wl.shared_pages = shared
     if build_pool:
         build_pools(wl, threads=threads)
     if spec.logits is not None:
@@ -234,6 +265,12 @@ def unit_tokens(wl: Workload, b: int, g: int, n: Optional[int] = None):
     D = spec.head_dim
     k32 = _rng(wl.seed, _T_K, b, g).standard_normal((n, D), dtype=np.float32)
     v32 = _rng(wl.seed, _T_V, b, g).standard_normal((n, D), dtype=np.float32)
+    if spec.prompt is not None:  # the group's prompt tokens come from the group's own streams
+        _, N, prompt = spec.prompt
+        m = min(prompt, n)
+        grp = b // N
+        k32[:m] = _rng(wl.seed, _T_PROMPT, _T_K, grp, g).standard_normal((m, D), dtype=np.float32)
+        v32[:m] = _rng(wl.seed, _T_PROMPT, _T_V, grp, g).standard_normal((m, D), dtype=np.float32)
     if spec.outlier_channels:
         k32[:, wl.outliers[g]] *= np.float32(spec.outlier_scale)
     if spec.planted_block and wl.plant_start[b, g] >= 0:

@@ -11,6 +11,20 @@ from sparse_attention_decode_page_amd import spdec as S
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# These checks pass fake device addresses that a rejected call never touches;
+# where a GPU is visible a wrong expectation could let one reach a kernel, so
+# the module only runs on hosts without one.
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only checks with fake device addresses")
+
+
 @pytest.fixture(scope="module")
 def L():
     if not os.path.exists(S.LIB_PATH):
@@ -26,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 15
+    assert len(names) == len(S.ABI_FUNCTIONS) == 17
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -159,3 +173,19 @@ def test_spec_accept_checks(L):
     assert call(k=65) == -2
     assert call(B=70000) == -2
     assert call(us=None) == -1
+
+
+def test_shared_prefix_checks(L):
+    d = _desc(batch=4)  # bf16, G = 4
+    ws = L.spdec_shared_workspace_bytes(ctypes.byref(d), 2)
+    assert ws > 0
+    assert L.spdec_shared_workspace_bytes(ctypes.byref(d), 3) == 0            # batch % N != 0
+    assert L.spdec_shared_workspace_bytes(ctypes.byref(d), 16) == 0           # N * G > 32
+    assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 3, FAKE, 0.1, FAKE, None, FAKE, ws, None) == -1
+    assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 0, FAKE, 0.1, FAKE, None, FAKE, ws, None) == -1
+    assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 2, None, 0.1, FAKE, None, FAKE, ws, None) == -1
+    assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 4, FAKE, 0.1, FAKE, None, FAKE, 0, None) == -3
+    assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 2, FAKE, 0.1, FAKE, None, FAKE, ws - 1, None) == -3
+    assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 2, FAKE, float("inf"), FAKE, None, FAKE, ws, None) == -1
+    f = _desc(batch=4, dtype=S.SPDEC_F32)
+    assert L.spdec_dense_decode_shared(ctypes.byref(f), FAKE, 2, FAKE, 0.1, FAKE, None, FAKE, ws, None) == -2

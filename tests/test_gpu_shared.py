@@ -1,0 +1,107 @@
+"""GPU parity of the shared-prefix dense decode (spdec_dense_decode_shared).
+
+Groups of N consecutive sequences share their prompt pages; the result must
+be the dense decode of every sequence: within 1e-2 max-abs of the fp64 oracle
+(bf16 KV) on every unit, and close to the per-sequence dense decode.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_decode_page_amd import spdec
+from sparse_attention_decode_page_amd import synth as S
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import gpu_support as GS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(spdec.LIB_PATH):
+        from sparse_attention_decode_page_amd import build
+        build.build()
+    spdec.lib()
+    assert torch.cuda.is_available()
+
+
+def _check(wl, shared, N, units):
+    spec = wl.spec
+    print(f"shared {spec.name}: N={N} G={spec.group} D={spec.head_dim} ps={spec.page_size} "
+          f"shared pages {shared.tolist()[:4]}", flush=True)
+    dw = GS.DeviceWorkload(wl)
+    sh = torch.from_numpy(shared.astype(np.int32)).cuda()
+    out, lse = spdec.dense_decode_shared(dw.cache, dw.q, N, sh)
+    od, ld = spdec.dense_decode(dw.cache, dw.q)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(out_h)) and np.all(np.isfinite(lse_h))
+    assert (out - od).abs().max().item() < TOL and (lse - ld).abs().max().item() < TOL
+    G = spec.group
+    scale = 1.0 / math.sqrt(spec.head_dim)
+    worst = [0.0, 0.0]
+    for (b, g) in units:
+        K, V = GS.unit_kv_f64(wl, b, g)
+        o, l = O.dense_decode_unit(GS.q_group_f64(wl, b, g), K, V, spec.page_size, scale)
+        e = np.abs(out_h[b, g * G:(g + 1) * G] - o).max()
+        el = np.abs(lse_h[b, g * G:(g + 1) * G] - l).max()
+        worst = [max(worst[0], e), max(worst[1], el)]
+        assert e <= TOL and el <= TOL, (b, g, e, el)
+    print(f"  {len(units)} units, worst out {worst[0]:.2e} lse {worst[1]:.2e}", flush=True)
+    return out, lse, dw, sh
+
+
+CASES = [
+    # (batch, Hq, Hkv, D, ps, gen lens, N, prompt tokens)
+    (8, 8, 2, 128, 16, ("uniform", 10, 300), 4, 200),     # prompt ends mid-page
+    (6, 4, 2, 64, 8, ("uniform", 1, 90), 3, 96),          # page size 8, prompt on a page boundary
+    (8, 16, 2, 128, 32, ("uniform", 40, 400), 4, 500),    # group 8: 32 rows per group unit
+    (4, 4, 4, 128, 64, ("uniform", 5, 200), 2, 700),      # one query head per KV head
+    (4, 8, 2, 128, 16, ("uniform", 50, 60), 1, 320),      # groups of one
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_shared_prefix_all_units(case):
+    B, Hq, Hkv, D, ps, gen, N, prompt = CASES[case]
+    spec = S.custom_spec(f"shared{case}", batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                         dtype="bf16", lens=gen, budget=("tokens", 64), outlier_channels=2,
+                         prompt=("shared", N, prompt))
+    wl = S.make_workload(spec, seed=case)
+    _check(wl, wl.shared_pages, N, [(b, g) for b in range(B) for g in range(Hkv)])
+
+
+def test_fewer_shared_pages_than_possible_and_none():
+    spec = S.custom_spec("shared-partial", batch=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("uniform", 30, 200), budget=("tokens", 64), prompt=("shared", 4, 400))
+    wl = S.make_workload(spec, seed=11)
+    units = [(b, g) for b in range(8) for g in range(2)]
+    # any count up to the truly shared pages is a valid split, including none
+    _check(wl, np.array([7, 0], dtype=np.int32), 4, units)
+    _check(wl, np.zeros(2, dtype=np.int32), 4, units)
+
+
+def test_shared_prefix_is_deterministic():
+    spec = S.custom_spec("shared-det", batch=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("uniform", 100, 900), budget=("tokens", 64), prompt=("shared", 4, 3000))
+    wl = S.make_workload(spec, seed=12)
+    dw = GS.DeviceWorkload(wl)
+    sh = torch.from_numpy(wl.shared_pages).cuda()
+    a = spdec.dense_decode_shared(dw.cache, dw.q, 4, sh)
+    b = spdec.dense_decode_shared(dw.cache, dw.q, 4, sh)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_shared_prefix_qwen3_8b_grouped_sampled():
+    wl = S.make_workload("qwen3-8b-grouped", seed=0)
+    _check(wl, wl.shared_pages, wl.spec.prompt[1], GS.sample_units(wl, 8, seed=5))
