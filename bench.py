@@ -19,8 +19,9 @@ reports the sparse path (select + sparse decode, each of K runs after a 1 GiB
 scrub read, the scrubs' own time subtracted) against HBM peak; `graph` times
 the step captured once in a HIP graph and replayed; `verify` times the dense
 verification of a 6-token draft (7 positions) and exact speculative sampling
-on the same cache; `cpu_baseline` times the CPU oracle on a bounded sample of
-the same step.
+on the same cache; `shared_prefix` times the dense decode of a grouped batch
+(8 prompts x 8 samples) per sequence and with shared prompt pages read once;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -52,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle sample")
     ap.add_argument("--no-verify", action="store_true", help="skip the verification / speculative-sampling rows")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix (grouped prompts) rows")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -223,6 +225,50 @@ def speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens):
     }
 
 
+def shared_prefix_rows(args, dev, timed_loop):
+    """Dense decode of a grouped batch (8 prompts x 8 samples, 16K-token shared prompts), per sequence and with
+    the shared prompt pages read once per group."""
+    import torch
+    from sparse_attention_decode_page_amd import spdec
+    from sparse_attention_decode_page_amd import synth as S
+    wl = S.make_workload("qwen3-8b-grouped", seed=args.seed)
+    spec = wl.spec
+    N = spec.prompt[1]
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kmm = torch.zeros((wl.num_phys, spec.num_kv_heads, 2, spec.head_dim), dtype=torch.bfloat16, device=dev)
+    cache = spdec.PagedCache(up(wl.k_pool), up(wl.v_pool), kmm, torch.from_numpy(wl.page_table).to(dev),
+                             torch.from_numpy(wl.lens.astype(np.int32)).to(dev), spec.num_q_heads)
+    q = up(wl.q)
+    sh = torch.from_numpy(wl.shared_pages).to(dev)
+    ws_d = torch.zeros(spdec.decode_workspace_bytes(cache, 0), dtype=torch.uint8, device=dev)
+    ws_s = torch.zeros(spdec.shared_workspace_bytes(cache, N), dtype=torch.uint8, device=dev)
+    o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        spdec.dense_decode(cache, q, out=o, lse=lse, workspace=ws_d)
+        spdec.dense_decode_shared(cache, q, N, sh, out=o, lse=lse, workspace=ws_s)
+    t_d = timed_loop(lambda i: spdec.dense_decode(cache, q, out=o, lse=lse, workspace=ws_d))
+    t_s = timed_loop(lambda i: spdec.dense_decode_shared(cache, q, N, sh, out=o, lse=lse, workspace=ws_s))
+    L = wl.lens.astype(np.int64)
+    per_tok = 2 * spec.num_kv_heads * spec.head_dim * 2
+    shared_tokens = int(wl.shared_pages.sum()) * spec.page_size
+    bytes_dense = int(L.sum() * per_tok)
+    bytes_shared = int((L.sum() - (N - 1) * shared_tokens) * per_tok)
+    del cache, kmm, q, ws_d, ws_s
+    torch.cuda.empty_cache()
+    return {
+        "workload": spec.name, "groups": spec.batch // N, "group_size": N, "prompt_tokens": spec.prompt[2],
+        "dense_us": t_d * 1e6, "dense_bytes": bytes_dense, "dense_GBps": bytes_dense / t_d / 1e9,
+        "shared_us": t_s * 1e6, "shared_bytes": bytes_shared, "shared_GBps": bytes_shared / t_s / 1e9,
+        "shared_frac_hbm": bytes_shared / t_s / 1e9 / HBM_PEAK_GBPS, "speedup": t_d / t_s,
+        "tokens_per_s": spec.batch / t_s,
+        "timing": "each call K times back to back under one event pair",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -382,6 +428,7 @@ def main():
     del graph
     verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 2 * K_steps) \
         if not args.no_verify else None
+    shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
 
     # algorithmic bytes averaged over the steps of each region (lengths grow by one per step)
     def mean_bytes(first_step):
@@ -445,6 +492,7 @@ def main():
                    "timing": "K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub, one event pair each",
                    "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6},
         "verify": verify,
+        "shared_prefix": shared,
         "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
                   "timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
         "rows": rows_out,
