@@ -32,6 +32,7 @@ namespace {
 constexpr int kSpecThreads = 256;
 constexpr int kSpecPer = 32;                          // entries per thread and chunk
 constexpr int kSpecChunk = kSpecThreads * kSpecPer;   // 8192
+constexpr int kSpecMaxDraft = 64;
 
 struct SpecArgs {
   const float* p;        // verifier logits, row (b, i) at p + (b * (k + 1) + i) * stride
@@ -136,44 +137,57 @@ __global__ __launch_bounds__(kSpecThreads) void spec_stats_kernel(SpecArgs a) {
   }
 }
 
-// Row normaliser (max, sum) from the chunk partials; lane-parallel, fixed order.
-__device__ __forceinline__ void fold_row(const SpecArgs& a, int row, float& M, float& Z) {
-  const float* pr = a.part + (int64_t)row * a.nchunk * 2;
-  float m = -INFINITY;
-  for (int j = threadIdx.x; j < a.nchunk; j += kWave) m = fmaxf(m, pr[2 * j]);
-  m = group_max<kWave>(m);
-  float s = 0.f;
-  for (int j = threadIdx.x; j < a.nchunk; j += kWave) s += exp2f(pr[2 * j] - m) * pr[2 * j + 1];
-  M = m;
-  Z = group_sum<kWave>(s);
-}
-
+// One wave per sequence. Every row's normaliser is folded at once (eight
+// lanes per row, eight rows per pass) and the logits at the drafted tokens
+// are fetched up front, so the accept chain itself is a short scan over
+// values already on chip.
 __global__ __launch_bounds__(kWave) void spec_decide_kernel(SpecArgs a) {
+  __shared__ float s_M[2 * kSpecMaxDraft + 1], s_Z[2 * kSpecMaxDraft + 1];
+  __shared__ float s_lp[kSpecMaxDraft], s_lq[kSpecMaxDraft];
   const int b = blockIdx.x;
-  int kept = a.k;
-  float Mp, Zp, Mq = 0.f, Zq = 1.f;
-  for (int i = 0; i < a.k; ++i) {
-    const int prow = b * (a.k + 1) + i;
-    const int qrow = a.batch * (a.k + 1) + b * a.k + i;
-    fold_row(a, prow, Mp, Zp);
-    fold_row(a, qrow, Mq, Zq);
-    const int x = min(max(a.draft[b * a.k + i], 0), a.vocab - 1);
-    const float px = exp2f(row_ptr(a, prow)[x] * a.c - Mp) / Zp;
-    const float qx = exp2f(row_ptr(a, qrow)[x] * a.c - Mq) / Zq;
-    if (!(a.u_accept[b * a.k + i] * qx < px)) {
-      kept = i;
-      break;
-    }
+  const int lane = threadIdx.x;
+  const int k = a.k;
+  const int nrows = 2 * k + 1;  // rows 0..k: verifier rows of b; k+1..2k: drafter rows of b
+  auto global_row = [&](int r) { return r <= k ? b * (k + 1) + r : a.batch * (k + 1) + b * k + (r - k - 1); };
+  // Logits at the drafts (lanes 0..k-1: verifier, lanes 32..32+k-1: drafter).
+  for (int i = lane % 32; i < k; i += 32) {
+    const int x = min(max(a.draft[b * k + i], 0), a.vocab - 1);
+    const int r = lane < 32 ? i : k + 1 + i;
+    const float v = row_ptr(a, global_row(r))[x];
+    if (lane < 32) s_lp[i] = v; else s_lq[i] = v;
   }
-  if (kept == a.k) fold_row(a, b * (a.k + 1) + a.k, Mp, Zp);
-  if (threadIdx.x == 0) {
+  // Row normalisers.
+  const int sub = lane % 8;
+  for (int base = 0; base < nrows; base += 8) {
+    const int r = base + lane / 8;
+    float m = -INFINITY, z = 0.f;
+    if (r < nrows) {
+      const float* pr = a.part + (int64_t)global_row(r) * a.nchunk * 2;
+      for (int j = sub; j < a.nchunk; j += 8) m = fmaxf(m, pr[2 * j]);
+    }
+    m = group_max<8>(m);
+    if (r < nrows) {
+      const float* pr = a.part + (int64_t)global_row(r) * a.nchunk * 2;
+      for (int j = sub; j < a.nchunk; j += 8) z += exp2f(pr[2 * j] - m) * pr[2 * j + 1];
+    }
+    z = group_sum<8>(z);
+    if (r < nrows && sub == 0) { s_M[r] = m; s_Z[r] = z; }
+  }
+  __syncthreads();
+  int kept = k;
+  for (int i = 0; i < k; ++i) {
+    const float px = exp2f(s_lp[i] * a.c - s_M[i]) / s_Z[i];
+    const float qx = exp2f(s_lq[i] * a.c - s_M[k + 1 + i]) / s_Z[k + 1 + i];
+    if (!(a.u_accept[b * k + i] * qx < px)) { kept = i; break; }
+  }
+  if (lane == 0) {
     a.n_accepted[b] = kept;
-    a.draw_row[2 * b + 0] = b * (a.k + 1) + kept;
-    a.draw_row[2 * b + 1] = kept < a.k ? a.batch * (a.k + 1) + b * a.k + kept : -1;
-    a.draw[4 * b + 0] = Mp;
-    a.draw[4 * b + 1] = 1.f / Zp;
-    a.draw[4 * b + 2] = Mq;
-    a.draw[4 * b + 3] = 1.f / Zq;
+    a.draw_row[2 * b + 0] = global_row(kept);
+    a.draw_row[2 * b + 1] = kept < k ? global_row(k + 1 + kept) : -1;
+    a.draw[4 * b + 0] = s_M[kept];
+    a.draw[4 * b + 1] = 1.f / s_Z[kept];
+    a.draw[4 * b + 2] = kept < k ? s_M[k + 1 + kept] : 0.f;
+    a.draw[4 * b + 3] = kept < k ? 1.f / s_Z[k + 1 + kept] : 1.f;
   }
 }
 
@@ -209,70 +223,107 @@ __global__ __launch_bounds__(kSpecThreads) void spec_chunk_kernel(SpecArgs a) {
   if (threadIdx.x == 0) a.csum[(int64_t)b * a.nchunk + ch] = s;
 }
 
+// Inclusive scan over the block in thread order (wave scans, then the wave
+// totals in order): the same fixed order on every run.
+__device__ __forceinline__ float block_incl_scan(float x, float* s_tot) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) s_tot[wave] = x;
+  __syncthreads();
+  float base = 0.f;
+  for (int w = 0; w < wave; ++w) base += s_tot[w];
+  return base + x;
+}
+
+// One workgroup per sequence: the chunk holding the draw (wave 0 scans the
+// chunk sums in order), then the chunk's weights staged through LDS so each
+// thread owns 32 consecutive tokens, a block scan in token order, and the
+// first token whose running sum passes the target.
 __global__ __launch_bounds__(kSpecThreads) void spec_sample_kernel(SpecArgs a) {
-  __shared__ float s_run[kSpecThreads];
-  __shared__ int s_pick[2];
+  __shared__ float s_w[kSpecChunk];
+  __shared__ float s_tot[kSpecThreads / kWave];
+  __shared__ float s_before, s_target;
+  __shared__ int s_pick, s_res[2];
   const int b = blockIdx.x;
+  const int lane = threadIdx.x % kWave;
   const float* cs = a.csum + (int64_t)b * a.nchunk;
-  if (threadIdx.x == 0) {
-    // Running sums in chunk order (the same order the scan below continues).
-    float total = 0.f;
-    for (int j = 0; j < a.nchunk; ++j) total += cs[j];
+  if (threadIdx.x < kWave) {
+    float total = 0.f;  // chunk sums in order (lane-strided partial sums folded in lane order)
+    for (int j0 = 0; j0 < a.nchunk; j0 += kWave) {
+      float v = j0 + lane < a.nchunk ? cs[j0 + lane] : 0.f;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_up(v, off);
+        if (lane >= off) v += y;
+      }
+      total += __shfl(v, kWave - 1);
+    }
     const float target = a.u_sample[b] * total;
-    float run = 0.f;
     int pick = -1, last = -1;
-    float before = 0.f;
-    for (int j = 0; j < a.nchunk; ++j) {
-      if (cs[j] > 0.f) last = j;
-      if (pick < 0 && run + cs[j] > target && cs[j] > 0.f) { pick = j; before = run; }
-      run += cs[j];
+    float before = 0.f, run = 0.f;
+    for (int j0 = 0; j0 < a.nchunk && pick < 0; j0 += kWave) {
+      const float c = j0 + lane < a.nchunk ? cs[j0 + lane] : 0.f;
+      float incl = c;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const uint64_t hit = __ballot(c > 0.f && run + incl > target);
+      const uint64_t pos = __ballot(c > 0.f);
+      if (pos) last = j0 + 63 - __clzll((long long)pos);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        pick = j0 + l;
+        before = run + __shfl(incl - c, l);
+      }
+      run += __shfl(incl, kWave - 1);
     }
-    if (pick < 0) {  // rounding left the target at or past the total: the last token with weight
-      pick = last;
-      before = -1.f;  // marks "take the last positive entry"
+    if (lane == 0) {
+      s_pick = pick >= 0 ? pick : last;
+      s_before = pick >= 0 ? before : -1.f;  // -1: rounding left the target past the total
+      s_target = target;
+      s_res[0] = INT_MAX;
+      s_res[1] = -1;
     }
-    s_pick[0] = pick;
-    s_run[0] = before;
-    s_run[1] = target;
   }
   __syncthreads();
-  const int pick = s_pick[0];
-  const float before = s_run[0], target = s_run[1];
-  __syncthreads();
+  const int pick = s_pick;
   if (pick < 0) {  // no weight anywhere (cannot happen for finite logits)
     if (threadIdx.x == 0) a.token[b] = 0;
     return;
   }
-  float w[kSpecPer];
-  draw_weights(a, b, pick * kSpecChunk, w, LoadRun());
-  const int i0 = pick * kSpecChunk + (int)threadIdx.x * kSpecPer;
-  // Thread totals, exclusive scan over threads in order.
-  float tot = 0.f;
+  const float before = s_before, target = s_target;
+  {  // weights of the chunk, loaded coalesced, staged in token order
+    float w[kSpecPer];
+    draw_weights(a, b, pick * kSpecChunk, w, LoadSpread<false>());
 #pragma unroll
-  for (int e = 0; e < kSpecPer; ++e) tot += w[e];
-  s_run[threadIdx.x] = tot;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = 0.f;
-    for (int t = 0; t < kSpecThreads; ++t) {
-      const float v = s_run[t];
-      s_run[t] = r;
-      r += v;
-    }
+    for (int j = 0; j < kSpecPer / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_w[4 * threadIdx.x + 4 * kSpecThreads * j + e] = w[4 * j + e];
   }
   __syncthreads();
+  float w[kSpecPer];
+  float tot = 0.f;
+#pragma unroll
+  for (int e = 0; e < kSpecPer; ++e) {
+    w[e] = s_w[threadIdx.x * kSpecPer + e];
+    tot += w[e];
+  }
+  const float incl = block_incl_scan(tot, s_tot);
+  const int i0 = pick * kSpecChunk + (int)threadIdx.x * kSpecPer;
   int found = INT_MAX, lastpos = -1;
-  float run = (before < 0.f ? 0.f : before) + s_run[threadIdx.x];
+  float run = (before < 0.f ? 0.f : before) + (incl - tot);
 #pragma unroll
   for (int e = 0; e < kSpecPer; ++e) {
     if (w[e] > 0.f && i0 + e < a.vocab) lastpos = i0 + e;
     run += w[e];
     if (before >= 0.f && found == INT_MAX && run > target && w[e] > 0.f) found = i0 + e;
   }
-  // Smallest found index; largest positive index for the fallback.
-  __shared__ int s_res[2];
-  if (threadIdx.x == 0) { s_res[0] = INT_MAX; s_res[1] = -1; }
-  __syncthreads();
   if (found != INT_MAX) atomicMin(&s_res[0], found);
   if (lastpos >= 0) atomicMax(&s_res[1], lastpos);
   __syncthreads();
