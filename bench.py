@@ -426,6 +426,13 @@ def main():
         graph.replay()
     gr_t = timed_loop(lambda i: graph.replay())
     del graph
+    # On-device tail statistics of the step's acceptance values (mean, lower 5th percentile).
+    tail_out = torch.empty(2, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        spdec.tail_stats(alpha, out=tail_out)
+    t_tail = timed_loop(lambda i: spdec.tail_stats(alpha, out=tail_out))
+    tail = {"us": t_tail * 1e6, "rows": R, "mean": float(tail_out[0]), "p5": float(tail_out[1]),
+            "timing": "K times back to back under one event pair"}
     verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 2 * K_steps) \
         if not args.no_verify else None
     shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
@@ -491,6 +498,7 @@ def main():
                    "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels),
                    "timing": "K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub, one event pair each",
                    "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6},
+        "tail_stats": tail,
         "verify": verify,
         "shared_prefix": shared,
         "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,

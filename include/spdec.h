@@ -279,6 +279,21 @@ spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int 
                               int64_t row_stride, float temperature, float* alpha, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * spdec_tail_stats - on-device tail statistics of the per-token acceptance
+ * (Sparrow project page, "Control Study 1": training stays stable while the
+ * lower 5th percentile of the per-token mismatch stays above a threshold,
+ * 0.86 in its takeaway), so a budget schedule can read them without a host
+ * round trip.
+ *
+ * out[0] = mean of alpha[0 .. rows), out[1] = its 5th percentile by linear
+ * interpolation between the order statistics at rank 0.05 * (rows - 1) (the
+ * numpy default). Computed in fp64 and rounded once to fp32.
+ * alpha: fp32 [rows] (device); out: fp32 [2] (device). 1 <= rows <= 8192
+ * (SPDEC_ERR_UNSUPPORTED above). No workspace.
+ */
+spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -244,4 +244,10 @@ spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int 
                                            static_cast<hipStream_t>(stream)));
 }
 
+spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream) {
+  if (!alpha || !out || rows < 1) return SPDEC_ERR_INVALID;
+  if (rows > spdec::kTailMaxRows) return SPDEC_ERR_UNSUPPORTED;
+  return from_hip(spdec::launch_tail_stats(alpha, rows, out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

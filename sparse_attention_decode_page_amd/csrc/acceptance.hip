@@ -154,6 +154,55 @@ __global__ __launch_bounds__(kWave) void acc_final_kernel(AccArgs x) {
   if (threadIdx.x == 0) x.alpha[r] = fminf(1.f, fmaxf(0.f, s));
 }
 
+// Tail statistics of the per-token acceptance (Sparrow project page,
+// "Control Study 1": the lower 5th percentile of the mismatch is the stability
+// signal; its takeaway threshold is 0.86): the mean and the 5th percentile
+// (linear interpolation between order statistics, rank 0.05 * (n - 1)) of n
+// values, in one workgroup. The values are sorted in LDS (bitonic, padded to a
+// power of two with +inf); the mean and the interpolation run in fp64 and are
+// rounded once, so both equal the exact statistics of the fp32 inputs up to
+// that rounding.
+constexpr int kTailThreads = 1024;
+
+__global__ __launch_bounds__(kTailThreads) void tail_stats_kernel(const float* __restrict__ alpha, int n,
+                                                                  float* __restrict__ out) {
+  __shared__ float s[kTailMaxRows];
+  __shared__ double s_sum[kTailThreads / kWave];
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  double part = 0.0;
+  for (int i = threadIdx.x; i < n2; i += kTailThreads) {
+    const float v = i < n ? alpha[i] : INFINITY;
+    s[i] = v;
+    if (i < n) part += (double)v;
+  }
+  part = group_sum<kWave>(part);
+  if (threadIdx.x % kWave == 0) s_sum[threadIdx.x / kWave] = part;
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += kTailThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const float a = s[i], b = s[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) { s[i] = b; s[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+    for (int w = 0; w < kTailThreads / kWave; ++w) sum += s_sum[w];
+    const double pos = 0.05 * (double)(n - 1);
+    const int lo = (int)floor(pos);
+    const int hi = min(lo + 1, n - 1);
+    out[0] = (float)(sum / n);
+    out[1] = (float)((double)s[lo] + (pos - lo) * ((double)s[hi] - (double)s[lo]));
+  }
+}
+
 int nchunks(int vocab) { return (vocab + kAccChunk - 1) / kAccChunk; }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -163,6 +212,11 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 size_t acceptance_workspace_bytes(int rows, int vocab) {
   const size_t n = (size_t)rows * nchunks(vocab);
   return align256(n * 4 * sizeof(float)) + align256(n * sizeof(float));
+}
+
+hipError_t launch_tail_stats(const float* alpha, int n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(tail_stats_kernel, dim3(1), dim3(kTailThreads), 0, s, alpha, n, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,

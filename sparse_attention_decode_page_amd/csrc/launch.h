@@ -77,6 +77,8 @@ size_t spec_accept_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_spec_accept(const float* p, const float* q, int batch, int k, int vocab, int64_t stride,
                               const int32_t* draft, const float* u_accept, const float* u_sample, float temperature,
                               int32_t* n_accepted, int32_t* token, void* ws, hipStream_t s);
+constexpr int kTailMaxRows = 8192;  // values the tail statistics sort in LDS
+hipError_t launch_tail_stats(const float* alpha, int n, float* out, hipStream_t s);
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
                              float* alpha, void* ws, hipStream_t s);
 

@@ -26,7 +26,7 @@ ABI_FUNCTIONS = (
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
-    "spdec_acceptance",
+    "spdec_acceptance", "spdec_tail_stats",
 )
 
 
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         "spdec_spec_accept": (I, [P, P, I, I, I, I64, P, P, P, F, P, P, P, SZ, P]),
         "spdec_acceptance_workspace_bytes": (SZ, [I, I]),
         "spdec_acceptance": (I, [P, P, I, I, I64, F, P, P, SZ, P]),
+        "spdec_tail_stats": (I, [P, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -336,3 +337,15 @@ def acceptance(logits_a, logits_b, temperature: float = 1.0, alpha=None, workspa
                                   float(temperature), _ptr(alpha), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream()), "spdec_acceptance")
     return alpha
+
+
+def tail_stats(alpha, out=None):
+    """Mean and lower 5th percentile (linear interpolation) of a 1-D float32 GPU tensor: a [2] tensor."""
+    if not isinstance(alpha, torch.Tensor) or alpha.dim() != 1:
+        raise ValueError("alpha must be a 1-D tensor")
+    _need(alpha, "alpha", torch.float32, (alpha.shape[0],))
+    if out is None:
+        out = torch.empty(2, dtype=torch.float32, device=alpha.device)
+    _need(out, "out", torch.float32, (2,))
+    _check(lib().spdec_tail_stats(_ptr(alpha), int(alpha.shape[0]), _ptr(out), _stream()), "spdec_tail_stats")
+    return out

@@ -40,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 17
+    assert len(names) == len(S.ABI_FUNCTIONS) == 18
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -189,3 +189,10 @@ def test_shared_prefix_checks(L):
     assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 2, FAKE, float("inf"), FAKE, None, FAKE, ws, None) == -1
     f = _desc(batch=4, dtype=S.SPDEC_F32)
     assert L.spdec_dense_decode_shared(ctypes.byref(f), FAKE, 2, FAKE, 0.1, FAKE, None, FAKE, ws, None) == -2
+
+
+def test_tail_stats_checks(L):
+    assert L.spdec_tail_stats(None, 10, FAKE, None) == -1
+    assert L.spdec_tail_stats(FAKE, 0, FAKE, None) == -1
+    assert L.spdec_tail_stats(FAKE, 10, None, None) == -1
+    assert L.spdec_tail_stats(FAKE, 8193, FAKE, None) == -2
