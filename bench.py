@@ -80,7 +80,10 @@ def algorithmic_bytes(spec, lens, budget_pages, cap, rows, vocab):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters_qwen3-8b-ragged.md")
-KERNEL_SOURCES = ("common.h", "launch.h", "decode.hip", "select.hip", "abi.hip")
+# The measured kernels (dense and sparse decode, scoring, top-B) and their launch
+# configuration (plans, resident grid); a change to any of these invalidates the
+# recorded counter traffic.
+KERNEL_SOURCES = ("common.h", "decode.hip", "select.hip", "grid.hip")
 
 
 def kernel_source_hash() -> str:

@@ -58,20 +58,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
-namespace spdec {
-
-hipError_t persistent_grid(const void* kernel, int block, size_t dyn_lds, int* grid) {
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, dyn_lds);
-  if (e != hipSuccess) return e;
-  *grid = cus * (per_cu > 0 ? per_cu : 1);
-  return hipSuccess;
-}
-
-}  // namespace spdec
-
 extern "C" {
 
 const char* spdec_status_string(int status) {
