@@ -251,9 +251,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
-#ifndef SPDEC_STREAM_ATTR
-#define SPDEC_STREAM_ATTR
-#endif
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -301,7 +298,7 @@ __device__ __forceinline__ int unit_entries(const StreamArgs& a, int u) {
 // the end and no workgroup is launched for an empty split. The wave that
 // finishes a unit records how many chunks the unit has for the merge.
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kDecodeThreads) SPDEC_STREAM_ATTR void decode_stream_kernel(StreamArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArgs a) {
   constexpr int NJ = D / 32;             // MFMAs per head set per tile
   constexpr int NSET = G > 4 ? 2 : 1;    // MFMA sets (G = 8 needs two)
   constexpr int HPS = G > 4 ? 4 : G;     // heads delivered per set
@@ -699,11 +696,7 @@ DecodePlan decode_plan(const CacheView& c, int max_budget_pages) {
   // split, fewer when the grid would leave compute units idle. The plan
   // depends only on the list capacity, so a sparse call whose capacity is
   // every page splits exactly like the dense one.
-#ifdef SPDEC_SPLIT_TOKENS
-  constexpr int kTargetTokens = SPDEC_SPLIT_TOKENS;
-#else
   constexpr int kTargetTokens = 512;
-#endif
   int pps = max(1, kTargetTokens / c.page_size);
   while (pps > 1 && units * ((p.list_pages + pps - 1) / pps) < 2048) pps >>= 1;
   pps = max(pps, (p.list_pages + kMaxSplits - 1) / kMaxSplits);

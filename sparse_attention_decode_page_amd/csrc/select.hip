@@ -26,11 +26,7 @@ namespace spdec {
 
 namespace {
 
-#ifdef SPDEC_SCORE_PAGES
-constexpr int kScorePages = SPDEC_SCORE_PAGES;
-#else
 constexpr int kScorePages = 256;   // pages per scoring workgroup
-#endif
 // Each of the 4 waves scores kScorePages/4 pages, PPI (>= 1) per load.
 static_assert(kScorePages % 64 == 0 && kScorePages >= 64, "pages per scoring workgroup");
 constexpr int kSelectThreads = 256;
