@@ -6,12 +6,19 @@
 // complete KV (S3R abstract). Both run the same kernel; only the page-list
 // iterator differs.
 //
-// Work decomposition: one workgroup per (split, sequence, KV head). A split is
-// a run of `pages_per_split` entries of the page list, so ragged lengths and
-// budgets become equal-sized work items. All G query heads of the KV head are
-// served by the same workgroup, so every K/V byte is read from HBM once.
+// Two decompositions share the plan and the merge order:
+//   * bf16 caches (the workloads measured here): a persistent stream-K kernel
+//     (decode_stream_kernel, below) in which every wave owns one contiguous
+//     range of the flattened (sequence x KV head, page-list entry) pairs, with
+//     q.K^T on the matrix cores; a second kernel merges each unit's chunks;
+//   * fp32 caches and batches too large for the stream plan: one workgroup per
+//     (split, sequence, KV head) (decode_split_kernel), a split being a run of
+//     `pages_per_split` list entries, merged by decode_merge_kernel.
+// Either way all G query heads of a KV head are served together, so every K/V
+// byte is read from HBM once, and every merge runs in a fixed order, so the
+// result is deterministic.
 //
-// Lane layout: a token row of D channels is spread over LPT = D/VEC lanes
+// Split kernel lane layout: a token row of D channels is spread over LPT = D/VEC lanes
 // that each hold one 16-byte chunk; one wave load instruction covers TPI =
 // 64/LPT tokens (1 KiB for bf16 D=128). Scores are LPT-lane butterfly sums.
 // Each group of LPT lanes keeps its own fp32 online softmax (running max m,
