@@ -29,8 +29,6 @@ namespace {
 constexpr int kScorePages = 256;   // pages per scoring workgroup
 // Each of the 4 waves scores kScorePages/4 pages, PPI (>= 1) per load.
 static_assert(kScorePages % 64 == 0 && kScorePages >= 64, "pages per scoring workgroup");
-constexpr int kSelectThreads = 256;
-constexpr size_t kSelectLdsKeyBytes = 60 * 1024;
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const void* __restrict__ qv,
@@ -229,125 +227,18 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Keys live in LDS when the page count allows it (KEYS_IN_LDS), otherwise
-// every pass re-reads the fp32 scores (L2-resident after the first pass).
-template <int NT, bool KEYS_IN_LDS>
-__global__ __launch_bounds__(NT) void select_topk_kernel(CacheView c, const int32_t* __restrict__ budget,
-                                                         int cap, const float* __restrict__ scores,
-                                                         int32_t* __restrict__ sel_idx,
-                                                         int32_t* __restrict__ sel_cnt) {
-  extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ int s_digit, s_above;
-  __shared__ int s_wave[NT / kWave][2];
-  const int unit = blockIdx.x;
-  const int b = unit / c.hkv;
-  const int tid = threadIdx.x;
-  const int L = c.seq_lens[b];
-  const int P = min((max(L, 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
-  int32_t* out = sel_idx + (int64_t)unit * cap;
-  const int K = min(min(max(budget[b], 2), cap), P);
-  if (K >= P) {
-    for (int i = tid; i < P; i += NT) out[i] = i;
-    if (tid == 0) sel_cnt[unit] = P;
-    return;
-  }
-  // Here 2 <= K < P, so P >= 3.
-  const int M = P - 2;
-  const int need = K - 2;
-  if (tid == 0) {
-    out[0] = 0;
-    out[K - 1] = P - 1;
-    sel_cnt[unit] = K;
-  }
-  if (need == 0) return;
-  const float* srow = scores + (int64_t)unit * c.max_pages + 1;
-  if constexpr (KEYS_IN_LDS) {
-    for (int i = tid; i < M; i += NT) keys[i] = score_key(srow[i]);
-    __syncthreads();
-  }
-  auto key = [&](int i) -> uint32_t {
-    if constexpr (KEYS_IN_LDS) return keys[i];
-    return score_key(srow[i]);
-  };
-
-  uint32_t prefix = 0, mask = 0;
-  int remaining = need;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < M; i += NT) {
-      const uint32_t k = key(i);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < kWave) {
-      // Lane l owns bins 255-4l .. 252-4l, scanned from the top.
-      const int top = 255 - 4 * tid;
-      const int c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
-      const int tot = c0 + c1 + c2 + c3;
-      const int incl = wave_incl_scan(tot);
-      const int excl = incl - tot;
-      if (excl < remaining && remaining <= incl) {
-        const int r = remaining - excl;
-        int digit, above;
-        if (r <= c0) { digit = top; above = excl; }
-        else if (r <= c0 + c1) { digit = top - 1; above = excl + c0; }
-        else if (r <= c0 + c1 + c2) { digit = top - 2; above = excl + c0 + c1; }
-        else { digit = top - 3; above = excl + c0 + c1 + c2; }
-        s_digit = digit;
-        s_above = above;
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)s_digit << shift;
-    mask |= 0xFFu << shift;
-    remaining -= s_above;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const int eq_take = remaining;  // keys equal to T still to take, in index order
-
-  // Ordered compaction: thread t owns a contiguous run of the middle pages.
-  const int per = (M + NT - 1) / NT;
-  const int i0 = min(tid * per, M);
-  const int i1 = min(i0 + per, M);
-  int gt = 0, eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t k = key(i);
-    gt += k > T;
-    eq += k == T;
-  }
-  const int lane = tid % kWave, wave = tid / kWave;
-  const int gt_incl = wave_incl_scan(gt);
-  const int eq_incl = wave_incl_scan(eq);
-  if (lane == kWave - 1) { s_wave[wave][0] = gt_incl; s_wave[wave][1] = eq_incl; }
-  __syncthreads();
-  int gt_before = gt_incl - gt, eq_before = eq_incl - eq;
-  for (int w = 0; w < wave; ++w) { gt_before += s_wave[w][0]; eq_before += s_wave[w][1]; }
-  int pos = 1 + gt_before + min(eq_before, eq_take);
-  int eq_seen = eq_before;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t k = key(i);
-    bool take = k > T;
-    if (k == T) { take = eq_seen < eq_take; ++eq_seen; }
-    if (take && pos < K - 1) out[pos++] = i + 1;  // pos never passes the local page's slot
-  }
-}
-
-// Register variant of the top-B select for P - 2 <= 256 * KPT middle pages.
-// Thread t holds the keys of middle pages [t*KPT, t*KPT + KPT) (index order,
-// so the compaction emits ascending pages). Radix digits are taken on
+// Top-B select for P - 2 <= NT * KPT middle pages, one workgroup of NT threads
+// per (sequence, KV head), keys in registers. Thread t holds the keys of
+// middle pages [t*KPT, t*KPT + KPT) (index order, so the compaction emits
+// ascending pages). Radix digits are taken on
 // key - min_key: the span of real scores is a few exponent steps, so the first
 // 8-bit digit already spreads the keys over the histogram and 2-3 passes
 // usually suffice.
-template <int KPT>
-__global__ __launch_bounds__(kSelectThreads) void select_topk_reg_kernel(CacheView c, const int32_t* __restrict__ budget,
-                                                                       int cap, const float* __restrict__ scores,
-                                                                       int32_t* __restrict__ sel_idx,
-                                                                       int32_t* __restrict__ sel_cnt) {
-  constexpr int NT = kSelectThreads;
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const int32_t* __restrict__ budget,
+                                                           int cap, const float* __restrict__ scores,
+                                                           int32_t* __restrict__ sel_idx,
+                                                           int32_t* __restrict__ sel_cnt) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_red[NT / kWave][2];
   __shared__ int s_digit, s_above;
@@ -501,28 +392,32 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
     e = c.head_dim == 64 ? score_impl<F32, 64>(c, q, scores, s) : score_impl<F32, 128>(c, q, scores, s);
   }
   if (e != hipSuccess) return e;
+  // Keys per thread stay at 8-32: lists longer than 2048 middle pages take
+  // 1024-thread workgroups (with few sequences, each unit's select is then
+  // spread over four times the lanes).
   const int middle = c.max_pages - 2;
-  const dim3 sgrid(c.batch * c.hkv), sblock(kSelectThreads);
-  if (middle <= kSelectThreads * 8) {
-    hipLaunchKernelGGL((select_topk_reg_kernel<8>), sgrid, sblock, 0, s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+  const dim3 sgrid(c.batch * c.hkv);
+  if (middle <= 256 * 8) {
+    hipLaunchKernelGGL((select_topk_reg_kernel<8, 256>), sgrid, dim3(256), 0, s, c, budget, max_budget, scores,
+                       sel_idx, sel_cnt);
     return hipGetLastError();
   }
-  if (middle <= kSelectThreads * 32) {
-    hipLaunchKernelGGL((select_topk_reg_kernel<32>), sgrid, sblock, 0, s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+  if (middle <= 1024 * 8) {
+    hipLaunchKernelGGL((select_topk_reg_kernel<8, 1024>), sgrid, dim3(1024), 0, s, c, budget, max_budget, scores,
+                       sel_idx, sel_cnt);
     return hipGetLastError();
   }
-  if (middle <= kSelectThreads * 64) {
-    hipLaunchKernelGGL((select_topk_reg_kernel<64>), sgrid, sblock, 0, s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+  if (middle <= 1024 * 16) {
+    hipLaunchKernelGGL((select_topk_reg_kernel<16, 1024>), sgrid, dim3(1024), 0, s, c, budget, max_budget, scores,
+                       sel_idx, sel_cnt);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)c.max_pages * sizeof(uint32_t);
-  if (lds <= kSelectLdsKeyBytes) {
-    hipLaunchKernelGGL((select_topk_kernel<kSelectThreads, true>), dim3(c.batch * c.hkv), dim3(kSelectThreads), lds,
-                       s, c, budget, max_budget, scores, sel_idx, sel_cnt);
-  } else {
-    hipLaunchKernelGGL((select_topk_kernel<kSelectThreads, false>), dim3(c.batch * c.hkv), dim3(kSelectThreads), 0,
-                       s, c, budget, max_budget, scores, sel_idx, sel_cnt);
+  if (middle <= 1024 * 32) {
+    hipLaunchKernelGGL((select_topk_reg_kernel<32, 1024>), sgrid, dim3(1024), 0, s, c, budget, max_budget, scores,
+                       sel_idx, sel_cnt);
+    return hipGetLastError();
   }
+  // The ABI caps the page table at 32768 pages, so the forms above cover every list.
   return hipGetLastError();
 }
 
