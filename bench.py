@@ -19,9 +19,9 @@ reports the sparse path (select + sparse decode, each of K runs after a 1 GiB
 scrub read, the scrubs' own time subtracted) against HBM peak; `graph` times
 the step captured once in a HIP graph and replayed; `verify` times the dense
 verification of a 6-token draft (7 positions) and exact speculative sampling
-on the same cache; `shared_prefix` times the dense decode of a grouped batch
-(8 prompts x 8 samples) per sequence and with shared prompt pages read once;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+on the same cache; `shared_prefix` times the dense decode and the page
+selection of a grouped batch (8 prompts x 8 samples) per sequence and with
+shared prompt pages read once; `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -255,14 +255,48 @@ def shared_prefix_rows(args, dev, timed_loop):
         spdec.dense_decode_shared(cache, q, N, sh, out=o, lse=lse, workspace=ws_s)
     t_d = timed_loop(lambda i: spdec.dense_decode(cache, q, out=o, lse=lse, workspace=ws_d))
     t_s = timed_loop(lambda i: spdec.dense_decode_shared(cache, q, N, sh, out=o, lse=lse, workspace=ws_s))
+    # Page selection of the same batch: every sequence scores its own pages, or
+    # the shared prompt pages are scored once per group.
+    spdec.build_meta(cache)
+    budget = torch.from_numpy(wl.budget_pages.astype(np.int32)).to(dev)
+    kb = int(max(2, wl.budget_pages.max()))
+    sel_idx = torch.zeros((spec.batch, spec.num_kv_heads, kb), dtype=torch.int32, device=dev)
+    sel_cnt = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
+    ws_sel = torch.zeros(spdec.select_workspace_bytes(cache, kb), dtype=torch.uint8, device=dev)
+    ws_sp = torch.zeros(spdec.decode_workspace_bytes(cache, kb), dtype=torch.uint8, device=dev)
+
+    def sel(shared):
+        if shared:
+            spdec.select_pages_shared(cache, q, N, sh, budget, kb, sel_idx, sel_cnt, workspace=ws_sel)
+        else:
+            spdec.select_pages(cache, q, budget, kb, sel_idx, sel_cnt, workspace=ws_sel)
+
+    def path(shared):
+        sel(shared)
+        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, kb, out=o, lse=lse, workspace=ws_sp)
+
+    for _ in range(3):
+        path(False)
+        path(True)
+    t_sel = timed_loop(lambda i: sel(False))
+    t_sel_s = timed_loop(lambda i: sel(True))
+    t_path = timed_loop(lambda i: path(False))
+    t_path_s = timed_loop(lambda i: path(True))
     L = wl.lens.astype(np.int64)
     per_tok = 2 * spec.num_kv_heads * spec.head_dim * 2
     shared_tokens = int(wl.shared_pages.sum()) * spec.page_size
     bytes_dense = int(L.sum() * per_tok)
     bytes_shared = int((L.sum() - (N - 1) * shared_tokens) * per_tok)
-    del cache, kmm, q, ws_d, ws_s
+    P = (L + spec.page_size - 1) // spec.page_size
+    per_summary = spec.num_kv_heads * 2 * spec.head_dim * 2
+    sum_bytes = int(P.sum() * per_summary)
+    sum_bytes_s = int((P.sum() - (N - 1) * int(wl.shared_pages.sum())) * per_summary)
+    del cache, kmm, q, ws_d, ws_s, ws_sel, ws_sp
     torch.cuda.empty_cache()
     return {
+        "select_us": t_sel * 1e6, "select_shared_us": t_sel_s * 1e6, "select_speedup": t_sel / t_sel_s,
+        "select_summary_bytes": sum_bytes, "select_shared_summary_bytes": sum_bytes_s,
+        "sparse_path_us": t_path * 1e6, "sparse_path_shared_select_us": t_path_s * 1e6,
         "workload": spec.name, "groups": spec.batch // N, "group_size": N, "prompt_tokens": spec.prompt[2],
         "dense_us": t_d * 1e6, "dense_bytes": bytes_dense, "dense_GBps": bytes_dense / t_d / 1e9,
         "shared_us": t_s * 1e6, "shared_bytes": bytes_shared, "shared_GBps": bytes_shared / t_s / 1e9,

@@ -154,6 +154,28 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spdec_select_pages_shared - spdec_select_pages for groups of sequences that
+ * share their leading pages (a prompt sampled several times; the Sparrow
+ * project page's cost model, "Control Study 2", charges the prompt once per
+ * group rather than once per sample).
+ *
+ * Groups as in spdec_dense_decode_shared: sequences n*N .. n*N + N - 1 (N =
+ * group_size) map logical pages 0 .. shared_pages[n] - 1 to the same physical
+ * pages, all full (device preconditions; those pages' summaries are read once
+ * per (group, KV head) through the first member's page table and bounded
+ * against each member's query). Scores, selection, outputs and workspace are
+ * those of spdec_select_pages: every score is the same fp32 value up to the
+ * fp64 summation order inside it.
+ *
+ * shared_pages: int32 [batch / N]. Requires a bf16 cache, batch % N == 0,
+ * 1 <= N <= 8 and batch * Hkv <= 16384 (SPDEC_ERR_UNSUPPORTED otherwise).
+ */
+spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, int group_size,
+                                       const int32_t* shared_pages, const int32_t* budget_pages,
+                                       int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spdec_sparse_decode - block-sparse decode attention over the selected pages
  * (Sparrow project page, "Insights": block-sparse attention; "Control Study
  * 2": reads only the budgeted KV).

@@ -112,6 +112,24 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
                                        static_cast<hipStream_t>(stream)));
 }
 
+spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, int group_size,
+                                       const int32_t* shared_pages, const int32_t* budget_pages,
+                                       int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.kminmax || !q || !budget_pages || !sel_idx || !sel_cnt || !shared_pages) return SPDEC_ERR_INVALID;
+  if (!aligned16(v.kminmax) || !aligned16(q)) return SPDEC_ERR_INVALID;
+  if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
+  if (group_size < 1 || v.batch % group_size != 0) return SPDEC_ERR_INVALID;
+  if (!spdec::select_shared_supported(v, group_size)) return SPDEC_ERR_UNSUPPORTED;
+  if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
+    return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_select_shared(v, q, budget_pages, max_budget_pages, group_size, shared_pages, sel_idx,
+                                              sel_cnt, scores_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t spdec_decode_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
   CacheView v;
   if (view_of(cache, &v) != SPDEC_OK || max_budget_pages < 0) return 0;

@@ -52,6 +52,12 @@ hipError_t launch_append_kv(const CacheView& c, const void* k_new, const void* v
 hipError_t launch_build_meta(const CacheView& c, hipStream_t s);
 hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
                          int32_t* sel_idx, int32_t* sel_cnt, float* scores, void* ws, hipStream_t s);
+// Selection with the shared leading pages of each group of group_size
+// sequences scored once per (group, KV head); same outputs as launch_select.
+bool select_shared_supported(const CacheView& c, int group_size);
+hipError_t launch_select_shared(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
+                                int group_size, const int32_t* shared_pages, int32_t* sel_idx, int32_t* sel_cnt,
+                                float* scores, void* ws, hipStream_t s);
 hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float scale, float* out, float* lse, void* ws, hipStream_t s);
 // Dense stream partials over each sequence's pages from first_page[b / group_size]

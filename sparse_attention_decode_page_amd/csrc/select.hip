@@ -105,9 +105,12 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
 // binary-searches its first unit and walks units until its range ends.
 constexpr int kStreamMinPages = 16;
 
+// first_page (optional): sequence b's list starts at logical page
+// first_page[b / group_size] (the pages before it are scored elsewhere).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const void* __restrict__ qv,
-                                                           float* __restrict__ scores) {
+                                                           float* __restrict__ scores,
+                                                           const int32_t* __restrict__ first_page, int group_size) {
   constexpr int VEC = T::VEC;
   constexpr int LPT = D / VEC;
   constexpr int PPI = kWave / LPT;
@@ -117,9 +120,11 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
   extern __shared__ int s_pre[];  // units + 1
   __shared__ int s_tmp[256 / kWave];
   const int units = c.batch * c.hkv;
+  auto first_of = [&](int b) { return first_page != nullptr ? max(first_page[b / group_size], 0) : 0; };
   for (int u = threadIdx.x; u < units; u += blockDim.x) {
-    const int L = max(c.seq_lens[u / c.hkv], 0);
-    s_pre[u] = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+    const int b = u / c.hkv;
+    const int L = max(c.seq_lens[b], 0);
+    s_pre[u] = max(min((L + c.page_size - 1) >> c.ps_log2, c.max_pages) - first_of(b), 0);
   }
   __syncthreads();
   block_exclusive_scan(s_pre, units, s_tmp);
@@ -154,8 +159,9 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
         qneg[e] += (double)fminf(f[e], 0.f);
       }
     }
-    float* srow = scores + (int64_t)u * c.max_pages;
-    // Pages [pb, pe) of this unit, in batches of BATCH load instructions
+    float* srow = scores + (int64_t)u * c.max_pages + first_of(b);
+    const int32_t* ptab = c.page_table + (int64_t)b * c.max_pages + first_of(b);
+    // Pages [pb, pe) of this unit's list, in batches of BATCH load instructions
     // (PPI pages each). Page-table entries come 64 at a time, one per lane:
     // win0 holds the current window, win1 the next one (fetched a window ahead).
     const int pb = pos - ubase, pe = seg_end - ubase;
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
       const int pg = pb + wi * kWave + lane;
       int ph = -1;
       if (pg < pe) {
-        const int t = c.page_table[(int64_t)b * c.max_pages + pg];
+        const int t = ptab[pg];
         ph = (t >= 0 && t < c.num_phys) ? t : -1;
       }
       return ph;
@@ -208,6 +214,153 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
         sc = group_sum<LPT>(sc);
         const int pl = (bt * BATCH + i) * PPI + lane / LPT;
         if (sub == 0 && phA[i] >= 0 && pb + pl < pe) srow[pb + pl] = (float)sc;
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) { loA[i] = loB[i]; hiA[i] = hiB[i]; phA[i] = phB[i]; }
+    }
+    pos = seg_end;
+    ++u;
+  }
+}
+
+// Scoring of the pages a group of N consecutive sequences shares (its prompt):
+// each shared page summary is read once per (group, KV head) and bounded
+// against every member's query group, instead of once per member. Units are
+// (group, KV head) over the group's first sequence's page table; a wave keeps
+// the members' signed query sums for its unit in LDS (its lanes' channels
+// only) and, for every batch of summaries, loops over the members. The
+// arithmetic per (member, page) is the single-sequence scoring's: fp64
+// accumulation, rounded once.
+constexpr int kSharedScoreMaxMembers = 8;
+
+// Orders one wave's LDS writes before its lanes' later reads (and the reverse).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void score_shared_kernel(CacheView c, const void* __restrict__ qv,
+                                                           float* __restrict__ scores,
+                                                           const int32_t* __restrict__ shared_pages, int N) {
+  constexpr int VEC = BF16::VEC;
+  constexpr int LPT = D / VEC;
+  constexpr int PPI = kWave / LPT;
+  constexpr int BATCH = 4;
+  static_assert((BATCH * PPI) <= kWave && kWave % (BATCH * PPI) == 0, "batches tile a page-table window");
+  using S = BF16::storage;
+  extern __shared__ int s_pre[];  // group units + 1
+  __shared__ int s_tmp[256 / kWave];
+  // [wave][member][lane's channel chunk][Qpos e=0..VEC-1, Qneg e=0..VEC-1]
+  __shared__ double s_qs[256 / kWave][kSharedScoreMaxMembers][LPT][2 * VEC];
+  const int groups = c.batch / N;
+  const int units = groups * c.hkv;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int n = u / c.hkv;
+    const int L = max(c.seq_lens[n * N], 0);
+    s_pre[u] = min(max(shared_pages[n], 0), min((L + c.page_size - 1) >> c.ps_log2, c.max_pages));
+  }
+  __syncthreads();
+  block_exclusive_scan(s_pre, units, s_tmp);
+  const int total = s_pre[units];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int wpb = blockDim.x / kWave;
+  const int64_t nw = (int64_t)gridDim.x * wpb;
+  const int64_t w = (int64_t)blockIdx.x * wpb + wave;
+  const int64_t R = max<int64_t>((total + nw - 1) / nw, kStreamMinPages);
+  if (w * R >= total) return;
+  int pos = (int)(w * R);
+  const int end = (int)min<int64_t>(pos + R, total);
+  int u = find_unit(s_pre, units, pos);
+  const int sub = lane % LPT;
+  const int d0 = sub * VEC;
+  const S* q = reinterpret_cast<const S*>(qv);
+  const S* mm = reinterpret_cast<const S*>(c.kminmax);
+  while (pos < end) {
+    const int n = u / c.hkv, g = u % c.hkv;
+    const int b0 = n * N;
+    const int ubase = s_pre[u];
+    const int seg_end = min(end, s_pre[u + 1]);
+    // Members' signed query sums for this wave's channel chunks (wave-private
+    // LDS: the wave's previous unit has finished reading it).
+    wave_sync();
+    for (int i = lane / LPT; i < N; i += PPI) {
+      double qpos[VEC], qneg[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) { qpos[e] = 0.0; qneg[e] = 0.0; }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float f[VEC];
+        unpack<BF16>(load16(q + ((int64_t)(b0 + i) * c.hq + g * G + h) * D + d0), f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          qpos[e] += (double)fmaxf(f[e], 0.f);
+          qneg[e] += (double)fminf(f[e], 0.f);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) { s_qs[wave][i][sub][e] = qpos[e]; s_qs[wave][i][sub][VEC + e] = qneg[e]; }
+    }
+    wave_sync();
+    const int32_t* ptab = c.page_table + (int64_t)b0 * c.max_pages;
+    const int pb = pos - ubase, pe = seg_end - ubase;
+    const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
+    auto fetch_window = [&](int wi) -> int {
+      const int pg = pb + wi * kWave + lane;
+      int ph = -1;
+      if (pg < pe) {
+        const int t = ptab[pg];
+        ph = (t >= 0 && t < c.num_phys) ? t : -1;
+      }
+      return ph;
+    };
+    int win0 = fetch_window(0), win1 = fetch_window(1);
+    int cur_win = 0;
+    auto issue = [&](int bt, u32x4* lo, u32x4* hi, int* phys) {
+      const int wi = (bt * BATCH * PPI) / kWave;
+      const int wsrc = wi == cur_win ? win0 : win1;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int pl = (bt * BATCH + i) * PPI + lane / LPT;
+        phys[i] = __shfl(wsrc, pl & (kWave - 1));
+        const int64_t row = ((int64_t)(phys[i] < 0 ? 0 : phys[i]) * c.hkv + g) * 2 * D + d0;
+        lo[i] = load16_stream(mm + row);
+        hi[i] = load16_stream(mm + row + D);
+      }
+    };
+    u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];
+    int phA[BATCH], phB[BATCH];
+    issue(0, loA, hiA, phA);
+    for (int bt = 0; bt < nbatch; ++bt) {
+      const int wnext = ((bt + 1) * BATCH * PPI) / kWave;
+      if (wnext != cur_win && bt + 1 < nbatch) {
+        win0 = win1;
+        cur_win = wnext;
+        win1 = fetch_window(wnext + 1);
+      }
+      if (bt + 1 < nbatch) issue(bt + 1, loB, hiB, phB);
+      float fl[BATCH][VEC], fh[BATCH][VEC];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) { unpack<BF16>(loA[i], fl[i]); unpack<BF16>(hiA[i], fh[i]); }
+      for (int m = 0; m < N; ++m) {
+        double qp[VEC], qn[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { qp[e] = s_qs[wave][m][sub][e]; qn[e] = s_qs[wave][m][sub][VEC + e]; }
+        float* srow = scores + ((int64_t)(b0 + m) * c.hkv + g) * c.max_pages;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          double sc = 0.0;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            sc = fma((double)fh[i][e], qp[e], sc);
+            sc = fma((double)fl[i][e], qn[e], sc);
+          }
+          sc = group_sum<LPT>(sc);
+          const int pl = (bt * BATCH + i) * PPI + lane / LPT;
+          if (sub == 0 && phA[i] >= 0 && pb + pl < pe) srow[pb + pl] = (float)sc;
+        }
       }
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) { loA[i] = loB[i]; hiA[i] = hiB[i]; phA[i] = phB[i]; }
@@ -351,14 +504,16 @@ __global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const 
 }
 
 template <typename T, int D, int G>
-hipError_t score_launch(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+hipError_t score_launch(const CacheView& c, const void* q, float* scores, hipStream_t s,
+                        const int32_t* first_page = nullptr, int group_size = 1) {
   const int units = c.batch * c.hkv;
   if (units <= kMaxStreamUnits) {
     const size_t lds = (size_t)(units + 1) * sizeof(int);
     int grid = 0;
     hipError_t e = persistent_grid(reinterpret_cast<const void*>(&score_stream_kernel<T, D, G>), 256, lds, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((score_stream_kernel<T, D, G>), dim3(grid), dim3(256), lds, s, c, q, scores);
+    hipLaunchKernelGGL((score_stream_kernel<T, D, G>), dim3(grid), dim3(256), lds, s, c, q, scores, first_page,
+                       group_size);
   } else {
     dim3 grid((c.max_pages + kScorePages - 1) / kScorePages, units);
     hipLaunchKernelGGL((score_pages_kernel<T, D, G>), grid, dim3(256), 0, s, c, q, scores);
@@ -376,6 +531,34 @@ hipError_t score_impl(const CacheView& c, const void* q, float* scores, hipStrea
   }
 }
 
+template <int D, int G>
+hipError_t score_shared_launch(const CacheView& c, const void* q, float* scores, const int32_t* shared_pages, int N,
+                               hipStream_t s) {
+  const int units = (c.batch / N) * c.hkv;
+  const size_t lds = (size_t)(units + 1) * sizeof(int);
+  int grid = 0;
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&score_shared_kernel<D, G>), 256, lds, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((score_shared_kernel<D, G>), dim3(grid), dim3(256), lds, s, c, q, scores, shared_pages, N);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return score_launch<BF16, D, G>(c, q, scores, s, shared_pages, N);  // each sequence's own pages
+}
+
+template <int D>
+hipError_t score_shared_impl(const CacheView& c, const void* q, float* scores, const int32_t* shared_pages, int N,
+                             hipStream_t s) {
+  switch (c.group) {
+    case 1: return score_shared_launch<D, 1>(c, q, scores, shared_pages, N, s);
+    case 2: return score_shared_launch<D, 2>(c, q, scores, shared_pages, N, s);
+    case 4: return score_shared_launch<D, 4>(c, q, scores, shared_pages, N, s);
+    default: return score_shared_launch<D, 8>(c, q, scores, shared_pages, N, s);
+  }
+}
+
+hipError_t launch_topk(const CacheView& c, const int32_t* budget, int max_budget, const float* scores,
+                       int32_t* sel_idx, int32_t* sel_cnt, hipStream_t s);
+
 }  // namespace
 
 size_t select_workspace_bytes(const CacheView& c) {
@@ -392,6 +575,28 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
     e = c.head_dim == 64 ? score_impl<F32, 64>(c, q, scores, s) : score_impl<F32, 128>(c, q, scores, s);
   }
   if (e != hipSuccess) return e;
+  return launch_topk(c, budget, max_budget, scores, sel_idx, sel_cnt, s);
+}
+
+bool select_shared_supported(const CacheView& c, int group_size) {
+  return c.dtype == SPDEC_BF16 && group_size >= 1 && group_size <= kSharedScoreMaxMembers &&
+         c.batch % group_size == 0 && (int64_t)c.batch * c.hkv <= kMaxStreamUnits;
+}
+
+hipError_t launch_select_shared(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
+                                int group_size, const int32_t* shared_pages, int32_t* sel_idx, int32_t* sel_cnt,
+                                float* scores_out, void* ws, hipStream_t s) {
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
+  hipError_t e = c.head_dim == 64 ? score_shared_impl<64>(c, q, scores, shared_pages, group_size, s)
+                                  : score_shared_impl<128>(c, q, scores, shared_pages, group_size, s);
+  if (e != hipSuccess) return e;
+  return launch_topk(c, budget, max_budget, scores, sel_idx, sel_cnt, s);
+}
+
+namespace {
+
+hipError_t launch_topk(const CacheView& c, const int32_t* budget, int max_budget, const float* scores,
+                       int32_t* sel_idx, int32_t* sel_cnt, hipStream_t s) {
   // Keys per thread stay at 8-32: lists longer than 2048 middle pages take
   // 1024-thread workgroups (with few sequences, each unit's select is then
   // spread over four times the lanes).
@@ -420,5 +625,7 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
   // The ABI caps the page table at 32768 pages, so the forms above cover every list.
   return hipGetLastError();
 }
+
+}  // namespace
 
 }  // namespace spdec

@@ -22,7 +22,8 @@ SPDEC_F32, SPDEC_BF16 = 0, 1
 
 ABI_FUNCTIONS = (
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
-    "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_decode_workspace_bytes",
+    "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_select_pages_shared",
+    "spdec_decode_workspace_bytes",
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
         "spdec_build_meta": (I, [D, P]),
         "spdec_select_workspace_bytes": (SZ, [D, I]),
         "spdec_select_pages": (I, [D, P, P, I, P, P, P, P, SZ, P]),
+        "spdec_select_pages_shared": (I, [D, P, I, P, P, I, P, P, P, P, SZ, P]),
         "spdec_decode_workspace_bytes": (SZ, [D, I]),
         "spdec_sparse_decode": (I, [D, P, P, P, I, F, P, P, P, SZ, P]),
         "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
@@ -189,6 +191,34 @@ def select_pages(cache: PagedCache, q, budget_pages, max_budget_pages: int, sel_
     _check(lib().spdec_select_pages(ctypes.byref(cache.desc), _ptr(q), _ptr(budget_pages), int(max_budget_pages),
                                     _ptr(sel_idx), _ptr(sel_cnt), _ptr(scores_out), ws_ptr, ws_bytes, _stream()),
            "spdec_select_pages")
+    return sel_idx, sel_cnt
+
+
+def select_pages_shared(cache: PagedCache, q, group_size: int, shared_pages, budget_pages, max_budget_pages: int,
+                        sel_idx=None, sel_cnt=None, scores_out=None, workspace=None):
+    """select_pages where groups of group_size consecutive sequences share shared_pages[n] leading pages."""
+    _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    _need(budget_pages, "budget_pages", torch.int32, (cache.batch,))
+    if int(group_size) < 1 or cache.batch % int(group_size) != 0:
+        raise ValueError("batch must be a multiple of group_size")
+    _need(shared_pages, "shared_pages", torch.int32, (cache.batch // int(group_size),))
+    dev = cache.device
+    if sel_idx is None:
+        sel_idx = torch.zeros((cache.batch, cache.num_kv_heads, max_budget_pages), dtype=torch.int32, device=dev)
+    if sel_cnt is None:
+        sel_cnt = torch.zeros((cache.batch, cache.num_kv_heads), dtype=torch.int32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, (cache.batch, cache.num_kv_heads, max_budget_pages))
+    _need(sel_cnt, "sel_cnt", torch.int32, (cache.batch, cache.num_kv_heads))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.float32, (cache.batch, cache.num_kv_heads, cache.max_pages))
+        ws_ptr, ws_bytes = _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size()
+    else:
+        workspace = _workspace(select_workspace_bytes(cache, max_budget_pages), dev, workspace)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check(lib().spdec_select_pages_shared(ctypes.byref(cache.desc), _ptr(q), int(group_size), _ptr(shared_pages),
+                                           _ptr(budget_pages), int(max_budget_pages), _ptr(sel_idx), _ptr(sel_cnt),
+                                           _ptr(scores_out), ws_ptr, ws_bytes, _stream()),
+           "spdec_select_pages_shared")
     return sel_idx, sel_cnt
 
 

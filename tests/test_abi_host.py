@@ -40,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 18
+    assert len(names) == len(S.ABI_FUNCTIONS) == 19
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -189,6 +189,28 @@ def test_shared_prefix_checks(L):
     assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 2, FAKE, float("inf"), FAKE, None, FAKE, ws, None) == -1
     f = _desc(batch=4, dtype=S.SPDEC_F32)
     assert L.spdec_dense_decode_shared(ctypes.byref(f), FAKE, 2, FAKE, 0.1, FAKE, None, FAKE, ws, None) == -2
+
+
+def test_select_shared_checks(L):
+    d = _desc(batch=4)  # bf16, G = 4
+    need = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
+
+    def call(N=2, sh=FAKE, q=FAKE, budget=FAKE, kmax=16, scores=None, ws=FAKE, nbytes=need, desc=d):
+        return L.spdec_select_pages_shared(ctypes.byref(desc), q, N, sh, budget, kmax, FAKE, FAKE, scores, ws,
+                                           nbytes, None)
+
+    assert call(N=3) == -1                 # batch % N != 0
+    assert call(N=0) == -1
+    assert call(sh=None) == -1
+    assert call(q=None) == -1
+    assert call(budget=None) == -1
+    assert call(kmax=1) == -1
+    assert call(nbytes=need - 1) == -3     # no scores_out: the scores live in the workspace
+    assert call(ws=None, nbytes=0) == -3
+    e = _desc(batch=16)
+    assert call(N=16, desc=e) == -2        # more than 8 members per group
+    f = _desc(batch=4, dtype=S.SPDEC_F32)
+    assert call(desc=f) == -2
 
 
 def test_tail_stats_checks(L):
