@@ -168,7 +168,7 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
  * fp64 summation order inside it.
  *
  * shared_pages: int32 [batch / N]. Requires a bf16 cache, batch % N == 0,
- * 1 <= N <= 8 and batch * Hkv <= 16384 (SPDEC_ERR_UNSUPPORTED otherwise).
+ * 1 <= N <= 8 and (batch / N + batch) * Hkv <= 8192 (SPDEC_ERR_UNSUPPORTED otherwise).
  */
 spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, int group_size,
                                        const int32_t* shared_pages, const int32_t* budget_pages,

@@ -58,10 +58,15 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Marks a loaded value as needed at this point, so that its load is not
+// sunk into a later branch: independent loads held together share one wait.
+__device__ __forceinline__ void hold(int& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void hold(u32x4& x) { asm volatile("" : "+v"(x)); }
+
 // Data-parallel-primitive lane exchange inside a 16-lane row.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
@@ -84,8 +89,8 @@ __device__ __forceinline__ float group_sum(float x) {
 template <int CTRL>
 __device__ __forceinline__ double dpp(double x) {
   const uint64_t u = __double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 

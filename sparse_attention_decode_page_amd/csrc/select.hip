@@ -105,12 +105,9 @@ __global__ __launch_bounds__(256) void score_pages_kernel(CacheView c, const voi
 // binary-searches its first unit and walks units until its range ends.
 constexpr int kStreamMinPages = 16;
 
-// first_page (optional): sequence b's list starts at logical page
-// first_page[b / group_size] (the pages before it are scored elsewhere).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const void* __restrict__ qv,
-                                                           float* __restrict__ scores,
-                                                           const int32_t* __restrict__ first_page, int group_size) {
+                                                           float* __restrict__ scores) {
   constexpr int VEC = T::VEC;
   constexpr int LPT = D / VEC;
   constexpr int PPI = kWave / LPT;
@@ -120,11 +117,17 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
   extern __shared__ int s_pre[];  // units + 1
   __shared__ int s_tmp[256 / kWave];
   const int units = c.batch * c.hkv;
-  auto first_of = [&](int b) { return first_page != nullptr ? max(first_page[b / group_size], 0) : 0; };
-  for (int u = threadIdx.x; u < units; u += blockDim.x) {
-    const int b = u / c.hkv;
-    const int L = max(c.seq_lens[b], 0);
-    s_pre[u] = max(min((L + c.page_size - 1) >> c.ps_log2, c.max_pages) - first_of(b), 0);
+  // Four units per thread per pass with clamped (always valid) indices, so
+  // that every load of a pass is in flight at once.
+  for (int u0 = threadIdx.x; u0 < units; u0 += 4 * blockDim.x) {
+    int L[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) L[k] = c.seq_lens[min(u0 + k * (int)blockDim.x, units - 1) / c.hkv];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = u0 + k * (int)blockDim.x;
+      if (u < units) s_pre[u] = min((max(L[k], 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
+    }
   }
   __syncthreads();
   block_exclusive_scan(s_pre, units, s_tmp);
@@ -146,36 +149,42 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
     const int b = u / c.hkv, g = u % c.hkv;
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);
+    float* srow = scores + (int64_t)u * c.max_pages;
+    const int32_t* ptab = c.page_table + (int64_t)b * c.max_pages;
+    // Pages [pb, pe) of this unit's list (pe > pb), in batches of BATCH load
+    // instructions (PPI pages each). Page-table entries come 64 at a time, one
+    // per lane, read at clamped indices so that no load waits on a branch:
+    // win0 holds the current window, win1 the next one (fetched a window ahead).
+    const int pb = pos - ubase, pe = seg_end - ubase;
+    const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
+    auto window_raw = [&](int wi) -> int { return ptab[min(pb + wi * kWave + lane, pe - 1)]; };
+    auto window_of = [&](int wi, int t) -> int {
+      return (pb + wi * kWave + lane < pe && t >= 0 && t < c.num_phys) ? t : -1;
+    };
+    auto fetch_window = [&](int wi) -> int { return window_of(wi, window_raw(wi)); };
+    int raw0 = window_raw(0), raw1 = window_raw(1);
+    // The query group's signed sums (loads in flight with the windows').
+    u32x4 qraw[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) qraw[h] = load16(q + ((int64_t)b * c.hq + g * G + h) * D + d0);
+    hold(raw0);
+    hold(raw1);
+#pragma unroll
+    for (int h = 0; h < G; ++h) hold(qraw[h]);
     double qpos[VEC], qneg[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) { qpos[e] = 0.0; qneg[e] = 0.0; }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float f[VEC];
-      unpack<T>(load16(q + ((int64_t)b * c.hq + g * G + h) * D + d0), f);
+      unpack<T>(qraw[h], f);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         qpos[e] += (double)fmaxf(f[e], 0.f);
         qneg[e] += (double)fminf(f[e], 0.f);
       }
     }
-    float* srow = scores + (int64_t)u * c.max_pages + first_of(b);
-    const int32_t* ptab = c.page_table + (int64_t)b * c.max_pages + first_of(b);
-    // Pages [pb, pe) of this unit's list, in batches of BATCH load instructions
-    // (PPI pages each). Page-table entries come 64 at a time, one per lane:
-    // win0 holds the current window, win1 the next one (fetched a window ahead).
-    const int pb = pos - ubase, pe = seg_end - ubase;
-    const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
-    auto fetch_window = [&](int wi) -> int {
-      const int pg = pb + wi * kWave + lane;
-      int ph = -1;
-      if (pg < pe) {
-        const int t = ptab[pg];
-        ph = (t >= 0 && t < c.num_phys) ? t : -1;
-      }
-      return ph;
-    };
-    int win0 = fetch_window(0), win1 = fetch_window(1);
+    int win0 = window_of(0, raw0), win1 = window_of(1, raw1);
     int cur_win = 0;
     auto issue = [&](int bt, u32x4* lo, u32x4* hi, int* phys) {
       const int wi = (bt * BATCH * PPI) / kWave;  // a batch never straddles two windows
@@ -223,14 +232,16 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
   }
 }
 
-// Scoring of the pages a group of N consecutive sequences shares (its prompt):
-// each shared page summary is read once per (group, KV head) and bounded
-// against every member's query group, instead of once per member. Units are
-// (group, KV head) over the group's first sequence's page table; a wave keeps
-// the members' signed query sums for its unit in LDS (its lanes' channels
-// only) and, for every batch of summaries, loops over the members. The
-// arithmetic per (member, page) is the single-sequence scoring's: fp64
-// accumulation, rounded once.
+// Scoring for groups of N consecutive sequences that share their leading
+// pages (a prompt sampled N times). Two kinds of units share one stream-K
+// space: (group, KV head) units over the group's shared pages, read once
+// through the first member's page table and bounded against all N members'
+// queries, then (sequence, KV head) units over each sequence's own pages.
+// A wave keeps the signed query sums of its unit's members in wave-private
+// LDS (only its lanes' channels) and, for every batch of page summaries,
+// loops over the members. The arithmetic per (member, page) is the
+// single-sequence scoring's: fp64 accumulation in the same order, rounded
+// once, so the scores are bit-identical to it.
 constexpr int kSharedScoreMaxMembers = 8;
 
 // Orders one wave's LDS writes before its lanes' later reads (and the reverse).
@@ -241,25 +252,47 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void score_shared_kernel(CacheView c, const void* __restrict__ qv,
-                                                           float* __restrict__ scores,
-                                                           const int32_t* __restrict__ shared_pages, int N) {
+__global__ __launch_bounds__(256) void score_grouped_kernel(CacheView c, const void* __restrict__ qv,
+                                                            float* __restrict__ scores,
+                                                            const int32_t* __restrict__ shared_pages, int N) {
   constexpr int VEC = BF16::VEC;
   constexpr int LPT = D / VEC;
   constexpr int PPI = kWave / LPT;
   constexpr int BATCH = 4;
   static_assert((BATCH * PPI) <= kWave && kWave % (BATCH * PPI) == 0, "batches tile a page-table window");
   using S = BF16::storage;
-  extern __shared__ int s_pre[];  // group units + 1
+  extern __shared__ int s_dyn[];  // s_pre: units + 1, then s_first: groups
   __shared__ int s_tmp[256 / kWave];
-  // [wave][member][lane's channel chunk][Qpos e=0..VEC-1, Qneg e=0..VEC-1]
-  __shared__ double s_qs[256 / kWave][kSharedScoreMaxMembers][LPT][2 * VEC];
+  // [wave][member][pair k][channel chunk]: pairs 0 .. VEC/2-1 hold the
+  // positive sums of the chunk's channels 2k, 2k+1, pairs VEC/2 .. VEC-1 the
+  // negative ones. Chunk-minor, so a wave's 16-byte reads are consecutive.
+  __shared__ double2 s_qs[256 / kWave][kSharedScoreMaxMembers][VEC][LPT];
   const int groups = c.batch / N;
-  const int units = groups * c.hkv;
-  for (int u = threadIdx.x; u < units; u += blockDim.x) {
-    const int n = u / c.hkv;
-    const int L = max(c.seq_lens[n * N], 0);
-    s_pre[u] = min(max(shared_pages[n], 0), min((L + c.page_size - 1) >> c.ps_log2, c.max_pages));
+  const int units_sh = groups * c.hkv;
+  const int units = units_sh + c.batch * c.hkv;
+  int* s_pre = s_dyn;
+  int* s_first = s_dyn + units + 1;
+  // Unit sizes. Four units per thread per pass with clamped (always valid)
+  // indices, so that every load of a pass is in flight at once.
+  for (int u0 = threadIdx.x; u0 < units; u0 += 4 * blockDim.x) {
+    int L[4], Sh[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = min(u0 + k * (int)blockDim.x, units - 1);
+      const int b = u < units_sh ? (u / c.hkv) * N : (u - units_sh) / c.hkv;
+      L[k] = c.seq_lens[b];
+      Sh[k] = shared_pages[b / N];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = u0 + k * (int)blockDim.x;
+      if (u < units) {
+        const int P = min((max(L[k], 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
+        const int S = max(Sh[k], 0);
+        s_pre[u] = u < units_sh ? min(S, P) : max(P - S, 0);
+        if (u < units_sh && u % c.hkv == 0) s_first[u / c.hkv] = S;
+      }
+    }
   }
   __syncthreads();
   block_exclusive_scan(s_pre, units, s_tmp);
@@ -279,44 +312,76 @@ __global__ __launch_bounds__(256) void score_shared_kernel(CacheView c, const vo
   const S* q = reinterpret_cast<const S*>(qv);
   const S* mm = reinterpret_cast<const S*>(c.kminmax);
   while (pos < end) {
-    const int n = u / c.hkv, g = u % c.hkv;
-    const int b0 = n * N;
+    int b0, g, members, first;
+    if (u < units_sh) {
+      b0 = (u / c.hkv) * N;
+      g = u % c.hkv;
+      members = N;
+      first = 0;
+    } else {
+      b0 = (u - units_sh) / c.hkv;
+      g = (u - units_sh) % c.hkv;
+      members = 1;
+      first = s_first[b0 / N];
+    }
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);
-    // Members' signed query sums for this wave's channel chunks (wave-private
-    // LDS: the wave's previous unit has finished reading it).
-    wave_sync();
-    for (int i = lane / LPT; i < N; i += PPI) {
+    const int pb = pos - ubase, pe = seg_end - ubase;
+    const int32_t* ptab = c.page_table + (int64_t)b0 * c.max_pages + first;
+    // Pages [pb, pe) of this unit's list (pe > pb); page-table entries come
+    // 64 at a time, one per lane, read at clamped indices so that no load
+    // waits on a branch.
+    const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
+    auto window_raw = [&](int wi) -> int { return ptab[min(pb + wi * kWave + lane, pe - 1)]; };
+    auto window_of = [&](int wi, int t) -> int {
+      return (pb + wi * kWave + lane < pe && t >= 0 && t < c.num_phys) ? t : -1;
+    };
+    auto fetch_window = [&](int wi) -> int { return window_of(wi, window_raw(wi)); };
+    int raw0 = window_raw(0), raw1 = window_raw(1);
+    // Members' signed query sums for this wave's channel chunks, loaded
+    // together with the page-table windows.
+    constexpr int MPL = (kSharedScoreMaxMembers + PPI - 1) / PPI;  // members per lane
+    u32x4 qraw[MPL][G];
+#pragma unroll
+    for (int k = 0; k < MPL; ++k) {
+      const int i = min(lane / LPT + k * PPI, members - 1);
+#pragma unroll
+      for (int h = 0; h < G; ++h) qraw[k][h] = load16(q + ((int64_t)(b0 + i) * c.hq + g * G + h) * D + d0);
+    }
+    hold(raw0);
+    hold(raw1);
+#pragma unroll
+    for (int k = 0; k < MPL; ++k) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) hold(qraw[k][h]);
+    }
+    wave_sync();  // the previous unit's reads of s_qs are done
+#pragma unroll
+    for (int k = 0; k < MPL; ++k) {
+      const int i = lane / LPT + k * PPI;
       double qpos[VEC], qneg[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) { qpos[e] = 0.0; qneg[e] = 0.0; }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float f[VEC];
-        unpack<BF16>(load16(q + ((int64_t)(b0 + i) * c.hq + g * G + h) * D + d0), f);
+        unpack<BF16>(qraw[k][h], f);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           qpos[e] += (double)fmaxf(f[e], 0.f);
           qneg[e] += (double)fminf(f[e], 0.f);
         }
       }
+      if (i < members) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) { s_qs[wave][i][sub][e] = qpos[e]; s_qs[wave][i][sub][VEC + e] = qneg[e]; }
+        for (int kk = 0; kk < VEC / 2; ++kk) {
+          s_qs[wave][i][kk][sub] = make_double2(qpos[2 * kk], qpos[2 * kk + 1]);
+          s_qs[wave][i][VEC / 2 + kk][sub] = make_double2(qneg[2 * kk], qneg[2 * kk + 1]);
+        }
+      }
     }
     wave_sync();
-    const int32_t* ptab = c.page_table + (int64_t)b0 * c.max_pages;
-    const int pb = pos - ubase, pe = seg_end - ubase;
-    const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
-    auto fetch_window = [&](int wi) -> int {
-      const int pg = pb + wi * kWave + lane;
-      int ph = -1;
-      if (pg < pe) {
-        const int t = ptab[pg];
-        ph = (t >= 0 && t < c.num_phys) ? t : -1;
-      }
-      return ph;
-    };
-    int win0 = fetch_window(0), win1 = fetch_window(1);
+    int win0 = window_of(0, raw0), win1 = window_of(1, raw1);
     int cur_win = 0;
     auto issue = [&](int bt, u32x4* lo, u32x4* hi, int* phys) {
       const int wi = (bt * BATCH * PPI) / kWave;
@@ -341,26 +406,52 @@ __global__ __launch_bounds__(256) void score_shared_kernel(CacheView c, const vo
         win1 = fetch_window(wnext + 1);
       }
       if (bt + 1 < nbatch) issue(bt + 1, loB, hiB, phB);
-      float fl[BATCH][VEC], fh[BATCH][VEC];
+      double fl[BATCH][VEC], fh[BATCH][VEC];
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) { unpack<BF16>(loA[i], fl[i]); unpack<BF16>(hiA[i], fh[i]); }
-      for (int m = 0; m < N; ++m) {
+      for (int i = 0; i < BATCH; ++i) {
+        float tl[VEC], th[VEC];
+        unpack<BF16>(loA[i], tl);
+        unpack<BF16>(hiA[i], th);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { fl[i][e] = (double)tl[e]; fh[i][e] = (double)th[e]; }
+      }
+      int st_ph = phA[0];
+#pragma unroll
+      for (int i = 1; i < BATCH; ++i) st_ph = sub == i ? phA[i] : st_ph;
+      const int st_page = pb + (bt * BATCH + sub) * PPI + lane / LPT;
+      const bool st_ok = sub < BATCH && st_ph >= 0 && st_page < pe;
+      float* srow_m = scores + ((int64_t)b0 * c.hkv + g) * c.max_pages + first + st_page;
+      for (int m = 0; m < members; ++m) {
         double qp[VEC], qn[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) { qp[e] = s_qs[wave][m][sub][e]; qn[e] = s_qs[wave][m][sub][VEC + e]; }
-        float* srow = scores + ((int64_t)(b0 + m) * c.hkv + g) * c.max_pages;
+        for (int k = 0; k < VEC / 2; ++k) {
+          const double2 a = s_qs[wave][m][k][sub];
+          const double2 b = s_qs[wave][m][VEC / 2 + k][sub];
+          qp[2 * k] = a.x; qp[2 * k + 1] = a.y;
+          qn[2 * k] = b.x; qn[2 * k + 1] = b.y;
+        }
+        // BATCH independent chains, each in the single-sequence order.
+        double sc[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) sc[i] = 0.0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+#pragma unroll
+          for (int i = 0; i < BATCH; ++i) {
+            sc[i] = fma(fh[i][e], qp[e], sc[i]);
+            sc[i] = fma(fl[i][e], qn[e], sc[i]);
+          }
+        }
+        // Every lane of a page's chunk group holds the page's sum; lane sub
+        // (< BATCH) of each group stores the score of its group's page in
+        // slot sub: one store instruction per member and batch.
+        float v = 0.f;
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
-          double sc = 0.0;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            sc = fma((double)fh[i][e], qp[e], sc);
-            sc = fma((double)fl[i][e], qn[e], sc);
-          }
-          sc = group_sum<LPT>(sc);
-          const int pl = (bt * BATCH + i) * PPI + lane / LPT;
-          if (sub == 0 && phA[i] >= 0 && pb + pl < pe) srow[pb + pl] = (float)sc;
+          const float r = (float)group_sum<LPT>(sc[i]);
+          v = sub == i ? r : v;
         }
+        if (st_ok) srow_m[(int64_t)m * c.hkv * c.max_pages] = v;
       }
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) { loA[i] = loB[i]; hiA[i] = hiB[i]; phA[i] = phB[i]; }
@@ -504,16 +595,14 @@ __global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const 
 }
 
 template <typename T, int D, int G>
-hipError_t score_launch(const CacheView& c, const void* q, float* scores, hipStream_t s,
-                        const int32_t* first_page = nullptr, int group_size = 1) {
+hipError_t score_launch(const CacheView& c, const void* q, float* scores, hipStream_t s) {
   const int units = c.batch * c.hkv;
   if (units <= kMaxStreamUnits) {
     const size_t lds = (size_t)(units + 1) * sizeof(int);
     int grid = 0;
     hipError_t e = persistent_grid(reinterpret_cast<const void*>(&score_stream_kernel<T, D, G>), 256, lds, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((score_stream_kernel<T, D, G>), dim3(grid), dim3(256), lds, s, c, q, scores, first_page,
-                       group_size);
+    hipLaunchKernelGGL((score_stream_kernel<T, D, G>), dim3(grid), dim3(256), lds, s, c, q, scores);
   } else {
     dim3 grid((c.max_pages + kScorePages - 1) / kScorePages, units);
     hipLaunchKernelGGL((score_pages_kernel<T, D, G>), grid, dim3(256), 0, s, c, q, scores);
@@ -534,15 +623,13 @@ hipError_t score_impl(const CacheView& c, const void* q, float* scores, hipStrea
 template <int D, int G>
 hipError_t score_shared_launch(const CacheView& c, const void* q, float* scores, const int32_t* shared_pages, int N,
                                hipStream_t s) {
-  const int units = (c.batch / N) * c.hkv;
-  const size_t lds = (size_t)(units + 1) * sizeof(int);
+  const int units = (c.batch / N + c.batch) * c.hkv;
+  const size_t lds = (size_t)(units + 1 + c.batch / N) * sizeof(int);
   int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&score_shared_kernel<D, G>), 256, lds, &grid);
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&score_grouped_kernel<D, G>), 256, lds, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((score_shared_kernel<D, G>), dim3(grid), dim3(256), lds, s, c, q, scores, shared_pages, N);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return score_launch<BF16, D, G>(c, q, scores, s, shared_pages, N);  // each sequence's own pages
+  hipLaunchKernelGGL((score_grouped_kernel<D, G>), dim3(grid), dim3(256), lds, s, c, q, scores, shared_pages, N);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -580,7 +667,7 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
 
 bool select_shared_supported(const CacheView& c, int group_size) {
   return c.dtype == SPDEC_BF16 && group_size >= 1 && group_size <= kSharedScoreMaxMembers &&
-         c.batch % group_size == 0 && (int64_t)c.batch * c.hkv <= kMaxStreamUnits;
+         c.batch % group_size == 0 && (int64_t)(c.batch / group_size + c.batch) * c.hkv <= kMaxStreamUnits;
 }
 
 hipError_t launch_select_shared(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
