@@ -21,7 +21,10 @@ the step captured once in a HIP graph and replayed; `verify` times the dense
 verification of a 6-token draft (7 positions) and exact speculative sampling
 on the same cache; `shared_prefix` times the dense decode and the page
 selection of a grouped batch (8 prompts x 8 samples) per sequence and with
-shared prompt pages read once; `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+shared prompt pages read once; `budget_control` runs the sparsity-schedule
+controller in a closed loop on the device (budgets, sparse path, a seeded
+random LM head, acceptance, tail statistics); `cpu_baseline` times the CPU
+oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -54,6 +57,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle sample")
     ap.add_argument("--no-verify", action="store_true", help="skip the verification / speculative-sampling rows")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix (grouped prompts) rows")
+    ap.add_argument("--no-control", action="store_true", help="skip the closed-loop budget controller rows")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -306,6 +310,74 @@ def shared_prefix_rows(args, dev, timed_loop):
     }
 
 
+def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap, timed_loop):
+    """Closed loop of the sparsity-schedule controller on the device: budgets -> selection -> sparse decode ->
+    a seeded random LM head (the plant stand-in: no model weights) -> acceptance against the dense output's
+    logits -> tail statistics -> controller -> budgets, with no host round trip inside the loop."""
+    import torch
+    from sparse_attention_decode_page_amd import spdec
+    B, H = spec.batch, spec.num_q_heads * spec.head_dim
+    vocab, sigma, steps = 151936, 3.0, 30
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 17)
+    w_lm = torch.randn((H, vocab), generator=gen, device=dev, dtype=torch.float32) * (sigma / H ** 0.5)
+    o_d, _ = spdec.dense_decode(cache, q)           # the reference on the cache as it now stands
+    logit_d = torch.matmul(o_d.reshape(B, H), w_lm)
+    logit_s = torch.empty_like(logit_d)
+    o_s = torch.empty_like(o_d)
+    l_s = torch.empty((B, spec.num_q_heads), dtype=torch.float32, device=dev)
+    al = torch.empty(B, dtype=torch.float32, device=dev)
+    ws_a = torch.zeros(spdec.acceptance_workspace_bytes(B, vocab), dtype=torch.uint8, device=dev)
+    prm = spdec.BudgetParams(target=0.86, gain=6.0, scale_min=1.0 / 64, scale_max=4.0, base_tokens=1024.0,
+                             tokens_per_token=0.1, page_size=spec.page_size, max_budget_pages=cap)
+    scale = torch.full((1,), 1.0 / 16, dtype=torch.float32, device=dev)   # start aggressive
+    bud = torch.empty(B, dtype=torch.int32, device=dev)
+    tails = torch.zeros((steps + 1, 2), dtype=torch.float32, device=dev)
+    tails[0, 1] = float("nan")                       # first step: no monitor value yet, schedule as it stands
+    buds = torch.zeros((steps, B), dtype=torch.int32, device=dev)
+
+    def control_step(k):
+        spdec.budget_update(tails[k], scale, cache.seq_lens, prm, budget_pages=bud)
+        buds[k].copy_(bud)
+        spdec.select_pages(cache, q, bud, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
+        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
+        torch.matmul(o_s.reshape(B, H), w_lm, out=logit_s)
+        spdec.acceptance(logit_s, logit_d, 1.0, alpha=al, workspace=ws_a)
+        spdec.tail_stats(al, out=tails[k + 1])
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for k in range(steps):
+        control_step(k)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_loop = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+    p5 = tails[1:, 1].cpu().numpy()
+    mb = buds.float().mean(dim=1).cpu().numpy()
+    within = np.abs(p5 - 0.86) <= 0.02
+    settled = next((k for k in range(steps) if within[k:].all()), None)
+    tail_fix = torch.tensor([0.0, 0.86], dtype=torch.float32, device=dev)
+    s_fix = torch.ones(1, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        spdec.budget_update(tail_fix, s_fix, cache.seq_lens, prm, budget_pages=bud)
+    t_upd = timed_loop(lambda i: spdec.budget_update(tail_fix, s_fix, cache.seq_lens, prm, budget_pages=bud))
+    del w_lm, logit_d, logit_s, ws_a
+    torch.cuda.empty_cache()
+    return {
+        "plant": f"sparse vs dense attention outputs of this cache through a seeded N(0, {sigma}^2/{H}) LM head, "
+                 f"vocab {vocab}, T = 1",
+        "target_p5": 0.86, "gain": 6.0, "schedule": "s * (1024 + 0.1 * L) tokens, pages of 16, 2 .. cap",
+        "start_scale": 1.0 / 16, "steps": steps, "p5": [round(float(x), 4) for x in p5],
+        "mean_budget_pages": [round(float(x), 1) for x in mb], "final_scale": float(scale.item()),
+        "settled_step": settled, "final_p5": float(p5[-1]),
+        "control_step_us": t_loop * 1e6, "update_us": t_upd * 1e6,
+        "timing": "control_step: the whole loop body (update, select, sparse decode, LM-head GEMM, acceptance, "
+                  "tail) averaged over the steps under one event pair; update: the controller call alone, "
+                  "K times back to back",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -473,6 +545,8 @@ def main():
     verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 2 * K_steps) \
         if not args.no_verify else None
     shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
+    control = budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap,
+                                  timed_loop) if not args.no_control else None
 
     # algorithmic bytes averaged over the steps of each region (lengths grow by one per step)
     def mean_bytes(first_step):
@@ -538,6 +612,7 @@ def main():
         "tail_stats": tail,
         "verify": verify,
         "shared_prefix": shared,
+        "budget_control": control,
         "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
                   "timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
         "rows": rows_out,

@@ -316,6 +316,44 @@ spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int 
  */
 spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream);
 
+/*
+ * spdec_budget_update - sparsity-schedule controller: one correction of the
+ * per-sequence budgets from the on-device tail statistic (Sparrow project
+ * page, "Control Study 1": the budget grows with the generated length so the
+ * per-token mismatch stays roughly constant, and the lower 5th percentile of
+ * the per-token acceptance is held at a threshold, 0.86 in its takeaway; the
+ * page gives no control law, so this one is a stated reading).
+ *
+ * With p5 = tail[1] (as written by spdec_tail_stats) and s = *scale:
+ *   s' = clamp(s * (1 + gain * (target - p5)), scale_min, scale_max)
+ *   budget_pages[b] = clamp(ceil(s' * (base_tokens + tokens_per_token * L_b) / page_size), 2, max_budget_pages)
+ * with L_b = seq_lens[b], every operation one fp32 rounding in that order (no
+ * fused multiply-add). A tail below the target raises every budget, one above
+ * it lowers them, one on target leaves them. A non-finite p5 leaves s
+ * unchanged; a non-finite or non-positive *scale restarts from scale_max.
+ * *scale is overwritten with s'.
+ *
+ * tail: fp32 [2] (device); scale: fp32 [1] (device, caller-owned state,
+ * e.g. 1.0 at the start); seq_lens: int32 [batch]; budget_pages: int32 [batch]
+ * out (may be the budget array spdec_select_pages reads next). Host checks:
+ * 0 < target <= 1, gain >= 0, 0 < scale_min <= scale_max, base_tokens >= 0,
+ * tokens_per_token >= 0 (all finite), page_size a power of two in 1 .. 2^15,
+ * 2 <= max_budget_pages <= 32768, 1 <= batch <= 65536 (SPDEC_ERR_INVALID
+ * otherwise). No workspace.
+ */
+typedef struct spdec_budget_params {
+  float target;            /* held 5th percentile of the acceptance */
+  float gain;              /* relative scale change per unit of (target - p5) */
+  float scale_min, scale_max;
+  float base_tokens;       /* schedule at length 0, in tokens */
+  float tokens_per_token;  /* schedule growth per cached token */
+  int32_t page_size;       /* tokens per page */
+  int32_t max_budget_pages;
+} spdec_budget_params;
+
+spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t* seq_lens, int batch,
+                                 const spdec_budget_params* params, int32_t* budget_pages, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -248,6 +248,24 @@ spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int 
                                            static_cast<hipStream_t>(stream)));
 }
 
+spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t* seq_lens, int batch,
+                                 const spdec_budget_params* params, int32_t* budget_pages, void* stream) {
+  if (!tail || !scale || !seq_lens || !params || !budget_pages) return SPDEC_ERR_INVALID;
+  const spdec_budget_params& p = *params;
+  auto fin = [](float x) { return isfinite(x); };
+  if (!fin(p.target) || !(p.target > 0.f) || !(p.target <= 1.f)) return SPDEC_ERR_INVALID;
+  if (!fin(p.gain) || !(p.gain >= 0.f)) return SPDEC_ERR_INVALID;
+  if (!fin(p.scale_min) || !fin(p.scale_max) || !(p.scale_min > 0.f) || !(p.scale_min <= p.scale_max))
+    return SPDEC_ERR_INVALID;
+  if (!fin(p.base_tokens) || !(p.base_tokens >= 0.f) || !fin(p.tokens_per_token) || !(p.tokens_per_token >= 0.f))
+    return SPDEC_ERR_INVALID;
+  if (p.page_size < 1 || p.page_size > (1 << 15) || (p.page_size & (p.page_size - 1)) != 0) return SPDEC_ERR_INVALID;
+  if (p.max_budget_pages < 2 || p.max_budget_pages > 32768) return SPDEC_ERR_INVALID;
+  if (batch < 1 || batch > 65536) return SPDEC_ERR_INVALID;
+  return from_hip(spdec::launch_budget_update(tail, scale, seq_lens, batch, p, budget_pages,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream) {
   if (!alpha || !out || rows < 1) return SPDEC_ERR_INVALID;
   if (rows > spdec::kTailMaxRows) return SPDEC_ERR_UNSUPPORTED;

@@ -342,8 +342,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArg
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);
     const int j = (int)(w - ubase / R);  // this wave's chunk of the unit
-    const int L = max(c.seq_lens[b], 0);
-    const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+    int L = c.seq_lens[b];
+    const int first = list_first<SPARSE>(a, b);
+    // List entries come 64 at a time, one per lane, read at clamped indices
+    // (entry < the unit's segment end) so that no load waits on a branch.
+    auto list_raw = [&](int wb) -> int {
+      const int e = min(wb + lane, seg_end - ubase - 1);
+      return SPARSE ? a.sel_idx[(int64_t)u * a.list_cap + e] : first + e;
+    };
+    int raw = list_raw(pos - ubase);
 
     // A operands: row r16 holds query head (r16 + 4*set) % G.
     u32x4 qa[NSET][NJ];
@@ -354,6 +361,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArg
       for (int jj = 0; jj < NJ; ++jj)
         qa[st][jj] = load16(qp + ((int64_t)b * c.hq + g * G + h) * D + 32 * jj + 8 * q4);
     }
+    // Length, queries and the first list window share one wait.
+    hold(L);
+    hold(raw);
+#pragma unroll
+    for (int st = 0; st < NSET; ++st) {
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) hold(qa[st][jj]);
+    }
+    L = max(L, 0);
+    const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
     float m[G], lsum[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -366,17 +383,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArg
     for (int wb = pos - ubase; wb < seg_end - ubase; wb += kWave) {
       // Window of up to 64 entries: lane i holds entry wb+i's physical page and valid tokens.
       const int nwin = min(kWave, seg_end - ubase - wb);
-      int phys_w = 0, valid_w = 0;
-      if (lane < nwin) {
-        const int logical = SPARSE ? a.sel_idx[(int64_t)u * a.list_cap + wb + lane] : list_first<SPARSE>(a, b) + wb + lane;
-        if (logical >= 0 && logical < P) {
-          const int ph = c.page_table[(int64_t)b * c.max_pages + logical];
-          if (ph >= 0 && ph < c.num_phys) {
-            phys_w = ph;
-            valid_w = min(c.page_size, L - logical * c.page_size);
-          }
-        }
-      }
+      if (wb != pos - ubase) raw = list_raw(wb);
+      const int logical = raw;
+      const int ph = c.page_table[(int64_t)b * c.max_pages + min(max(logical, 0), c.max_pages - 1)];
+      const bool ok = lane < nwin && logical >= 0 && logical < P && ph >= 0 && ph < c.num_phys;
+      const int phys_w = ok ? ph : 0;
+      const int valid_w = ok ? min(c.page_size, L - logical * c.page_size) : 0;
       const int ntiles = ((nwin << c.ps_log2) + 15) >> 4;
 
       // Tiles of 16 stream tokens. For every supported page size the entry of

@@ -85,6 +85,8 @@ hipError_t launch_spec_accept(const float* p, const float* q, int batch, int k, 
                               int32_t* n_accepted, int32_t* token, void* ws, hipStream_t s);
 constexpr int kTailMaxRows = 8192;  // values the tail statistics sort in LDS
 hipError_t launch_tail_stats(const float* alpha, int n, float* out, hipStream_t s);
+hipError_t launch_budget_update(const float* tail, float* state, const int32_t* seq_lens, int batch,
+                                const spdec_budget_params& p, int32_t* budget, hipStream_t s);
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
                              float* alpha, void* ws, hipStream_t s);
 

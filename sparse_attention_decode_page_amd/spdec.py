@@ -27,7 +27,7 @@ ABI_FUNCTIONS = (
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
-    "spdec_acceptance", "spdec_tail_stats",
+    "spdec_acceptance", "spdec_tail_stats", "spdec_budget_update",
 )
 
 
@@ -39,6 +39,15 @@ class CacheDesc(ctypes.Structure):
         ("num_phys_pages", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("kminmax", ctypes.c_void_p),
         ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+class BudgetParams(ctypes.Structure):
+    """Mirror of ``struct spdec_budget_params`` (controller settings)."""
+    _fields_ = [
+        ("target", ctypes.c_float), ("gain", ctypes.c_float), ("scale_min", ctypes.c_float),
+        ("scale_max", ctypes.c_float), ("base_tokens", ctypes.c_float), ("tokens_per_token", ctypes.c_float),
+        ("page_size", ctypes.c_int32), ("max_budget_pages", ctypes.c_int32),
     ]
 
 
@@ -75,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "spdec_acceptance_workspace_bytes": (SZ, [I, I]),
         "spdec_acceptance": (I, [P, P, I, I, I64, F, P, P, SZ, P]),
         "spdec_tail_stats": (I, [P, I, P, P]),
+        "spdec_budget_update": (I, [P, P, P, I, ctypes.POINTER(BudgetParams), P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -379,3 +389,20 @@ def tail_stats(alpha, out=None):
     _need(out, "out", torch.float32, (2,))
     _check(lib().spdec_tail_stats(_ptr(alpha), int(alpha.shape[0]), _ptr(out), _stream()), "spdec_tail_stats")
     return out
+
+
+def budget_update(tail, scale, seq_lens, params: BudgetParams, budget_pages=None):
+    """One controller step on the device: tail [2] (mean, p5), scale [1] state (updated in place),
+    seq_lens [batch] int32 -> budget_pages [batch] int32."""
+    _need(tail, "tail", torch.float32, (2,))
+    _need(scale, "scale", torch.float32, (1,))
+    if not isinstance(seq_lens, torch.Tensor) or seq_lens.dim() != 1:
+        raise ValueError("seq_lens must be a 1-D tensor")
+    batch = int(seq_lens.shape[0])
+    _need(seq_lens, "seq_lens", torch.int32, (batch,))
+    if budget_pages is None:
+        budget_pages = torch.empty(batch, dtype=torch.int32, device=seq_lens.device)
+    _need(budget_pages, "budget_pages", torch.int32, (batch,))
+    _check(lib().spdec_budget_update(_ptr(tail), _ptr(scale), _ptr(seq_lens), batch, ctypes.byref(params),
+                                     _ptr(budget_pages), _stream()), "spdec_budget_update")
+    return budget_pages

@@ -40,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 19
+    assert len(names) == len(S.ABI_FUNCTIONS) == 20
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -211,6 +211,35 @@ def test_select_shared_checks(L):
     assert call(N=16, desc=e) == -2        # more than 8 members per group
     f = _desc(batch=4, dtype=S.SPDEC_F32)
     assert call(desc=f) == -2
+
+
+def test_budget_update_checks(L):
+    def call(batch=64, tail=FAKE, scale=FAKE, lens=FAKE, out=FAKE, **kw):
+        p = dict(target=0.86, gain=0.5, scale_min=0.125, scale_max=8.0, base_tokens=1024.0, tokens_per_token=0.125,
+                 page_size=16, max_budget_pages=256)
+        p.update(kw)
+        prm = S.BudgetParams(**p)
+        return L.spdec_budget_update(tail, scale, lens, batch, ctypes.byref(prm), out, None)
+
+    assert call(tail=None) == -1
+    assert call(scale=None) == -1
+    assert call(lens=None) == -1
+    assert call(out=None) == -1
+    assert call(batch=0) == -1
+    assert call(batch=65537) == -1
+    assert call(target=0.0) == -1
+    assert call(target=1.5) == -1
+    assert call(target=float("nan")) == -1
+    assert call(gain=-0.1) == -1
+    assert call(gain=float("inf")) == -1
+    assert call(scale_min=0.0) == -1
+    assert call(scale_min=2.0, scale_max=1.0) == -1
+    assert call(base_tokens=-1.0) == -1
+    assert call(tokens_per_token=-0.5) == -1
+    assert call(page_size=12) == -1
+    assert call(page_size=0) == -1
+    assert call(max_budget_pages=1) == -1
+    assert call(max_budget_pages=40000) == -1
 
 
 def test_tail_stats_checks(L):
