@@ -8,5 +8,6 @@ from .page_sparse import __all__ as _page_sparse_all
 from .speculative import *  # noqa: F401,F403
 from .speculative import __all__ as _speculative_all
 from . import control  # noqa: F401  (the sparsity-schedule controller: oracle.control)
+from . import top_p  # noqa: F401  (score-mass page selection: oracle.top_p)
 
 __all__ = list(_page_sparse_all) + list(_speculative_all)
