@@ -21,7 +21,8 @@ the step captured once in a HIP graph and replayed; `verify` times the dense
 verification of a 6-token draft (7 positions) and exact speculative sampling
 on the same cache; `shared_prefix` times the dense decode and the page
 selection of a grouped batch (8 prompts x 8 samples) per sequence and with
-shared prompt pages read once; `budget_control` runs the sparsity-schedule
+shared prompt pages read once; `top_p` times score-mass page selection
+beside the Top-B one; `budget_control` runs the sparsity-schedule
 controller in a closed loop on the device (budgets, sparse path, a seeded
 random LM head, acceptance, tail statistics); `cpu_baseline` times the CPU
 oracle on a bounded sample of the same step.
@@ -58,6 +59,7 @@ def parse():
     ap.add_argument("--no-verify", action="store_true", help="skip the verification / speculative-sampling rows")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix (grouped prompts) rows")
     ap.add_argument("--no-control", action="store_true", help="skip the closed-loop budget controller rows")
+    ap.add_argument("--no-top-p", action="store_true", help="skip the score-mass (top-p) selection rows")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -378,6 +380,50 @@ def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_
     }
 
 
+def top_p_rows(spec, cache, q, budget, dev, timed_loop):
+    """Score-mass (top-p) selection on the step's cache: its time beside the Top-B selection's, the pages it
+    keeps without a cap (the budget then follows the query) and under the per-sequence budgets, and the
+    sparse path with it."""
+    import torch
+    from sparse_attention_decode_page_amd import spdec
+    cap = cache.max_pages
+    sel_idx = torch.zeros((spec.batch, spec.num_kv_heads, cap), dtype=torch.int32, device=dev)
+    sel_cnt = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
+    ws_sel = torch.zeros(spdec.select_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
+    ws_sp = torch.zeros(spdec.decode_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
+    o_s = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+    l_s = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
+    res = {"score_scale": 1.0 / (spec.group * math.sqrt(spec.head_dim))}
+
+    def topb():
+        spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
+
+    for _ in range(3):
+        topb()
+    res["select_top_b_us"] = timed_loop(lambda i: topb()) * 1e6
+    res["top_b_mean_pages"] = float(sel_cnt.float().mean())
+    for name, p, bud in (("p0.5", 0.5, None), ("p0.9", 0.9, None), ("p0.9_budget_capped", 0.9, budget)):
+        def sel(p=p, bud=bud):
+            spdec.select_pages_top_p(cache, q, p, cap, budget_pages=bud, sel_idx=sel_idx, sel_cnt=sel_cnt,
+                                     workspace=ws_sel)
+
+        def path(p=p, bud=bud):
+            sel(p, bud)
+            spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
+
+        for _ in range(3):
+            path()
+        t_sel = timed_loop(lambda i: sel())
+        kept = sel_cnt.float()
+        t_path = timed_loop(lambda i: path())
+        res[name] = {"select_us": t_sel * 1e6, "mean_pages": float(kept.mean()), "min_pages": float(kept.min()),
+                     "max_pages": float(kept.max()), "sparse_path_us": t_path * 1e6}
+    del sel_idx, sel_cnt, ws_sel, ws_sp
+    torch.cuda.empty_cache()
+    res["timing"] = "each call K times back to back under one event pair"
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -545,6 +591,7 @@ def main():
     verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 2 * K_steps) \
         if not args.no_verify else None
     shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
+    topp = top_p_rows(spec, cache, q, budget, dev, timed_loop) if not args.no_top_p else None
     control = budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap,
                                   timed_loop) if not args.no_control else None
 
@@ -612,6 +659,7 @@ def main():
         "tail_stats": tail,
         "verify": verify,
         "shared_prefix": shared,
+        "top_p": topp,
         "budget_control": control,
         "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
                   "timing": "the step captured once in a HIP graph, replayed K times, one event pair"},

@@ -154,6 +154,30 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spdec_select_pages_top_p - score-mass (top-p) page selection: the budget
+ * follows the query instead of being fixed (the RTPurbo abstract on the first
+ * page of the source set argues for dynamic top-p over fixed top-k; the
+ * page-level form is a stated reading).
+ *
+ * Scores s_p as in spdec_select_pages. Page masses w_p = exp(score_scale *
+ * (s_p - max_q s_q)) (fp64). Pages 0 and P-1 are always kept; the pages
+ * 1 .. P-2 are taken in the Top-B order (score descending, lower index first
+ * on equal scores) while the kept mass is below top_p * sum_p w_p and fewer
+ * than K_cap pages are kept, K_cap = min(max(budget_pages[b], 2),
+ * max_budget_pages, P) (budget_pages nullable: then min(max_budget_pages, P)).
+ * P <= 2 keeps every page. The sums run in a fixed order (deterministic).
+ *
+ * 0 < top_p <= 1, score_scale >= 0 (finite; 1/(G*sqrt(D)) reads the bound,
+ * which sums the G query heads, as a per-head logit). Outputs and workspace
+ * as spdec_select_pages. Requires max_pages_per_seq - 2 <= 8192
+ * (SPDEC_ERR_UNSUPPORTED otherwise).
+ */
+spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, float top_p, float score_scale,
+                                      const int32_t* budget_pages, int max_budget_pages, int32_t* sel_idx,
+                                      int32_t* sel_cnt, float* scores_out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * spdec_select_pages_shared - spdec_select_pages for groups of sequences that
  * share their leading pages (a prompt sampled several times; the Sparrow
  * project page's cost model, "Control Study 2", charges the prompt once per

@@ -112,6 +112,25 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
                                        static_cast<hipStream_t>(stream)));
 }
 
+spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, float top_p, float score_scale,
+                                      const int32_t* budget_pages, int max_budget_pages, int32_t* sel_idx,
+                                      int32_t* sel_cnt, float* scores_out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.kminmax || !q || !sel_idx || !sel_cnt) return SPDEC_ERR_INVALID;
+  if (!aligned16(v.kminmax) || !aligned16(q)) return SPDEC_ERR_INVALID;
+  if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
+  if (!isfinite(top_p) || !(top_p > 0.f) || !(top_p <= 1.f)) return SPDEC_ERR_INVALID;
+  if (!isfinite(score_scale) || !(score_scale >= 0.f)) return SPDEC_ERR_INVALID;
+  if (v.max_pages - 2 > spdec::kTopPMaxMiddle) return SPDEC_ERR_UNSUPPORTED;
+  if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
+    return SPDEC_ERR_WORKSPACE;
+  return from_hip(spdec::launch_select_top_p(v, q, top_p, score_scale, budget_pages, max_budget_pages, sel_idx,
+                                             sel_cnt, scores_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
 spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, int group_size,
                                        const int32_t* shared_pages, const int32_t* budget_pages,
                                        int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,

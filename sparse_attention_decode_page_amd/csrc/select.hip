@@ -652,15 +652,16 @@ size_t select_workspace_bytes(const CacheView& c) {
   return (size_t)c.batch * c.hkv * c.max_pages * sizeof(float);
 }
 
+hipError_t launch_score(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+  if (c.dtype == SPDEC_BF16)
+    return c.head_dim == 64 ? score_impl<BF16, 64>(c, q, scores, s) : score_impl<BF16, 128>(c, q, scores, s);
+  return c.head_dim == 64 ? score_impl<F32, 64>(c, q, scores, s) : score_impl<F32, 128>(c, q, scores, s);
+}
+
 hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budget, int max_budget, int32_t* sel_idx,
                          int32_t* sel_cnt, float* scores_out, void* ws, hipStream_t s) {
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
-  hipError_t e;
-  if (c.dtype == SPDEC_BF16) {
-    e = c.head_dim == 64 ? score_impl<BF16, 64>(c, q, scores, s) : score_impl<BF16, 128>(c, q, scores, s);
-  } else {
-    e = c.head_dim == 64 ? score_impl<F32, 64>(c, q, scores, s) : score_impl<F32, 128>(c, q, scores, s);
-  }
+  hipError_t e = launch_score(c, q, scores, s);
   if (e != hipSuccess) return e;
   return launch_topk(c, budget, max_budget, scores, sel_idx, sel_cnt, s);
 }

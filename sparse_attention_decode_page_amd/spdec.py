@@ -22,7 +22,7 @@ SPDEC_F32, SPDEC_BF16 = 0, 1
 
 ABI_FUNCTIONS = (
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
-    "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_select_pages_shared",
+    "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_select_pages_shared", "spdec_select_pages_top_p",
     "spdec_decode_workspace_bytes",
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         "spdec_select_workspace_bytes": (SZ, [D, I]),
         "spdec_select_pages": (I, [D, P, P, I, P, P, P, P, SZ, P]),
         "spdec_select_pages_shared": (I, [D, P, I, P, P, I, P, P, P, P, SZ, P]),
+        "spdec_select_pages_top_p": (I, [D, P, F, F, P, I, P, P, P, P, SZ, P]),
         "spdec_decode_workspace_bytes": (SZ, [D, I]),
         "spdec_sparse_decode": (I, [D, P, P, P, I, F, P, P, P, SZ, P]),
         "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
@@ -201,6 +202,35 @@ def select_pages(cache: PagedCache, q, budget_pages, max_budget_pages: int, sel_
     _check(lib().spdec_select_pages(ctypes.byref(cache.desc), _ptr(q), _ptr(budget_pages), int(max_budget_pages),
                                     _ptr(sel_idx), _ptr(sel_cnt), _ptr(scores_out), ws_ptr, ws_bytes, _stream()),
            "spdec_select_pages")
+    return sel_idx, sel_cnt
+
+
+def select_pages_top_p(cache: PagedCache, q, top_p: float, max_budget_pages: int, score_scale: Optional[float] = None,
+                       budget_pages=None, sel_idx=None, sel_cnt=None, scores_out=None, workspace=None):
+    """Score-mass page selection: keep pages (sink, local, then by score) until top_p of the page mass;
+    score_scale defaults to 1/(G*sqrt(D)); budget_pages (optional) caps each sequence."""
+    _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    if budget_pages is not None:
+        _need(budget_pages, "budget_pages", torch.int32, (cache.batch,))
+    if score_scale is None:
+        score_scale = 1.0 / ((cache.num_q_heads // cache.num_kv_heads) * math.sqrt(cache.head_dim))
+    dev = cache.device
+    if sel_idx is None:
+        sel_idx = torch.zeros((cache.batch, cache.num_kv_heads, max_budget_pages), dtype=torch.int32, device=dev)
+    if sel_cnt is None:
+        sel_cnt = torch.zeros((cache.batch, cache.num_kv_heads), dtype=torch.int32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, (cache.batch, cache.num_kv_heads, max_budget_pages))
+    _need(sel_cnt, "sel_cnt", torch.int32, (cache.batch, cache.num_kv_heads))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.float32, (cache.batch, cache.num_kv_heads, cache.max_pages))
+        ws_ptr, ws_bytes = _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size()
+    else:
+        workspace = _workspace(select_workspace_bytes(cache, max_budget_pages), dev, workspace)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check(lib().spdec_select_pages_top_p(ctypes.byref(cache.desc), _ptr(q), float(top_p), float(score_scale),
+                                          _ptr(budget_pages), int(max_budget_pages), _ptr(sel_idx), _ptr(sel_cnt),
+                                          _ptr(scores_out), ws_ptr, ws_bytes, _stream()),
+           "spdec_select_pages_top_p")
     return sel_idx, sel_cnt
 
 

@@ -40,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 20
+    assert len(names) == len(S.ABI_FUNCTIONS) == 21
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -211,6 +211,26 @@ def test_select_shared_checks(L):
     assert call(N=16, desc=e) == -2        # more than 8 members per group
     f = _desc(batch=4, dtype=S.SPDEC_F32)
     assert call(desc=f) == -2
+
+
+def test_select_top_p_checks(L):
+    d = _desc(batch=4)
+    need = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
+
+    def call(p=0.9, c=0.05, kmax=16, q=FAKE, ws=FAKE, nbytes=need, desc=d):
+        return L.spdec_select_pages_top_p(ctypes.byref(desc), q, p, c, None, kmax, FAKE, FAKE, None, ws, nbytes, None)
+
+    assert call(p=0.0) == -1
+    assert call(p=1.5) == -1
+    assert call(p=float("nan")) == -1
+    assert call(c=-1.0) == -1
+    assert call(c=float("inf")) == -1
+    assert call(kmax=1) == -1
+    assert call(q=None) == -1
+    assert call(nbytes=need - 1) == -3
+    assert call(ws=None, nbytes=0) == -3
+    big = _desc(batch=1, max_pages_per_seq=8195, num_phys_pages=9000)
+    assert call(desc=big, nbytes=1 << 30) == -2          # 8193 middle pages: more than one sort holds
 
 
 def test_budget_update_checks(L):
