@@ -165,12 +165,13 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
  * on equal scores) while the kept mass is below top_p * sum_p w_p and fewer
  * than K_cap pages are kept, K_cap = min(max(budget_pages[b], 2),
  * max_budget_pages, P) (budget_pages nullable: then min(max_budget_pages, P)).
- * P <= 2 keeps every page. The sums run in a fixed order (deterministic).
+ * P <= 2 keeps every page. Masses are summed as 2^-48 fixed-point integers
+ * (order-independent, so the result is deterministic); the target is
+ * ceil(top_p * total) in those units.
  *
  * 0 < top_p <= 1, score_scale >= 0 (finite; 1/(G*sqrt(D)) reads the bound,
  * which sums the G query heads, as a per-head logit). Outputs and workspace
- * as spdec_select_pages. Requires max_pages_per_seq - 2 <= 8192
- * (SPDEC_ERR_UNSUPPORTED otherwise).
+ * as spdec_select_pages.
  */
 spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, float top_p, float score_scale,
                                       const int32_t* budget_pages, int max_budget_pages, int32_t* sel_idx,

@@ -124,7 +124,6 @@ spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, f
   if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
   if (!isfinite(top_p) || !(top_p > 0.f) || !(top_p <= 1.f)) return SPDEC_ERR_INVALID;
   if (!isfinite(score_scale) || !(score_scale >= 0.f)) return SPDEC_ERR_INVALID;
-  if (v.max_pages - 2 > spdec::kTopPMaxMiddle) return SPDEC_ERR_UNSUPPORTED;
   if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_select_top_p(v, q, top_p, score_scale, budget_pages, max_budget_pages, sel_idx,

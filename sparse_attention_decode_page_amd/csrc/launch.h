@@ -55,7 +55,6 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
 // Page scores of every (sequence, KV head) into scores[unit][max_pages].
 hipError_t launch_score(const CacheView& c, const void* q, float* scores, hipStream_t s);
 // Score-mass (top-p) selection: scoring, then the kept set per unit.
-constexpr int kTopPMaxMiddle = 8192;  // middle pages a unit's sort holds in LDS
 hipError_t launch_select_top_p(const CacheView& c, const void* q, float top_p, float score_scale,
                                const int32_t* budget, int max_budget, int32_t* sel_idx, int32_t* sel_cnt,
                                float* scores, void* ws, hipStream_t s);

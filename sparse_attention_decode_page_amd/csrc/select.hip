@@ -478,76 +478,72 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // key - min_key: the span of real scores is a few exponent steps, so the first
 // 8-bit digit already spreads the keys over the histogram and 2-3 passes
 // usually suffice.
+template <int NT>
+struct TopBShared {
+  uint32_t hist[256];
+  uint32_t red[NT / kWave][2];
+  int digit, above;
+  int wave_sums[NT / kWave][2];
+};
+
+// The keys of middle pages 1 .. M (M = P - 2) and their block minimum and
+// significant bit count.
 template <int KPT, int NT>
-__global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const int32_t* __restrict__ budget,
-                                                           int cap, const float* __restrict__ scores,
-                                                           int32_t* __restrict__ sel_idx,
-                                                           int32_t* __restrict__ sel_cnt) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_red[NT / kWave][2];
-  __shared__ int s_digit, s_above;
-  __shared__ int s_wave[NT / kWave][2];
-  const int unit = blockIdx.x;
-  const int b = unit / c.hkv;
+__device__ __forceinline__ void load_keys(const float* srow, int M, uint32_t (&key)[KPT], uint32_t& kmin, int& nbits,
+                                          TopBShared<NT>& sh) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int L = c.seq_lens[b];
-  const int P = min((max(L, 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
-  int32_t* out = sel_idx + (int64_t)unit * cap;
-  const int K = min(min(max(budget[b], 2), cap), P);
-  if (K >= P) {
-    for (int i = tid; i < P; i += NT) out[i] = i;
-    if (tid == 0) sel_cnt[unit] = P;
-    return;
-  }
-  const int M = P - 2;
-  const int need = K - 2;
-  if (tid == 0) {
-    out[0] = 0;
-    out[K - 1] = P - 1;
-    sel_cnt[unit] = K;
-  }
-  if (need == 0) return;
-  const float* srow = scores + (int64_t)unit * c.max_pages + 1;
   const int i0 = tid * KPT;
-  uint32_t key[KPT];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  kmin = 0xFFFFFFFFu;
+  uint32_t kmax = 0u;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     const int i = i0 + r;
-    key[r] = i < M ? score_key(srow[i]) : 0u;
+    key[r] = i < M ? score_key(srow[i + 1]) : 0u;
     if (i < M) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
   }
-  // block min / max of the keys
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
   }
-  if (lane == 0) { s_red[wave][0] = kmin; s_red[wave][1] = kmax; }
+  if (lane == 0) { sh.red[wave][0] = kmin; sh.red[wave][1] = kmax; }
   __syncthreads();
-  kmin = s_red[0][0];
-  kmax = s_red[0][1];
+  kmin = sh.red[0][0];
+  kmax = sh.red[0][1];
 #pragma unroll
-  for (int w = 1; w < NT / kWave; ++w) { kmin = min(kmin, s_red[w][0]); kmax = max(kmax, s_red[w][1]); }
+  for (int w = 1; w < NT / kWave; ++w) { kmin = min(kmin, sh.red[w][0]); kmax = max(kmax, sh.red[w][1]); }
   const uint32_t span = kmax - kmin;
-  const int nbits = span == 0 ? 0 : 32 - __clz((int)span);
+  nbits = span == 0 ? 0 : 32 - __clz((int)span);
+  __syncthreads();  // red is reused
+}
 
+template <int KPT, int NT>
+__device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M, int need, uint32_t T, int eq_take,
+                                               int32_t* out, TopBShared<NT>& sh);
+
+// Writes the `need` highest keys of the middle pages (equal keys in page
+// order) ascending to out[1 .. need].
+template <int KPT, int NT>
+__device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int need, uint32_t kmin, int nbits,
+                                         int32_t* out, TopBShared<NT>& sh) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int i0 = tid * KPT;
   uint32_t prefix = 0, mask = 0;
   int remaining = need;
   for (int hi = nbits; hi > 0; hi -= 8) {
     const int lo = max(hi - 8, 0);
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const uint32_t off = key[r] - kmin;
-      if (i0 + r < M && (off & mask) == prefix) atomicAdd(&hist[(off >> lo) & dmask], 1u);
+      if (i0 + r < M && (off & mask) == prefix) atomicAdd(&sh.hist[(off >> lo) & dmask], 1u);
     }
     __syncthreads();
     if (tid < kWave) {
       const int top = 255 - 4 * tid;
-      const int c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+      const int c0 = sh.hist[top], c1 = sh.hist[top - 1], c2 = sh.hist[top - 2], c3 = sh.hist[top - 3];
       const int tot = c0 + c1 + c2 + c3;
       const int incl = wave_incl_scan(tot);
       const int excl = incl - tot;
@@ -558,19 +554,26 @@ __global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const 
         else if (rr <= c0 + c1) { digit = top - 1; above = excl + c0; }
         else if (rr <= c0 + c1 + c2) { digit = top - 2; above = excl + c0 + c1; }
         else { digit = top - 3; above = excl + c0 + c1 + c2; }
-        s_digit = digit;
-        s_above = above;
+        sh.digit = digit;
+        sh.above = above;
       }
     }
     __syncthreads();
-    prefix |= (uint32_t)s_digit << lo;
+    prefix |= (uint32_t)sh.digit << lo;
     mask |= dmask << lo;
-    remaining -= s_above;
+    remaining -= sh.above;
     __syncthreads();
   }
-  const uint32_t T = kmin + prefix;
-  const int eq_take = remaining;
+  write_selected<KPT, NT>(key, M, need, kmin + prefix, remaining, out, sh);
+}
 
+// Writes the middle pages with key > T and the first eq_take pages with key
+// == T (page order) ascending to out[1 .. need].
+template <int KPT, int NT>
+__device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M, int need, uint32_t T, int eq_take,
+                                               int32_t* out, TopBShared<NT>& sh) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int i0 = tid * KPT;
   int gt = 0, eq = 0;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
@@ -578,10 +581,10 @@ __global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const 
   }
   const int gt_incl = wave_incl_scan(gt);
   const int eq_incl = wave_incl_scan(eq);
-  if (lane == kWave - 1) { s_wave[wave][0] = gt_incl; s_wave[wave][1] = eq_incl; }
+  if (lane == kWave - 1) { sh.wave_sums[wave][0] = gt_incl; sh.wave_sums[wave][1] = eq_incl; }
   __syncthreads();
   int gt_before = gt_incl - gt, eq_before = eq_incl - eq;
-  for (int w = 0; w < wave; ++w) { gt_before += s_wave[w][0]; eq_before += s_wave[w][1]; }
+  for (int w = 0; w < wave; ++w) { gt_before += sh.wave_sums[w][0]; eq_before += sh.wave_sums[w][1]; }
   int pos = 1 + gt_before + min(eq_before, eq_take);
   int eq_seen = eq_before;
 #pragma unroll
@@ -589,8 +592,217 @@ __global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const 
     if (i0 + r < M) {
       bool take = key[r] > T;
       if (key[r] == T) { take = eq_seen < eq_take; ++eq_seen; }
-      if (take && pos < K - 1) out[pos++] = i0 + r + 1;
+      if (take && pos <= need) out[pos++] = i0 + r + 1;
     }
+  }
+}
+
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const int32_t* __restrict__ budget,
+                                                           int cap, const float* __restrict__ scores,
+                                                           int32_t* __restrict__ sel_idx,
+                                                           int32_t* __restrict__ sel_cnt) {
+  __shared__ TopBShared<NT> sh;
+  const int unit = blockIdx.x;
+  const int b = unit / c.hkv;
+  const int tid = threadIdx.x;
+  const int L = c.seq_lens[b];
+  const int P = min((max(L, 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  int32_t* out = sel_idx + (int64_t)unit * cap;
+  const int K = min(min(max(budget[b], 2), cap), P);
+  if (K >= P) {
+    for (int i = tid; i < P; i += NT) out[i] = i;
+    if (tid == 0) sel_cnt[unit] = P;
+    return;
+  }
+  if (tid == 0) {
+    out[0] = 0;
+    out[K - 1] = P - 1;
+    sel_cnt[unit] = K;
+  }
+  if (K == 2) return;
+  uint32_t key[KPT], kmin;
+  int nbits;
+  load_keys<KPT, NT>(scores + (int64_t)unit * c.max_pages, P - 2, key, kmin, nbits, sh);
+  emit_top<KPT, NT>(key, P - 2, K - 2, kmin, nbits, out, sh);
+}
+
+// Score-mass (top-p) selection over the same keys. The page masses
+// w = exp(c (s - max s)) (fp64, so w <= 1) are summed as 2^-48 fixed-point
+// integers: integer sums do not depend on their order, which keeps the
+// histograms deterministic under LDS atomics. MSB-first radix passes on the
+// keys find the smallest count of middle pages, in the Top-B order, whose
+// mass with the two forced pages reaches ceil(top_p * total); the count is
+// capped, and emit_top writes that many pages exactly as the Top-B select
+// would.
+constexpr double kMassOne = 281474976710656.0;  // 2^48
+
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) void select_topp_reg_kernel(CacheView c, const float* __restrict__ scores,
+                                                           float top_p, float score_scale,
+                                                           const int32_t* __restrict__ budget, int cap,
+                                                           int32_t* __restrict__ sel_idx,
+                                                           int32_t* __restrict__ sel_cnt) {
+  __shared__ TopBShared<NT> sh;
+  __shared__ unsigned long long s_mass[256];
+  __shared__ unsigned long long s_msum[NT / kWave];
+  __shared__ float s_fmax[NT / kWave];
+  __shared__ unsigned long long s_mabove, s_wtie;
+  __shared__ int s_cabove, s_found;
+  const int unit = blockIdx.x;
+  const int b = unit / c.hkv;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int L = c.seq_lens[b];
+  const int P = min((max(L, 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  int32_t* out = sel_idx + (int64_t)unit * cap;
+  if (P <= 2) {
+    if (tid < P) out[tid] = tid;
+    if (tid == 0) sel_cnt[unit] = P;
+    return;
+  }
+  const int kcap = min(min(budget != nullptr ? max(budget[b], 2) : cap, cap), P);
+  const float* srow = scores + (int64_t)unit * c.max_pages;
+  const int M = P - 2;
+  const int i0 = tid * KPT;
+  uint32_t key[KPT], kmin;
+  int nbits;
+  load_keys<KPT, NT>(srow, M, key, kmin, nbits, sh);
+
+  // Masses: the largest score, then fixed-point w for the middle pages.
+  float mx = -INFINITY;
+  for (int i = tid; i < P; i += NT) mx = fmaxf(mx, srow[i]);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) s_fmax[wave] = mx;
+  __syncthreads();
+  mx = s_fmax[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) mx = fmaxf(mx, s_fmax[w]);
+  const double cs = (double)score_scale, dm = (double)mx;
+  auto fixed_mass = [&](float s) {
+    return (unsigned long long)(exp(cs * ((double)s - dm)) * kMassOne + 0.5);
+  };
+  // Up to 16 keys per thread the masses stay in registers; 32 recompute them
+  // (the same value every time) rather than spill.
+  constexpr bool kKeep = KPT <= 16;
+  unsigned long long wf[kKeep ? KPT : 1];
+  auto mass_of = [&](int r) -> unsigned long long {
+    if constexpr (kKeep) return wf[r];
+    return i0 + r < M ? fixed_mass(srow[i0 + r + 1]) : 0ull;
+  };
+  unsigned long long local = 0;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const unsigned long long m = i0 + r < M ? fixed_mass(srow[i0 + r + 1]) : 0ull;
+    if constexpr (kKeep) wf[r] = m;
+    local += m;
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) local += __shfl_xor(local, off);
+  if (lane == 0) s_msum[wave] = local;
+  __syncthreads();
+  unsigned long long middle = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) middle += s_msum[w];
+  const unsigned long long forced = fixed_mass(srow[0]) + fixed_mass(srow[P - 1]);
+  const double tgt = ceil((double)top_p * (double)(forced + middle));
+  int k_mass;
+  uint32_t T_mass = 0;
+  int eq_mass = 0;
+  if ((double)forced >= tgt) {
+    k_mass = 0;
+  } else {
+    // Mass still needed from the middle pages (the crossing exists unless
+    // rounding put the target above the whole mass: then every page is kept).
+    unsigned long long rem = (unsigned long long)tgt - forced;
+    uint32_t prefix = 0, mask = 0;
+    int cnt_above = 0;
+    bool found = rem <= middle;
+    for (int hi = nbits; hi > 0 && found; hi -= 8) {
+      const int lo = max(hi - 8, 0);
+      const uint32_t dmask = (1u << (hi - lo)) - 1u;
+      for (int i = tid; i < 256; i += NT) { sh.hist[i] = 0; s_mass[i] = 0ull; }
+      if (tid == 0) s_found = 0;
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const uint32_t off = key[r] - kmin;
+        if (i0 + r < M && (off & mask) == prefix) {
+          const uint32_t d = (off >> lo) & dmask;
+          atomicAdd(&sh.hist[d], 1u);
+          atomicAdd(&s_mass[d], mass_of(r));
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        const int top = 255 - 4 * tid;
+        const unsigned long long m0 = s_mass[top], m1 = s_mass[top - 1], m2 = s_mass[top - 2], m3 = s_mass[top - 3];
+        const unsigned long long tot = m0 + m1 + m2 + m3;
+        unsigned long long incl = tot;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const unsigned long long y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
+        }
+        const unsigned long long excl = incl - tot;
+        const int c0 = sh.hist[top], c1 = sh.hist[top - 1], c2 = sh.hist[top - 2];
+        const int ctot = c0 + c1 + c2 + sh.hist[top - 3];
+        const int cincl = wave_incl_scan(ctot);
+        const int cexcl = cincl - ctot;
+        if (excl < rem && rem <= incl) {
+          const unsigned long long rr = rem - excl;
+          int digit;
+          unsigned long long above;
+          int cab;
+          if (rr <= m0) { digit = top; above = excl; cab = cexcl; }
+          else if (rr <= m0 + m1) { digit = top - 1; above = excl + m0; cab = cexcl + c0; }
+          else if (rr <= m0 + m1 + m2) { digit = top - 2; above = excl + m0 + m1; cab = cexcl + c0 + c1; }
+          else { digit = top - 3; above = excl + m0 + m1 + m2; cab = cexcl + c0 + c1 + c2; }
+          sh.digit = digit;
+          s_mabove = above;
+          s_cabove = cab;
+          s_found = 1;
+        }
+      }
+      __syncthreads();
+      found = s_found != 0;
+      if (found) {
+        prefix |= (uint32_t)sh.digit << lo;
+        mask |= dmask << lo;
+        rem -= s_mabove;
+        cnt_above += s_cabove;
+      }
+      __syncthreads();
+    }
+    if (found) {
+      // Pages with the threshold key share one score, hence one mass.
+      const uint32_t T = kmin + prefix;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r)
+        if (i0 + r < M && key[r] == T) s_wtie = mass_of(r);
+      __syncthreads();
+      const unsigned long long wt = s_wtie;
+      eq_mass = wt > 0 ? (int)((rem + wt - 1) / wt) : M;
+      k_mass = cnt_above + eq_mass;
+      T_mass = T;
+    } else {
+      k_mass = M;
+    }
+  }
+  const int need = min(min(k_mass, M), kcap - 2);
+  const int K = need + 2;
+  if (tid == 0) {
+    out[0] = 0;
+    out[K - 1] = P - 1;
+    sel_cnt[unit] = K;
+  }
+  if (need == 0) return;
+  if (need == k_mass && k_mass < M) {
+    // The mass decided the count: its threshold key and tie share are the
+    // Top-B order's cut for exactly this many pages.
+    write_selected<KPT, NT>(key, M, need, T_mass, eq_mass, out, sh);
+  } else {
+    emit_top<KPT, NT>(key, M, need, kmin, nbits, out, sh);
   }
 }
 
@@ -664,6 +876,31 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
   hipError_t e = launch_score(c, q, scores, s);
   if (e != hipSuccess) return e;
   return launch_topk(c, budget, max_budget, scores, sel_idx, sel_cnt, s);
+}
+
+hipError_t launch_select_top_p(const CacheView& c, const void* q, float top_p, float score_scale,
+                               const int32_t* budget, int max_budget, int32_t* sel_idx, int32_t* sel_cnt,
+                               float* scores_out, void* ws, hipStream_t s) {
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
+  hipError_t e = launch_score(c, q, scores, s);
+  if (e != hipSuccess) return e;
+  // Size classes as for the Top-B select (8-32 keys per thread).
+  const int middle = c.max_pages - 2;
+  const dim3 grid(c.batch * c.hkv);
+  if (middle <= 256 * 8) {
+    hipLaunchKernelGGL((select_topp_reg_kernel<8, 256>), grid, dim3(256), 0, s, c, scores, top_p, score_scale, budget,
+                       max_budget, sel_idx, sel_cnt);
+  } else if (middle <= 1024 * 8) {
+    hipLaunchKernelGGL((select_topp_reg_kernel<8, 1024>), grid, dim3(1024), 0, s, c, scores, top_p, score_scale,
+                       budget, max_budget, sel_idx, sel_cnt);
+  } else if (middle <= 1024 * 16) {
+    hipLaunchKernelGGL((select_topp_reg_kernel<16, 1024>), grid, dim3(1024), 0, s, c, scores, top_p, score_scale,
+                       budget, max_budget, sel_idx, sel_cnt);
+  } else {
+    hipLaunchKernelGGL((select_topp_reg_kernel<32, 1024>), grid, dim3(1024), 0, s, c, scores, top_p, score_scale,
+                       budget, max_budget, sel_idx, sel_cnt);
+  }
+  return hipGetLastError();
 }
 
 bool select_shared_supported(const CacheView& c, int group_size) {

@@ -1,8 +1,9 @@
 """GPU parity of score-mass (top-p) page selection (spdec_select_pages_top_p).
 
-The kept count is an integer decided by floating point: it must equal the
-oracle's except where the oracle's kept mass lies within 1e-6 (relative) of
-the target on either side of its last page (then it may differ by one). The
+The kept count is an integer decided by floating point (fp64 sums in the
+oracle, 2^-48 fixed-point sums on the GPU): it must equal the oracle's except
+where the oracle's kept mass lies within 1e-6 (relative) of the target on
+either side of its last page (then it may differ by one). The
 kept set must be the Top-K set of the oracle's fp64 scores for the kept count,
 outside the 1e-6 score tie band at the cut.
 """
@@ -122,12 +123,13 @@ def test_top_p_without_cap_and_full_mass():
     _check(wl, 1.0, units, use_budget=False, c=0.0, expect_all=True)   # flat masses, all of them: every page
 
 
-def test_top_p_rejects_long_tables():
-    spec = S.custom_spec("topp-long", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=8,
-                         dtype="bf16", lens=("fixed", 65600), budget=("tokens", 64))   # 8200 pages
-    dw = GS.DeviceWorkload(S.make_workload(spec, seed=0))
-    with pytest.raises(RuntimeError):
-        spdec.select_pages_top_p(dw.cache, dw.q, 0.9, 16)
+@pytest.mark.parametrize("tokens", [65600, 96000, 140000])
+def test_top_p_long_tables(tokens):
+    # 8200, 12000 and 17500 pages: 1024-thread workgroups with 8, 16 and 32 keys per thread
+    spec = S.custom_spec(f"topp-long{tokens}", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=8,
+                         dtype="bf16", lens=("fixed", tokens), budget=("tokens", 64), outlier_channels=2)
+    wl = S.make_workload(spec, seed=3)
+    _check(wl, 0.7, [(0, 0), (0, 1)], use_budget=False)
 
 
 @pytest.mark.slow
