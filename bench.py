@@ -620,7 +620,7 @@ def main():
     # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
     traffic = counter_traffic() if spec.name == WORKLOAD else None
     dense_kernels = ["decode_stream_kernel<128,4,false>", "stream_merge_kernel<128,false>"]
-    sparse_kernels = ["score_stream_kernel<BF16,128,4>", "select_topk_reg_kernel<8>",
+    sparse_kernels = ["score_stream_kernel<BF16,128,4>", "select_topk_reg_kernel<8,256>",
                       "decode_stream_kernel<128,4,true>", "stream_merge_kernel<128,true>"]
 
     def traffic_of(names):
