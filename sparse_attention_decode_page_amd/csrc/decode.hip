@@ -261,6 +261,8 @@ constexpr float kLazyRescale = 8.0f;  // log2 units
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+constexpr int kDecodeMinRange = 4;  // entries: the shortest wave range worth its start-up
+
 struct StreamArgs {
   CacheView c;
   const void* q;
@@ -315,15 +317,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArg
   const CacheView& c = a.c;
   extern __shared__ int s_pre[];         // units + 1
   __shared__ int s_tmp[kDecodeWaves];
+  __shared__ int s_emax[kDecodeWaves];
   const int units = c.batch * c.hkv;
-  for (int u = threadIdx.x; u < units; u += kDecodeThreads) s_pre[u] = unit_entries<SPARSE>(a, u);
+  int emax = 0;
+  for (int u = threadIdx.x; u < units; u += kDecodeThreads) {
+    const int e = unit_entries<SPARSE>(a, u);
+    s_pre[u] = e;
+    emax = max(emax, e);
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) emax = max(emax, __shfl_xor(emax, off));
+  if (threadIdx.x % kWave == 0) s_emax[threadIdx.x / kWave] = emax;
   __syncthreads();
   block_exclusive_scan(s_pre, units, s_tmp);
+#pragma unroll
+  for (int i = 0; i < kDecodeWaves; ++i) emax = max(emax, s_emax[i]);
   const int total = s_pre[units];
   const int lane = threadIdx.x % kWave;
   const int64_t nw = (int64_t)gridDim.x * kDecodeWaves;
   const int64_t w = (int64_t)blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
-  const int64_t R = max<int64_t>((total + nw - 1) / nw, a.rmin);
+  // Ranges of at least ceil(longest list / (jmax - 1)) entries keep every
+  // unit within jmax chunks; the longest list is measured here, so short
+  // lists under a large capacity still spread over every wave.
+  const int64_t rmin = min<int64_t>(a.rmin, max((emax + a.jmax - 2) / (a.jmax - 1), kDecodeMinRange));
+  const int64_t R = max<int64_t>((total + nw - 1) / nw, rmin);
   if (w * R >= total) return;
   int pos = (int)(w * R);
   const int end = (int)min<int64_t>(pos + R, total);
