@@ -9,8 +9,7 @@
 //   pass 2: per chunk, the row's global normalisers from the pass-1 partials
 //           (fixed order), then sum_v min(p_v, q_v) over the chunk;
 //   pass 3: per row, the chunk sums in index order, clamped to [0, 1].
-// The second read of the logits in pass 2 comes from the L2 / last-level cache
-// right after pass 1. No float atomics: results are run-to-run identical.
+// No float atomics: results are run-to-run identical.
 #include "common.h"
 #include "launch.h"
 
@@ -84,16 +83,25 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
   return r;
 }
 
+// Entries times c, each a rounded product (never fused into a later
+// subtraction), so both passes see the same scaled values.
+__device__ __forceinline__ void scale_entries(float* va, float* vb, float c) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) {
+    va[i] = va[i] * c;
+    vb[i] = vb[i] * c;
+  }
+}
+
+// Pass 1 on one chunk: loads both rows' entries (scaled by c) into va, vb and
+// writes the chunk's (max, sum) pair of each row.
 template <bool ALIGNED>
-__global__ __launch_bounds__(kAccThreads) void acc_stats_kernel(AccArgs x) {
-  __shared__ float sh[kAccThreads / kWave];
-  const int r = blockIdx.y, ch = blockIdx.x;
+__device__ __forceinline__ void chunk_stats(const AccArgs& x, int r, int ch, float* va, float* vb, float* sh) {
   const int base = ch * kAccChunk;
-  float va[kAccPer], vb[kAccPer];
   load_row<ALIGNED, kPass1Stream>(x.a + (int64_t)r * x.stride, x.vocab, base, va);
   load_row<ALIGNED, kPass1Stream>(x.b + (int64_t)r * x.stride, x.vocab, base, vb);
-#pragma unroll
-  for (int i = 0; i < kAccPer; ++i) { va[i] *= x.c; vb[i] *= x.c; }
+  scale_entries(va, vb, x.c);
   float ma = va[0], mb = vb[0];
 #pragma unroll
   for (int i = 1; i < kAccPer; ++i) { ma = fmaxf(ma, va[i]); mb = fmaxf(mb, vb[i]); }
@@ -110,6 +118,53 @@ __global__ __launch_bounds__(kAccThreads) void acc_stats_kernel(AccArgs x) {
   }
 }
 
+// The row normalisers from the pass-1 partials (fixed order), by the first wave.
+__device__ __forceinline__ void row_norms(const AccArgs& x, int r, float* s_norm) {
+  if (threadIdx.x < kWave) {
+    // Lane i folds chunks i, i+64, ...
+    const float* p = x.part + (int64_t)r * x.nchunk * 4;
+    float ma = kNegBig, mb = kNegBig;
+    for (int j = threadIdx.x; j < x.nchunk; j += kWave) { ma = fmaxf(ma, p[4 * j]); mb = fmaxf(mb, p[4 * j + 2]); }
+    ma = group_max<kWave>(ma);
+    mb = group_max<kWave>(mb);
+    float sa = 0.f, sb = 0.f;
+    for (int j = threadIdx.x; j < x.nchunk; j += kWave) {
+      sa = fmaf(exp2f(p[4 * j] - ma), p[4 * j + 1], sa);
+      sb = fmaf(exp2f(p[4 * j + 2] - mb), p[4 * j + 3], sb);
+    }
+    sa = group_sum<kWave>(sa);
+    sb = group_sum<kWave>(sb);
+    if (threadIdx.x == 0) { s_norm[0] = ma; s_norm[1] = 1.f / sa; s_norm[2] = mb; s_norm[3] = 1.f / sb; }
+  }
+  __syncthreads();
+}
+
+// Pass 2 on one chunk from its scaled entries: sum_v min(p_v, q_v).
+__device__ __forceinline__ void chunk_min(const AccArgs& x, int r, int ch, const float* va, const float* vb,
+                                          const float* s_norm, float* sh) {
+  const float ma = s_norm[0], ia = s_norm[1], mb = s_norm[2], ib = s_norm[3];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) s += fminf(exp2f(va[i] - ma) * ia, exp2f(vb[i] - mb) * ib);
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) x.csum[(int64_t)r * x.nchunk + ch] = s;
+}
+
+// Pass 3 for one row: the chunk sums in index order, clamped, by one wave.
+__device__ __forceinline__ void row_final(const AccArgs& x, int r) {
+  float s = 0.f;
+  for (int j = threadIdx.x; j < x.nchunk; j += kWave) s += x.csum[(int64_t)r * x.nchunk + j];
+  s = group_sum<kWave>(s);
+  if (threadIdx.x == 0) x.alpha[r] = fminf(1.f, fmaxf(0.f, s));
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kAccThreads) void acc_stats_kernel(AccArgs x) {
+  __shared__ float sh[kAccThreads / kWave];
+  float va[kAccPer], vb[kAccPer];
+  chunk_stats<ALIGNED>(x, blockIdx.y, blockIdx.x, va, vb, sh);
+}
+
 template <bool ALIGNED>
 __global__ __launch_bounds__(kAccThreads) void acc_min_kernel(AccArgs x) {
   __shared__ float sh[kAccThreads / kWave];
@@ -121,38 +176,12 @@ __global__ __launch_bounds__(kAccThreads) void acc_min_kernel(AccArgs x) {
   const int base = ch * kAccChunk;
   load_row<ALIGNED, kPass2Stream>(x.a + (int64_t)r * x.stride, x.vocab, base, va);
   load_row<ALIGNED, kPass2Stream>(x.b + (int64_t)r * x.stride, x.vocab, base, vb);
-  if (threadIdx.x < kWave) {
-    // Row normalisers from the chunk partials: lane i folds chunks i, i+64, ...
-    const float* p = x.part + (int64_t)r * x.nchunk * 4;
-    float ma = kNegBig, mb = kNegBig;
-    for (int j = threadIdx.x; j < x.nchunk; j += kWave) { ma = fmaxf(ma, p[4 * j]); mb = fmaxf(mb, p[4 * j + 2]); }
-    ma = group_max<kWave>(ma);
-    mb = group_max<kWave>(mb);
-    float sa = 0.f, sb = 0.f;
-    for (int j = threadIdx.x; j < x.nchunk; j += kWave) {
-      sa += exp2f(p[4 * j] - ma) * p[4 * j + 1];
-      sb += exp2f(p[4 * j + 2] - mb) * p[4 * j + 3];
-    }
-    sa = group_sum<kWave>(sa);
-    sb = group_sum<kWave>(sb);
-    if (threadIdx.x == 0) { s_norm[0] = ma; s_norm[1] = 1.f / sa; s_norm[2] = mb; s_norm[3] = 1.f / sb; }
-  }
-  __syncthreads();
-  const float ma = s_norm[0], ia = s_norm[1], mb = s_norm[2], ib = s_norm[3];
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kAccPer; ++i) s += fminf(exp2f(va[i] * x.c - ma) * ia, exp2f(vb[i] * x.c - mb) * ib);
-  s = block_sum(s, sh);
-  if (threadIdx.x == 0) x.csum[(int64_t)r * x.nchunk + ch] = s;
+  row_norms(x, r, s_norm);
+  scale_entries(va, vb, x.c);
+  chunk_min(x, r, ch, va, vb, s_norm, sh);
 }
 
-__global__ __launch_bounds__(kWave) void acc_final_kernel(AccArgs x) {
-  const int r = blockIdx.x;
-  float s = 0.f;
-  for (int j = threadIdx.x; j < x.nchunk; j += kWave) s += x.csum[(int64_t)r * x.nchunk + j];
-  s = group_sum<kWave>(s);
-  if (threadIdx.x == 0) x.alpha[r] = fminf(1.f, fmaxf(0.f, s));
-}
+__global__ __launch_bounds__(kWave) void acc_final_kernel(AccArgs x) { row_final(x, blockIdx.x); }
 
 // Tail statistics of the per-token acceptance (Sparrow project page,
 // "Control Study 1": the lower 5th percentile of the mismatch is the stability
