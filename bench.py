@@ -130,39 +130,45 @@ def cpu_baseline(wl, steps_tokens, seconds: float):
         return _cpu_baseline(O, wl, steps_tokens, seconds)
 
 
-def _cpu_baseline(O, wl, steps_tokens, seconds):
+def _oracle_sequence(O, wl, kn, vn, b):
+    """The oracle's step for sequence b (all KV heads); returns the timed seconds (the cache as it stands
+    before the step is gathered, decoded and summarised untimed)."""
     spec = wl.spec
     ps, G, D = spec.page_size, spec.group, spec.head_dim
     scale = 1.0 / math.sqrt(D)
+    state = []
+    for g in range(spec.num_kv_heads):
+        L = int(wl.lens[b])
+        K = O.to_f64(O.gather_tokens(wl.k_pool, wl.page_table[b], L, g, ps), spec.dtype)
+        V = O.to_f64(O.gather_tokens(wl.v_pool, wl.page_table[b], L, g, ps), spec.dtype)
+        kmin, kmax = O.page_minmax(K, ps)
+        state.append((K, V, kmin, kmax))
+    t0 = time.perf_counter()
+    for g, (K, V, kmin, kmax) in enumerate(state):
+        k_new = O.to_f64(kn[b, g], spec.dtype)
+        v_new = O.to_f64(vn[b, g], spec.dtype)
+        L = K.shape[0]
+        K = np.concatenate([K, k_new[None]])
+        V = np.concatenate([V, v_new[None]])
+        p, slot = divmod(L, ps)
+        if p == kmin.shape[0]:
+            kmin = np.concatenate([kmin, k_new[None]])
+            kmax = np.concatenate([kmax, k_new[None]])
+        kmin[p], kmax[p] = O.append_minmax(kmin[p], kmax[p], k_new, slot)
+        qg = O.to_f64(wl.q[b, g * G:(g + 1) * G], spec.dtype)
+        pages = O.select_pages(O.page_scores(qg, kmin, kmax), int(wl.budget_pages[b]))
+        O.decode_unit(qg, K, V, pages, ps, scale)
+        O.dense_decode_unit(qg, K, V, ps, scale)
+    O.acceptance(wl.logits_a[b], wl.logits_b[b], spec.temperature)
+    return time.perf_counter() - t0
+
+
+def _cpu_baseline(O, wl, steps_tokens, seconds):
+    spec = wl.spec
     kn, vn = steps_tokens
     t_total, n_seq = 0.0, 0
     for b in range(spec.batch):
-        # untimed: the cache as it stands before the step (gathered, decoded, summarised)
-        state = []
-        for g in range(spec.num_kv_heads):
-            L = int(wl.lens[b])
-            K = O.to_f64(O.gather_tokens(wl.k_pool, wl.page_table[b], L, g, ps), spec.dtype)
-            V = O.to_f64(O.gather_tokens(wl.v_pool, wl.page_table[b], L, g, ps), spec.dtype)
-            kmin, kmax = O.page_minmax(K, ps)
-            state.append((K, V, kmin, kmax))
-        t0 = time.perf_counter()
-        for g, (K, V, kmin, kmax) in enumerate(state):
-            k_new = O.to_f64(kn[b, g], spec.dtype)
-            v_new = O.to_f64(vn[b, g], spec.dtype)
-            L = K.shape[0]
-            K = np.concatenate([K, k_new[None]])
-            V = np.concatenate([V, v_new[None]])
-            p, slot = divmod(L, ps)
-            if p == kmin.shape[0]:
-                kmin = np.concatenate([kmin, k_new[None]])
-                kmax = np.concatenate([kmax, k_new[None]])
-            kmin[p], kmax[p] = O.append_minmax(kmin[p], kmax[p], k_new, slot)
-            qg = O.to_f64(wl.q[b, g * G:(g + 1) * G], spec.dtype)
-            pages = O.select_pages(O.page_scores(qg, kmin, kmax), int(wl.budget_pages[b]))
-            O.decode_unit(qg, K, V, pages, ps, scale)
-            O.dense_decode_unit(qg, K, V, ps, scale)
-        O.acceptance(wl.logits_a[b], wl.logits_b[b], spec.temperature)
-        t_total += time.perf_counter() - t0
+        t_total += _oracle_sequence(O, wl, kn, vn, b)
         n_seq += 1
         if t_total >= seconds:
             break
@@ -170,6 +176,48 @@ def _cpu_baseline(O, wl, steps_tokens, seconds):
             "sample": f"full step (append, select, sparse, dense, acceptance) for {n_seq} of {spec.batch} "
                       f"sequences x {spec.num_kv_heads} KV heads, fp64 NumPy, 1 thread; "
                       f"{t_total:.1f} s of CPU time"}
+
+
+_POOL_STATE = {}
+
+
+def _pool_worker(seqs):
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    st = _POOL_STATE
+    with threadpool_limits(limits=1):
+        return sum(_oracle_sequence(O, st["wl"], st["kn"], st["vn"], b) for b in seqs)
+
+
+def cpu_baseline_pool(wl, steps_tokens):
+    """The same oracle step over every sequence with one worker process per host core (forked, one BLAS
+    thread each), sequences split into contiguous groups; throughput = sequences / the slowest worker's
+    timed seconds. Runs before the GPU is touched, so the workers are plain forks of a CPU-only process."""
+    import multiprocessing as mp
+    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    spec = wl.spec
+    _POOL_STATE.update(wl=wl, kn=steps_tokens[0], vn=steps_tokens[1])
+    groups = [list(g) for g in np.array_split(np.arange(spec.batch), n) if len(g)]
+    with mp.get_context("fork").Pool(len(groups)) as pool:
+        times = pool.map(_pool_worker, groups)
+    _POOL_STATE.clear()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": spec.batch / max(times), "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
+            "cpu_model": model,
+            "sample": f"full step for all {spec.batch} sequences in {len(groups)} forked workers (one BLAS thread "
+                      f"each); slowest worker {max(times):.2f} s, sum {sum(times):.1f} s of CPU time"}
+
+
+def env_info(torch):
+    """Device, runtime and library versions of the run."""
+    p = torch.cuda.get_device_properties(0)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip, "torch": torch.__version__}
 
 
 VERIFY_POSITIONS = 7  # k = 6 drafted tokens plus the bonus position (S3R's measured setting)
@@ -436,16 +484,22 @@ def main():
     from sparse_attention_decode_page_amd import spdec
     from sparse_attention_decode_page_amd import synth as S
 
+    K_steps, W = args.steps, args.warmup
+    t_setup = time.perf_counter()
+    wl = S.make_workload(args.workload, seed=args.seed, headroom=5 * K_steps + 2 * W + 2)
+    spec = wl.spec
+    pool_baseline = None
+    if not args.no_cpu_baseline:
+        # all host cores, before any GPU state exists in this process (the workers are forks)
+        t_first = S.append_tokens(wl, 0)
+        pool_baseline = cpu_baseline_pool(wl, (t_first[0], t_first[1]))
+        t_setup = time.perf_counter()
     if not os.path.exists(spdec.LIB_PATH):
         from sparse_attention_decode_page_amd import build
         build.build()
     spdec.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    K_steps, W = args.steps, args.warmup
-    t_setup = time.perf_counter()
-    wl = S.make_workload(args.workload, seed=args.seed, headroom=3 * K_steps + 2 * W + 2)
-    spec = wl.spec
     assert spec.logits is not None, "the step needs logit rows for the acceptance row"
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
 
@@ -516,10 +570,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_total = t_ev[0].elapsed_time(t_ev[1]) * 1e-3
+    # Two more regions of K steps the same way (the first one above is `value`;
+    # the three together give a median of three runs). Their appends reuse the
+    # step tokens: only the timing matters here.
+    repeats = [spec.batch * K_steps / gpu_total]
+    for rep in range(2):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for i in range(K_steps):
+            step((W + i) % len(new_tokens))
+        ev[1].record()
+        torch.cuda.synchronize()
+        repeats.append(spec.batch * K_steps / (ev[0].elapsed_time(ev[1]) * 1e-3))
     # Per-row breakdown: K more steps with an event between rows (each row's
     # time then includes the short hold-up after the event before it).
     for i in range(K_steps):
-        step(W + K_steps + i, row_ev[i])
+        step((W + K_steps + i) % len(new_tokens), row_ev[i])
     torch.cuda.synchronize()
     per_row = {r: [] for r in rows}
     for i in range(K_steps):
@@ -588,7 +654,7 @@ def main():
     t_tail = timed_loop(lambda i: spdec.tail_stats(alpha, out=tail_out))
     tail = {"us": t_tail * 1e6, "rows": R, "mean": float(tail_out[0]), "p5": float(tail_out[1]),
             "timing": "K times back to back under one event pair"}
-    verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 2 * K_steps) \
+    verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 5 * K_steps + W) \
         if not args.no_verify else None
     shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
     topp = top_p_rows(spec, cache, q, budget, dev, timed_loop) if not args.no_top_p else None
@@ -604,8 +670,10 @@ def main():
                 acc[r] += b_i[r] / K_steps
         return acc
 
-    byt = mean_bytes(K_steps)
-    final_bytes = algorithmic_bytes(spec, lens_before + 2 * K_steps, wl.budget_pages, cap, R, V)
+    # appends so far: the value region (K), its two repeats (2K), then the row breakdown (K); the sparse and
+    # dense regions run on the cache after those 4K appends
+    byt = mean_bytes(3 * K_steps)
+    final_bytes = algorithmic_bytes(spec, lens_before + 4 * K_steps, wl.budget_pages, cap, R, V)
     mean_t = {r: float(np.mean(per_row[r])) for r in rows}
     med_t = {r: float(np.median(per_row[r])) for r in rows}
     rows_out = {r: {"us_mean": mean_t[r] * 1e6, "us_median": med_t[r] * 1e6, "bytes": int(byt[r]),
@@ -664,6 +732,9 @@ def main():
         "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
                   "timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
         "rows": rows_out,
+        "value_runs": {"tokens_per_s": repeats, "median": float(np.median(repeats)),
+                       "timing": "the value region and two more regions of K steps, one event pair each"},
+        "env": env_info(torch),
         "step_us_median": float(np.median(step_s)) * 1e6,
         "wall_s_timed": wall,
         "setup_s": t_setup,
@@ -679,6 +750,7 @@ def main():
         kn = np.stack([t[0] for t in new_tokens[:1]])[0]
         vn = np.stack([t[1] for t in new_tokens[:1]])[0]
         result["cpu_baseline"] = cpu_baseline(wl, (kn, vn), args.cpu_seconds)
+        result["cpu_baseline_all_cores"] = pool_baseline
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
