@@ -114,3 +114,70 @@ def test_graph_replay_matches_eager(dtype, D, ps):
         graphed.alpha.zero_()
     lens = graphed.dw.seq_lens.cpu().numpy()
     assert np.array_equal(lens, wl.lens + steps)
+
+
+def test_control_loop_graph_replay_matches_eager():
+    """The on-device loop of the next rows: tail statistics -> budget controller -> Top-B and top-p selection ->
+    sparse decode, captured once; every replay must equal the same calls run eagerly (state carried in the
+    controller's scale on the device between steps, no host round trip)."""
+    steps = 4
+    spec = S.custom_spec("graph-ctl", batch=6, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("uniform", 300, 3000), budget=("tokens", 256), outlier_channels=2)
+    wl = S.make_workload(spec, seed=8)
+    r = np.random.default_rng(8)
+    alphas = [torch.from_numpy(np.clip(1 - r.exponential(0.05 + 0.03 * i, 64), 0, 1).astype(np.float32)).cuda()
+              for i in range(steps)]
+    prm = spdec.BudgetParams(target=0.86, gain=4.0, scale_min=0.05, scale_max=4.0, base_tokens=256.0,
+                             tokens_per_token=0.05, page_size=16, max_budget_pages=64)
+
+    class Loop:
+        def __init__(self):
+            self.dw = GS.DeviceWorkload(wl)
+            spdec.build_meta(self.dw.cache)
+            c, dev = self.dw.cache, "cuda"
+            self.alpha = torch.empty(64, dtype=torch.float32, device=dev)
+            self.tail = torch.empty(2, dtype=torch.float32, device=dev)
+            self.scale = torch.ones(1, dtype=torch.float32, device=dev)
+            self.budget = torch.empty(spec.batch, dtype=torch.int32, device=dev)
+            self.si = torch.zeros((spec.batch, spec.num_kv_heads, 64), dtype=torch.int32, device=dev)
+            self.sc = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
+            self.pi = torch.zeros_like(self.si)
+            self.pc = torch.zeros_like(self.sc)
+            self.ws_sel = torch.zeros(spdec.select_workspace_bytes(c, 64), dtype=torch.uint8, device=dev)
+            self.ws_sp = torch.zeros(spdec.decode_workspace_bytes(c, 64), dtype=torch.uint8, device=dev)
+            self.o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
+
+        def run(self):
+            c, q = self.dw.cache, self.dw.q
+            spdec.tail_stats(self.alpha, out=self.tail)
+            spdec.budget_update(self.tail, self.scale, self.dw.seq_lens, prm, budget_pages=self.budget)
+            spdec.select_pages(c, q, self.budget, 64, sel_idx=self.si, sel_cnt=self.sc, workspace=self.ws_sel)
+            spdec.select_pages_top_p(c, q, 0.9, 64, budget_pages=self.budget, sel_idx=self.pi, sel_cnt=self.pc,
+                                     workspace=self.ws_sel)
+            spdec.sparse_decode(c, q, self.pi, self.pc, 64, out=self.o, lse=self.lse, workspace=self.ws_sp)
+
+        def snapshot(self):
+            return {n: t.clone() for n, t in (("tail", self.tail), ("scale", self.scale), ("budget", self.budget),
+                                                ("si", self.si), ("sc", self.sc), ("pi", self.pi), ("pc", self.pc),
+                                                ("o", self.o), ("lse", self.lse))}
+
+    eager, graphed = Loop(), Loop()
+    graphed.alpha.copy_(alphas[0])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        eager.alpha.copy_(alphas[i])
+        eager.run()
+        torch.cuda.synchronize()
+        graphed.alpha.copy_(alphas[i])
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = eager.snapshot(), graphed.snapshot()
+        for name in a:
+            assert torch.equal(a[name], b[name]), (i, name)
+        graphed.o.fill_(float("nan"))
+    assert float(graphed.scale.item()) != 1.0      # the controller moved the schedule
