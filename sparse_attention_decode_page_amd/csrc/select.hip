@@ -526,7 +526,7 @@ __device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M
 template <int KPT, int NT>
 __device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int need, uint32_t kmin, int nbits,
                                          int32_t* out, TopBShared<NT>& sh) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x;
   const int i0 = tid * KPT;
   uint32_t prefix = 0, mask = 0;
   int remaining = need;
