@@ -86,10 +86,6 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
   return r;
 }
 
-// 2^x on the transcendental unit (v_exp_f32: about 1 ulp; results below the
-// smallest normal flush to zero, far below what the sums can see).
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Entries times c, each a rounded product (never fused into a later
 // subtraction), so both passes see the same scaled values.
 __device__ __forceinline__ void scale_entries(float* va, float* vb, float c) {

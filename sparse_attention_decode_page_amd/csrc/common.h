@@ -58,6 +58,11 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// 2^x on the transcendental unit (v_exp_f32, about 1 ulp) without the
+// wrapper that computes results below the smallest normal: in softmax weights
+// those are far below what the sums can see, and they flush to zero here.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Marks a loaded value as needed at this point, so that its load is not
 // sunk into a later branch: independent loads held together share one wait.
 __device__ __forceinline__ void hold(int& x) { asm volatile("" : "+v"(x)); }

@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArg
         if (grow) {  // uniform across the wave: every lane sees the same tile maxima
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float alpha = exp2f(m[h] - mnew[h]);
+            const float alpha = fast_exp2(m[h] - mnew[h]);
             lsum[h] *= alpha;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArg
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          p[h] = exp2f(p[h] - m[h]);
+          p[h] = fast_exp2(p[h] - m[h]);
           lsum[h] += p[h];
         }
 #pragma unroll

@@ -289,7 +289,7 @@ void verify_stream_kernel(VerifyArgs a) {
           const bool up = tmax > m[st] + kVerifyLazyRescale;
           if (__ballot(up) != 0ull) {  // some row of the set raises its maximum
             const float mnew = up ? tmax : m[st];
-            const float alpha = exp2f(m[st] - mnew);
+            const float alpha = fast_exp2(m[st] - mnew);
             m[st] = mnew;
             lsum[st] *= alpha;
             float ar[4];  // factors of the accumulator rows 4 q4 + r (held by lanes 0..15)
@@ -303,7 +303,7 @@ void verify_stream_kernel(VerifyArgs a) {
           vs16x4_t pa;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t pb = bf16_bits_rne(exp2f(s[e] - m[st]));
+            const uint32_t pb = bf16_bits_rne(fast_exp2(s[e] - m[st]));
             lsum[st] += __uint_as_float(pb << 16);  // the normaliser sums the same rounded weights
             pa[e] = (short)pb;
           }
