@@ -132,6 +132,17 @@ def test_edge_shapes_all_units(case, seed):
     _check_path(wl, GS.sample_units(wl, 10 ** 9))
 
 
+def test_more_units_than_the_stream_grid_holds():
+    """More (sequence, KV head) units than the persistent grids' unit table holds (8192): scoring falls back to
+    one workgroup per (unit, page block) and the decode to fixed splits; both must still match the oracle."""
+    spec = S.custom_spec("many-units", batch=1040, num_q_heads=8, num_kv_heads=8, head_dim=64, page_size=16,
+                         dtype="bf16", lens=("uniform", 1, 160), budget=("tokens", 48), outlier_channels=2)
+    wl = S.make_workload(spec, seed=4)
+    assert spec.batch * spec.num_kv_heads > 8192
+    say("case many-units: 1040 x 8 units")
+    _check_path(wl, GS.sample_units(wl, 48, seed=4))
+
+
 def test_exact_ties_go_to_lower_index():
     """Pages with identical keys tie exactly in fp32 and fp64; the lower index must win."""
     say("case exact ties")
