@@ -306,8 +306,11 @@ __device__ __forceinline__ int unit_entries(const StreamArgs& a, int u) {
 // partial (m, l, acc) per unit segment it covers, so every wave works until
 // the end and no workgroup is launched for an empty split. The wave that
 // finishes a unit records how many chunks the unit has for the merge.
+// G = 8 is held to two waves per SIMD: left alone, the compiler takes 286
+// registers for D = 128 (one wave per SIMD, 3.1 TB/s on a 2.5 GB dense pass);
+// within 256 it needs no spill and streams at 5.3 TB/s.
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArgs a) {
+__global__ __launch_bounds__(kDecodeThreads, G > 4 ? 2 : 1) void decode_stream_kernel(StreamArgs a) {
   constexpr int NJ = D / 32;             // MFMAs per head set per tile
   constexpr int NSET = G > 4 ? 2 : 1;    // MFMA sets (G = 8 needs two)
   constexpr int HPS = G > 4 ? 4 : G;     // heads delivered per set

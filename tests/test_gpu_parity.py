@@ -143,6 +143,16 @@ def test_more_units_than_the_stream_grid_holds():
     _check_path(wl, GS.sample_units(wl, 48, seed=4))
 
 
+def test_eight_query_heads_per_kv_head_many_chunks():
+    """G = 8 (64 query / 8 KV heads, D 128: the two-set MFMA form of the stream decode) on lists long enough
+    that every unit is split over several waves and merged."""
+    spec = S.custom_spec("g8", batch=6, num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=16, dtype="bf16",
+                         lens=("uniform", 3000, 20000), budget=("tokens", 2048), outlier_channels=4)
+    wl = S.make_workload(spec, seed=8)
+    say("case G8: 6 x 8 units, 64/8 heads")
+    _check_path(wl, GS.sample_units(wl, 12, seed=8))
+
+
 def test_exact_ties_go_to_lower_index():
     """Pages with identical keys tie exactly in fp32 and fp64; the lower index must win."""
     say("case exact ties")
