@@ -626,6 +626,13 @@ def main():
     t_scrub = timed_loop(lambda i: scrub_read())
     t_scrub_sparse = timed_loop(lambda i: (scrub_read(), sparse_path()))
     sp_t = t_scrub_sparse - t_scrub
+    # The two calls of the path apart, each after its own scrub (selection: scoring + Top-B; sparse decode:
+    # split-KV attention over the kept pages + merge).
+    t_scrub_sel = timed_loop(lambda i: (scrub_read(), spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx,
+                                                                         sel_cnt=sel_cnt, workspace=ws_sel)))
+    t_scrub_dec = timed_loop(lambda i: (scrub_read(), spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s,
+                                                                          lse=l_s, workspace=ws_sp)))
+    sel_t, dec_t = t_scrub_sel - t_scrub, t_scrub_dec - t_scrub
     sp_t_warm = timed_loop(lambda i: sparse_path())
     del scrub, scrub_out
     # Dense verifier alone, the same way: its average call duration is the
@@ -723,7 +730,13 @@ def main():
                    "eff_GBps": sparse_gbps, "frac_hbm": sparse_gbps / HBM_PEAK_GBPS,
                    "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels),
                    "timing": "K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub, one event pair each",
-                   "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6},
+                   "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6,
+                   "select_pages": {"us": sel_t * 1e6, "bytes": int(final_bytes["select_pages"]),
+                                    "frac_hbm": final_bytes["select_pages"] / sel_t / 1e9 / HBM_PEAK_GBPS,
+                                    "traffic": traffic_of(sparse_kernels[:2])},
+                   "sparse_decode": {"us": dec_t * 1e6, "bytes": int(final_bytes["sparse_decode"]),
+                                     "frac_hbm": final_bytes["sparse_decode"] / dec_t / 1e9 / HBM_PEAK_GBPS,
+                                     "traffic": traffic_of(sparse_kernels[2:])}},
         "tail_stats": tail,
         "verify": verify,
         "shared_prefix": shared,

@@ -10,7 +10,8 @@
 //   * bf16 caches (the workloads measured here): a persistent stream-K kernel
 //     (decode_stream_kernel, below) in which every wave owns one contiguous
 //     range of the flattened (sequence x KV head, page-list entry) pairs, with
-//     q.K^T on the matrix cores; a second kernel merges each unit's chunks;
+//     q.K^T on the matrix cores (and P.V too for eight query heads per KV
+//     head, decode_stream_g8_kernel); a second kernel merges each unit's chunks;
 //   * fp32 caches and batches too large for the stream plan: one workgroup per
 //     (split, sequence, KV head) (decode_split_kernel), a split being a run of
 //     `pages_per_split` list entries, merged by decode_merge_kernel.
@@ -247,8 +248,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
 // every row group of the output sees every head), B = 16 tokens x 32 channels
 // of K loaded straight from the page (lane l: token l%16, channels
 // 32j+8(l/16)..+8), D = 16 rows x 16 tokens in four fp32 registers per lane:
-// lane l holds token l%16 and rows 4(l/16)..+3, i.e. heads 0..3 (a second set
-// of MFMAs with rows shifted by 4 supplies heads 4..7 when G = 8). Softmax
+// lane l holds token l%16 and rows 4(l/16)..+3, i.e. every head once (G <= 4;
+// eight heads take the transposed form further below). Softmax
 // state is kept per head and is uniform across the wave; the running maximum
 // is only raised when a tile exceeds it by more than 2^8, so the O(G*D)
 // rescale of the accumulator is rare. P.V stays on the VALU with V rows read
@@ -306,14 +307,10 @@ __device__ __forceinline__ int unit_entries(const StreamArgs& a, int u) {
 // partial (m, l, acc) per unit segment it covers, so every wave works until
 // the end and no workgroup is launched for an empty split. The wave that
 // finishes a unit records how many chunks the unit has for the merge.
-// G = 8 is held to two waves per SIMD: left alone, the compiler takes 286
-// registers for D = 128 (one wave per SIMD, 3.1 TB/s on a 2.5 GB dense pass);
-// within 256 it needs no spill and streams at 5.3 TB/s.
 template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kDecodeThreads, G > 4 ? 2 : 1) void decode_stream_kernel(StreamArgs a) {
-  constexpr int NJ = D / 32;             // MFMAs per head set per tile
-  constexpr int NSET = G > 4 ? 2 : 1;    // MFMA sets (G = 8 needs two)
-  constexpr int HPS = G > 4 ? 4 : G;     // heads delivered per set
+__global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArgs a) {
+  static_assert(G <= 4, "eight heads per KV head use decode_stream_g8_kernel");
+  constexpr int NJ = D / 32;             // MFMAs per tile
   constexpr int LPT = D / 8;             // lanes per V row
   constexpr int TPI = kWave / LPT;       // V rows per load instruction
   constexpr int NV = 16 / TPI;           // V load instructions per tile
@@ -372,23 +369,16 @@ __global__ __launch_bounds__(kDecodeThreads, G > 4 ? 2 : 1) void decode_stream_k
     };
     int raw = list_raw(pos - ubase);
 
-    // A operands: row r16 holds query head (r16 + 4*set) % G.
-    u32x4 qa[NSET][NJ];
+    // A operands: row r16 holds query head r16 % G.
+    u32x4 qa[NJ];
 #pragma unroll
-    for (int st = 0; st < NSET; ++st) {
-      const int h = (r16 + 4 * st) % G;
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj)
-        qa[st][jj] = load16(qp + ((int64_t)b * c.hq + g * G + h) * D + 32 * jj + 8 * q4);
-    }
+    for (int jj = 0; jj < NJ; ++jj)
+      qa[jj] = load16(qp + ((int64_t)b * c.hq + g * G + r16 % G) * D + 32 * jj + 8 * q4);
     // Length, queries and the first list window share one wait.
     hold(L);
     hold(raw);
 #pragma unroll
-    for (int st = 0; st < NSET; ++st) {
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) hold(qa[st][jj]);
-    }
+    for (int jj = 0; jj < NJ; ++jj) hold(qa[jj]);
     L = max(L, 0);
     const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
     float m[G], lsum[G], acc[G][8];
@@ -460,22 +450,15 @@ __global__ __launch_bounds__(kDecodeThreads, G > 4 ? 2 : 1) void decode_stream_k
       load_tile(0, kA, vA, tA);
       for (int t = 0; t < ntiles; ++t) {
         if (t + 1 < ntiles) load_tile(t + 1, kB, vB, tB);
+        // Row 4 q4 + r holds head r % G, so d[h] is head h's score of the lane's token.
         float sc[G];
-#pragma unroll
-        for (int st = 0; st < NSET; ++st) {
+        {
           f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int jj = 0; jj < NJ; ++jj)
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[st][jj]), as_bf16x8(kA[jj]), d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[jj]), as_bf16x8(kA[jj]), d, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < HPS; ++r) {
-            if constexpr (G <= 4) {
-              sc[r] = d[r];
-            } else {
-              const int h = (4 * q4 + r + 4 * st) % G;
-              if (h < 4) sc[r] = d[r]; else sc[4 + r] = d[r];
-            }
-          }
+          for (int h = 0; h < G; ++h) sc[h] = d[h];
         }
         const bool kok = k_ok(t, tA);
         float p[G], mnew[G];
@@ -554,6 +537,256 @@ __global__ __launch_bounds__(kDecodeThreads, G > 4 ? 2 : 1) void decode_stream_k
         }
         if (seg_end == s_pre[u + 1]) a.count[u] = j + 1;
       }
+    }
+    pos = seg_end;
+    ++u;
+  }
+}
+
+// G = 8 variant: heads on the MFMA rows and P.V on the matrix cores.
+//
+// With eight heads the VALU form spends 256 FMAs and 32 lane fetches per lane
+// on P.V for every 16-token tile, which caps the dense pass near 5.4 TB/s.
+// Here the scores are computed transposed, S^T = K Q^T
+// (v_mfma_f32_16x16x32_bf16: K rows as they lie in the page are the A
+// operand, the eight heads, repeated on rows 8..15, the B operand), which
+// leaves lane l holding head l % 8 for tokens 4(l/16) .. +3: the A layout of
+// v_mfma_f32_16x16x16_bf16, so the weights feed P.V without a lane exchange.
+// For the B operand each lane loads, for its own four tokens, the chunk of
+// DPC = D/16 channels starting at DPC (l % 16): column n of block jb then
+// stands for channel DPC n + jb (no transpose). Each fp32 weight enters P.V
+// as the sum of three bf16 values (hi + mid + lo, each the rounded remainder
+// of the previous), which carries all 24 bits of its significand, so the
+// products and fp32 sums match the VALU form up to summation order.
+template <int DPC> struct VChunk;
+template <> struct VChunk<8> { using type = u32x4; };
+template <> struct VChunk<4> { typedef uint32_t type __attribute__((ext_vector_type(2))); };
+
+__device__ __forceinline__ u32x4 load_vchunk(const uint16_t* p, u32x4*) { return load16_stream(p); }
+__device__ __forceinline__ VChunk<4>::type load_vchunk(const uint16_t* p, VChunk<4>::type*) {
+  return __builtin_nontemporal_load(reinterpret_cast<const VChunk<4>::type*>(p));
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs of either sign).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16) & 0xFFFFu;
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(kDecodeThreads, 2) void decode_stream_g8_kernel(StreamArgs a) {
+  constexpr int G = 8;
+  constexpr int NJ = D / 32;   // S^T MFMA steps (16x16x32)
+  constexpr int NB = D / 16;   // P.V column blocks (16x16x16)
+  constexpr int DPC = D / 16;  // V channels per lane and token
+  using VC = typename VChunk<DPC>::type;
+  const CacheView& c = a.c;
+  extern __shared__ int s_pre[];  // units + 1
+  __shared__ int s_tmp[kDecodeWaves];
+  __shared__ int s_emax[kDecodeWaves];
+  const int units = c.batch * c.hkv;
+  int emax = 0;
+  for (int u = threadIdx.x; u < units; u += kDecodeThreads) {
+    const int e = unit_entries<SPARSE>(a, u);
+    s_pre[u] = e;
+    emax = max(emax, e);
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) emax = max(emax, __shfl_xor(emax, off));
+  if (threadIdx.x % kWave == 0) s_emax[threadIdx.x / kWave] = emax;
+  __syncthreads();
+  block_exclusive_scan(s_pre, units, s_tmp);
+#pragma unroll
+  for (int i = 0; i < kDecodeWaves; ++i) emax = max(emax, s_emax[i]);
+  const int total = s_pre[units];
+  const int lane = threadIdx.x % kWave;
+  const int64_t nw = (int64_t)gridDim.x * kDecodeWaves;
+  const int64_t w = (int64_t)blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
+  const int64_t rmin = min<int64_t>(a.rmin, max((emax + a.jmax - 2) / (a.jmax - 1), kDecodeMinRange));
+  const int64_t R = max<int64_t>((total + nw - 1) / nw, rmin);
+  if (w * R >= total) return;
+  int pos = (int)(w * R);
+  const int end = (int)min<int64_t>(pos + R, total);
+  int u = find_unit(s_pre, units, pos);
+
+  const int r16 = lane % 16;  // K: token of the tile; scores, P and V: head row / V column
+  const int q4 = lane / 16;   // K: channel group; scores: tokens 4 q4 .. +3
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(c.k_pool);
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(c.v_pool);
+
+  while (pos < end) {
+    const int b = u / c.hkv, g = u % c.hkv;
+    const int ubase = s_pre[u];
+    const int seg_end = min(end, s_pre[u + 1]);
+    const int j = (int)(w - ubase / R);
+    int L = c.seq_lens[b];
+    const int first = list_first<SPARSE>(a, b);
+    auto list_raw = [&](int wb) -> int {
+      const int e = min(wb + lane, seg_end - ubase - 1);
+      return SPARSE ? a.sel_idx[(int64_t)u * a.list_cap + e] : first + e;
+    };
+    int raw = list_raw(pos - ubase);
+    // B operands of S^T: head r16 % 8, channels 32 jj + 8 q4 .. +8.
+    u32x4 qb[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+      qb[jj] = load16(qp + ((int64_t)b * c.hq + g * G + (r16 & 7)) * D + 32 * jj + 8 * q4);
+    hold(L);
+    hold(raw);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) hold(qb[jj]);
+    L = max(L, 0);
+    const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+    // Softmax state of row r16 (uniform over its four lanes; lsum is this
+    // lane's share). o[jb]: rows 4 q4 .. +3, channel DPC r16 + jb.
+    float m = kNegBig, lsum = 0.f;
+    f32x4_t o[NB];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) o[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int wb = pos - ubase; wb < seg_end - ubase; wb += kWave) {
+      const int nwin = min(kWave, seg_end - ubase - wb);
+      if (wb != pos - ubase) raw = list_raw(wb);
+      const int logical = raw;
+      const int ph = c.page_table[(int64_t)b * c.max_pages + min(max(logical, 0), c.max_pages - 1)];
+      const bool ok = lane < nwin && logical >= 0 && logical < P && ph >= 0 && ph < c.num_phys;
+      const int phys_w = ok ? ph : 0;
+      const int valid_w = ok ? min(c.page_size, L - logical * c.page_size) : 0;
+      const int ntiles = ((nwin << c.ps_log2) + 15) >> 4;
+
+      auto page_base = [&](int e, int& valid) -> int64_t {
+        const int ee = min(e, kWave - 1);
+        const int phs = __builtin_amdgcn_readlane(phys_w, ee);
+        valid = e < nwin ? __builtin_amdgcn_readlane(valid_w, ee) : 0;
+        return (((int64_t)phs * c.hkv + g) << c.ps_log2) * D;
+      };
+      // kv0 / kv1: valid tokens of the tile's one or two entries (two when ps = 8).
+      struct TileValid { int kv0, kv1; };
+      auto load_tile = [&](int t, u32x4* kr, VC* vr, TileValid& tv) {
+        const int e0 = (t * 16) >> c.ps_log2;
+        const int64_t base0 = page_base(e0, tv.kv0);
+        int64_t base1 = base0;
+        tv.kv1 = 0;
+        if (c.page_size < 16) base1 = page_base(e0 + 1, tv.kv1);
+        {
+          const int slot = (t * 16 + r16) & (c.page_size - 1);
+          const bool second = c.page_size < 16 && r16 >= c.page_size;
+          const int va = second ? tv.kv1 : tv.kv0;
+          const uint16_t* src = kp + (second ? base1 : base0) + (slot < va ? slot : 0) * D + 8 * q4;
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) kr[jj] = load16_stream(src + 32 * jj);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * q4 + e;
+          const int slot = (t * 16 + k) & (c.page_size - 1);
+          const bool second = c.page_size < 16 && k >= c.page_size;
+          const int va = second ? tv.kv1 : tv.kv0;
+          vr[e] = load_vchunk(vp + (second ? base1 : base0) + (slot < va ? slot : 0) * D + DPC * r16,
+                              static_cast<VC*>(nullptr));
+        }
+      };
+
+      // K double-buffered; V chunks become B operands at the top of each
+      // iteration, after which the next tile's loads may overwrite them.
+      u32x4 kA[NJ], kB[NJ];
+      VC vR[4];
+      TileValid tA, tB;
+      load_tile(0, kA, vR, tA);
+      for (int t = 0; t < ntiles; ++t) {
+        bool tok_ok[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * q4 + e;
+          const int slot = (t * 16 + k) & (c.page_size - 1);
+          const int va = (c.page_size < 16 && k >= c.page_size) ? tA.kv1 : tA.kv0;
+          tok_ok[e] = slot < va;
+        }
+        s16x4_t vb[NB];
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+          short h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wd = vR[e][jb >> 1];
+            h[e] = tok_ok[e] ? (short)((jb & 1) ? (wd >> 16) : (wd & 0xFFFFu)) : (short)0;
+          }
+          vb[jb] = s16x4_t{h[0], h[1], h[2], h[3]};
+        }
+        if (t + 1 < ntiles) load_tile(t + 1, kB, vR, tB);
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kA[jj]), as_bf16x8(qb[jj]), d, 0, 0, 0);
+        float sv[4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = tok_ok[e] ? d[e] * a.qk_scale : -INFINITY;
+          tmax = fmaxf(tmax, sv[e]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool up = tmax > m + kLazyRescale;
+        if (__ballot(up) != 0ull) {  // some row raises its maximum
+          const float mnew = up ? tmax : m;
+          const float alpha = fast_exp2(m - mnew);
+          m = mnew;
+          lsum *= alpha;
+          float ar[4];  // factors of the accumulator rows 4 q4 + r
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+          for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[jb][r] *= ar[r];
+        }
+        s16x4_t p1, p2, p3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = fast_exp2(sv[e] - m);
+          lsum += pe;
+          const uint32_t h1 = bf16_rne(pe);
+          const float r1 = pe - __uint_as_float(h1 << 16);
+          const uint32_t h2 = bf16_rne(r1);
+          const float r2 = r1 - __uint_as_float(h2 << 16);
+          p1[e] = (short)h1;
+          p2[e] = (short)h2;
+          p3[e] = (short)bf16_rne(r2);
+        }
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+          o[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p1, vb[jb], o[jb], 0, 0, 0);
+          o[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p2, vb[jb], o[jb], 0, 0, 0);
+          o[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p3, vb[jb], o[jb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) kA[jj] = kB[jj];
+        tA = tB;
+      }
+    }
+
+    // Close the segment: each row's l over its four token groups.
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (j < a.jmax) {
+      const int64_t slot0 = ((int64_t)u * a.jmax + j) * G;
+      if (q4 < 2) {  // rows 4 q4 + r < 8 are the heads; rows 8..15 repeat them
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* dst = a.part_acc + (slot0 + 4 * q4 + r) * D + DPC * r16;
+#pragma unroll
+          for (int jb = 0; jb < NB; ++jb) dst[jb] = o[jb][r];
+        }
+      }
+      if (q4 == 0 && r16 < G) {
+        a.part_ml[(slot0 + r16) * 2 + 0] = m;
+        a.part_ml[(slot0 + r16) * 2 + 1] = lsum;
+      }
+      if (lane == 0 && seg_end == s_pre[u + 1]) a.count[u] = j + 1;
     }
     pos = seg_end;
     ++u;
@@ -672,29 +905,36 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
   return a.c.head_dim == 64 ? decode_g<F32, 64, SPARSE>(a, s) : decode_g<F32, 128, SPARSE>(a, s);
 }
 
+
+// The stream kernel for group size G (G = 8: the matrix-core P.V form).
+template <int D, int G, bool SPARSE>
+hipError_t stream_kernel_launch(const StreamArgs& a, hipStream_t s) {
+  const int units = a.c.batch * a.c.hkv;
+  const size_t lds = (size_t)(units + 1) * sizeof(int);
+  const void* fn;
+  if constexpr (G == 8)
+    fn = reinterpret_cast<const void*>(&decode_stream_g8_kernel<D, SPARSE>);
+  else
+    fn = reinterpret_cast<const void*>(&decode_stream_kernel<D, G, SPARSE>);
+  int grid = 0;
+  hipError_t e = persistent_grid(fn, kDecodeThreads, lds, &grid);
+  if (e != hipSuccess) return e;
+  if constexpr (G == 8)
+    hipLaunchKernelGGL((decode_stream_g8_kernel<D, SPARSE>), dim3(grid), dim3(kDecodeThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<D, G, SPARSE>), dim3(grid), dim3(kDecodeThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 // The dense stream kernel alone (partials and per-unit chunk counts, no merge).
 template <int D, int G>
 hipError_t stream_partials_impl(const StreamArgs& a, hipStream_t s) {
-  const int units = a.c.batch * a.c.hkv;
-  const size_t lds = (size_t)(units + 1) * sizeof(int);
-  int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&decode_stream_kernel<D, G, false>), kDecodeThreads,
-                                 lds, &grid);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_stream_kernel<D, G, false>), dim3(grid), dim3(kDecodeThreads), lds, s, a);
-  return hipGetLastError();
+  return stream_kernel_launch<D, G, false>(a, s);
 }
 
 template <int D, int G, bool SPARSE>
 hipError_t stream_impl(const StreamArgs& a, hipStream_t s) {
-  const int units = a.c.batch * a.c.hkv;
-  const size_t lds = (size_t)(units + 1) * sizeof(int);
-  int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&decode_stream_kernel<D, G, SPARSE>), kDecodeThreads,
-                                 lds, &grid);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_stream_kernel<D, G, SPARSE>), dim3(grid), dim3(kDecodeThreads), lds, s, a);
-  e = hipGetLastError();
+  hipError_t e = stream_kernel_launch<D, G, SPARSE>(a, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_merge_kernel<D, SPARSE>), dim3(a.c.batch * a.c.hq), dim3(kWave), 0, s, a);
   return hipGetLastError();
