@@ -794,37 +794,63 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_stream_g8_kernel(Str
 }
 
 // Merge of the stream partials of one (sequence, query head), chunks in order.
+// The first kMergePre chunks' partials (slots below jmax always lie inside the
+// workspace) are requested together with the chunk count, so a unit of up to
+// kMergePre chunks costs one round trip to memory; later chunks are read after.
+constexpr int kMergePre = 8;
+
 template <int D, bool SPARSE>
 __global__ __launch_bounds__(kWave) void stream_merge_kernel(StreamArgs a) {
   constexpr int DPL = D / kWave;
-  __shared__ float s_w[kMaxSplits];
   const CacheView& c = a.c;
   const int bh = blockIdx.x;
   const int b = bh / c.hq, h = bh % c.hq;
   const int u = b * c.hkv + h / c.group;
   const int hh = h % c.group;
   const int lane = threadIdx.x;
+  auto ml_of = [&](int jj) { return a.part_ml + (((int64_t)u * a.jmax + jj) * c.group + hh) * 2; };
+  auto acc_of = [&](int jj) { return a.part_acc + (((int64_t)u * a.jmax + jj) * c.group + hh) * D + lane * DPL; };
+  // Lane jj's chunk (m, l) and the leading chunks' accumulators, at clamped slots.
+  const float* ml0 = ml_of(min(lane, a.jmax - 1));
+  const float m0 = ml0[0], l0 = ml0[1];
+  float pre[kMergePre][DPL];
+#pragma unroll
+  for (int i = 0; i < kMergePre; ++i) {
+    const float* src = acc_of(min(i, a.jmax - 1));
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) pre[i][e] = src[e];
+  }
   const int n = unit_entries<SPARSE>(a, u);
   const int J = n > 0 ? min(max(a.count[u], 0), a.jmax) : 0;
-  float M = kNegBig;
-  for (int jj = lane; jj < J; jj += kWave) M = fmaxf(M, a.part_ml[(((int64_t)u * a.jmax + jj) * c.group + hh) * 2]);
+  float M = lane < J ? m0 : kNegBig;
+  for (int jj = lane + kWave; jj < J; jj += kWave) M = fmaxf(M, ml_of(jj)[0]);
   M = group_max<kWave>(M);
-  float Ls = 0.f;
-  for (int jj = lane; jj < J; jj += kWave) {
-    const float* ml = a.part_ml + (((int64_t)u * a.jmax + jj) * c.group + hh) * 2;
-    const float wgt = exp2f(ml[0] - M);
-    s_w[jj] = wgt;
-    Ls += wgt * ml[1];
+  // Lane jj holds chunk jj's weight; chunks past the wave width (long lists
+  // only) recompute theirs where they are used.
+  float Ls = 0.f, w_own = 0.f;
+  if (lane < J) {
+    w_own = exp2f(m0 - M);
+    Ls += w_own * l0;
+  }
+  for (int jj = lane + kWave; jj < J; jj += kWave) {
+    const float* ml = ml_of(jj);
+    Ls += exp2f(ml[0] - M) * ml[1];
   }
   Ls = group_sum<kWave>(Ls);
-  __syncthreads();
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-#pragma unroll 4
-  for (int jj = 0; jj < J; ++jj) {
-    const float wgt = s_w[jj];
-    const float* src = a.part_acc + (((int64_t)u * a.jmax + jj) * c.group + hh) * D + lane * DPL;
+#pragma unroll
+  for (int i = 0; i < kMergePre; ++i) {
+    if (i < J) {
+      const float wgt = __shfl(w_own, i);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, pre[i][e], o[e]);
+    }
+  }
+  for (int jj = kMergePre; jj < J; ++jj) {
+    const float wgt = jj < kWave ? __shfl(w_own, jj) : exp2f(ml_of(jj)[0] - M);
+    const float* src = acc_of(jj);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, src[e], o[e]);
   }

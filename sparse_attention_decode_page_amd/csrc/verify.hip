@@ -35,7 +35,6 @@ namespace {
 constexpr int kVerifyThreads = 256;
 constexpr int kVerifyWaves = kVerifyThreads / kWave;
 constexpr float kVerifyLazyRescale = 8.0f;  // log2 units
-constexpr int kVerifyMaxChunks = 2048;       // merge staging (jmax never exceeds 1024)
 
 typedef __bf16 vbf16x8_t __attribute__((ext_vector_type(8)));
 typedef short vs16x4_t __attribute__((ext_vector_type(4)));
@@ -350,10 +349,14 @@ void verify_stream_kernel(VerifyArgs a) {
 }
 
 // One wave per output row (sequence, position, query head): chunks in index order.
+// The first kVerifyMergePre chunks' partials (slots below jmax lie inside the
+// workspace) are requested together with the chunk count: one round trip for
+// a unit of that many chunks.
+constexpr int kVerifyMergePre = 8;
+
 template <int D>
 __global__ __launch_bounds__(kWave) void verify_merge_kernel(VerifyArgs a) {
   constexpr int DPL = D / kWave;
-  __shared__ float s_w[kVerifyMaxChunks];
   const CacheView& c = a.c;
   const int orow = blockIdx.x;  // ((b * T + t) * Hq + hq)
   const int hq = orow % c.hq;
@@ -362,27 +365,49 @@ __global__ __launch_bounds__(kWave) void verify_merge_kernel(VerifyArgs a) {
   const int u = b * c.hkv + hq / c.group;
   const int row = t * c.group + hq % c.group;
   const int lane = threadIdx.x;
+  auto ml_of = [&](int jj) { return a.part_ml + (((int64_t)u * a.jmax + jj) * a.rows + row) * 2; };
+  auto acc_of = [&](int jj) { return a.part_acc + (((int64_t)u * a.jmax + jj) * a.rows + row) * D + lane * DPL; };
+  const float* ml0 = ml_of(min(lane, a.jmax - 1));
+  const float m0 = ml0[0], l0 = ml0[1];
+  float pre[kVerifyMergePre][DPL];
+#pragma unroll
+  for (int i = 0; i < kVerifyMergePre; ++i) {
+    const float* src = acc_of(min(i, a.jmax - 1));
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) pre[i][e] = src[e];
+  }
   const int L = max(c.seq_lens[b], 0);
   const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
   const int J = P > 0 ? min(max(a.count[u], 0), a.jmax) : 0;
-  float M = kNegBig;
-  for (int jj = lane; jj < J; jj += kWave) M = fmaxf(M, a.part_ml[(((int64_t)u * a.jmax + jj) * a.rows + row) * 2]);
+  float M = lane < J ? m0 : kNegBig;
+  for (int jj = lane + kWave; jj < J; jj += kWave) M = fmaxf(M, ml_of(jj)[0]);
   M = group_max<kWave>(M);
-  float Ls = 0.f;
-  for (int jj = lane; jj < J; jj += kWave) {
-    const float* ml = a.part_ml + (((int64_t)u * a.jmax + jj) * a.rows + row) * 2;
-    const float wgt = exp2f(ml[0] - M);
-    s_w[jj] = wgt;
-    Ls += wgt * ml[1];
+  // Lane jj holds chunk jj's weight; chunks past the wave width (long lists
+  // only) recompute theirs where they are used.
+  float Ls = 0.f, w_own = 0.f;
+  if (lane < J) {
+    w_own = exp2f(m0 - M);
+    Ls += w_own * l0;
+  }
+  for (int jj = lane + kWave; jj < J; jj += kWave) {
+    const float* ml = ml_of(jj);
+    Ls += exp2f(ml[0] - M) * ml[1];
   }
   Ls = group_sum<kWave>(Ls);
-  __syncthreads();
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int jj = 0; jj < J; ++jj) {
-    const float wgt = s_w[jj];
-    const float* src = a.part_acc + (((int64_t)u * a.jmax + jj) * a.rows + row) * D + lane * DPL;
+#pragma unroll
+  for (int i = 0; i < kVerifyMergePre; ++i) {
+    if (i < J) {
+      const float wgt = __shfl(w_own, i);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, pre[i][e], o[e]);
+    }
+  }
+  for (int jj = kVerifyMergePre; jj < J; ++jj) {
+    const float wgt = jj < kWave ? __shfl(w_own, jj) : exp2f(ml_of(jj)[0] - M);
+    const float* src = acc_of(jj);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, src[e], o[e]);
   }
