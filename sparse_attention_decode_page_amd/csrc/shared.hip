@@ -21,8 +21,6 @@ namespace spdec {
 
 namespace {
 
-constexpr int kSharedMaxChunks = 2048;  // jmax of both passes (each at most 1024)
-
 struct SharedMergeArgs {
   CacheView c;
   int group_size;
@@ -39,16 +37,43 @@ struct SharedMergeArgs {
   float* lse;                 // [batch][Hq] or null
 };
 
+// The leading kSharedMergePre chunks of each pass (slots below that pass's
+// jmax lie inside the workspace) are requested together with the chunk
+// counts, so a merge over that many chunks per pass costs one round trip.
+constexpr int kSharedMergePre = 8;
+
 template <int D>
 __global__ __launch_bounds__(kWave) void shared_merge_kernel(SharedMergeArgs a) {
   constexpr int DPL = D / kWave;
-  __shared__ float s_w[kSharedMaxChunks];
+  constexpr int NP = kSharedMergePre;
   const CacheView& c = a.c;
   const int bh = blockIdx.x;
   const int b = bh / c.hq, h = bh % c.hq;
   const int g = h / c.group, hh = h % c.group;
   const int n = b / a.group_size, i = b % a.group_size;
   const int lane = threadIdx.x;
+  const int up = n * c.hkv + g, us = b * c.hkv + g;
+  const int rp = i * c.group + hh;
+  auto ml_p = [&](int j) { return a.ml_p + (((int64_t)up * a.jmax_p + j) * a.rows_p + rp) * 2; };
+  auto ml_s = [&](int j) { return a.ml_s + (((int64_t)us * a.jmax_s + j) * c.group + hh) * 2; };
+  auto acc_p = [&](int j) { return a.acc_p + (((int64_t)up * a.jmax_p + j) * a.rows_p + rp) * D + lane * DPL; };
+  auto acc_s = [&](int j) { return a.acc_s + (((int64_t)us * a.jmax_s + j) * c.group + hh) * D + lane * DPL; };
+  // Requested up front, at clamped slots: lane j's (m, l) of both passes and
+  // the leading accumulators of both passes.
+  const float* mlp0 = ml_p(min(lane, a.jmax_p - 1));
+  const float* mls0 = ml_s(min(lane, a.jmax_s - 1));
+  const float mp0 = mlp0[0], lp0 = mlp0[1], ms0 = mls0[0], ls0 = mls0[1];
+  float pre_p[NP][DPL], pre_s[NP][DPL];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const float* sp = acc_p(min(k, a.jmax_p - 1));
+    const float* ss = acc_s(min(k, a.jmax_s - 1));
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      pre_p[k][e] = sp[e];
+      pre_s[k][e] = ss[e];
+    }
+  }
   // Entry counts exactly as the two passes derived them.
   const int b0 = n * a.group_size;
   const int L0 = max(c.seq_lens[b0], 0);
@@ -58,40 +83,77 @@ __global__ __launch_bounds__(kWave) void shared_merge_kernel(SharedMergeArgs a) 
   const int L = max(c.seq_lens[b], 0);
   const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
   const int ns = max(P - S, 0);
-  const int up = n * c.hkv + g, us = b * c.hkv + g;
   const int Jp = np > 0 ? min(max(a.count_p[up], 0), a.jmax_p) : 0;
   const int Js = ns > 0 ? min(max(a.count_s[us], 0), a.jmax_s) : 0;
-  const int rp = i * c.group + hh;
-  auto ml_of = [&](int j) -> const float* {  // chunk j: prefix chunks first, then suffix chunks
-    return j < Jp ? a.ml_p + (((int64_t)up * a.jmax_p + j) * a.rows_p + rp) * 2
-                  : a.ml_s + (((int64_t)us * a.jmax_s + (j - Jp)) * c.group + hh) * 2;
-  };
-  auto acc_of = [&](int j) -> const float* {
-    return j < Jp ? a.acc_p + (((int64_t)up * a.jmax_p + j) * a.rows_p + rp) * D
-                  : a.acc_s + (((int64_t)us * a.jmax_s + (j - Jp)) * c.group + hh) * D;
-  };
   const int J = Jp + Js;
-  float M = kNegBig;
-  for (int j = lane; j < J; j += kWave) M = fmaxf(M, ml_of(j)[0]);
+  // Chunk j of the merge order: prefix chunk j for j < Jp, else suffix chunk j - Jp.
+  auto ml_of = [&](int j) -> const float* { return j < Jp ? ml_p(j) : ml_s(j - Jp); };
+  // Lane j's own chunk (j < 64): prefix slot j, or suffix slot j - Jp, which
+  // lane j - Jp requested.
+  const float msh = __shfl(ms0, max(lane - Jp, 0));
+  const float lsh = __shfl(ls0, max(lane - Jp, 0));
+  const float m0 = lane < Jp ? mp0 : msh;
+  const float l0 = lane < Jp ? lp0 : lsh;
+  float M = lane < J ? m0 : kNegBig;
+  for (int j = lane + kWave; j < J; j += kWave) M = fmaxf(M, ml_of(j)[0]);
   M = group_max<kWave>(M);
-  float Ls = 0.f;
-  for (int j = lane; j < J; j += kWave) {
+  // Lane j holds merge chunk j's weight; chunks past the wave width recompute
+  // theirs where they are used.
+  float Ls = 0.f, w_own = 0.f;
+  if (lane < J) {
+    w_own = exp2f(m0 - M);
+    Ls += w_own * l0;
+  }
+  for (int j = lane + kWave; j < J; j += kWave) {
     const float* ml = ml_of(j);
-    const float wgt = exp2f(ml[0] - M);
-    s_w[j] = wgt;
-    Ls += wgt * ml[1];
+    Ls += exp2f(ml[0] - M) * ml[1];
   }
   Ls = group_sum<kWave>(Ls);
-  __syncthreads();
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int j = 0; j < J; ++j) {
-    const float wgt = s_w[j];
-    const float* src = acc_of(j) + lane * DPL;
+  auto weight = [&](int j) { return j < kWave ? __shfl(w_own, j) : exp2f(ml_of(j)[0] - M); };
+  // Chunks [k0, k1) of one pass (merge-order index base + k), NP loads in
+  // flight at a time (at clamped slots; unused ones are never summed).
+  auto accum = [&](auto acc_of, int jmax, int k0, int k1, int base) {
+    for (int kb = k0; kb < k1; kb += NP) {
+      float v[NP][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, src[e], o[e]);
+      for (int q = 0; q < NP; ++q) {
+        const float* src = acc_of(min(kb + q, jmax - 1));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) v[q][e] = src[e];
+      }
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        if (kb + q < k1) {
+          const float wgt = weight(base + kb + q);
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, v[q][e], o[e]);
+        }
+      }
+    }
+  };
+  // Prefix chunks, then suffix chunks, each in index order; the first NP of
+  // each pass come from the up-front loads.
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    if (k < Jp) {
+      const float wgt = weight(k);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, pre_p[k][e], o[e]);
+    }
   }
+  accum(acc_p, a.jmax_p, NP, Jp, 0);
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    if (k < Js) {
+      const float wgt = weight(Jp + k);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, pre_s[k][e], o[e]);
+    }
+  }
+  accum(acc_s, a.jmax_s, NP, Js, Jp);
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) a.out[(int64_t)bh * D + lane * DPL + e] = o[e] * inv;

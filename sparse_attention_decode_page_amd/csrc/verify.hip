@@ -405,11 +405,25 @@ __global__ __launch_bounds__(kWave) void verify_merge_kernel(VerifyArgs a) {
       for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, pre[i][e], o[e]);
     }
   }
-  for (int jj = kVerifyMergePre; jj < J; ++jj) {
-    const float wgt = jj < kWave ? __shfl(w_own, jj) : exp2f(ml_of(jj)[0] - M);
-    const float* src = acc_of(jj);
+  // Later chunks (long lists), kVerifyMergePre loads in flight at a time, at clamped
+  // slots (unused ones are never summed).
+  for (int jb = kVerifyMergePre; jb < J; jb += kVerifyMergePre) {
+    float v[kVerifyMergePre][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, src[e], o[e]);
+    for (int q = 0; q < kVerifyMergePre; ++q) {
+      const float* src = acc_of(min(jb + q, a.jmax - 1));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) v[q][e] = src[e];
+    }
+#pragma unroll
+    for (int q = 0; q < kVerifyMergePre; ++q) {
+      const int jj = jb + q;
+      if (jj < J) {
+        const float wgt = jj < kWave ? __shfl(w_own, jj) : exp2f(ml_of(jj)[0] - M);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, v[q][e], o[e]);
+      }
+    }
   }
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
