@@ -92,6 +92,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters_qwen3-8b-ragged.
 KERNEL_SOURCES = ("common.h", "decode.hip", "select.hip", "grid.hip")
 
 
+def describe_lens(spec) -> str:
+    kind = spec.lens[0]
+    if kind == "uniform":
+        return f"uniform {spec.lens[1]}..{spec.lens[2]} per sequence"
+    if kind == "fixed":
+        return f"{spec.lens[1]} per sequence"
+    return str(spec.lens)
+
+
+def describe_budget(spec) -> str:
+    kind = spec.budget[0]
+    if kind == "linear":
+        return f"{spec.budget[1]}->{spec.budget[2]} tokens, linear in length"
+    if kind == "tokens":
+        return f"{spec.budget[1]} tokens"
+    return str(spec.budget)
+
+
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
@@ -714,11 +732,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded draws shaped like a Qwen3-8B decode layer; no weights or datasets)",
+        "dtype": spec.dtype,
+        "data": f"synthetic (seeded draws of the {spec.name} workload; no weights or datasets)",
         "config": {"workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads,
                    "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
-                   "context": "uniform 8192..32768 per sequence", "budget": "1024->4096 tokens, linear in length",
+                   "context": describe_lens(spec), "budget": describe_budget(spec),
                    "acceptance_rows": R, "vocab": V, "accumulate": "fp32",
                    "step": "append_kv + select_pages + sparse_decode + dense_decode + acceptance"},
         "roofline": {"bound": "hbm", "achieved": dense_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

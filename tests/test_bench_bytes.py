@@ -1,0 +1,40 @@
+"""The bench's algorithmic byte counts (the roofline numerators), checked by brute force on tiny shapes.
+
+Every valid token's K and V row once for the dense decode; the valid tokens of the pages the oracle's
+Top-B selection keeps for the sparse decode (whatever the scores, since the kept pages other than the
+last are always full); kmin + kmax of every page for the selection; both logit rows for the acceptance.
+"""
+import numpy as np
+import pytest
+
+import bench
+import oracle as O
+from sparse_attention_decode_page_amd import synth as S
+
+
+@pytest.mark.parametrize("dtype,D,ps", [("bf16", 128, 16), ("f32", 64, 8), ("bf16", 64, 32)])
+def test_algorithmic_bytes_brute_force(dtype, D, ps):
+    rng = np.random.default_rng(D + ps)
+    B, Hkv = 5, 3
+    spec = S.custom_spec("bytes", batch=B, num_q_heads=2 * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                         dtype=dtype, lens=("list", [1, ps, ps + 1, 7 * ps - 3, 40 * ps]), budget=("pages", [1] * B))
+    lens = np.asarray(spec.lens[1], dtype=np.int64)
+    budget = rng.integers(0, 12, size=B)
+    cap, rows, vocab = 9, 3, 1000
+    elt = 2 if dtype == "bf16" else 4
+    got = bench.algorithmic_bytes(spec, lens, budget, cap, rows, vocab)
+    sparse = dense = meta = 0
+    for b in range(B):
+        L = int(lens[b])
+        P = (L + ps - 1) // ps
+        valid = [min(ps, L - p * ps) for p in range(P)]
+        for g in range(Hkv):
+            keep = O.select_pages(rng.standard_normal(P), min(int(budget[b]), cap))
+            sparse += sum(valid[p] for p in keep) * 2 * D * elt
+            dense += L * 2 * D * elt
+            meta += P * 2 * D * elt
+    assert got["sparse_decode"] == sparse
+    assert got["dense_decode"] == dense
+    assert got["select_pages"] == meta
+    assert got["acceptance"] == 2 * rows * vocab * 4
+    assert got["append_kv"] == B * Hkv * (2 * D * elt + 2 * 2 * D * elt)
