@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix (grouped prompts) rows")
     ap.add_argument("--no-control", action="store_true", help="skip the closed-loop budget controller rows")
     ap.add_argument("--no-top-p", action="store_true", help="skip the score-mass (top-p) selection rows")
+    ap.add_argument("--no-second-shape", action="store_true",
+                    help="skip the Qwen3-1.7B-shaped decode layer (sparse path and dense decode)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -297,6 +299,78 @@ def speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens):
         "accept_us": t_s * 1e6, "accept_bytes": acc_bytes, "accept_GBps": acc_bytes / t_s / 1e9,
         "mean_kept_drafts": float(kept.mean()),
         "timing": "each call K times back to back under one event pair",
+    }
+
+
+def other_shape_rows(args, dev, timed_loop, name="qwen3-1.7b-L16k"):
+    """The sparse path and the dense decode on the second decode-layer shape (Qwen3-1.7B: 32 sequences of 16384
+    tokens, 16 query / 8 KV heads, 2048-token budget), timed like the main line: the sparse calls after a 1 GiB
+    scrub read, the dense call back to back."""
+    import torch
+    from sparse_attention_decode_page_amd import spdec
+    from sparse_attention_decode_page_amd import synth as S
+    wl = S.make_workload(name, seed=args.seed)
+    spec = wl.spec
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kmm = torch.zeros((wl.num_phys, spec.num_kv_heads, 2, spec.head_dim), dtype=torch.bfloat16, device=dev)
+    cache = spdec.PagedCache(up(wl.k_pool), up(wl.v_pool), kmm, torch.from_numpy(wl.page_table).to(dev),
+                             torch.from_numpy(wl.lens.astype(np.int32)).to(dev), spec.num_q_heads)
+    spdec.build_meta(cache)
+    q = up(wl.q)
+    budget = torch.from_numpy(wl.budget_pages.astype(np.int32)).to(dev)
+    cap = int(max(2, wl.budget_pages.max()))
+    sel_idx = torch.zeros((spec.batch, spec.num_kv_heads, cap), dtype=torch.int32, device=dev)
+    sel_cnt = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
+    ws_sel = torch.zeros(spdec.select_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
+    ws_sp = torch.zeros(spdec.decode_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
+    ws_de = torch.zeros(spdec.decode_workspace_bytes(cache, 0), dtype=torch.uint8, device=dev)
+    o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    scrub_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def scrub_read():
+        torch.sum(scrub, dim=0, out=scrub_out)
+
+    def sel():
+        spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
+
+    def dec():
+        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o, lse=lse, workspace=ws_sp)
+
+    def dense():
+        spdec.dense_decode(cache, q, out=o, lse=lse, workspace=ws_de)
+
+    for _ in range(3):
+        scrub_read()
+        sel()
+        dec()
+        dense()
+    t_scrub = timed_loop(lambda i: scrub_read())
+    t_path = timed_loop(lambda i: (scrub_read(), sel(), dec())) - t_scrub
+    t_sel = timed_loop(lambda i: (scrub_read(), sel())) - t_scrub
+    t_dec = timed_loop(lambda i: (scrub_read(), dec())) - t_scrub
+    t_dense = timed_loop(lambda i: dense())
+    byt = algorithmic_bytes(spec, wl.lens, wl.budget_pages, cap, 0, 0)
+    b_path = byt["select_pages"] + byt["sparse_decode"]
+    del cache, kmm, q, ws_sel, ws_sp, ws_de, scrub, scrub_out
+    torch.cuda.empty_cache()
+
+    def row(t, b):
+        return {"us": t * 1e6, "bytes": int(b), "GBps": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS}
+
+    return {
+        "workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads, "kv_heads": spec.num_kv_heads,
+        "head_dim": spec.head_dim, "page_size": spec.page_size, "context": describe_lens(spec),
+        "budget": describe_budget(spec),
+        "sparse_path": dict(row(t_path, b_path), tokens_per_s=spec.batch / t_path),
+        "select_pages": row(t_sel, byt["select_pages"]),
+        "sparse_decode": row(t_dec, byt["sparse_decode"]),
+        "dense_decode": dict(row(t_dense, byt["dense_decode"]), tokens_per_s=spec.batch / t_dense),
+        "timing": "sparse calls: K x (1 GiB scrub read, call) minus K x scrub; dense: K calls back to back",
     }
 
 
@@ -682,6 +756,7 @@ def main():
     verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 5 * K_steps + W) \
         if not args.no_verify else None
     shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
+    shape2 = other_shape_rows(args, dev, timed_loop) if not args.no_second_shape else None
     topp = top_p_rows(spec, cache, q, budget, dev, timed_loop) if not args.no_top_p else None
     control = budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap,
                                   timed_loop) if not args.no_control else None
@@ -758,6 +833,7 @@ def main():
         "tail_stats": tail,
         "verify": verify,
         "shared_prefix": shared,
+        "qwen3_1_7b": shape2,
         "top_p": topp,
         "budget_control": control,
         "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
