@@ -15,10 +15,12 @@
 //     query rows are the B operand; the result leaves lane l holding query row
 //     l % 16 for tokens 4(l / 16) .. +3;
 //   * that is exactly the A-operand layout of v_mfma_f32_16x16x16_bf16, so
-//     P (rounded to bf16) feeds P.V directly; V is staged per wave in LDS
-//     transposed ([channel][token]) so the B operand (4 consecutive tokens of
-//     one channel) is one 8-byte LDS read.
-// Query rows are padded to 16 * NSETS (NSETS <= 2, R <= 32). The softmax is
+//     P (rounded to bf16) feeds P.V directly. For the B operand each lane
+//     loads, for its own four tokens, the chunk of D/16 channels starting at
+//     (D/16)(l % 16): column n of block j then stands for channel
+//     (D/16) n + j, so V needs no transpose and no LDS.
+// Query rows are padded to 16 * NSETS (NSETS <= 2, R <= 32) and parked in
+// LDS (each lane reads back what it wrote) to keep two waves per SIMD. The softmax is
 // online in fp32 (log2 domain) with the running maximum raised only when a
 // tile exceeds it by 2^8. The (unit, page) pairs are streamed persistently
 // exactly like the single-query dense decode; partials are merged per output
