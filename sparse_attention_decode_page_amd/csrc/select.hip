@@ -14,11 +14,12 @@
 // Selection (Top-k pages under a KV budget, Sparrow project page "Control
 // Study 2"; sink/local pages always kept): K = min(max(budget,2), cap, P);
 // pages 0 and P-1 are forced, the other K-2 are the largest scores of 1..P-2
-// with ties to the lower index. A 4-pass MSB-first radix select on
-// order-preserving uint32 keys in LDS finds the cut key T and how many keys
-// equal to T are taken; one ordered compaction then emits the kept pages
-// already ascending, and equal keys are taken in index order, which is the
-// tie rule.
+// with ties to the lower index. An MSB-first 8-bit radix select on
+// order-preserving uint32 keys (offset by the unit's smallest key, so only the
+// significant bits take passes: usually 2-3) with LDS histograms finds the
+// cut key T and how many keys equal to T are taken; one ordered compaction
+// then emits the kept pages already ascending, and equal keys are taken in
+// index order, which is the tie rule.
 #include "common.h"
 #include "launch.h"
 
