@@ -268,8 +268,9 @@ spdec_status spdec_dense_decode_shared(const spdec_cache* cache, const void* q, 
  * cores), merged by log-sum-exp in a fixed order.
  *
  * q: [batch][T][Hq][D] bf16; out: fp32 [batch][T][Hq][D]; lse: nullable fp32
- * [batch][T][Hq]. Requires a bf16 cache, 1 <= T <= 16 and G * T <= 32
- * (SPDEC_ERR_UNSUPPORTED otherwise); seq_lens[b] >= T is a device
+ * [batch][T][Hq]. Requires a bf16 cache, 1 <= T <= 16 and G * T <= 64
+ * (SPDEC_ERR_UNSUPPORTED otherwise; above 32 query rows per KV head the
+ * cache is read twice, once per 32 rows); seq_lens[b] >= T is a device
  * precondition (a row with no visible token returns zeros and lse = -inf).
  * Workspace: spdec_verify_workspace_bytes(cache, T), zero-filled once.
  */

@@ -19,7 +19,8 @@
 //     loads, for its own four tokens, the chunk of D/16 channels starting at
 //     (D/16)(l % 16): column n of block j then stands for channel
 //     (D/16) n + j, so V needs no transpose and no LDS.
-// Query rows are padded to 16 * NSETS (NSETS <= 2, R <= 32) and parked in
+// Query rows are padded to 16 * NSETS (NSETS <= 2, 32 rows per pass; 33 to 64
+// rows take two passes over the cache) and parked in
 // LDS (each lane reads back what it wrote) to keep two waves per SIMD. The softmax is
 // online in fp32 (log2 domain) with the running maximum raised only when a
 // tile exceeds it by 2^8. The (unit, page) pairs are streamed persistently
@@ -74,6 +75,7 @@ struct VerifyArgs {
   int T;             // verify: positions per sequence; shared prefix: sequences per group
   const int32_t* shared;  // shared prefix: leading pages of each group (read once for the group)
   int rows;          // G * T query rows per unit
+  int row0;          // first of the (at most 16 * NSETS) rows this launch computes
   int jmax, rmin;    // stream plan of the dense decode
   float qk_scale;    // softmax scale * log2(e)
   float* part_acc;   // [units][jmax][rows][D]
@@ -139,15 +141,16 @@ void verify_stream_kernel(VerifyArgs a) {
     const int L = max(c.seq_lens[b], 0);
     const int P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
 
-    // B operands of S^T = K Q^T: set st, lane l holds query row 16 st + l % 16
-    // (position t = row / G, head g G + row % G), channels 32 jj + 8 (l / 16).
+    // B operands of S^T = K Q^T: set st, lane l holds query row
+    // row0 + 16 st + l % 16 (position t = row / G, head g G + row % G),
+    // channels 32 jj + 8 (l / 16).
     // They are parked in this wave's LDS rows (each lane later reads back
     // exactly what it wrote). lim: last token index the row may attend; -1
     // for padding rows.
     int lim[NSETS];
 #pragma unroll
     for (int st = 0; st < NSETS; ++st) {
-      const int row = 16 * st + r16;
+      const int row = a.row0 + 16 * st + r16;
       lim[st] = -1;
       const uint16_t* src = qp;
       if (row < a.rows) {
@@ -163,7 +166,7 @@ void verify_stream_kernel(VerifyArgs a) {
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
         const u32x4 v = row < a.rows ? load16(src + 32 * jj) : u32x4{0u, 0u, 0u, 0u};
-        __builtin_memcpy(qs + row * D + 32 * jj + 8 * q4, &v, sizeof(v));
+        __builtin_memcpy(qs + (16 * st + r16) * D + 32 * jj + 8 * q4, &v, sizeof(v));
       }
     }
     // Softmax state of the lane's row (uniform over the four lanes of a row);
@@ -330,14 +333,14 @@ void verify_stream_kernel(VerifyArgs a) {
       for (int st = 0; st < NSETS; ++st) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * st + 4 * q4 + r;
+          const int row = a.row0 + 16 * st + 4 * q4 + r;
           if (row < a.rows) {
             float* dst = a.part_acc + (slot0 + row) * D + DPC * r16;
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) dst[jb] = o[st][jb][r];
           }
         }
-        const int row = 16 * st + r16;
+        const int row = a.row0 + 16 * st + r16;
         if (q4 == 0 && row < a.rows) {
           a.part_ml[(slot0 + row) * 2 + 0] = m[st];
           a.part_ml[(slot0 + row) * 2 + 1] = lsum[st];
@@ -445,9 +448,14 @@ hipError_t stream_launch(const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Up to 32 rows in one pass; 33 .. 64 rows (eight heads per KV head at
+// k >= 4, say) in two passes of 32 rows over the same stream plan, each
+// reading the K/V once more, into the same partial slots.
 template <int D, int NSETS>
-hipError_t verify_impl(const VerifyArgs& a, hipStream_t s) {
-  hipError_t e = stream_launch<D, NSETS, false>(a, s);
+hipError_t verify_impl(const VerifyArgs& a0, hipStream_t s) {
+  VerifyArgs a = a0;
+  hipError_t e = hipSuccess;
+  for (a.row0 = 0; a.row0 < a.rows && e == hipSuccess; a.row0 += 16 * NSETS) e = stream_launch<D, NSETS, false>(a, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_merge_kernel<D>), dim3(a.c.batch * a.T * a.c.hq), dim3(kWave), 0, s, a);
   return hipGetLastError();
@@ -458,7 +466,7 @@ size_t align256v(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool verify_supported(const CacheView& c, int T) {
-  return c.dtype == SPDEC_BF16 && T >= 1 && T <= 16 && c.group * T <= 32 &&
+  return c.dtype == SPDEC_BF16 && T >= 1 && T <= 16 && c.group * T <= 64 &&
          (int64_t)c.batch * c.hkv <= kMaxStreamUnits;
 }
 
@@ -478,6 +486,7 @@ hipError_t launch_verify(const CacheView& c, const void* q, int T, float scale, 
   a.T = T;
   a.shared = nullptr;
   a.rows = c.group * T;
+  a.row0 = 0;
   a.jmax = p.jmax;
   a.rmin = p.rmin;
   a.qk_scale = scale * kLog2e;
@@ -503,6 +512,7 @@ hipError_t launch_prefix_partials(const CacheView& c, const void* q, int group_s
   a.T = group_size;
   a.shared = shared_pages;
   a.rows = c.group * group_size;
+  a.row0 = 0;
   a.jmax = jmax;
   a.rmin = rmin;
   a.qk_scale = scale * kLog2e;

@@ -137,8 +137,13 @@ def test_verify_checks(L):
     d = _desc()  # bf16, G = 4
     ws = L.spdec_verify_workspace_bytes(ctypes.byref(d), 7)
     assert ws > 0
-    assert L.spdec_verify_workspace_bytes(ctypes.byref(d), 9) == 0           # G * T = 36 > 32
-    assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 9, 0.1, FAKE, None, FAKE, ws, None) == -2
+    assert L.spdec_verify_workspace_bytes(ctypes.byref(d), 9) > ws            # G * T = 36: two 32-row passes
+    assert L.spdec_verify_workspace_bytes(ctypes.byref(d), 17) == 0           # T > 16
+    assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 17, 0.1, FAKE, None, FAKE, ws, None) == -2
+    d8 = _desc(num_q_heads=16)                                                  # G = 8
+    assert L.spdec_verify_workspace_bytes(ctypes.byref(d8), 8) > 0            # G * T = 64
+    assert L.spdec_verify_workspace_bytes(ctypes.byref(d8), 9) == 0           # G * T = 72 > 64
+    assert L.spdec_verify_decode(ctypes.byref(d8), FAKE, 9, 0.1, FAKE, None, FAKE, ws, None) == -2
     assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 0, 0.1, FAKE, None, FAKE, ws, None) == -1
     assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 7, 0.0, FAKE, None, FAKE, ws, None) == -1
     assert L.spdec_verify_decode(ctypes.byref(d), FAKE, 7, 0.1, None, None, FAKE, ws, None) == -1

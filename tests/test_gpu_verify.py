@@ -72,6 +72,9 @@ CASES = [
     (2, 4, 2, 64, 16, ("uniform", 200, 260), 16),     # 16 positions, group 2
     (4, 8, 2, 128, 16, ("fixed", 7), 7),              # the cache holds only the verified tokens
     (3, 8, 2, 128, 16, ("uniform", 17, 40), 7),       # shorter than two pages
+    (2, 16, 2, 128, 16, ("uniform", 300, 1800), 7),   # group 8 at k = 6: 56 rows, two 32-row passes
+    (2, 8, 2, 64, 8, ("uniform", 100, 700), 16),      # group 4, 16 positions: 64 rows
+    (3, 16, 2, 128, 32, ("uniform", 40, 1200), 5),    # group 8: 40 rows (second pass 8 rows)
 ]
 
 
