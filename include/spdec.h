@@ -244,8 +244,9 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
  * and the two partials are merged by log-sum-exp in a fixed order.
  *
  * q: [batch][Hq][D] bf16; shared_pages: int32 [batch / N]; out, lse as for
- * spdec_dense_decode. Requires a bf16 cache, batch % N == 0 and N * G <= 32
- * (SPDEC_ERR_UNSUPPORTED otherwise). Workspace:
+ * spdec_dense_decode. Requires a bf16 cache, batch % N == 0 and N * G <= 64
+ * (SPDEC_ERR_UNSUPPORTED otherwise; above 32 query rows per (group, KV head)
+ * the shared pages are read twice, once per 32 rows). Workspace:
  * spdec_shared_workspace_bytes(cache, N), zero-filled once.
  */
 size_t spdec_shared_workspace_bytes(const spdec_cache* cache, int group_size);

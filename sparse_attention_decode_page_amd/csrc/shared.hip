@@ -191,7 +191,7 @@ SharedLayout shared_layout(const CacheView& c, int group_size) {
 }  // namespace
 
 bool shared_supported(const CacheView& c, int group_size) {
-  return c.dtype == SPDEC_BF16 && group_size >= 1 && c.batch % group_size == 0 && c.group * group_size <= 32 &&
+  return c.dtype == SPDEC_BF16 && group_size >= 1 && c.batch % group_size == 0 && c.group * group_size <= 64 &&
          (int64_t)c.batch * c.hkv <= kMaxStreamUnits;
 }
 

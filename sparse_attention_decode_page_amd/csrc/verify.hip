@@ -521,9 +521,12 @@ hipError_t launch_prefix_partials(const CacheView& c, const void* q, int group_s
   a.count = count;
   a.out = nullptr;
   a.lse = nullptr;
-  const bool two = a.rows > 16;
-  if (c.head_dim == 64) return two ? stream_launch<64, 2, true>(a, s) : stream_launch<64, 1, true>(a, s);
-  return two ? stream_launch<128, 2, true>(a, s) : stream_launch<128, 1, true>(a, s);
+  if (a.rows <= 16) return c.head_dim == 64 ? stream_launch<64, 1, true>(a, s) : stream_launch<128, 1, true>(a, s);
+  // 17 .. 64 rows: passes of 32 rows over the same plan (33 .. 64 rows read the shared pages twice).
+  hipError_t e = hipSuccess;
+  for (a.row0 = 0; a.row0 < a.rows && e == hipSuccess; a.row0 += 32)
+    e = c.head_dim == 64 ? stream_launch<64, 2, true>(a, s) : stream_launch<128, 2, true>(a, s);
+  return e;
 }
 
 }  // namespace spdec

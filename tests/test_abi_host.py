@@ -185,7 +185,9 @@ def test_shared_prefix_checks(L):
     ws = L.spdec_shared_workspace_bytes(ctypes.byref(d), 2)
     assert ws > 0
     assert L.spdec_shared_workspace_bytes(ctypes.byref(d), 3) == 0            # batch % N != 0
-    assert L.spdec_shared_workspace_bytes(ctypes.byref(d), 16) == 0           # N * G > 32
+    d32 = _desc(batch=32)
+    assert L.spdec_shared_workspace_bytes(ctypes.byref(d32), 16) > 0          # N * G = 64: two 32-row passes
+    assert L.spdec_shared_workspace_bytes(ctypes.byref(d32), 32) == 0         # N * G > 64
     assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 3, FAKE, 0.1, FAKE, None, FAKE, ws, None) == -1
     assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 0, FAKE, 0.1, FAKE, None, FAKE, ws, None) == -1
     assert L.spdec_dense_decode_shared(ctypes.byref(d), FAKE, 2, None, 0.1, FAKE, None, FAKE, ws, None) == -1

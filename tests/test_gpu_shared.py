@@ -65,6 +65,8 @@ CASES = [
     (8, 16, 2, 128, 32, ("uniform", 40, 400), 4, 500),    # group 8: 32 rows per group unit
     (4, 4, 4, 128, 64, ("uniform", 5, 200), 2, 700),      # one query head per KV head
     (4, 8, 2, 128, 16, ("uniform", 50, 60), 1, 320),      # groups of one
+    (16, 16, 2, 128, 16, ("uniform", 20, 300), 8, 600),   # group 8 x 8 samples: 64 rows, two 32-row passes
+    (12, 8, 2, 64, 8, ("uniform", 1, 120), 12, 250),      # 12 samples x group 4: 48 rows (second pass 16)
 ]
 
 
