@@ -132,6 +132,34 @@ def test_edge_shapes_all_units(case, seed):
     _check_path(wl, GS.sample_units(wl, 10 ** 9))
 
 
+def _random_shape(seed):
+    r = np.random.default_rng(1000 + seed)
+    dt = "f32" if r.random() < 0.3 else "bf16"
+    D = int(r.choice([64, 128]))
+    Hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4, 8]))
+    ps = int(r.choice([8, 16, 32, 64]))
+    B = int(r.integers(1, 6))
+    # lengths anywhere up to 60 pages, half of them on or next to a page boundary
+    lens = [int(r.integers(1, 60 * ps)) if r.random() < 0.5 else max(1, int(r.integers(0, 40)) * ps + int(r.integers(-1, 2)))
+            for _ in range(B)]
+    budget = [int(r.integers(0, 40)) for _ in range(B)]
+    return dt, D, Hkv * G, Hkv, ps, lens, budget
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_all_units(seed):
+    """Seeded random shapes (dtype, head dim, group, page size, ragged lengths on and off page boundaries,
+    budgets from 0 to 39 pages), every unit against the oracle."""
+    dt, D, Hq, Hkv, ps, lens, bud = _random_shape(seed)
+    say(f"case random {seed}: {dt} D{D} Hq{Hq}/Hkv{Hkv} ps{ps} lens {lens} budget {bud}")
+    spec = S.custom_spec(f"rand{seed}", batch=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                         page_size=ps, dtype=dt, lens=("list", lens), budget=("pages", bud),
+                         outlier_channels=4 if dt == "bf16" else 0)
+    wl = S.make_workload(spec, seed=seed, headroom=int(np.random.default_rng(seed).integers(0, 3 * ps)))
+    _check_path(wl, GS.sample_units(wl, 10 ** 9))
+
+
 def test_more_units_than_the_stream_grid_holds():
     """More (sequence, KV head) units than the persistent grids' unit table holds (8192): scoring falls back to
     one workgroup per (unit, page block) and the decode to fixed splits; both must still match the oracle."""
