@@ -80,6 +80,23 @@ def test_shared_prefix_all_units(case):
     _check(wl, wl.shared_pages, N, [(b, g) for b in range(B) for g in range(Hkv)])
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_prefix_random_shapes(seed):
+    """Seeded random groups: samples per group, group size (N * G up to 64), page size, prompt length."""
+    r = np.random.default_rng(3000 + seed)
+    G = int(r.choice([1, 2, 4, 8]))
+    N = int(r.integers(1, min(12, 64 // G) + 1))
+    groups = int(r.integers(1, 3))
+    D = int(r.choice([64, 128]))
+    ps = int(r.choice([8, 16, 32, 64]))
+    prompt = int(r.integers(1, 30 * ps))
+    spec = S.custom_spec(f"shared-rand{seed}", batch=N * groups, num_q_heads=2 * G, num_kv_heads=2, head_dim=D,
+                         page_size=ps, dtype="bf16", lens=("uniform", 1, 10 * ps), budget=("tokens", 64),
+                         outlier_channels=2, prompt=("shared", N, prompt))
+    wl = S.make_workload(spec, seed=seed)
+    _check(wl, wl.shared_pages, N, [(b, g) for b in range(N * groups) for g in range(2)])
+
+
 def test_fewer_shared_pages_than_possible_and_none():
     spec = S.custom_spec("shared-partial", batch=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
                          dtype="bf16", lens=("uniform", 30, 200), budget=("tokens", 64), prompt=("shared", 4, 400))

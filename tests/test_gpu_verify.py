@@ -87,6 +87,23 @@ def test_verify_small_all_units(case):
     _check(wl, T, [(b, g) for b in range(B) for g in range(Hkv)], seed=case)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_verify_random_shapes(seed):
+    """Seeded random shapes: group, positions (G * T up to 64), head dim, page size, ragged lengths."""
+    r = np.random.default_rng(2000 + seed)
+    G = int(r.choice([1, 2, 4, 8]))
+    T = int(r.integers(1, min(16, 64 // G) + 1))
+    Hkv = int(r.choice([1, 2]))
+    D = int(r.choice([64, 128]))
+    ps = int(r.choice([8, 16, 32, 64]))
+    B = int(r.integers(1, 4))
+    spec = S.custom_spec(f"verify-rand{seed}", batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                         page_size=ps, dtype="bf16", lens=("uniform", T, 40 * ps), budget=("tokens", 64),
+                         outlier_channels=2)
+    wl = S.make_workload(spec, seed=seed)
+    _check(wl, T, [(b, g) for b in range(B) for g in range(Hkv)], seed=seed)
+
+
 def test_verify_one_position_matches_dense_decode():
     spec = S.custom_spec("verify-dense", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
                          dtype="bf16", lens=("uniform", 100, 2000), budget=("tokens", 64))
