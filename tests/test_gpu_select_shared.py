@@ -84,6 +84,25 @@ def test_select_shared_matches_select(case):
     _check(wl, wl.shared_pages, N, GS.sample_units(wl, 6, seed=case))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_select_shared_random_shapes(seed):
+    """Seeded random groups (1-8 members, any group size, page size, prompt and generated lengths, budgets)."""
+    r = np.random.default_rng(4000 + seed)
+    N = int(r.integers(1, 9))
+    groups = int(r.integers(1, 4))
+    G = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.choice([1, 2]))
+    D = int(r.choice([64, 128]))
+    ps = int(r.choice([8, 16, 32, 64]))
+    prompt = int(r.integers(1, 60 * ps))
+    spec = S.custom_spec(f"selshared-rand{seed}", batch=N * groups, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                         head_dim=D, page_size=ps, dtype="bf16", lens=("uniform", 1, 30 * ps),
+                         budget=("tokens", int(r.integers(2, 40)) * ps), outlier_channels=2,
+                         prompt=("shared", N, prompt))
+    wl = S.make_workload(spec, seed=seed)
+    _check(wl, wl.shared_pages, N, [(b, g) for b in range(N * groups) for g in range(Hkv)])
+
+
 def test_select_shared_fewer_shared_pages_and_none():
     spec = S.custom_spec("selshared-partial", batch=8, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
                          dtype="bf16", lens=("uniform", 30, 200), budget=("tokens", 128), prompt=("shared", 4, 400))

@@ -114,6 +114,24 @@ def test_top_p_small_all_units(case, top_p):
     _check(wl, top_p, [(b, g) for b in range(B) for g in range(Hkv)])
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_top_p_random_shapes(seed):
+    """Seeded random shapes, p and score scale, with and without the per-sequence cap."""
+    r = np.random.default_rng(5000 + seed)
+    G = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.choice([1, 2]))
+    D = int(r.choice([64, 128]))
+    ps = int(r.choice([8, 16, 32, 64]))
+    B = int(r.integers(1, 4))
+    spec = S.custom_spec(f"topp-rand{seed}", batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                         page_size=ps, dtype="bf16", lens=("uniform", 1, 200 * ps),
+                         budget=("tokens", int(r.integers(2, 60)) * ps), outlier_channels=2)
+    wl = S.make_workload(spec, seed=seed)
+    top_p = float(r.uniform(0.05, 0.995))
+    c = float(r.uniform(0.2, 3.0)) / (G * math.sqrt(D))
+    _check(wl, top_p, [(b, g) for b in range(B) for g in range(Hkv)], use_budget=bool(r.random() < 0.5), c=c)
+
+
 def test_top_p_without_cap_and_full_mass():
     spec = S.custom_spec("topp-nocap", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
                          dtype="bf16", lens=("uniform", 100, 2500), budget=("tokens", 64), outlier_channels=2)
