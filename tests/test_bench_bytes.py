@@ -38,3 +38,15 @@ def test_algorithmic_bytes_brute_force(dtype, D, ps):
     assert got["select_pages"] == meta
     assert got["acceptance"] == 2 * rows * vocab * 4
     assert got["append_kv"] == B * Hkv * (2 * D * elt + 2 * 2 * D * elt)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asking for more exits with status 2 and says why (before touching any GPU)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
