@@ -181,3 +181,35 @@ def test_control_loop_graph_replay_matches_eager():
             assert torch.equal(a[name], b[name]), (i, name)
         graphed.o.fill_(float("nan"))
     assert float(graphed.scale.item()) != 1.0      # the controller moved the schedule
+
+
+def test_side_streams_and_concurrent_calls_match_the_default_stream():
+    """Calls follow torch's current stream: the path run on two side streams at once (two caches, separate
+    workspaces) gives bitwise the results of the same calls run one after the other on the default stream."""
+    wls = []
+    for i, (B, Hq, Hkv, lens) in enumerate(((6, 32, 8, ("uniform", 3000, 9000)), (4, 16, 8, ("uniform", 2000, 6000)))):
+        spec = S.custom_spec(f"streams{i}", batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, page_size=16,
+                             dtype="bf16", lens=lens, budget=("tokens", 1024), outlier_channels=4)
+        wls.append(GS.DeviceWorkload(S.make_workload(spec, seed=70 + i)))
+
+    def run(dw):
+        c = dw.cache
+        spdec.build_meta(c)
+        idx, cnt = spdec.select_pages(c, dw.q, dw.budget, dw.max_budget)
+        o_s, l_s = spdec.sparse_decode(c, dw.q, idx, cnt, dw.max_budget)
+        o_d, l_d = spdec.dense_decode(c, dw.q)
+        return [idx, cnt, o_s, l_s, o_d, l_d]
+
+    ref = [run(dw) for dw in wls]
+    torch.cuda.synchronize()
+    ref = [[t.clone() for t in r] for r in ref]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for s, dw in zip(streams, wls):
+        with torch.cuda.stream(s):
+            outs.append(run(dw))
+    torch.cuda.synchronize()
+    for r, o in zip(ref, outs):
+        for a, b in zip(r, o):
+            assert torch.equal(a, b)
