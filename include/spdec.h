@@ -210,7 +210,9 @@ spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, 
  *   z_t = scale * q_h . k_t,  out_h = sum_t e^{z_t} v_t / sum_t e^{z_t},
  *   lse_h = ln sum_t e^{z_t}
  * computed in fp32 as split-KV partials with an online softmax, merged by
- * log-sum-exp in a fixed order (deterministic, no float atomics).
+ * log-sum-exp in a fixed order (deterministic, no float atomics). A sequence
+ * with seq_lens[b] == 0 attends over no token: its rows of out are zeros and
+ * its lse is -inf (an empty softmax sum is 0; the pages do not cover it).
  *
  * q: [batch][Hq][D] cache dtype; out: fp32 [batch][Hq][D]; lse: nullable fp32
  * [batch][Hq]. sel_idx/sel_cnt as written by spdec_select_pages with the same

@@ -150,7 +150,11 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
 
     z_t = scale * q . k_t ; o = sum_t e^{z_t - m} v_t / sum_t e^{z_t - m} with
     m = max_t z_t ; lse = m + ln sum_t e^{z_t - m}. Returns (o [D], lse).
+    With no token at all the pages say nothing; the output is taken as zeros
+    and lse as ln 0 = -inf.
     """
+    if K.shape[0] == 0:  # no token in the cache: an empty sum, zeros and ln 0
+        return np.zeros(V.shape[1]), -math.inf
     z = scale * (K @ np.asarray(q, dtype=np.float64))
     m = z.max()
     w = np.exp(z - m)

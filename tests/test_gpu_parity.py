@@ -52,7 +52,8 @@ def _check_path(wl, units, full_units_props=True):
     out_s_h, lse_s_h = out_s.cpu().numpy(), lse_s.cpu().numpy()
     out_d_h, lse_d_h = out_d.cpu().numpy(), lse_d.cpu().numpy()
     assert np.all(np.isfinite(out_s_h)) and np.all(np.isfinite(out_d_h))
-    assert np.all(np.isfinite(lse_s_h)) and np.all(np.isfinite(lse_d_h))
+    live = wl.lens > 0  # a sequence with no token has lse = -inf
+    assert np.all(np.isfinite(lse_s_h[live])) and np.all(np.isfinite(lse_d_h[live]))
     ps, G = spec.page_size, spec.group
     if full_units_props:
         for b in range(spec.batch):
@@ -158,6 +159,26 @@ def test_random_shapes_all_units(seed):
                          outlier_channels=4 if dt == "bf16" else 0)
     wl = S.make_workload(spec, seed=seed, headroom=int(np.random.default_rng(seed).integers(0, 3 * ps)))
     _check_path(wl, GS.sample_units(wl, 10 ** 9))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_empty_sequences(dt):
+    """Sequences holding no token: no page is kept, the outputs are zeros and lse is -inf (an empty softmax
+    sum), and the other sequences of the batch are unaffected."""
+    say(f"case empty sequences ({dt})")
+    spec = S.custom_spec(f"empty-{dt}", batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, dtype=dt,
+                         lens=("list", [0, 40, 0, 300]), budget=("pages", [4, 4, 4, 6]),
+                         outlier_channels=4 if dt == "bf16" else 0)
+    wl = S.make_workload(spec, seed=12, headroom=16)
+    dw, sel_idx_h, sel_cnt_h = _check_path(wl, [(1, 0), (1, 1), (3, 0), (3, 1)], full_units_props=False)
+    assert np.all(sel_cnt_h[[0, 2]] == 0)
+    out_s, lse_s = spdec.sparse_decode(dw.cache, dw.q, torch.from_numpy(sel_idx_h).cuda(),
+                                       torch.from_numpy(sel_cnt_h).cuda(), dw.max_budget)
+    out_d, lse_d = spdec.dense_decode(dw.cache, dw.q)
+    torch.cuda.synchronize()
+    for o, l in ((out_s, lse_s), (out_d, lse_d)):
+        assert torch.all(o[[0, 2]] == 0) and torch.all(torch.isneginf(l[[0, 2]]))
+        assert torch.all(torch.isfinite(l[[1, 3]]))
 
 
 def test_more_units_than_the_stream_grid_holds():

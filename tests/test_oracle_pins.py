@@ -240,6 +240,24 @@ def test_attention_closed_forms():
     np.testing.assert_allclose(o, Vc[0], rtol=1e-14)
 
 
+def test_empty_sequence_conventions():
+    # no token: the sum of weights is empty (0), so lse = ln 0 and the output is taken as zeros;
+    # the empty sequence keeps no page and scores none
+    D = 8
+    o, lse = O.attention(RNG.standard_normal(D), np.zeros((0, D)), np.zeros((0, D)), 0.5)
+    assert np.array_equal(o, np.zeros(D)) and lse == -np.inf
+    kmin, kmax = O.page_minmax(np.zeros((0, D)), 16)
+    assert kmin.shape == (0, D) and O.select_pages(O.page_scores(np.ones((2, D)), kmin, kmax), 5).size == 0
+    o, lse = O.dense_decode_unit(np.ones((2, D)), np.zeros((0, D)), np.zeros((0, D)), 16, 0.5)
+    assert np.array_equal(o, np.zeros((2, D))) and np.all(lse == -np.inf)
+    # the convention is the identity of the log-sum-exp merge: adding the empty set changes nothing
+    K, V = RNG.standard_normal((5, D)), RNG.standard_normal((5, D))
+    q = RNG.standard_normal(D)
+    full = O.attention(q, K, V, 0.5)
+    o, lse = O.lse_merge([full, O.attention(q, K[:0], V[:0], 0.5)])
+    assert np.array_equal(o, full[0]) and lse == full[1]
+
+
 def test_lse_merge_of_splits_equals_unsplit():
     L, D = 97, 32
     q = RNG.standard_normal(D)
