@@ -33,7 +33,8 @@
  *   memory without a sync): 0 <= seq_lens[b] <= max_pages_per_seq*page_size;
  *   page-table entries of pages in use are in [0, num_phys_pages); inputs are
  *   finite. Kernels never dereference an out-of-range physical page or page
- *   index: such a page is treated as holding no token.
+ *   index: such a page is treated as holding no token. spdec_check_inputs
+ *   counts violations of these preconditions on the device.
  * Threading: calls keep no global state; concurrent calls on different
  *   streams must not share a workspace.
  */
@@ -382,6 +383,40 @@ typedef struct spdec_budget_params {
 
 spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t* seq_lens, int batch,
                                  const spdec_budget_params* params, int32_t* budget_pages, void* stream);
+
+/*
+ * spdec_check_inputs - counts, on the device, violations of the data
+ * preconditions that the other calls assume without checking (a debug aid:
+ * it reads the page table, the lengths and, when given, the selection, the
+ * query and the shared-page counts once; the hot calls skip that read).
+ *
+ * report: int32 [SPDEC_CHECK_WORDS], overwritten (stream-ordered) with
+ *   [0] sequences whose seq_lens[b] is outside [0, max_pages_per_seq*page_size];
+ *   [1] page-table entries of live pages (logical page < P_b = ceil(L_b/ps),
+ *       L_b clamped to that range) outside [0, num_phys_pages);
+ *   [2] (sequence, KV head) rows of a selection that spdec_select_pages with
+ *       this max_budget_pages could not have written: sel_cnt outside
+ *       [0, min(max_budget_pages, P_b)], or an entry among the first sel_cnt
+ *       outside [0, P_b) or not above the entry before it (entries ascend
+ *       strictly; repeated pages would be counted twice);
+ *   [3] non-finite values of q [batch][Hq][D] (cache dtype);
+ *   [4] groups n of group_size sequences (the shared-prefix calls' layout)
+ *       whose shared_pages[n] is outside [0, max_pages_per_seq], exceeds the
+ *       full pages floor(L/ps) of a member, or whose first shared_pages[n]
+ *       page-table entries differ between members;
+ *   [5] SPDEC_CHECK_FIRST: the lowest sequence with a violation in [0]..[4]
+ *       (a group's first sequence for [4]), or batch if there is none;
+ *   [6], [7] zero.
+ * q, sel_idx/sel_cnt (both or neither; max_budget_pages >= 1 with them) and
+ * shared_pages (then group_size >= 1 divides batch) are nullable: a null
+ * pointer skips its check. Only the descriptor's sizes index the arrays, so
+ * any values in them are safe to check; the pools and summaries are not read.
+ */
+#define SPDEC_CHECK_WORDS 8
+#define SPDEC_CHECK_FIRST 5
+spdec_status spdec_check_inputs(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int max_budget_pages, int group_size,
+                                const int32_t* shared_pages, int32_t* report, void* stream);
 
 #ifdef __cplusplus
 }

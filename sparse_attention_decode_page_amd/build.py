@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libspdec.so")
-SOURCES = ["abi.hip", "grid.hip", "meta.hip", "select.hip", "decode.hip", "verify.hip", "shared.hip", "speculative.hip", "acceptance.hip", "control.hip"]
+SOURCES = ["abi.hip", "grid.hip", "meta.hip", "select.hip", "decode.hip", "verify.hip", "shared.hip", "speculative.hip", "acceptance.hip", "control.hip", "check.hip"]
 
 # Packed-FP32 VALU instructions are switched off for all device code.
 HIP_FLAGS = [

@@ -284,6 +284,21 @@ spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t*
                                               static_cast<hipStream_t>(stream)));
 }
 
+spdec_status spdec_check_inputs(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, int max_budget_pages, int group_size,
+                                const int32_t* shared_pages, int32_t* report, void* stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (report == nullptr) return SPDEC_ERR_INVALID;
+  if ((sel_idx == nullptr) != (sel_cnt == nullptr)) return SPDEC_ERR_INVALID;
+  if (sel_idx != nullptr && max_budget_pages < 1) return SPDEC_ERR_INVALID;
+  if (shared_pages != nullptr && (group_size < 1 || v.batch % group_size != 0)) return SPDEC_ERR_INVALID;
+  return from_hip(spdec::launch_check(v, q, sel_idx, sel_cnt, sel_idx ? max_budget_pages : 0,
+                                      shared_pages ? group_size : 1, shared_pages, report,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream) {
   if (!alpha || !out || rows < 1) return SPDEC_ERR_INVALID;
   if (rows > spdec::kTailMaxRows) return SPDEC_ERR_UNSUPPORTED;

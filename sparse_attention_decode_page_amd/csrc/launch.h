@@ -93,6 +93,9 @@ constexpr int kTailMaxRows = 8192;  // values the tail statistics sort in LDS
 hipError_t launch_tail_stats(const float* alpha, int n, float* out, hipStream_t s);
 hipError_t launch_budget_update(const float* tail, float* state, const int32_t* seq_lens, int batch,
                                 const spdec_budget_params& p, int32_t* budget, hipStream_t s);
+// Precondition counts of spdec_check_inputs into report[SPDEC_CHECK_WORDS].
+hipError_t launch_check(const CacheView& c, const void* q, const int32_t* sel_idx, const int32_t* sel_cnt,
+                        int max_budget, int group_size, const int32_t* shared_pages, int32_t* report, hipStream_t s);
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
                              float* alpha, void* ws, hipStream_t s);
 

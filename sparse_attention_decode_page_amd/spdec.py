@@ -27,8 +27,9 @@ ABI_FUNCTIONS = (
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
-    "spdec_acceptance", "spdec_tail_stats", "spdec_budget_update",
+    "spdec_acceptance", "spdec_tail_stats", "spdec_budget_update", "spdec_check_inputs",
 )
+SPDEC_CHECK_WORDS, SPDEC_CHECK_FIRST = 8, 5
 
 
 class CacheDesc(ctypes.Structure):
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
         "spdec_acceptance": (I, [P, P, I, I, I64, F, P, P, SZ, P]),
         "spdec_tail_stats": (I, [P, I, P, P]),
         "spdec_budget_update": (I, [P, P, P, I, ctypes.POINTER(BudgetParams), P, P]),
+        "spdec_check_inputs": (I, [D, P, P, P, I, I, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -436,3 +438,30 @@ def budget_update(tail, scale, seq_lens, params: BudgetParams, budget_pages=None
     _check(lib().spdec_budget_update(_ptr(tail), _ptr(scale), _ptr(seq_lens), batch, ctypes.byref(params),
                                      _ptr(budget_pages), _stream()), "spdec_budget_update")
     return budget_pages
+
+
+CHECK_FIELDS = ("bad_lengths", "bad_page_entries", "bad_selection_rows", "nonfinite_q", "bad_shared_groups",
+                "first_bad_sequence")
+
+
+def check_inputs(cache: PagedCache, q=None, sel_idx=None, sel_cnt=None, max_budget_pages: int = 0,
+                 group_size: int = 1, shared_pages=None, report=None) -> dict:
+    """Device-side precondition counts (``spdec_check_inputs``); synchronises to read them back."""
+    if report is None:
+        report = torch.empty(SPDEC_CHECK_WORDS, dtype=torch.int32, device=cache.page_table.device)
+    _need(report, "report", torch.int32, (SPDEC_CHECK_WORDS,))
+    if q is not None:
+        _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    if sel_idx is not None:
+        _need(sel_idx, "sel_idx", torch.int32, (cache.batch, cache.num_kv_heads, max_budget_pages))
+    if sel_cnt is not None:
+        _need(sel_cnt, "sel_cnt", torch.int32, (cache.batch, cache.num_kv_heads))
+    if shared_pages is not None:
+        if group_size < 1 or cache.batch % group_size:
+            raise ValueError("group_size must divide the batch")
+        _need(shared_pages, "shared_pages", torch.int32, (cache.batch // group_size,))
+    _check(lib().spdec_check_inputs(ctypes.byref(cache.desc), _ptr(q), _ptr(sel_idx), _ptr(sel_cnt),
+                                    max_budget_pages, group_size, _ptr(shared_pages), _ptr(report), _stream()),
+           "spdec_check_inputs")
+    vals = report.cpu().tolist()
+    return dict(zip(CHECK_FIELDS, vals[:len(CHECK_FIELDS)]))

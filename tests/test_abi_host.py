@@ -40,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 21
+    assert len(names) == len(S.ABI_FUNCTIONS) == 22
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -274,3 +274,17 @@ def test_tail_stats_checks(L):
     assert L.spdec_tail_stats(FAKE, 0, FAKE, None) == -1
     assert L.spdec_tail_stats(FAKE, 10, None, None) == -1
     assert L.spdec_tail_stats(FAKE, 8193, FAKE, None) == -2
+
+
+def test_check_inputs_checks(L):
+    d = _desc(batch=4)
+    chk = L.spdec_check_inputs
+    assert chk(ctypes.byref(d), FAKE, FAKE, FAKE, 8, 2, FAKE, None, None) == -1       # no report
+    assert chk(ctypes.byref(d), None, FAKE, None, 8, 1, None, FAKE, None) == -1       # sel_idx without sel_cnt
+    assert chk(ctypes.byref(d), None, None, FAKE, 8, 1, None, FAKE, None) == -1       # sel_cnt without sel_idx
+    assert chk(ctypes.byref(d), None, FAKE, FAKE, 0, 1, None, FAKE, None) == -1       # selection with no capacity
+    assert chk(ctypes.byref(d), None, None, None, 0, 3, FAKE, FAKE, None) == -1       # group does not divide batch
+    assert chk(ctypes.byref(d), None, None, None, 0, 0, FAKE, FAKE, None) == -1
+    assert chk(None, None, None, None, 0, 1, None, FAKE, None) == -1
+    bad = _desc(batch=4, head_dim=96)
+    assert chk(ctypes.byref(bad), None, None, None, 0, 1, None, FAKE, None) == -2
