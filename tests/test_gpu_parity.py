@@ -290,6 +290,63 @@ def test_physical_placement_invariance():
         assert torch.equal(a, b)
 
 
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_pools_past_four_gib(dt):
+    """The same pages placed past 2^31 pool elements (byte offsets past 4 GiB, as a 288 GB device allows):
+    build, append, selection, both decodes and the verification give the bits they give on a compact pool."""
+    say(f"case pools past 2^31 elements, {dt}")
+    spec = S.custom_spec("far", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, dtype=dt,
+                         lens=("list", [700, 1500, 33]), budget=("pages", [8, 20, 64]), outlier_channels=2)
+    wl = S.make_workload(spec, seed=6, headroom=16)
+    off = (1 << 31) // (spec.num_kv_heads * spec.page_size * spec.head_dim) + 7
+    n = wl.num_phys
+    rng = np.random.default_rng(6)
+    k_new32 = rng.standard_normal((spec.batch, spec.num_kv_heads, spec.head_dim), dtype=np.float32)
+    v_new32 = rng.standard_normal((spec.batch, spec.num_kv_heads, spec.head_dim), dtype=np.float32)
+    conv = (lambda x: S.f32_to_bf16_bits(x)) if dt == "bf16" else (lambda x: x)
+    k_new, v_new = GS.to_device_storage(conv(k_new32), dt), GS.to_device_storage(conv(v_new32), dt)
+    vq = None
+    if dt == "bf16":
+        vq = GS.to_device_storage(S.f32_to_bf16_bits(
+            rng.standard_normal((spec.batch, 3, spec.num_q_heads, spec.head_dim), dtype=np.float32)), dt)
+
+    def run(dw, far):
+        c = dw.cache
+        spdec.build_meta(c)
+        res = list(GS.run_select(dw))
+        res += list(spdec.sparse_decode(c, dw.q, res[0], res[1], dw.max_budget))
+        res += list(spdec.dense_decode(c, dw.q))
+        if vq is not None:
+            res += list(spdec.verify_decode(c, vq))
+        spdec.append_kv(c, k_new, v_new)
+        res += list(spdec.dense_decode(c, dw.q))
+        base = off if far else 0
+        res += [dw.k_pool[base:base + n].clone(), dw.v_pool[base:base + n].clone(), dw.kminmax[base:base + n].clone()]
+        torch.cuda.synchronize()
+        return [t.cpu() for t in res]
+
+    near = run(GS.DeviceWorkload(wl), False)
+    dw = GS.DeviceWorkload(wl)
+    tdt = dw.k_pool.dtype
+    shape = (off + n,) + tuple(dw.k_pool.shape[1:])
+    print(f"  far pools: {2 * shape[0] * np.prod(shape[1:]) * dw.k_pool.element_size() / 2**30:.1f} GiB", flush=True)
+    kb = torch.zeros(shape, dtype=tdt, device="cuda")
+    vb = torch.zeros(shape, dtype=tdt, device="cuda")
+    kb[off:] = dw.k_pool
+    vb[off:] = dw.v_pool
+    mb = torch.zeros((off + n,) + tuple(dw.kminmax.shape[1:]), dtype=tdt, device="cuda")
+    pt = torch.where(dw.page_table >= 0, dw.page_table + off, dw.page_table)
+    dw.k_pool, dw.v_pool, dw.kminmax, dw.page_table = kb, vb, mb, pt
+    dw.seq_lens = torch.from_numpy(wl.lens.astype(np.int32)).cuda()
+    dw.cache = spdec.PagedCache(kb, vb, mb, pt, dw.seq_lens, spec.num_q_heads)
+    far = run(dw, True)
+    for i, (a, b) in enumerate(zip(near, far)):
+        assert torch.equal(a, b), i
+    del dw, kb, vb, mb
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ append ---
 
 @pytest.mark.parametrize("dt,D,ps", [("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 8), ("bf16", 64, 64)])
