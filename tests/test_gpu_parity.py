@@ -202,6 +202,18 @@ def test_eight_query_heads_per_kv_head_many_chunks():
     _check_path(wl, GS.sample_units(wl, 12, seed=8))
 
 
+
+@pytest.mark.parametrize("tokens", [131100, 262144])
+def test_longest_page_tables(tokens):
+    """Page tables of 16388 pages and of 32768, the largest the interface takes (page size 8): the Top-B cut
+    with 32 keys per thread in 1024-thread workgroups, scoring and both decodes over the longest lists."""
+    spec = S.custom_spec(f"longest{tokens}", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=8,
+                         dtype="bf16", lens=("fixed", tokens), budget=("tokens", 2048), outlier_channels=2)
+    wl = S.make_workload(spec, seed=12)
+    assert wl.page_table.shape[1] in (16388, 32768)
+    say(f"case longest page table: {wl.page_table.shape[1]} pages")
+    _check_path(wl, [(0, 0), (0, 1)])
+
 def test_exact_ties_go_to_lower_index():
     """Pages with identical keys tie exactly in fp32 and fp64; the lower index must win."""
     say("case exact ties")
