@@ -129,7 +129,7 @@ def test_check_counts_planted_violations(seed):
         [0, 0, 0, 0, 0, batch]
 
     # plant one kind of violation per affected sequence, all after the first few sequences
-    lens[5], lens[9] = -3, maxp * ps + 1
+    lens[5], lens[9] = (-3, maxp * ps + 1) if seed % 2 else (-2**31, 2**31 - 1)
     b = 6
     P = -(-int(lens[b]) // ps)
     if P:
@@ -143,7 +143,8 @@ def test_check_counts_planted_violations(seed):
     sel_cnt[10, 1] = 1
     for i, v in enumerate(specials):  # four distinct positions
         q_bits[11, i % (G * hkv), i] = v
-    shared[1] = maxp + 1
+    shared[1] = maxp + 1 if seed % 2 else 2**31 - 1
+    sel_cnt[4, 0] = -2**31
     pt[batch - 1, 0] = (pt[batch - 1, 0] + 1) % num_phys if shared[-1] > 0 else pt[batch - 1, 0]
 
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -189,3 +190,34 @@ def test_check_is_repeatable_and_overwrites_the_report():
         r = spdec.check_inputs(cache, report=report)
         assert [r[k] for k in spdec.CHECK_FIELDS] == [0, 1, 0, 0, 0, 3]
         assert report[6:].cpu().tolist() == [0, 0]
+
+
+def test_check_replays_from_a_graph():
+    """The checker captured into a HIP graph (its report cleared by a kernel, not a memset) gives the eager
+    counts on every replay, also after the inputs change between replays."""
+    import ctypes
+    rng = np.random.default_rng(9)
+    lens = rng.integers(1, 300, size=6)
+    pt = rng.integers(0, 64, size=(6, 20))
+    pt[2, 0] = 64
+    cache = _cache(pt, lens, 64, 2, 8, 64, 16)
+    report = torch.zeros(spdec.SPDEC_CHECK_WORDS, dtype=torch.int32, device="cuda")
+    L = spdec.lib()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        st = L.spdec_check_inputs(ctypes.byref(cache.desc), None, None, None, 0, 1, None,
+                                  ctypes.c_void_p(report.data_ptr()),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == spdec.SPDEC_OK
+    for rep in range(3):
+        if rep == 2:  # one more bad length between replays
+            cache.seq_lens[4] = -1
+            torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = report.cpu().tolist()
+        eager = spdec.check_inputs(cache)
+        assert got[:6] == [eager[k] for k in spdec.CHECK_FIELDS], (rep, got)
+        assert got[:2] == ([0, 1] if rep < 2 else [1, 1]) and got[5] == 2
