@@ -104,7 +104,7 @@ def _check_path(wl, units, full_units_props=True):
 # ------------------------------------------------------------- small cases ---
 
 def test_tiny_all_units():
-    say("case tiny (fp32, D64, G2, L1024, ps16, budget 16 pages)")
+    say("case tiny (fp32, D 64, G 2, 1024 tokens, page size 16, budget 16 pages)")
     wl = S.make_workload("tiny", seed=0)
     _check_path(wl, GS.sample_units(wl, 10 ** 9))
 
