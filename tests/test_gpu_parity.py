@@ -43,6 +43,9 @@ def _check_path(wl, units, full_units_props=True):
     c = dw.cache
     spdec.build_meta(c)
     sel_idx, sel_cnt, scores = GS.run_select(dw)
+    # the inputs meet the documented preconditions and the selection has the form the decode takes
+    pre = spdec.check_inputs(c, q=dw.q, sel_idx=sel_idx, sel_cnt=sel_cnt, max_budget_pages=dw.max_budget)
+    assert pre["first_bad_sequence"] == spec.batch, pre
     out_s, lse_s = spdec.sparse_decode(c, dw.q, sel_idx, sel_cnt, dw.max_budget)
     out_d, lse_d = spdec.dense_decode(c, dw.q)
     torch.cuda.synchronize()

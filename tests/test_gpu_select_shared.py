@@ -45,6 +45,10 @@ def _check(wl, shared, N, units):
     idx, cnt = spdec.select_pages_shared(c, dw.q, N, sh, dw.budget, dw.max_budget, scores_out=scores)
     # the same call through the workspace (no scores out)
     idx2, cnt2 = spdec.select_pages_shared(c, dw.q, N, sh, dw.budget, dw.max_budget)
+    # inputs meet the documented preconditions and the selection is of the form the decode takes
+    pre = spdec.check_inputs(c, q=dw.q, sel_idx=idx, sel_cnt=cnt, max_budget_pages=dw.max_budget, group_size=N,
+                             shared_pages=sh)
+    assert pre["first_bad_sequence"] == spec.batch, pre
     torch.cuda.synchronize()
     P = np.minimum((wl.lens + spec.page_size - 1) // spec.page_size, c.max_pages)
     s_h, r_h = scores.cpu().numpy(), ref_scores.cpu().numpy()

@@ -38,6 +38,8 @@ def _check(wl, shared, N, units):
           f"shared pages {shared.tolist()[:4]}", flush=True)
     dw = GS.DeviceWorkload(wl)
     sh = torch.from_numpy(shared.astype(np.int32)).cuda()
+    pre = spdec.check_inputs(dw.cache, q=dw.q, group_size=N, shared_pages=sh)  # the documented preconditions hold
+    assert pre["first_bad_sequence"] == spec.batch, pre
     out, lse = spdec.dense_decode_shared(dw.cache, dw.q, N, sh)
     od, ld = spdec.dense_decode(dw.cache, dw.q)
     torch.cuda.synchronize()
