@@ -64,6 +64,9 @@ def _check(wl, top_p, units, use_budget=True, c=None, expect_all=False):
     idx, cnt = spdec.select_pages_top_p(cache, dw.q, top_p, cap, score_scale=c32, budget_pages=budget,
                                         scores_out=scores)
     idx2, cnt2 = spdec.select_pages_top_p(cache, dw.q, top_p, cap, score_scale=c32, budget_pages=budget)
+    # the kept sets have the form the sparse decode takes (ascending pages below the page count, at most cap)
+    pre = spdec.check_inputs(cache, q=dw.q, sel_idx=idx, sel_cnt=cnt, max_budget_pages=cap)
+    assert pre["first_bad_sequence"] == cache.batch, pre
     torch.cuda.synchronize()
     assert torch.equal(cnt, cnt2)
     idx_h, cnt_h, idx2_h = idx.cpu().numpy(), cnt.cpu().numpy(), idx2.cpu().numpy()
