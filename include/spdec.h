@@ -407,9 +407,11 @@ spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t*
  *   [5] SPDEC_CHECK_FIRST: the lowest sequence with a violation in [0]..[4]
  *       (a group's first sequence for [4]), or batch if there is none;
  *   [6], [7] zero.
- * q, sel_idx/sel_cnt (both or neither; max_budget_pages >= 1 with them) and
- * shared_pages (then group_size >= 1 divides batch) are nullable: a null
- * pointer skips its check. Only the descriptor's sizes index the arrays, so
+ * Layouts: q [batch][Hq][D] (cache dtype); sel_idx int32
+ * [batch][Hkv][max_budget_pages]; sel_cnt int32 [batch][Hkv]; shared_pages
+ * int32 [batch / group_size]. q, sel_idx/sel_cnt (both or neither;
+ * max_budget_pages >= 1 with them) and shared_pages (then group_size >= 1
+ * divides batch) are nullable: a null pointer skips its check. Only the descriptor's sizes index the arrays, so
  * any values in them are safe to check; the pools and summaries are not read.
  */
 #define SPDEC_CHECK_WORDS 8
