@@ -76,6 +76,7 @@ CASES = [
     (4, 4, 4, 128, 64, ("uniform", 5, 200), 2, 4000, ("tokens", 512)),   # one query head per KV head
     (4, 8, 2, 128, 16, ("uniform", 50, 60), 1, 320, ("tokens", 64)),     # groups of one
     (16, 8, 2, 128, 16, ("uniform", 100, 3000), 8, 9000, ("tokens", 1024)),  # long shared prompt
+    (6, 4, 2, 64, 8, ("list", [0, 0, 0, 0, 5, 1]), 3, 96, ("tokens", 48)),  # members holding only the prompt
 ]
 
 

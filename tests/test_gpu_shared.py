@@ -69,6 +69,7 @@ CASES = [
     (4, 8, 2, 128, 16, ("uniform", 50, 60), 1, 320),      # groups of one
     (16, 16, 2, 128, 16, ("uniform", 20, 300), 8, 600),   # group 8 x 8 samples: 64 rows, two 32-row passes
     (12, 8, 2, 64, 8, ("uniform", 1, 120), 12, 250),      # 12 samples x group 4: 48 rows (second pass 16)
+    (6, 4, 2, 64, 8, ("list", [0, 0, 0, 0, 5, 1]), 3, 96),  # members holding only the prompt (no own page)
 ]
 
 
@@ -120,6 +121,31 @@ def test_shared_prefix_is_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
+
+
+def test_reused_workspace_after_members_lose_their_own_pages():
+    """One workspace across calls: first nothing shared (every member's pages go through the per-sample pass),
+    then the whole prompt shared, so members holding only the prompt have no per-sample chunk at all. The second
+    call must equal the same call on a fresh workspace bit for bit (no count or partial left from the first)."""
+    spec = S.custom_spec("shared-reuse", batch=6, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=8,
+                         dtype="bf16", lens=("list", [0, 0, 0, 0, 5, 1]), budget=("tokens", 64),
+                         outlier_channels=2, prompt=("shared", 3, 96))
+    wl = S.make_workload(spec, seed=13)
+    dw = GS.DeviceWorkload(wl)
+    ws = torch.zeros(spdec.shared_workspace_bytes(dw.cache, 3), dtype=torch.uint8, device="cuda")
+    none = torch.zeros(2, dtype=torch.int32, device="cuda")
+    full = torch.from_numpy(wl.shared_pages.astype(np.int32)).cuda()
+    spdec.dense_decode_shared(dw.cache, dw.q, 3, none, workspace=ws)
+    o1, l1 = spdec.dense_decode_shared(dw.cache, dw.q, 3, full, workspace=ws)
+    o2, l2 = spdec.dense_decode_shared(dw.cache, dw.q, 3, full)
+    o3, l3 = spdec.dense_decode_shared(dw.cache, dw.q, 3, none, workspace=ws)
+    o4, l4 = spdec.dense_decode_shared(dw.cache, dw.q, 3, none)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+    od, ld = spdec.dense_decode(dw.cache, dw.q)
+    torch.cuda.synchronize()
+    assert (o1 - od).abs().max().item() < TOL and (l1 - ld).abs().max().item() < TOL
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
