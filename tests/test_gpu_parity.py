@@ -280,6 +280,48 @@ def test_determinism_bitwise():
             assert torch.equal(a, b)
 
 
+
+def test_reused_decode_workspace_across_calls():
+    """One decode workspace across calls whose units have many, few and no chunks (selections of the full
+    budget, of two pages, and counts cut to zero on some units), then a dense call: every result equals the same
+    call on a fresh workspace bit for bit (no chunk count or partial survives from an earlier call)."""
+    say("case reused decode workspace")
+    spec = S.custom_spec("reuse", batch=5, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16, dtype="bf16",
+                         lens=("list", [4000, 700, 2500, 33, 1800]), budget=("pages", [120, 30, 90, 4, 60]),
+                         outlier_channels=2)
+    wl = S.make_workload(spec, seed=14)
+    dw = GS.DeviceWorkload(wl)
+    c = dw.cache
+    spdec.build_meta(c)
+    cap = dw.max_budget
+    nbytes = max(spdec.decode_workspace_bytes(c, cap), spdec.decode_workspace_bytes(c, 0))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    calls = []
+    for budget in (dw.budget, torch.full_like(dw.budget, 2), dw.budget):
+        si, sc = spdec.select_pages(c, dw.q, budget, cap)
+        calls.append((si, sc))
+    si, sc = calls[0]
+    sc_cut = sc.clone()
+    sc_cut[1] = 0
+    sc_cut[3, :2] = 0
+    calls.append((si, sc_cut))
+    for k, (si, sc) in enumerate(calls):
+        o1, l1 = spdec.sparse_decode(c, dw.q, si, sc, cap, workspace=ws)
+        o2, l2 = spdec.sparse_decode(c, dw.q, si, sc, cap)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), k
+    od1, ld1 = spdec.dense_decode(c, dw.q, workspace=ws)
+    od2, ld2 = spdec.dense_decode(c, dw.q)
+    torch.cuda.synchronize()
+    assert torch.equal(od1, od2) and torch.equal(ld1, ld2)
+    # units whose count was cut to zero attend over nothing: zeros and lse = -inf
+    o, l = spdec.sparse_decode(c, dw.q, si, sc_cut, cap, workspace=ws)
+    torch.cuda.synchronize()
+    G = spec.group
+    assert torch.all(o[1] == 0) and torch.all(torch.isneginf(l[1]))
+    assert torch.all(o[3, :2 * G] == 0) and torch.all(torch.isneginf(l[3, :2 * G]))
+    assert torch.all(torch.isfinite(l[3, 2 * G:]))
+
 def test_physical_placement_invariance():
     say("case physical permutation")
     spec = S.custom_spec("perm", batch=3, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16, dtype="bf16",
