@@ -127,6 +127,23 @@ def test_verify_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+
+def test_verify_reused_workspace_across_position_counts():
+    """One workspace across verification calls of 7, 1, 16 and 7 positions (different row counts and chunk
+    layouts): each equals the same call on a fresh workspace bit for bit."""
+    spec = S.custom_spec("verify-reuse", batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("list", [3000, 40, 1200, 700]), budget=("tokens", 64))
+    wl = S.make_workload(spec, seed=15)
+    dw = GS.DeviceWorkload(wl)
+    nbytes = max(spdec.verify_workspace_bytes(dw.cache, T) for T in (1, 7, 16))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for k, T in enumerate((7, 1, 16, 7)):
+        q = GS.to_device_storage(_queries(spec, T, 20 + k), "bf16")
+        o1, l1 = spdec.verify_decode(dw.cache, q, workspace=ws)
+        o2, l2 = spdec.verify_decode(dw.cache, q)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), T
+
 def test_verify_rejects_unsupported():
     spec = S.custom_spec("verify-f32", batch=1, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
                          dtype="f32", lens=("fixed", 64), budget=("tokens", 64))
