@@ -503,6 +503,23 @@ def test_acceptance_ragged_vocab_and_unaligned_rows(V):
     _acc_check(a, b, 2.5, stride=V + 1)
 
 
+
+def test_acceptance_reused_workspace():
+    """One acceptance workspace across calls of different row counts, vocabularies and temperatures: each
+    equals the same call on a fresh workspace bit for bit."""
+    say("case acceptance reused workspace")
+    r = np.random.default_rng(16)
+    shapes = [(8, 50000, 1.0), (3, 1000, 0.7), (8, 50000, 1.3), (64, 4097, 1.0)]
+    nbytes = max(spdec.acceptance_workspace_bytes(R, V) for R, V, _ in shapes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for R, V, T in shapes:
+        a = torch.from_numpy(r.normal(0, 3, (R, V)).astype(np.float32)).cuda()
+        b = a + torch.from_numpy(r.normal(0, 0.3, (R, V)).astype(np.float32)).cuda()
+        x1 = spdec.acceptance(a, b, T, workspace=ws)
+        x2 = spdec.acceptance(a, b, T)
+        torch.cuda.synchronize()
+        assert torch.equal(x1, x2), (R, V, T)
+
 def test_acceptance_full_size():
     say("case acceptance 64 x 151936")
     spec = S.SPECS["qwen3-8b-L32k-acceptance"]
