@@ -145,3 +145,20 @@ def test_spec_accept_is_deterministic():
     a = _run(p, q, draft, ua, us)
     b = _run(p, q, draft, ua, us)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_spec_accept_reused_workspace():
+    """One workspace across calls of different batch, draft length, vocabulary and temperature: each result
+    equals the same call on a fresh workspace."""
+    shapes = [(16, 6, 30000, 1.0), (3, 2, 1000, 0.7), (16, 6, 30000, 1.2), (4, 0, 5000, 1.0)]
+    nbytes = max(spdec.spec_accept_workspace_bytes(B, k, V) for B, k, V, _ in shapes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for i, (B, k, V, T) in enumerate(shapes):
+        p, q, draft, ua, us = _inputs(B, k, V, 40 + i, temperature=T)
+        args = [torch.from_numpy(p).cuda(), torch.from_numpy(q).cuda() if k > 0 else None,
+                torch.from_numpy(draft).cuda() if k > 0 else None, torch.from_numpy(ua).cuda() if k > 0 else None,
+                torch.from_numpy(us).cuda()]
+        n1, t1 = spdec.spec_accept(*args, temperature=T, workspace=ws)
+        n2, t2 = spdec.spec_accept(*args, temperature=T)
+        torch.cuda.synchronize()
+        assert torch.equal(n1, n2) and torch.equal(t1, t2), (B, k, V, T)
