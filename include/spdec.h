@@ -322,14 +322,44 @@ spdec_status spdec_spec_accept(const float* p_logits, const float* q_logits, int
  * computed in fp32 with a fixed reduction order and clamped to [0, 1].
  *
  * logits_a, logits_b: fp32 rows of `vocab` entries, row r at r*row_stride
- * (elements); alpha: fp32 [rows] out. temperature > 0. rows >= 1,
- * 1 <= vocab <= 2^28. Workspace: spdec_acceptance_workspace_bytes(rows, vocab).
- * The mean and lower 5th percentile of alpha are host-side statistics.
+ * (elements); alpha: fp32 [rows] out. temperature > 0. 1 <= rows <= 65535,
+ * 1 <= vocab <= 2^28. Workspace: spdec_acceptance_workspace_bytes(rows, vocab);
+ * its first 96 KiB must be zero before the first call (every call leaves them
+ * zero, whatever its shape), so one zero-filled workspace serves any sequence
+ * of shapes.
+ *
+ * When all rows' 10240-entry chunks fit on the device at once (rows *
+ * ceil(vocab / 10240) at most the resident workgroups of its kernel, e.g. 64
+ * rows of 151936 on 256 compute units), every logit is read once: the chunks
+ * of a row exchange their partial normalisers through the workspace and wait
+ * for each other with a bounded wait (a chunk that stops waiting reads its
+ * row again, with identical results). Otherwise two passes read the logits
+ * twice. Either way the result is run-to-run identical; the two forms may
+ * differ in the last bits.
+ * The mean and lower 5th percentile of alpha: spdec_tail_stats.
  */
 size_t spdec_acceptance_workspace_bytes(int rows, int vocab);
 spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab,
                               int64_t row_stride, float temperature, float* alpha, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * spdec_acceptance_ex - spdec_acceptance with its form and wait made explicit
+ * (for tests and diagnostics; same arguments, results and workspace otherwise).
+ *
+ * force_path: -1 automatic (as spdec_acceptance), 1 single read
+ *   (SPDEC_ERR_UNSUPPORTED if the rows' chunks do not fit the device at once),
+ *   2 two passes.
+ * spin_limit: polls of a row's partial normalisers before a waiting chunk
+ *   reads the row itself; -1 = the default (16384), 0 = never wait.
+ * fallbacks: device int32 [1], nullable: incremented by every single-read
+ *   chunk that stopped waiting (the caller clears it).
+ * path_taken: host int32, nullable: set to the form launched (1 or 2).
+ */
+spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, int rows, int vocab,
+                                 int64_t row_stride, float temperature, float* alpha, void* workspace,
+                                 size_t workspace_bytes, int force_path, int spin_limit, int32_t* fallbacks,
+                                 int32_t* path_taken, void* stream);
 
 /*
  * spdec_tail_stats - on-device tail statistics of the per-token acceptance

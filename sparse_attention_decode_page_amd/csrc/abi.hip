@@ -253,17 +253,41 @@ size_t spdec_acceptance_workspace_bytes(int rows, int vocab) {
   return spdec::acceptance_workspace_bytes(rows, vocab);
 }
 
-spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab, int64_t row_stride,
-                              float temperature, float* alpha, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+static spdec_status acceptance_args(const float* logits_a, const float* logits_b, int rows, int vocab,
+                                    int64_t row_stride, float temperature, float* alpha) {
   if (!logits_a || !logits_b || !alpha) return SPDEC_ERR_INVALID;
   if (rows < 1 || vocab < 1 || vocab > (1 << 28) || row_stride < vocab) return SPDEC_ERR_INVALID;
   if (rows > 65535) return SPDEC_ERR_UNSUPPORTED;
   if (!(temperature > 0.f) || !isfinite(temperature)) return SPDEC_ERR_INVALID;
+  return SPDEC_OK;
+}
+
+spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab, int64_t row_stride,
+                              float temperature, float* alpha, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const spdec_status st = acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
+  if (st != SPDEC_OK) return st;
   if (workspace == nullptr || workspace_bytes < spdec::acceptance_workspace_bytes(rows, vocab))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_acceptance(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha, workspace,
-                                           static_cast<hipStream_t>(stream)));
+                                           static_cast<hipStream_t>(stream), nullptr));
+}
+
+spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, int rows, int vocab,
+                                 int64_t row_stride, float temperature, float* alpha, void* workspace,
+                                 size_t workspace_bytes, int force_path, int spin_limit, int32_t* fallbacks,
+                                 int32_t* path_taken, void* stream) {
+  const spdec_status st = acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
+  if (st != SPDEC_OK) return st;
+  if (force_path != -1 && force_path != 1 && force_path != 2) return SPDEC_ERR_INVALID;
+  if (spin_limit < -1) return SPDEC_ERR_INVALID;
+  if (workspace == nullptr || workspace_bytes < spdec::acceptance_workspace_bytes(rows, vocab))
+    return SPDEC_ERR_WORKSPACE;
+  spdec::AcceptanceDiag diag{force_path, spin_limit, fallbacks, path_taken};
+  const hipError_t e = spdec::launch_acceptance(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha,
+                                                workspace, static_cast<hipStream_t>(stream), &diag);
+  if (e == hipErrorInvalidValue && force_path == 1) return SPDEC_ERR_UNSUPPORTED;
+  return from_hip(e);
 }
 
 spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t* seq_lens, int batch,

@@ -96,7 +96,19 @@ hipError_t launch_budget_update(const float* tail, float* state, const int32_t* 
 // Precondition counts of spdec_check_inputs into report[SPDEC_CHECK_WORDS].
 hipError_t launch_check(const CacheView& c, const void* q, const int32_t* sel_idx, const int32_t* sel_cnt,
                         int max_budget, int group_size, const int32_t* shared_pages, int32_t* report, hipStream_t s);
+// Bytes at the start of an acceptance workspace that must be zero before its
+// first call; every call leaves them zero.
+size_t acceptance_sync_bytes();
+// Polls of a row's chunk pairs before a single-read workgroup reads the row itself.
+constexpr int kAcceptanceSpinLimit = 1 << 14;
+// Options of the acceptance launch (null: automatic path, default wait).
+struct AcceptanceDiag {
+  int force_path;   // -1 automatic, 1 single read, 2 two passes
+  int spin_limit;   // -1 default
+  int* fallbacks;   // device int32, nullable: single-read workgroups that stopped waiting
+  int* path;        // host, nullable: the path taken (1 or 2)
+};
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
-                             float* alpha, void* ws, hipStream_t s);
+                             float* alpha, void* ws, hipStream_t s, const AcceptanceDiag* diag);
 
 }  // namespace spdec

@@ -40,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 22
+    assert len(names) == len(S.ABI_FUNCTIONS) == 23
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -126,6 +126,19 @@ def test_acceptance_checks(L):
     assert L.spdec_acceptance(FAKE, FAKE, 0, 151936, 151936, 1.0, FAKE, FAKE, ws, None) == -1
     assert L.spdec_acceptance(FAKE, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws - 1, None) == -3
     assert L.spdec_acceptance(None, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws, None) == -1
+    # the single-read form's sync region leads every workspace (zero between calls)
+    assert L.spdec_acceptance_workspace_bytes(1, 1) >= 96 * 1024
+
+
+def test_acceptance_ex_checks(L):
+    ws = L.spdec_acceptance_workspace_bytes(64, 151936)
+    ex = L.spdec_acceptance_ex
+    assert ex(FAKE, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws, 3, -1, None, None, None) == -1     # bad form
+    assert ex(FAKE, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws, 0, -1, None, None, None) == -1
+    assert ex(FAKE, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws, 1, -2, None, None, None) == -1     # bad limit
+    assert ex(FAKE, FAKE, 64, 151936, 151936, 0.0, FAKE, FAKE, ws, -1, -1, None, None, None) == -1    # T = 0
+    assert ex(FAKE, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws - 1, 2, 0, None, None, None) == -3
+    assert ex(FAKE, None, 64, 151936, 151936, 1.0, FAKE, FAKE, ws, -1, -1, None, None, None) == -1
 
 
 def test_struct_layout_matches_header():
