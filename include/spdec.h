@@ -344,6 +344,24 @@ spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int 
                               size_t workspace_bytes, void* stream);
 
 /*
+ * spdec_acceptance_noalloc - spdec_acceptance for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): same arguments and results, no workspace.
+ *
+ * Its workspace is a SPDEC_NOALLOC_SCRATCH_BYTES device array inside the
+ * library, one per GPU, held until the process ends; its address is looked
+ * up on the first call on each device (with that device current). The call
+ * allocates nothing. Shapes whose spdec_acceptance_workspace_bytes exceeds
+ * the array (above 1332 rows of 151936 entries) return
+ * SPDEC_ERR_UNSUPPORTED without launching. Every call on one GPU uses the same
+ * array: calls that overlap on one GPU (other streams, other host threads)
+ * race and give undefined results; calls on one stream are ordered and safe.
+ */
+#define SPDEC_NOALLOC_SCRATCH_BYTES (2u << 20)
+spdec_status spdec_acceptance_noalloc(const float* logits_a, const float* logits_b, int rows, int vocab,
+                                      int64_t row_stride, float temperature, float* alpha, void* stream);
+
+/*
  * spdec_acceptance_ex - spdec_acceptance with its form and wait made explicit
  * (for tests and diagnostics; same arguments, results and workspace otherwise).
  *

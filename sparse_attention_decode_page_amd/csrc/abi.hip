@@ -253,7 +253,9 @@ size_t spdec_acceptance_workspace_bytes(int rows, int vocab) {
   return spdec::acceptance_workspace_bytes(rows, vocab);
 }
 
-static spdec_status acceptance_args(const float* logits_a, const float* logits_b, int rows, int vocab,
+}  // extern "C"
+
+spdec_status spdec::acceptance_args(const float* logits_a, const float* logits_b, int rows, int vocab,
                                     int64_t row_stride, float temperature, float* alpha) {
   if (!logits_a || !logits_b || !alpha) return SPDEC_ERR_INVALID;
   if (rows < 1 || vocab < 1 || vocab > (1 << 28) || row_stride < vocab) return SPDEC_ERR_INVALID;
@@ -262,10 +264,12 @@ static spdec_status acceptance_args(const float* logits_a, const float* logits_b
   return SPDEC_OK;
 }
 
+extern "C" {
+
 spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab, int64_t row_stride,
                               float temperature, float* alpha, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  const spdec_status st = acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
+  const spdec_status st = spdec::acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
   if (st != SPDEC_OK) return st;
   if (workspace == nullptr || workspace_bytes < spdec::acceptance_workspace_bytes(rows, vocab))
     return SPDEC_ERR_WORKSPACE;
@@ -277,7 +281,7 @@ spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, i
                                  int64_t row_stride, float temperature, float* alpha, void* workspace,
                                  size_t workspace_bytes, int force_path, int spin_limit, int32_t* fallbacks,
                                  int32_t* path_taken, void* stream) {
-  const spdec_status st = acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
+  const spdec_status st = spdec::acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
   if (st != SPDEC_OK) return st;
   if (force_path != -1 && force_path != 1 && force_path != 2) return SPDEC_ERR_INVALID;
   if (spin_limit < -1) return SPDEC_ERR_INVALID;

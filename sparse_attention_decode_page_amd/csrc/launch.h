@@ -110,5 +110,8 @@ struct AcceptanceDiag {
 };
 hipError_t launch_acceptance(const float* a, const float* b, int rows, int vocab, int64_t stride, float temperature,
                              float* alpha, void* ws, hipStream_t s, const AcceptanceDiag* diag);
+// Host-side argument checks shared by the acceptance entry points.
+spdec_status acceptance_args(const float* logits_a, const float* logits_b, int rows, int vocab, int64_t row_stride,
+                             float temperature, float* alpha);
 
 }  // namespace spdec

@@ -27,7 +27,7 @@ ABI_FUNCTIONS = (
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
-    "spdec_acceptance", "spdec_acceptance_ex", "spdec_tail_stats", "spdec_budget_update", "spdec_check_inputs",
+    "spdec_acceptance", "spdec_acceptance_ex", "spdec_acceptance_noalloc", "spdec_tail_stats", "spdec_budget_update", "spdec_check_inputs",
 )
 SPDEC_CHECK_WORDS, SPDEC_CHECK_FIRST = 8, 5
 
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "spdec_spec_accept": (I, [P, P, I, I, I, I64, P, P, P, F, P, P, P, SZ, P]),
         "spdec_acceptance_workspace_bytes": (SZ, [I, I]),
         "spdec_acceptance": (I, [P, P, I, I, I64, F, P, P, SZ, P]),
+        "spdec_acceptance_noalloc": (I, [P, P, I, I, I64, F, P, P]),
         "spdec_acceptance_ex": (I, [P, P, I, I, I64, F, P, P, SZ, I, I, P, ctypes.POINTER(ctypes.c_int32), P]),
         "spdec_tail_stats": (I, [P, I, P, P]),
         "spdec_budget_update": (I, [P, P, P, I, ctypes.POINTER(BudgetParams), P, P]),
@@ -409,6 +410,25 @@ def acceptance(logits_a, logits_b, temperature: float = 1.0, alpha=None, workspa
     _check(lib().spdec_acceptance(_ptr(logits_a), _ptr(logits_b), rows, vocab, logits_a.stride(0),
                                   float(temperature), _ptr(alpha), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream()), "spdec_acceptance")
+    return alpha
+
+
+def acceptance_noalloc(logits_a, logits_b, temperature: float = 1.0, alpha=None):
+    """spdec_acceptance on the library's own per-GPU scratch array (no workspace argument, nothing allocated by
+    the call; `alpha` may be passed in to keep the call allocation-free on the Python side too)."""
+    for t, n in ((logits_a, "logits_a"), (logits_b, "logits_b")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or t.dim() != 2:
+            raise ValueError(f"{n} must be a 2-D float32 GPU tensor")
+        if t.stride(1) != 1:
+            raise ValueError(f"{n} rows must be contiguous")
+    if logits_a.shape != logits_b.shape or logits_a.stride(0) != logits_b.stride(0):
+        raise ValueError("logits_a and logits_b must share shape and row stride")
+    rows, vocab = logits_a.shape
+    if alpha is None:
+        alpha = torch.empty(rows, dtype=torch.float32, device=logits_a.device)
+    _need(alpha, "alpha", torch.float32, (rows,))
+    _check(lib().spdec_acceptance_noalloc(_ptr(logits_a), _ptr(logits_b), rows, vocab, logits_a.stride(0),
+                                          float(temperature), _ptr(alpha), _stream()), "spdec_acceptance_noalloc")
     return alpha
 
 

@@ -40,7 +40,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 23
+    assert len(names) == len(S.ABI_FUNCTIONS) == 24
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -128,6 +128,17 @@ def test_acceptance_checks(L):
     assert L.spdec_acceptance(None, FAKE, 64, 151936, 151936, 1.0, FAKE, FAKE, ws, None) == -1
     # the single-read form's sync region leads every workspace (zero between calls)
     assert L.spdec_acceptance_workspace_bytes(1, 1) >= 96 * 1024
+
+
+def test_acceptance_noalloc_checks(L):
+    na = L.spdec_acceptance_noalloc
+    assert na(FAKE, FAKE, 64, 151936, 151936, 0.0, FAKE, None) == -1      # T = 0
+    assert na(FAKE, FAKE, 64, 151936, 100, 1.0, FAKE, None) == -1         # stride < vocab
+    assert na(None, FAKE, 64, 151936, 151936, 1.0, FAKE, None) == -1
+    assert na(FAKE, FAKE, 0, 151936, 151936, 1.0, FAKE, None) == -1
+    # beyond the library's scratch array (2 MiB): refused before anything touches the runtime
+    assert L.spdec_acceptance_workspace_bytes(1333, 151936) > (2 << 20) >= L.spdec_acceptance_workspace_bytes(1332, 151936)
+    assert na(FAKE, FAKE, 1333, 151936, 151936, 1.0, FAKE, None) == -2
 
 
 def test_acceptance_ex_checks(L):
