@@ -15,7 +15,9 @@
 //     query rows are the B operand; the result leaves lane l holding query row
 //     l % 16 for tokens 4(l / 16) .. +3;
 //   * that is exactly the A-operand layout of v_mfma_f32_16x16x16_bf16, so
-//     P (rounded to bf16) feeds P.V directly. For the B operand each lane
+//     P feeds P.V directly, each fp32 weight as three bf16 terms (its whole
+//     significand, so the verified outputs match the single-query dense
+//     decode up to summation order). For the B operand each lane
 //     loads, for its own four tokens, the chunk of D/16 channels starting at
 //     (D/16)(l % 16): column n of block j then stands for channel
 //     (D/16) n + j, so V needs no transpose and no LDS.
@@ -304,16 +306,29 @@ void verify_stream_kernel(VerifyArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) o[st][jb][r] *= ar[r];
           }
-          vs16x4_t pa;
+          // Each fp32 weight enters P.V as three bf16 terms (hi + mid + lo,
+          // each the rounded remainder of the previous): all 24 bits of its
+          // significand, so the products match fp32 weights and the result
+          // matches the single-query dense decode up to summation order.
+          vs16x4_t p1, p2, p3;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t pb = bf16_bits_rne(fast_exp2(s[e] - m[st]));
-            lsum[st] += __uint_as_float(pb << 16);  // the normaliser sums the same rounded weights
-            pa[e] = (short)pb;
+            const float pe = fast_exp2(s[e] - m[st]);
+            lsum[st] += pe;
+            const uint32_t h1 = bf16_bits_rne(pe);
+            const float r1 = pe - __uint_as_float(h1 << 16);
+            const uint32_t h2 = bf16_bits_rne(r1);
+            const float r2 = r1 - __uint_as_float(h2 << 16);
+            p1[e] = (short)h1;
+            p2[e] = (short)h2;
+            p3[e] = (short)bf16_bits_rne(r2);
           }
 #pragma unroll
-          for (int jb = 0; jb < NB; ++jb)
-            o[st][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[jb], o[st][jb], 0, 0, 0);
+          for (int jb = 0; jb < NB; ++jb) {
+            o[st][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p1, vb[jb], o[st][jb], 0, 0, 0);
+            o[st][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p2, vb[jb], o[st][jb], 0, 0, 0);
+            o[st][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p3, vb[jb], o[st][jb], 0, 0, 0);
+          }
         }
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) kA[jj] = kB[jj];

@@ -21,6 +21,7 @@ import gpu_support as GS  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
+SAME = 1e-5  # against the per-sequence dense decode
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -45,7 +46,8 @@ def _check(wl, shared, N, units):
     torch.cuda.synchronize()
     out_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
     assert np.all(np.isfinite(out_h)) and np.all(np.isfinite(lse_h))
-    assert (out - od).abs().max().item() < TOL and (lse - ld).abs().max().item() < TOL
+    # the prefix pass feeds P.V each weight's whole significand: the per-sequence decode up to summation order
+    assert (out - od).abs().max().item() < SAME and (lse - ld).abs().max().item() < SAME
     G = spec.group
     scale = 1.0 / math.sqrt(spec.head_dim)
     worst = [0.0, 0.0]
@@ -145,7 +147,7 @@ def test_reused_workspace_after_members_lose_their_own_pages():
     assert torch.equal(o3, o4) and torch.equal(l3, l4)
     od, ld = spdec.dense_decode(dw.cache, dw.q)
     torch.cuda.synchronize()
-    assert (o1 - od).abs().max().item() < TOL and (l1 - ld).abs().max().item() < TOL
+    assert (o1 - od).abs().max().item() < SAME and (l1 - ld).abs().max().item() < SAME
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
