@@ -294,9 +294,11 @@ spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int nu
  *         the k + 1 verified positions), q_i = softmax(q_logits row (b, i) / T),
  *         i = 0..k-1 (the drafter's logits the drafts were sampled from);
  *   draft i is kept while u_accept[b][i] * q_i(x_i) < p_i(x_i), in order;
- *   at the first rejection j, next_token[b] is drawn from max(0, p_j - q_j),
- *   and when all k are kept from p_k. A draw with uniform u = u_sample[b]
- *   takes the first token whose running weight sum exceeds u times the total.
+ *   at the first rejection j, next_token[b] is drawn from max(0, p_j - q_j)
+ *   (from p_j itself when that residual has no weight at any token, i.e.
+ *   p_j = q_j up to rounding), and when all k are kept from p_k. A draw with
+ *   uniform u = u_sample[b] takes the first token whose running weight sum
+ *   exceeds u times the total.
  * num_accepted[b] = number of kept drafts. Everything in fp32 with fixed
  * reduction orders; decisions whose margin is within fp32 rounding may differ
  * from an exact computation.

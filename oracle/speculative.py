@@ -32,6 +32,10 @@ Readings where the pages are silent (listed in the design notes):
   (inverse CDF in token order).
 * Logits are divided by the temperature before the softmax (as for the
   acceptance measure).
+* A rejection whose residual max(0, p_j - q_j) has no mass (p_j <= q_j at
+  every token, i.e. p_j = q_j up to rounding, where the residual's
+  normalisation is undefined) draws from p_j itself, the distribution the
+  emitted token must follow.
 """
 from __future__ import annotations
 
@@ -94,5 +98,6 @@ def speculative_accept(p_logits: np.ndarray, q_logits: np.ndarray, draft, u_acce
         q = softmax_t(q_logits[i], temperature)
         x = int(draft[i])
         if not (u_accept[i] * q[x] < p[x]):
-            return i, inverse_cdf_draw(np.maximum(p - q, 0.0), u_sample)
+            residual = np.maximum(p - q, 0.0)
+            return i, inverse_cdf_draw(residual if residual.sum() > 0.0 else p, u_sample)
     return k, inverse_cdf_draw(softmax_t(p_logits[k], temperature), u_sample)

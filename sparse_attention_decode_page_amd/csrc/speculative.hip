@@ -175,10 +175,13 @@ __global__ __launch_bounds__(kWave) void spec_decide_kernel(SpecArgs a) {
   }
   __syncthreads();
   int kept = k;
-  for (int i = 0; i < k; ++i) {
-    const float px = exp2f(s_lp[i] * a.c - s_M[i]) / s_Z[i];
-    const float qx = exp2f(s_lq[i] * a.c - s_M[k + 1 + i]) / s_Z[k + 1 + i];
-    if (!(a.u_accept[b * k + i] * qx < px)) { kept = i; break; }
+  {  // products rounded on their own, as in the draw weights
+#pragma clang fp contract(off)
+    for (int i = 0; i < k; ++i) {
+      const float px = exp2f(s_lp[i] * a.c - s_M[i]) / s_Z[i];
+      const float qx = exp2f(s_lq[i] * a.c - s_M[k + 1 + i]) / s_Z[k + 1 + i];
+      if (!(a.u_accept[b * k + i] * qx < px)) { kept = i; break; }
+    }
   }
   if (lane == 0) {
     a.n_accepted[b] = kept;
@@ -192,11 +195,15 @@ __global__ __launch_bounds__(kWave) void spec_decide_kernel(SpecArgs a) {
 }
 
 // Draw weights of sequence b's draw row at the entries LOAD places in w:
-// p_v, or max(0, p_v - q_v) after a rejection (the same fp32 operations for
-// every entry in both layouts).
+// p_v, or max(0, p_v - q_v) after a rejection unless from_p (the same fp32
+// operations for every entry in both layouts).
+// Every product is rounded on its own (no fused multiply-add), so identical
+// verifier and drafter rows give a residual of exact zeros.
 template <typename Load>
-__device__ __forceinline__ void draw_weights(const SpecArgs& a, int b, int base, float* w, Load load) {
-  const int prow = a.draw_row[2 * b + 0], qrow = a.draw_row[2 * b + 1];
+__device__ __forceinline__ void draw_weights(const SpecArgs& a, int b, int base, float* w, Load load,
+                                             bool from_p = false) {
+#pragma clang fp contract(off)
+  const int prow = a.draw_row[2 * b + 0], qrow = from_p ? -1 : a.draw_row[2 * b + 1];
   const float Mp = a.draw[4 * b + 0], iZp = a.draw[4 * b + 1];
   float x[kSpecPer];
   load(row_ptr(a, prow), a.vocab, base, x);
@@ -239,68 +246,95 @@ __device__ __forceinline__ float block_incl_scan(float x, float* s_tot) {
   return base + x;
 }
 
+// The chunk holding the draw of target u * total over chunk sums cs (wave 0,
+// in chunk order): s_pick (or the last chunk with weight when rounding left
+// the target past the total, then s_before = -1; -1 when no chunk has weight),
+// s_before = the running sum before the picked chunk, s_target.
+__device__ __forceinline__ void pick_chunk(const float* cs, int nchunk, float u, int* s_pick, float* s_before,
+                                           float* s_target) {
+  const int lane = threadIdx.x % kWave;
+  float total = 0.f;  // chunk sums in order (lane-strided partial sums folded in lane order)
+  for (int j0 = 0; j0 < nchunk; j0 += kWave) {
+    float v = j0 + lane < nchunk ? cs[j0 + lane] : 0.f;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float y = __shfl_up(v, off);
+      if (lane >= off) v += y;
+    }
+    total += __shfl(v, kWave - 1);
+  }
+  const float target = u * total;
+  int pick = -1, last = -1;
+  float before = 0.f, run = 0.f;
+  for (int j0 = 0; j0 < nchunk && pick < 0; j0 += kWave) {
+    const float c = j0 + lane < nchunk ? cs[j0 + lane] : 0.f;
+    float incl = c;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const uint64_t hit = __ballot(c > 0.f && run + incl > target);
+    const uint64_t pos = __ballot(c > 0.f);
+    if (pos) last = j0 + 63 - __clzll((long long)pos);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      pick = j0 + l;
+      before = run + __shfl(incl - c, l);
+    }
+    run += __shfl(incl, kWave - 1);
+  }
+  if (lane == 0) {
+    *s_pick = pick >= 0 ? pick : last;
+    *s_before = pick >= 0 ? before : -1.f;  // -1: rounding left the target past the total
+    *s_target = target;
+  }
+}
+
 // One workgroup per sequence: the chunk holding the draw (wave 0 scans the
 // chunk sums in order), then the chunk's weights staged through LDS so each
 // thread owns 32 consecutive tokens, a block scan in token order, and the
-// first token whose running sum passes the target.
+// first token whose running sum passes the target. A rejection whose residual
+// has no weight anywhere (p_j <= q_j at every token, p_j = q_j up to
+// rounding) draws from p_j instead: its chunk sums are taken here first.
 __global__ __launch_bounds__(kSpecThreads) void spec_sample_kernel(SpecArgs a) {
   __shared__ float s_w[kSpecChunk];
   __shared__ float s_tot[kSpecThreads / kWave];
   __shared__ float s_before, s_target;
   __shared__ int s_pick, s_res[2];
   const int b = blockIdx.x;
-  const int lane = threadIdx.x % kWave;
-  const float* cs = a.csum + (int64_t)b * a.nchunk;
-  if (threadIdx.x < kWave) {
-    float total = 0.f;  // chunk sums in order (lane-strided partial sums folded in lane order)
-    for (int j0 = 0; j0 < a.nchunk; j0 += kWave) {
-      float v = j0 + lane < a.nchunk ? cs[j0 + lane] : 0.f;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float y = __shfl_up(v, off);
-        if (lane >= off) v += y;
-      }
-      total += __shfl(v, kWave - 1);
-    }
-    const float target = a.u_sample[b] * total;
-    int pick = -1, last = -1;
-    float before = 0.f, run = 0.f;
-    for (int j0 = 0; j0 < a.nchunk && pick < 0; j0 += kWave) {
-      const float c = j0 + lane < a.nchunk ? cs[j0 + lane] : 0.f;
-      float incl = c;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const uint64_t hit = __ballot(c > 0.f && run + incl > target);
-      const uint64_t pos = __ballot(c > 0.f);
-      if (pos) last = j0 + 63 - __clzll((long long)pos);
-      if (hit) {
-        const int l = __ffsll((long long)hit) - 1;
-        pick = j0 + l;
-        before = run + __shfl(incl - c, l);
-      }
-      run += __shfl(incl, kWave - 1);
-    }
-    if (lane == 0) {
-      s_pick = pick >= 0 ? pick : last;
-      s_before = pick >= 0 ? before : -1.f;  // -1: rounding left the target past the total
-      s_target = target;
-      s_res[0] = INT_MAX;
-      s_res[1] = -1;
-    }
+  float* cs = a.csum + (int64_t)b * a.nchunk;
+  if (threadIdx.x < kWave) pick_chunk(cs, a.nchunk, a.u_sample[b], &s_pick, &s_before, &s_target);
+  if (threadIdx.x == 0) {
+    s_res[0] = INT_MAX;
+    s_res[1] = -1;
   }
   __syncthreads();
+  const bool from_p = s_pick < 0 && a.draw_row[2 * b + 1] >= 0;
+  if (from_p) {
+    for (int ch = 0; ch < a.nchunk; ++ch) {
+      float w[kSpecPer];
+      draw_weights(a, b, ch * kSpecChunk, w, LoadSpread<false>(), true);
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < kSpecPer; ++e) t += w[e];
+      t = block_reduce_sum(t, s_tot);
+      if (threadIdx.x == 0) cs[ch] = t;
+    }
+    __threadfence_block();
+    __syncthreads();
+    if (threadIdx.x < kWave) pick_chunk(cs, a.nchunk, a.u_sample[b], &s_pick, &s_before, &s_target);
+    __syncthreads();
+  }
   const int pick = s_pick;
-  if (pick < 0) {  // no weight anywhere (cannot happen for finite logits)
-    if (threadIdx.x == 0) a.token[b] = 0;
+  if (pick < 0) {  // no weight anywhere (cannot happen for finite logits: p has positive mass)
+    if (threadIdx.x == 0) a.token[b] = -1;
     return;
   }
   const float before = s_before, target = s_target;
   {  // weights of the chunk, loaded coalesced, staged in token order
     float w[kSpecPer];
-    draw_weights(a, b, pick * kSpecChunk, w, LoadSpread<false>());
+    draw_weights(a, b, pick * kSpecChunk, w, LoadSpread<false>(), from_p);
 #pragma unroll
     for (int j = 0; j < kSpecPer / 4; ++j)
 #pragma unroll

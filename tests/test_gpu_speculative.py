@@ -49,6 +49,35 @@ def _inputs(B, k, V, seed, sigma=2.0, noise=0.5, same=False, temperature=1.0):
     return p, q, draft, ua, us
 
 
+def _draw_weights(p, q, n, k, temperature):
+    """The weights the emitted token is drawn from after n kept drafts (the oracle's reading: a residual with no
+    mass draws from p_n)."""
+    pp = O.softmax_t(p[n], temperature)
+    if n == k:
+        return pp
+    w = np.maximum(pp - O.softmax_t(q[n], temperature), 0.0)
+    return w if w.sum() > 0.0 else pp
+
+
+def _band_consistent(p, q, draft, ua, temperature, n_gpu, tok_gpu, i_band):
+    """The GPU took an accept decision inside the fp32/fp64 band at position i_band: every decision outside the
+    band must still match, and the token must carry weight in the row the GPU's count implies."""
+    k = draft.shape[0]
+    assert i_band <= n_gpu <= k, (i_band, n_gpu)
+    for j in range(k):
+        if j == i_band or j > n_gpu:
+            continue
+        pp = O.softmax_t(p[j], temperature)
+        qq = O.softmax_t(q[j], temperature)
+        x = int(draft[j])
+        lhs, rhs = float(ua[j]) * qq[x], pp[x]
+        if abs(lhs - rhs) <= ACCEPT_BAND * max(lhs, rhs, 1e-30):
+            continue
+        assert (lhs < rhs) == (j < n_gpu), (j, n_gpu, lhs, rhs)
+    w = _draw_weights(p, q, n_gpu, k, temperature)
+    assert 0 <= tok_gpu < w.shape[0] and w[tok_gpu] > 0.0, (n_gpu, tok_gpu)
+
+
 def _oracle_checked(p, q, draft, ua, us, temperature, n_gpu, tok_gpu):
     """Compare one sequence; returns 'exact', 'band' or raises."""
     k = draft.shape[0]
@@ -60,6 +89,7 @@ def _oracle_checked(p, q, draft, ua, us, temperature, n_gpu, tok_gpu):
         x = int(draft[i])
         lhs, rhs = float(ua[i]) * qq[x], pp[x]
         if abs(lhs - rhs) <= ACCEPT_BAND * max(lhs, rhs, 1e-30):
+            _band_consistent(p, q, draft, ua, temperature, n_gpu, tok_gpu, i)
             return "band"
         if not lhs < rhs:
             n_or = i
@@ -70,8 +100,7 @@ def _oracle_checked(p, q, draft, ua, us, temperature, n_gpu, tok_gpu):
     if tok_gpu == tok_ref:
         return "exact"
     # a different token is allowed only when the draw target sits on a boundary within the band
-    pp = O.softmax_t(p[n_ref], temperature)
-    w = np.maximum(pp - O.softmax_t(q[n_ref], temperature), 0.0) if n_ref < k else pp
+    w = _draw_weights(p, q, n_ref, k, temperature)
     cdf = np.cumsum(w)
     Z = cdf[-1]
     target = float(us) * Z
@@ -132,6 +161,24 @@ def test_identical_distributions_keep_every_draft():
     ua = np.minimum(ua, np.float32(0.999))
     n, tok = _check_all(p, q, draft, ua, us)
     assert np.all(n == 6)
+
+
+def test_rejection_with_no_residual_mass_draws_from_verifier():
+    """Identical verifier and drafter logits with an accept uniform of 1 (one past the documented range, which
+    forces a rejection at the first position): the residual has no mass anywhere, and the token is drawn from
+    the verifier's own distribution, as in the oracle."""
+    p, q, draft, ua, us = _inputs(12, 3, 20000, 8, same=True)
+    ua = np.ones_like(ua)
+    # every accept test sits exactly on its boundary (1 * q(x) == p(x)), so all are in the band by construction
+    n, tok = _check_all(p, q, draft, ua, us, max_band=12)
+    assert np.all(n == 0)
+    for b in range(12):
+        n_ref, tok_ref = O.speculative_accept(p[b], q[b], draft[b], ua[b].astype(np.float64), float(us[b]))
+        assert n_ref == 0
+        if int(tok[b]) != tok_ref:  # only a draw target on a token boundary (fp32 vs fp64) may differ
+            cdf = np.cumsum(O.softmax_t(p[b, 0], 1.0))
+            target = float(us[b]) * cdf[-1]
+            assert abs(target - cdf[min(int(tok[b]), tok_ref)]) <= DRAW_BAND * cdf[-1], (b, int(tok[b]), tok_ref)
 
 
 def test_temperature_and_padded_unaligned_rows():

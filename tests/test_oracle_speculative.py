@@ -157,6 +157,21 @@ def test_rejection_draws_from_positive_residual_only():
         assert m == 0 and tok != 0
 
 
+def test_rejection_with_no_residual_mass_draws_from_verifier():
+    # identical distributions and an accept uniform of 1 (one past the documented range, which forces the
+    # rejection): the residual max(0, p - q) is 0 everywhere, so the token is drawn from p itself, exactly as an
+    # inverse-CDF draw over p (searchsorted on its cumulative sums) gives it
+    r = _rng(11)
+    a = r.standard_normal((2, 12))
+    p = np.exp(a[0] - a[0].max())
+    p /= p.sum()
+    cdf = np.cumsum(p)
+    for us in _grid(61):
+        m, tok = O.speculative_accept(a, a[:1].copy(), [5], [1.0], us)
+        assert m == 0
+        assert tok == int(np.searchsorted(cdf, us * cdf[-1], side="right"))
+
+
 def test_temperature_divides_logits():
     r = _rng(3)
     a = r.standard_normal((2, 10))
