@@ -1,31 +1,30 @@
 #!/usr/bin/env python3
-"""Benchmark: one decode step of query-aware page-sparse attention with its dense
-verifier and the acceptance measure, on one GPU.
+"""Benchmark: query-aware page-sparse decode attention on one GPU.
 
-A step is one pass of the whole hot path over one batch: append_kv (new token
-into the paged cache + page key summaries) -> select_pages (Quest-style page
-bounds, top-B with sink/local pages) -> sparse_decode (split-KV attention over
-the kept pages) -> dense_decode (the same attention over every page) ->
-acceptance (sum_v min(p, q) over 64 x 151936 logit rows). Inputs are seeded
-synthetic data shaped like a Qwen3-8B decode layer with ragged 8K-32K contexts;
-everything is resident in HBM before timing starts.
+The timed step is the sparse path of one decode layer: select_pages (Quest-style
+page bounds over the page summaries, Top-B with sink and local pages) then
+sparse_decode (split-KV attention over the kept pages, LSE merge), on a batch
+shaped like a Qwen3-8B decode layer with ragged 8K-32K contexts (64 sequences,
+32 query / 8 KV heads, head dim 128, page size 16, budgets 1024-4096 tokens
+linear in length). Inputs are seeded synthetic data, resident in HBM before
+timing starts.
 
-Prints ONE JSON line. `value` is decode tokens/s of the full step (batch / step
-time) over K back-to-back steps timed with one pair of HIP events. Per-row
-times come from K further steps with HIP events recorded between the rows on
-the stream the kernels run on; `roofline` is for the dominant kernel (dense
-decode, its call run K times back to back under one event pair). `sparse`
-reports the sparse path (select + sparse decode, each of K runs after a 1 GiB
-scrub read, the scrubs' own time subtracted) against HBM peak; `graph` times
-the step captured once in a HIP graph and replayed; `verify` times the dense
-verification of a 6-token draft (7 positions) and exact speculative sampling
-on the same cache; `shared_prefix` times the dense decode and the page
-selection of a grouped batch (8 prompts x 8 samples) per sequence and with
-shared prompt pages read once; `top_p` times score-mass page selection
-beside the Top-B one; `budget_control` runs the sparsity-schedule
-controller in a closed loop on the device (budgets, sparse path, a seeded
-random LM head, acceptance, tail statistics); `cpu_baseline` times the CPU
-oracle on a bounded sample of the same step.
+Prints ONE JSON line. `value` is decode tokens/s of the sparse path: batch /
+the path's time, each of K runs after a 1 GiB scrub read (so neither L2 nor
+the last-level cache holds the previous run's pages) with the K scrubs' own
+time subtracted, the median of three interleaved regions. `sparse` gives its
+effective KV GB/s (selected K/V plus every page summary, valid tokens only)
+and fraction of 8 TB/s, and its two calls apart; `roofline` is for the
+dominant kernel, the sparse_decode call. `full_step` times the whole hot path
+(append_kv, select_pages, sparse_decode, dense_decode, acceptance over 64 x
+151936 logit rows) back to back, with a per-row breakdown and HIP-graph
+replay. `dense` and `acceptance` time those calls alone; `qwen3_1_7b`,
+`long_context` (4 sequences of 131072 tokens at page sizes 8/16/32/64) and
+`acceptance_pass` (64 sequences of 32768 tokens, with the acceptance of 64
+logit-row pairs, its mean and lower 5th percentile) repeat the measurement on
+the other decode-layer shapes; `verify`, `shared_prefix`, `top_p` and
+`budget_control` time the next rows; `cpu_baseline` times the CPU oracle's
+sparse path on the same workload.
 """
 from __future__ import annotations
 
@@ -43,6 +42,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "sparse decode attn tokens/s + effective KV GB/s (% HBM peak), 1 MI355X"
+HOST_CPU_SHARE = 16  # host cores per GPU on the measuring machine: worker pools stay within them
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "qwen3-8b-ragged"
 
@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--no-top-p", action="store_true", help="skip the score-mass (top-p) selection rows")
     ap.add_argument("--no-second-shape", action="store_true",
                     help="skip the Qwen3-1.7B-shaped decode layer (sparse path and dense decode)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 131072-token page-size sweep (4 sequences, page sizes 8/16/32/64)")
+    ap.add_argument("--no-acceptance-pass", action="store_true",
+                    help="skip the 32768-token batch with its acceptance over 64 x 151936 logit pairs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -151,8 +155,9 @@ def cpu_baseline(wl, steps_tokens, seconds: float):
 
 
 def _oracle_sequence(O, wl, kn, vn, b):
-    """The oracle's step for sequence b (all KV heads); returns the timed seconds (the cache as it stands
-    before the step is gathered, decoded and summarised untimed)."""
+    """The oracle's step for sequence b (all KV heads); returns the timed seconds of the whole step and of its
+    sparse path (page scores, selection, sparse attention), the cache as it stands before the step gathered,
+    decoded and summarised untimed."""
     spec = wl.spec
     ps, G, D = spec.page_size, spec.group, spec.head_dim
     scale = 1.0 / math.sqrt(D)
@@ -163,6 +168,7 @@ def _oracle_sequence(O, wl, kn, vn, b):
         V = O.to_f64(O.gather_tokens(wl.v_pool, wl.page_table[b], L, g, ps), spec.dtype)
         kmin, kmax = O.page_minmax(K, ps)
         state.append((K, V, kmin, kmax))
+    t_sparse = 0.0
     t0 = time.perf_counter()
     for g, (K, V, kmin, kmax) in enumerate(state):
         k_new = O.to_f64(kn[b, g], spec.dtype)
@@ -176,26 +182,31 @@ def _oracle_sequence(O, wl, kn, vn, b):
             kmax = np.concatenate([kmax, k_new[None]])
         kmin[p], kmax[p] = O.append_minmax(kmin[p], kmax[p], k_new, slot)
         qg = O.to_f64(wl.q[b, g * G:(g + 1) * G], spec.dtype)
+        ts = time.perf_counter()
         pages = O.select_pages(O.page_scores(qg, kmin, kmax), int(wl.budget_pages[b]))
         O.decode_unit(qg, K, V, pages, ps, scale)
+        t_sparse += time.perf_counter() - ts
         O.dense_decode_unit(qg, K, V, ps, scale)
     O.acceptance(wl.logits_a[b], wl.logits_b[b], spec.temperature)
-    return time.perf_counter() - t0
+    return time.perf_counter() - t0, t_sparse
 
 
 def _cpu_baseline(O, wl, steps_tokens, seconds):
     spec = wl.spec
     kn, vn = steps_tokens
-    t_total, n_seq = 0.0, 0
+    t_total, t_sparse, n_seq = 0.0, 0.0, 0
     for b in range(spec.batch):
-        t_total += _oracle_sequence(O, wl, kn, vn, b)
+        t, ts = _oracle_sequence(O, wl, kn, vn, b)
+        t_total += t
+        t_sparse += ts
         n_seq += 1
         if t_total >= seconds:
             break
-    return {"value": n_seq / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"full step (append, select, sparse, dense, acceptance) for {n_seq} of {spec.batch} "
-                      f"sequences x {spec.num_kv_heads} KV heads, fp64 NumPy, 1 thread; "
-                      f"{t_total:.1f} s of CPU time"}
+    return {"value": n_seq / t_sparse, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"sparse path (page scores, Top-B selection, sparse attention) of {n_seq} of {spec.batch} "
+                      f"sequences x {spec.num_kv_heads} KV heads, fp64 NumPy, 1 thread, timed inside the "
+                      f"oracle's full step (append, select, sparse, dense, acceptance: {t_total:.1f} s of CPU time)",
+            "full_step_tokens_per_s": n_seq / t_total}
 
 
 _POOL_STATE = {}
@@ -206,7 +217,8 @@ def _pool_worker(seqs):
     from threadpoolctl import threadpool_limits
     st = _POOL_STATE
     with threadpool_limits(limits=1):
-        return sum(_oracle_sequence(O, st["wl"], st["kn"], st["vn"], b) for b in seqs)
+        ts = [_oracle_sequence(O, st["wl"], st["kn"], st["vn"], b) for b in seqs]
+    return sum(t for t, _ in ts), sum(t for _, t in ts)
 
 
 def cpu_baseline_pool(wl, steps_tokens):
@@ -214,23 +226,28 @@ def cpu_baseline_pool(wl, steps_tokens):
     thread each), sequences split into contiguous groups; throughput = sequences / the slowest worker's
     timed seconds. Runs before the GPU is touched, so the workers are plain forks of a CPU-only process."""
     import multiprocessing as mp
-    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    affinity = len(os.sched_getaffinity(0))
+    n = max(1, min(affinity, HOST_CPU_SHARE))
     spec = wl.spec
     _POOL_STATE.update(wl=wl, kn=steps_tokens[0], vn=steps_tokens[1])
     groups = [list(g) for g in np.array_split(np.arange(spec.batch), n) if len(g)]
     with mp.get_context("fork").Pool(len(groups)) as pool:
-        times = pool.map(_pool_worker, groups)
+        res = pool.map(_pool_worker, groups)
     _POOL_STATE.clear()
+    times = [t for t, _ in res]
+    sparse_times = [t for _, t in res]
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": spec.batch / max(times), "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
-            "cpu_model": model,
-            "sample": f"full step for all {spec.batch} sequences in {len(groups)} forked workers (one BLAS thread "
-                      f"each); slowest worker {max(times):.2f} s, sum {sum(times):.1f} s of CPU time"}
+    return {"value": spec.batch / max(sparse_times), "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
+            "affinity_cores": affinity, "cpu_model": model,
+            "sample": f"sparse path (page scores, Top-B selection, sparse attention) of all {spec.batch} sequences "
+                      f"in {len(groups)} forked workers (one BLAS thread each; the host's share is "
+                      f"{HOST_CPU_SHARE} cores per GPU); slowest worker {max(sparse_times):.2f} s",
+            "full_step_tokens_per_s": spec.batch / max(times)}
 
 
 def env_info(torch):
@@ -302,14 +319,52 @@ def speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens):
     }
 
 
-def other_shape_rows(args, dev, timed_loop, name="qwen3-1.7b-L16k"):
-    """The sparse path and the dense decode on the second decode-layer shape (Qwen3-1.7B: 32 sequences of 16384
-    tokens, 16 query / 8 KV heads, 2048-token budget), timed like the main line: the sparse calls after a 1 GiB
-    scrub read, the dense call back to back."""
+def make_timers(dev, K):
+    """timed_loop(body): mean seconds per call of K calls back to back under one event pair (on torch's current
+    stream, the stream every spdec call is enqueued on). scrubbed(body): seconds per call when each call follows
+    a 1 GiB scrub read (so neither L2 nor the 256 MB last-level cache holds what the previous call read),
+    K x (scrub, call) minus K x scrub, the two loops interleaved three times and the median taken."""
+    import torch
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    scrub_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def scrub_read():
+        # a read, not a write: written lines would be written back while the timed call runs
+        torch.sum(scrub, dim=0, out=scrub_out)
+
+    def timed_loop(body):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for i in range(K):
+            body(i)
+        evs[1].record()
+        torch.cuda.synchronize()
+        return evs[0].elapsed_time(evs[1]) * 1e-3 / K
+
+    def scrubbed(body, reps=3, runs=None):
+        for _ in range(2):
+            scrub_read()
+            body(0)
+        diffs = []
+        for _ in range(reps):
+            t0 = timed_loop(lambda i: scrub_read())
+            t1 = timed_loop(lambda i: (scrub_read(), body(i)))
+            diffs.append(t1 - t0)
+        if runs is not None:
+            runs.extend(diffs)
+        return float(np.median(diffs))
+
+    return timed_loop, scrubbed, (scrub, scrub_out)
+
+
+def _row(t, b):
+    return {"us": t * 1e6, "bytes": int(b), "GBps": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS}
+
+
+def upload_cache(wl, dev):
     import torch
     from sparse_attention_decode_page_amd import spdec
-    from sparse_attention_decode_page_amd import synth as S
-    wl = S.make_workload(name, seed=args.seed)
     spec = wl.spec
 
     def up(x):
@@ -319,7 +374,20 @@ def other_shape_rows(args, dev, timed_loop, name="qwen3-1.7b-L16k"):
     cache = spdec.PagedCache(up(wl.k_pool), up(wl.v_pool), kmm, torch.from_numpy(wl.page_table).to(dev),
                              torch.from_numpy(wl.lens.astype(np.int32)).to(dev), spec.num_q_heads)
     spdec.build_meta(cache)
-    q = up(wl.q)
+    return cache, up(wl.q)
+
+
+def layer_rows(args, dev, timers, name, acceptance=False):
+    """One decode-layer workload: the sparse path and its two calls (each call after a scrub read), the dense
+    decode back to back, tokens/s, algorithmic GB/s and the fraction of 8 TB/s; with acceptance, the acceptance
+    of the workload's logit rows (after a scrub read) and their mean and lower 5th percentile on the device."""
+    import torch
+    from sparse_attention_decode_page_amd import spdec
+    from sparse_attention_decode_page_amd import synth as S
+    timed_loop, scrubbed, _ = timers
+    wl = S.make_workload(name, seed=args.seed)
+    spec = wl.spec
+    cache, q = upload_cache(wl, dev)
     budget = torch.from_numpy(wl.budget_pages.astype(np.int32)).to(dev)
     cap = int(max(2, wl.budget_pages.max()))
     sel_idx = torch.zeros((spec.batch, spec.num_kv_heads, cap), dtype=torch.int32, device=dev)
@@ -329,49 +397,62 @@ def other_shape_rows(args, dev, timed_loop, name="qwen3-1.7b-L16k"):
     ws_de = torch.zeros(spdec.decode_workspace_bytes(cache, 0), dtype=torch.uint8, device=dev)
     o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
-    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    scrub_out = torch.empty((), dtype=torch.float32, device=dev)
 
-    def scrub_read():
-        torch.sum(scrub, dim=0, out=scrub_out)
-
-    def sel():
+    def sel(i=0):
         spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
 
-    def dec():
+    def dec(i=0):
         spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o, lse=lse, workspace=ws_sp)
 
-    def dense():
+    def dense(i=0):
         spdec.dense_decode(cache, q, out=o, lse=lse, workspace=ws_de)
 
     for _ in range(3):
-        scrub_read()
         sel()
         dec()
         dense()
-    t_scrub = timed_loop(lambda i: scrub_read())
-    t_path = timed_loop(lambda i: (scrub_read(), sel(), dec())) - t_scrub
-    t_sel = timed_loop(lambda i: (scrub_read(), sel())) - t_scrub
-    t_dec = timed_loop(lambda i: (scrub_read(), dec())) - t_scrub
-    t_dense = timed_loop(lambda i: dense())
+    t_path = scrubbed(lambda i: (sel(), dec()))
+    t_sel = scrubbed(sel)
+    t_dec = scrubbed(dec)
+    t_dense = timed_loop(dense)
     byt = algorithmic_bytes(spec, wl.lens, wl.budget_pages, cap, 0, 0)
     b_path = byt["select_pages"] + byt["sparse_decode"]
-    del cache, kmm, q, ws_sel, ws_sp, ws_de, scrub, scrub_out
-    torch.cuda.empty_cache()
-
-    def row(t, b):
-        return {"us": t * 1e6, "bytes": int(b), "GBps": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS}
-
-    return {
+    res = {
         "workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads, "kv_heads": spec.num_kv_heads,
         "head_dim": spec.head_dim, "page_size": spec.page_size, "context": describe_lens(spec),
         "budget": describe_budget(spec),
-        "sparse_path": dict(row(t_path, b_path), tokens_per_s=spec.batch / t_path),
-        "select_pages": row(t_sel, byt["select_pages"]),
-        "sparse_decode": row(t_dec, byt["sparse_decode"]),
-        "dense_decode": dict(row(t_dense, byt["dense_decode"]), tokens_per_s=spec.batch / t_dense),
-        "timing": "sparse calls: K x (1 GiB scrub read, call) minus K x scrub; dense: K calls back to back",
+        "sparse_path": dict(_row(t_path, b_path), tokens_per_s=spec.batch / t_path),
+        "select_pages": _row(t_sel, byt["select_pages"]),
+        "sparse_decode": _row(t_dec, byt["sparse_decode"]),
+        "dense_decode": dict(_row(t_dense, byt["dense_decode"]), tokens_per_s=spec.batch / t_dense),
+        "sparse_over_dense": t_dense / t_path,
+        "timing": "sparse calls: median of 3 x (K x (1 GiB scrub read, call) minus K x scrub); dense: K calls back "
+                  "to back",
     }
+    if acceptance:
+        la = torch.from_numpy(wl.logits_a).to(dev)
+        lb = torch.from_numpy(wl.logits_b).to(dev)
+        R, V = wl.logits_a.shape
+        ws_a = torch.zeros(spdec.acceptance_workspace_bytes(R, V), dtype=torch.uint8, device=dev)
+        alpha = torch.empty(R, dtype=torch.float32, device=dev)
+        tail = torch.empty(2, dtype=torch.float32, device=dev)
+
+        def acc(i=0, path=-1):
+            spdec.acceptance_ex(la, lb, spec.temperature, alpha=alpha, workspace=ws_a, force_path=path)
+
+        t_acc = scrubbed(acc)
+        t_acc2 = scrubbed(lambda i: acc(i, 2))
+        acc()
+        spdec.tail_stats(alpha, out=tail)
+        torch.cuda.synchronize()
+        res["acceptance"] = dict(_row(t_acc, 2 * R * V * 4), rows=R, vocab=V, temperature=spec.temperature,
+                                 mean=float(tail[0]), p5=float(tail[1]),
+                                 two_pass_us=t_acc2 * 1e6,
+                                 timing="median of 3 x (K x (1 GiB scrub read, call) minus K x scrub)")
+        del la, lb, ws_a
+    del cache, q, ws_sel, ws_sp, ws_de, sel_idx, sel_cnt
+    torch.cuda.empty_cache()
+    return res
 
 
 def shared_prefix_rows(args, dev, timed_loop):
@@ -582,7 +663,7 @@ def main():
     spec = wl.spec
     pool_baseline = None
     if not args.no_cpu_baseline:
-        # all host cores, before any GPU state exists in this process (the workers are forks)
+        # all of the host's share of cores, before any GPU state exists in this process (the workers are forks)
         t_first = S.append_tokens(wl, 0)
         pool_baseline = cpu_baseline_pool(wl, (t_first[0], t_first[1]))
         t_setup = time.perf_counter()
@@ -614,7 +695,7 @@ def main():
     la = torch.from_numpy(wl.logits_a).to(dev)
     lb = torch.from_numpy(wl.logits_b).to(dev)
     R, V = wl.logits_a.shape
-    # preallocated outputs and workspaces: the timed loop allocates nothing
+    # preallocated outputs and workspaces: the timed loops allocate nothing
     sel_idx = torch.zeros((spec.batch, spec.num_kv_heads, cap), dtype=torch.int32, device=dev)
     sel_cnt = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
     ws_sel = torch.zeros(spdec.select_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
@@ -629,6 +710,22 @@ def main():
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 
+    def sel(i=0):
+        spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
+
+    def dec(i=0):
+        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
+
+    def sparse_path(i=0):
+        sel()
+        dec()
+
+    def dense(i=0):
+        spdec.dense_decode(cache, q, out=o_d, lse=l_d, workspace=ws_de)
+
+    def acc(i=0, path=-1):
+        spdec.acceptance_ex(la, lb, spec.temperature, alpha=alpha, workspace=ws_acc, force_path=path)
+
     rows = ["append_kv", "select_pages", "sparse_decode", "dense_decode", "acceptance"]
     row_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)] for _ in range(K_steps)]
 
@@ -637,11 +734,11 @@ def main():
         rec(0)
         spdec.append_kv(cache, k_new[i], v_new[i])
         rec(1)
-        spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
+        sel()
         rec(2)
-        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
+        dec()
         rec(3)
-        spdec.dense_decode(cache, q, out=o_d, lse=l_d, workspace=ws_de)
+        dense()
         rec(4)
         spdec.acceptance(la, lb, spec.temperature, alpha=alpha, workspace=ws_acc)
         rec(5)
@@ -649,153 +746,107 @@ def main():
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
-    lens_before = wl.lens.astype(np.int64) + W
-    # Timed region: K whole steps back to back, one event pair around them. An
-    # event recorded between two launches holds the next one back by a few
-    # microseconds, so none is recorded inside the steps here.
-    t_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    appended = W
+    timers = make_timers(dev, K_steps)
+    timed_loop, scrubbed, _ = timers
+
+    # --- value: the sparse path (select_pages + sparse_decode) on the cache as it stands, each of K runs after a
+    # 1 GiB scrub read, the K scrubs' own time subtracted; three interleaved regions, median.
+    lens_sparse = wl.lens.astype(np.int64) + appended
     t0 = time.perf_counter()
-    t_ev[0].record()
+    value_runs = []
+    sp_t = scrubbed(sparse_path, reps=3, runs=value_runs)
+    wall = time.perf_counter() - t0
+    sel_t = scrubbed(sel)
+    dec_t = scrubbed(dec)
+    sp_t_warm = timed_loop(sparse_path)
+    byt_sp = algorithmic_bytes(spec, lens_sparse, wl.budget_pages, cap, R, V)
+    sp_b = byt_sp["select_pages"] + byt_sp["sparse_decode"]
+    value = spec.batch / sp_t
+
+    # --- the whole hot path (all five rows) back to back, K steps under one event pair; then K steps with an
+    # event between rows (each row's time then includes the short hold-up after the event before it).
+    lens_full = wl.lens.astype(np.int64) + appended
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
     for i in range(K_steps):
         step(W + i)
-    t_ev[1].record()
+    ev[1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_total = t_ev[0].elapsed_time(t_ev[1]) * 1e-3
-    # Two more regions of K steps the same way (the first one above is `value`;
-    # the three together give a median of three runs). Their appends reuse the
-    # step tokens: only the timing matters here.
-    repeats = [spec.batch * K_steps / gpu_total]
-    for rep in range(2):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for i in range(K_steps):
-            step((W + i) % len(new_tokens))
-        ev[1].record()
-        torch.cuda.synchronize()
-        repeats.append(spec.batch * K_steps / (ev[0].elapsed_time(ev[1]) * 1e-3))
-    # Per-row breakdown: K more steps with an event between rows (each row's
-    # time then includes the short hold-up after the event before it).
+    full_t = ev[0].elapsed_time(ev[1]) * 1e-3 / K_steps
+    appended += K_steps
     for i in range(K_steps):
         step((W + K_steps + i) % len(new_tokens), row_ev[i])
     torch.cuda.synchronize()
+    appended += K_steps
     per_row = {r: [] for r in rows}
     for i in range(K_steps):
         for j, r in enumerate(rows):
             per_row[r].append(row_ev[i][j].elapsed_time(row_ev[i][j + 1]) * 1e-3)
-    step_s = [row_ev[i][0].elapsed_time(row_ev[i][len(rows)]) * 1e-3 for i in range(K_steps)]
-    # Sparse path alone: select_pages + sparse_decode K times on the cache as
-    # it stands after the steps above, each time right after a 1 GiB scrub
-    # read (so neither L2 nor the last-level cache holds the previous
-    # iteration's pages), one event pair around all K; the same K scrubs timed
-    # alone are subtracted. The scrub reads (a sum into a preallocated scalar)
-    # rather than writes: a written scrub leaves dirty lines whose write-back
-    # would be charged to the kernels that follow, which the real step never
-    # sees (its previous rows only read the cache).
-    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    scrub_out = torch.empty((), dtype=torch.float32, device=dev)
-
-    def timed_loop(body):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        evs[0].record()
-        for i in range(K_steps):
-            body(i)
-        evs[1].record()
-        torch.cuda.synchronize()
-        return evs[0].elapsed_time(evs[1]) * 1e-3 / K_steps
-
-    def sparse_path():
-        spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
-        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
-
-    def scrub_read():
-        torch.sum(scrub, dim=0, out=scrub_out)
-
-    for _ in range(2):  # untimed: the reduction's first call sets up its workspace
-        scrub_read()
-        sparse_path()
-    t_scrub = timed_loop(lambda i: scrub_read())
-    t_scrub_sparse = timed_loop(lambda i: (scrub_read(), sparse_path()))
-    sp_t = t_scrub_sparse - t_scrub
-    # The two calls of the path apart, each after its own scrub (selection: scoring + Top-B; sparse decode:
-    # split-KV attention over the kept pages + merge).
-    t_scrub_sel = timed_loop(lambda i: (scrub_read(), spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx,
-                                                                         sel_cnt=sel_cnt, workspace=ws_sel)))
-    t_scrub_dec = timed_loop(lambda i: (scrub_read(), spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s,
-                                                                          lse=l_s, workspace=ws_sp)))
-    sel_t, dec_t = t_scrub_sel - t_scrub, t_scrub_dec - t_scrub
-    sp_t_warm = timed_loop(lambda i: sparse_path())
-    del scrub, scrub_out
-    # Dense verifier alone, the same way: its average call duration is the
-    # roofline's denominator.
-    de_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    de_ev[0].record()
+    byt_full = {r: 0.0 for r in rows}
     for i in range(K_steps):
-        spdec.dense_decode(cache, q, out=o_d, lse=l_d, workspace=ws_de)
-    de_ev[1].record()
-    torch.cuda.synchronize()
-    de_t = de_ev[0].elapsed_time(de_ev[1]) * 1e-3 / K_steps
-    # The whole step captured once into a HIP graph and replayed K times (the
-    # decode path is replayed from graphs in the pages' rollout engine); each
-    # replay appends the same captured token.
+        b_i = algorithmic_bytes(spec, lens_full + i + 1, wl.budget_pages, cap, R, V)
+        for r in rows:
+            byt_full[r] += b_i[r] / K_steps
+    mean_t = {r: float(np.mean(per_row[r])) for r in rows}
+    rows_out = {r: {"us_mean": mean_t[r] * 1e6, "us_median": float(np.median(per_row[r])) * 1e6,
+                    "bytes": int(byt_full[r]), "GBps": byt_full[r] / mean_t[r] / 1e9,
+                    "frac_hbm": byt_full[r] / mean_t[r] / 1e9 / HBM_PEAK_GBPS} for r in rows}
+
+    # --- calls on the cache as it now stands: dense decode back to back, acceptance after a scrub read
+    lens_now = wl.lens.astype(np.int64) + appended
+    byt_now = algorithmic_bytes(spec, lens_now, wl.budget_pages, cap, R, V)
+    de_t = timed_loop(dense)
+    acc_t = scrubbed(acc)
+    acc2_t = scrubbed(lambda i: acc(i, 2))
+    acc_warm = timed_loop(acc)
+    # --- the whole step captured once into a HIP graph and replayed K times (each replay appends the same
+    # captured token)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step(0)
     for _ in range(W):
         graph.replay()
     gr_t = timed_loop(lambda i: graph.replay())
+    appended += W + K_steps
     del graph
-    # On-device tail statistics of the step's acceptance values (mean, lower 5th percentile).
+    # --- on-device tail statistics of the step's acceptance values
     tail_out = torch.empty(2, dtype=torch.float32, device=dev)
     for _ in range(3):
         spdec.tail_stats(alpha, out=tail_out)
     t_tail = timed_loop(lambda i: spdec.tail_stats(alpha, out=tail_out))
     tail = {"us": t_tail * 1e6, "rows": R, "mean": float(tail_out[0]), "p5": float(tail_out[1]),
             "timing": "K times back to back under one event pair"}
-    verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens_before + 5 * K_steps + W) \
+    verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, wl.lens.astype(np.int64) + appended) \
         if not args.no_verify else None
-    shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
-    shape2 = other_shape_rows(args, dev, timed_loop) if not args.no_second_shape else None
     topp = top_p_rows(spec, cache, q, budget, dev, timed_loop) if not args.no_top_p else None
     control = budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap,
                                   timed_loop) if not args.no_control else None
+    del cache, k_pool, v_pool, kminmax, k_new, v_new, ws_sp, ws_de, ws_sel
+    torch.cuda.empty_cache()
+    shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
+    shape2 = layer_rows(args, dev, timers, "qwen3-1.7b-L16k") if not args.no_second_shape else None
+    long_ctx = None
+    if not args.no_long:
+        long_ctx = {f"ps{ps}": layer_rows(args, dev, timers, f"long-131k-ps{ps}") for ps in (8, 16, 32, 64)}
+    acc_pass = layer_rows(args, dev, timers, "qwen3-8b-L32k-acceptance", acceptance=True) \
+        if not args.no_acceptance_pass else None
 
-    # algorithmic bytes averaged over the steps of each region (lengths grow by one per step)
-    def mean_bytes(first_step):
-        acc = {r: 0.0 for r in rows}
-        for i in range(K_steps):
-            b_i = algorithmic_bytes(spec, lens_before + first_step + i + 1, wl.budget_pages, cap, R, V)
-            for r in rows:
-                acc[r] += b_i[r] / K_steps
-        return acc
-
-    # appends so far: the value region (K), its two repeats (2K), then the row breakdown (K); the sparse and
-    # dense regions run on the cache after those 4K appends
-    byt = mean_bytes(3 * K_steps)
-    final_bytes = algorithmic_bytes(spec, lens_before + 4 * K_steps, wl.budget_pages, cap, R, V)
-    mean_t = {r: float(np.mean(per_row[r])) for r in rows}
-    med_t = {r: float(np.median(per_row[r])) for r in rows}
-    rows_out = {r: {"us_mean": mean_t[r] * 1e6, "us_median": med_t[r] * 1e6, "bytes": int(byt[r]),
-                    "GBps": byt[r] / mean_t[r] / 1e9, "frac_hbm": byt[r] / mean_t[r] / 1e9 / HBM_PEAK_GBPS}
-                for r in rows}
-    ms_per_step = gpu_total / K_steps * 1e3
-    value = spec.batch / (gpu_total / K_steps)
-    sp_b = final_bytes["select_pages"] + final_bytes["sparse_decode"]
-    sp_t_rows = mean_t["select_pages"] + mean_t["sparse_decode"]
-    dense_gbps = final_bytes["dense_decode"] / de_t / 1e9
-    sparse_gbps = sp_b / sp_t / 1e9
     # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
     traffic = counter_traffic() if spec.name == WORKLOAD else None
+    dec_kernels = ["decode_stream_kernel<128,4,true>", "stream_merge_kernel<128,true>"]
+    sel_kernels = ["score_stream_kernel<BF16,128,4>", "select_topk_reg_kernel<8,256>"]
     dense_kernels = ["decode_stream_kernel<128,4,false>", "stream_merge_kernel<128,false>"]
-    sparse_kernels = ["score_stream_kernel<BF16,128,4>", "select_topk_reg_kernel<8,256>",
-                      "decode_stream_kernel<128,4,true>", "stream_merge_kernel<128,true>"]
+    acc_kernels = ["acc_one_read_kernel<true>"]
 
     def traffic_of(names):
         if traffic is None or any(n not in traffic for n in names):
             return None
         return int(sum(traffic[n] for n in names))
 
+    dec_gbps = byt_sp["sparse_decode"] / dec_t / 1e9
+    sparse_gbps = sp_b / sp_t / 1e9
+    acc_bytes = 2 * R * V * 4
     result = {
         "metric": METRIC,
         "value": value,
@@ -803,7 +854,7 @@ def main():
         "n_gpus": 1,
         "steps": K_steps,
         "warmup": W,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": sp_t * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -811,39 +862,45 @@ def main():
         "data": f"synthetic (seeded draws of the {spec.name} workload; no weights or datasets)",
         "config": {"workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads,
                    "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
-                   "context": describe_lens(spec), "budget": describe_budget(spec),
-                   "acceptance_rows": R, "vocab": V, "accumulate": "fp32",
-                   "step": "append_kv + select_pages + sparse_decode + dense_decode + acceptance"},
-        "roofline": {"bound": "hbm", "achieved": dense_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dense_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(dense_kernels),
-                     "kernel": "dense_decode call: " + " + ".join(dense_kernels),
-                     "bytes_per_launch": int(final_bytes["dense_decode"]), "us_per_launch": de_t * 1e6,
-                     "timing": "dense_decode back to back, K times, one event pair"},
-        "sparse": {"tokens_per_s": spec.batch / sp_t, "us": sp_t * 1e6, "bytes": int(sp_b),
-                   "eff_GBps": sparse_gbps, "frac_hbm": sparse_gbps / HBM_PEAK_GBPS,
-                   "traffic": traffic_of(sparse_kernels), "kernels": " + ".join(sparse_kernels),
-                   "timing": "K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub, one event pair each",
-                   "us_no_scrub": sp_t_warm * 1e6, "us_with_row_events": sp_t_rows * 1e6,
-                   "select_pages": {"us": sel_t * 1e6, "bytes": int(final_bytes["select_pages"]),
-                                    "frac_hbm": final_bytes["select_pages"] / sel_t / 1e9 / HBM_PEAK_GBPS,
-                                    "traffic": traffic_of(sparse_kernels[:2])},
-                   "sparse_decode": {"us": dec_t * 1e6, "bytes": int(final_bytes["sparse_decode"]),
-                                     "frac_hbm": final_bytes["sparse_decode"] / dec_t / 1e9 / HBM_PEAK_GBPS,
-                                     "traffic": traffic_of(sparse_kernels[2:])}},
+                   "context": describe_lens(spec), "budget": describe_budget(spec), "accumulate": "fp32",
+                   "step": "select_pages + sparse_decode (the sparse path: page scores, Top-B, split-KV attention "
+                           "over the kept pages, LSE merge), each step after a 1 GiB scrub read",
+                   "tokens_per_step": spec.batch},
+        "roofline": {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(dec_kernels),
+                     "kernel": "sparse_decode call: " + " + ".join(dec_kernels),
+                     "bytes_per_launch": int(byt_sp["sparse_decode"]), "us_per_launch": dec_t * 1e6,
+                     "timing": "median of 3 x (K x (1 GiB scrub read, sparse_decode) minus K x scrub)"},
+        "sparse": {"tokens_per_s": value, "us": sp_t * 1e6, "bytes": int(sp_b), "eff_GBps": sparse_gbps,
+                   "frac_hbm": sparse_gbps / HBM_PEAK_GBPS,
+                   "traffic": traffic_of(sel_kernels + dec_kernels), "kernels": " + ".join(sel_kernels + dec_kernels),
+                   "timing": "median of 3 x (K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub)",
+                   "us_no_scrub": sp_t_warm * 1e6,
+                   "select_pages": dict(_row(sel_t, byt_sp["select_pages"]), traffic=traffic_of(sel_kernels)),
+                   "sparse_decode": dict(_row(dec_t, byt_sp["sparse_decode"]), traffic=traffic_of(dec_kernels))},
+        "value_runs": {"tokens_per_s": [spec.batch / t for t in value_runs], "median": value,
+                       "timing": "three interleaved regions of K (scrub, sparse path) and K scrubs"},
+        "dense": dict(_row(de_t, byt_now["dense_decode"]), tokens_per_s=spec.batch / de_t,
+                      traffic=traffic_of(dense_kernels), kernels=" + ".join(dense_kernels),
+                      timing="dense_decode K times back to back, one event pair"),
+        "acceptance": dict(_row(acc_t, acc_bytes), traffic=traffic_of(acc_kernels), rows=R, vocab=V,
+                           two_pass_us=acc2_t * 1e6, us_no_scrub=acc_warm * 1e6, kernels=" + ".join(acc_kernels),
+                           timing="median of 3 x (K x (1 GiB scrub read, acceptance) minus K x scrub)"),
+        "full_step": {"tokens_per_s": spec.batch / full_t, "ms_per_step": full_t * 1e3,
+                      "step": "append_kv + select_pages + sparse_decode + dense_decode + acceptance",
+                      "timing": "K steps back to back, one event pair", "rows": rows_out,
+                      "graph_ms_per_step": gr_t * 1e3,
+                      "graph_timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
         "tail_stats": tail,
         "verify": verify,
         "shared_prefix": shared,
         "qwen3_1_7b": shape2,
+        "long_context": long_ctx,
+        "acceptance_pass": acc_pass,
         "top_p": topp,
         "budget_control": control,
-        "graph": {"ms_per_step": gr_t * 1e3, "tokens_per_s": spec.batch / gr_t,
-                  "timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
-        "rows": rows_out,
-        "value_runs": {"tokens_per_s": repeats, "median": float(np.median(repeats)),
-                       "timing": "the value region and two more regions of K steps, one event pair each"},
         "env": env_info(torch),
-        "step_us_median": float(np.median(step_s)) * 1e6,
-        "wall_s_timed": wall,
+        "wall_s_value_region": wall,
         "setup_s": t_setup,
     }
     if args.copy_probe:
