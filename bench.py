@@ -23,7 +23,8 @@ replay. `dense` and `acceptance` time those calls alone; `qwen3_1_7b`,
 `acceptance_pass` (64 sequences of 32768 tokens, with the acceptance of 64
 logit-row pairs, its mean and lower 5th percentile) repeat the measurement on
 the other decode-layer shapes; `verify`, `shared_prefix`, `top_p` and
-`budget_control` time the next rows; `cpu_baseline` times the CPU oracle's
+`monitor` (streaming tail statistics over a 2M-token window) and `budget_control` (the
+controller in a closed loop fed by the monitor) time the next rows; `cpu_baseline` times the CPU oracle's
 sparse path on the same workload.
 """
 from __future__ import annotations
@@ -536,11 +537,12 @@ def shared_prefix_rows(args, dev, timed_loop):
 def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap, timed_loop):
     """Closed loop of the sparsity-schedule controller on the device: budgets -> selection -> sparse decode ->
     a seeded random LM head (the plant stand-in: no model weights) -> acceptance against the dense output's
-    logits -> tail statistics -> controller -> budgets, with no host round trip inside the loop."""
+    logits -> streaming tail monitor over the last steps' tokens -> controller -> budgets, with no host round
+    trip inside the loop."""
     import torch
     from sparse_attention_decode_page_amd import spdec
     B, H = spec.batch, spec.num_q_heads * spec.head_dim
-    vocab, sigma, steps = 151936, 3.0, 30
+    vocab, sigma, steps, window_steps = 151936, 3.0, 30, 4
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed + 17)
     w_lm = torch.randn((H, vocab), generator=gen, device=dev, dtype=torch.float32) * (sigma / H ** 0.5)
@@ -551,6 +553,7 @@ def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_
     l_s = torch.empty((B, spec.num_q_heads), dtype=torch.float32, device=dev)
     al = torch.empty(B, dtype=torch.float32, device=dev)
     ws_a = torch.zeros(spdec.acceptance_workspace_bytes(B, vocab), dtype=torch.uint8, device=dev)
+    mon = spdec.TailMonitor(window_steps * B)   # the tail over the last window_steps steps' tokens
     prm = spdec.BudgetParams(target=0.86, gain=6.0, scale_min=1.0 / 64, scale_max=4.0, base_tokens=1024.0,
                              tokens_per_token=0.1, page_size=spec.page_size, max_budget_pages=cap)
     scale = torch.full((1,), 1.0 / 16, dtype=torch.float32, device=dev)   # start aggressive
@@ -566,7 +569,8 @@ def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_
         spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
         torch.matmul(o_s.reshape(B, H), w_lm, out=logit_s)
         spdec.acceptance(logit_s, logit_d, 1.0, alpha=al, workspace=ws_a)
-        spdec.tail_stats(al, out=tails[k + 1])
+        mon.append(al)
+        mon.stats(out=tails[k + 1])
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
@@ -594,11 +598,41 @@ def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_
         "start_scale": 1.0 / 16, "steps": steps, "p5": [round(float(x), 4) for x in p5],
         "mean_budget_pages": [round(float(x), 1) for x in mb], "final_scale": float(scale.item()),
         "settled_step": settled, "final_p5": float(p5[-1]),
+        "monitor_window_tokens": window_steps * B,
         "control_step_us": t_loop * 1e6, "update_us": t_upd * 1e6,
         "timing": "control_step: the whole loop body (update, select, sparse decode, LM-head GEMM, acceptance, "
-                  "tail) averaged over the steps under one event pair; update: the controller call alone, "
-                  "K times back to back",
+                  "monitor append and statistics) averaged over the steps under one event pair; update: the "
+                  "controller call alone, K times back to back",
     }
+
+
+def monitor_rows(args, dev, timed_loop, batch=64, tokens=32768):
+    """The streaming tail monitor over a rollout's tokens: a window of batch x tokens per-token acceptance values
+    (2,097,152 for 64 sequences of 32768 tokens), filled with acceptance-like values; the append of one decode
+    step's batch and the statistics (mean and exact lower 5th percentile) of the full window."""
+    import torch
+    from sparse_attention_decode_page_amd import spdec
+    cap = batch * tokens
+    r = np.random.default_rng(args.seed + 23)
+    vals = np.clip(1.0 - np.abs(r.standard_normal(cap)) * 0.03 - (r.random(cap) < 0.05) * r.random(cap) * 0.5,
+                   0, 1).astype(np.float32)
+    mon = spdec.TailMonitor(cap, device=dev)
+    mon.append(torch.from_numpy(vals).to(dev))
+    step_vals = torch.from_numpy(vals[:batch].copy()).to(dev)
+    out = torch.empty(2, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        mon.stats(out=out)
+    t_stats = timed_loop(lambda i: mon.stats(out=out))
+    t_append = timed_loop(lambda i: mon.append(step_vals))
+    mon.stats(out=out)
+    torch.cuda.synchronize()
+    res = {"window": cap, "stats_us": t_stats * 1e6, "append_us": t_append * 1e6, "append_values": batch,
+           "stats_GBps": cap * 4 * 3 / t_stats / 1e9, "mean": float(out[0]), "p5": float(out[1]),
+           "timing": "each call K times back to back under one event pair (stats reads the window in three "
+                     "histogram passes and, when no tie covers the next rank, once more)"}
+    del mon, step_vals
+    torch.cuda.empty_cache()
+    return res
 
 
 def top_p_rows(spec, cache, q, budget, dev, timed_loop):
@@ -820,6 +854,7 @@ def main():
     verify = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, wl.lens.astype(np.int64) + appended) \
         if not args.no_verify else None
     topp = top_p_rows(spec, cache, q, budget, dev, timed_loop) if not args.no_top_p else None
+    monitor = monitor_rows(args, dev, timed_loop) if not args.no_control else None
     control = budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap,
                                   timed_loop) if not args.no_control else None
     del cache, k_pool, v_pool, kminmax, k_new, v_new, ws_sp, ws_de, ws_sel
@@ -892,6 +927,7 @@ def main():
                       "graph_ms_per_step": gr_t * 1e3,
                       "graph_timing": "the step captured once in a HIP graph, replayed K times, one event pair"},
         "tail_stats": tail,
+        "monitor": monitor,
         "verify": verify,
         "shared_prefix": shared,
         "qwen3_1_7b": shape2,

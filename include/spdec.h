@@ -397,6 +397,33 @@ spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, i
 spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream);
 
 /*
+ * spdec_monitor_* - streaming tail monitor of the per-token acceptance over a
+ * rollout's tokens (Sparrow project page, "Control Study 1": training stays
+ * stable while the lower 5th percentile of the per-token mismatch stays above
+ * a threshold, 0.86 in its takeaway), kept entirely on the device so a budget
+ * schedule reads it every step without a host round trip.
+ *
+ * monitor: device workspace of spdec_monitor_workspace_bytes(capacity) bytes
+ *   holding a ring of the `capacity` most recent values and a 64-bit count of
+ *   values appended; it must be zero-filled before its first use (a fresh
+ *   window) or reset with spdec_monitor_reset. 1 <= capacity <= 2^28 (the
+ *   query returns 0 outside). Calls on one monitor must be stream-ordered.
+ * spdec_monitor_reset: starts a new window (count = 0).
+ * spdec_monitor_append: appends alpha[0 .. n) (device fp32, n >= 0; of a batch
+ *   longer than capacity only its last capacity values are kept).
+ * spdec_monitor_stats: out[0] = mean and out[1] = lower 5th percentile (linear
+ *   interpolation between the order statistics at rank 0.05 * (m - 1), the
+ *   numpy default) of the m = min(count, capacity) values in the window,
+ *   exact up to one rounding of each to fp32 (the mean sums in fp64 in a fixed
+ *   order). out is the layout spdec_budget_update reads. An empty window
+ *   gives NaN for both (the controller then keeps its state).
+ */
+size_t spdec_monitor_workspace_bytes(int capacity);
+spdec_status spdec_monitor_reset(void* monitor, int capacity, void* stream);
+spdec_status spdec_monitor_append(void* monitor, int capacity, const float* alpha, int n, void* stream);
+spdec_status spdec_monitor_stats(void* monitor, int capacity, float* out, void* stream);
+
+/*
  * spdec_budget_update - sparsity-schedule controller: one correction of the
  * per-sequence budgets from the on-device tail statistic (Sparrow project
  * page, "Control Study 1": the budget grows with the generated length so the

@@ -46,7 +46,7 @@ __all__ = [
     "decode_bf16", "to_f64", "page_count", "gather_tokens", "page_minmax", "append_minmax",
     "page_scores", "select_pages", "attention", "tokens_of_pages", "decode_unit",
     "sparse_decode_unit", "dense_decode_unit", "softmax_t", "acceptance", "total_variation",
-    "tail_stats", "lse_merge",
+    "tail_stats", "monitor_window", "lse_merge",
 ]
 
 
@@ -231,6 +231,14 @@ def acceptance(a: np.ndarray, b: np.ndarray, temperature: float = 1.0) -> float:
 def total_variation(a: np.ndarray, b: np.ndarray, temperature: float = 1.0) -> float:
     """Total-variation distance 1/2 sum_v |p_v - q_v| of the two tempered softmaxes."""
     return 0.5 * float(np.abs(softmax_t(a, temperature) - softmax_t(b, temperature)).sum())
+
+
+def monitor_window(batches, capacity: int) -> np.ndarray:
+    """The values a rollout's tail monitor holds after appending `batches` (arrays of per-token acceptance, in
+    order) to a window of `capacity` values: the most recent min(total, capacity) of them (Sparrow project page,
+    "Control Study 1": the statistic is taken over the rollout's tokens; the window bounds its memory)."""
+    vals = np.concatenate([np.asarray(b, dtype=np.float64).ravel() for b in batches]) if batches else np.zeros(0)
+    return vals[max(0, vals.shape[0] - capacity):]
 
 
 def tail_stats(alphas) -> tuple:

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libspdec.so")
 SOURCES = ["abi.hip", "grid.hip", "meta.hip", "select.hip", "decode.hip", "verify.hip", "shared.hip", "speculative.hip",
-           "acceptance.hip", "control.hip", "check.hip", "noalloc.hip"]
+           "acceptance.hip", "control.hip", "check.hip", "noalloc.hip", "monitor.hip"]
 
 # Packed-FP32 VALU instructions are switched off for all device code.
 HIP_FLAGS = [

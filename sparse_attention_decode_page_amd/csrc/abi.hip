@@ -327,6 +327,30 @@ spdec_status spdec_check_inputs(const spdec_cache* cache, const void* q, const i
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t spdec_monitor_workspace_bytes(int capacity) {
+  if (capacity < 1 || capacity > spdec::kMonitorMaxCapacity) return 0;
+  return spdec::monitor_workspace_bytes(capacity);
+}
+
+spdec_status spdec_monitor_reset(void* monitor, int capacity, void* stream) {
+  if (!monitor) return SPDEC_ERR_INVALID;
+  if (capacity < 1 || capacity > spdec::kMonitorMaxCapacity) return SPDEC_ERR_INVALID;
+  return from_hip(spdec::launch_monitor_reset(monitor, capacity, static_cast<hipStream_t>(stream)));
+}
+
+spdec_status spdec_monitor_append(void* monitor, int capacity, const float* alpha, int n, void* stream) {
+  if (!monitor || (n > 0 && !alpha) || n < 0) return SPDEC_ERR_INVALID;
+  if (capacity < 1 || capacity > spdec::kMonitorMaxCapacity) return SPDEC_ERR_INVALID;
+  if (n == 0) return SPDEC_OK;
+  return from_hip(spdec::launch_monitor_append(monitor, capacity, alpha, n, static_cast<hipStream_t>(stream)));
+}
+
+spdec_status spdec_monitor_stats(void* monitor, int capacity, float* out, void* stream) {
+  if (!monitor || !out) return SPDEC_ERR_INVALID;
+  if (capacity < 1 || capacity > spdec::kMonitorMaxCapacity) return SPDEC_ERR_INVALID;
+  return from_hip(spdec::launch_monitor_stats(monitor, capacity, out, static_cast<hipStream_t>(stream)));
+}
+
 spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream) {
   if (!alpha || !out || rows < 1) return SPDEC_ERR_INVALID;
   if (rows > spdec::kTailMaxRows) return SPDEC_ERR_UNSUPPORTED;

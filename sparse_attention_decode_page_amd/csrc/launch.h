@@ -91,6 +91,12 @@ hipError_t launch_spec_accept(const float* p, const float* q, int batch, int k, 
                               int32_t* n_accepted, int32_t* token, void* ws, hipStream_t s);
 constexpr int kTailMaxRows = 8192;  // values the tail statistics sort in LDS
 hipError_t launch_tail_stats(const float* alpha, int n, float* out, hipStream_t s);
+// Streaming tail monitor (ring of per-token acceptance values; capacity <= kMonitorMaxCapacity).
+constexpr int kMonitorMaxCapacity = 1 << 28;
+size_t monitor_workspace_bytes(int capacity);
+hipError_t launch_monitor_reset(void* ws, int capacity, hipStream_t s);
+hipError_t launch_monitor_append(void* ws, int capacity, const float* alpha, int n, hipStream_t s);
+hipError_t launch_monitor_stats(void* ws, int capacity, float* out, hipStream_t s);
 hipError_t launch_budget_update(const float* tail, float* state, const int32_t* seq_lens, int batch,
                                 const spdec_budget_params& p, int32_t* budget, hipStream_t s);
 // Precondition counts of spdec_check_inputs into report[SPDEC_CHECK_WORDS].

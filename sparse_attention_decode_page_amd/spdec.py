@@ -27,7 +27,8 @@ ABI_FUNCTIONS = (
     "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
-    "spdec_acceptance", "spdec_acceptance_ex", "spdec_acceptance_noalloc", "spdec_tail_stats", "spdec_budget_update", "spdec_check_inputs",
+    "spdec_acceptance", "spdec_acceptance_ex", "spdec_acceptance_noalloc", "spdec_tail_stats",
+    "spdec_monitor_workspace_bytes", "spdec_monitor_reset", "spdec_monitor_append", "spdec_monitor_stats", "spdec_budget_update", "spdec_check_inputs",
 )
 SPDEC_CHECK_WORDS, SPDEC_CHECK_FIRST = 8, 5
 
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
         "spdec_acceptance_noalloc": (I, [P, P, I, I, I64, F, P, P]),
         "spdec_acceptance_ex": (I, [P, P, I, I, I64, F, P, P, SZ, I, I, P, ctypes.POINTER(ctypes.c_int32), P]),
         "spdec_tail_stats": (I, [P, I, P, P]),
+        "spdec_monitor_workspace_bytes": (SZ, [I]),
+        "spdec_monitor_reset": (I, [P, I, P]),
+        "spdec_monitor_append": (I, [P, I, P, I, P]),
+        "spdec_monitor_stats": (I, [P, I, P, P]),
         "spdec_budget_update": (I, [P, P, P, I, ctypes.POINTER(BudgetParams), P, P]),
         "spdec_check_inputs": (I, [D, P, P, P, I, I, P, P, P]),
     }
@@ -457,6 +462,38 @@ def acceptance_ex(logits_a, logits_b, temperature: float = 1.0, alpha=None, work
                                      int(force_path), int(spin_limit), _ptr(fallbacks), ctypes.byref(path),
                                      _stream()), "spdec_acceptance_ex")
     return alpha, int(path.value)
+
+
+class TailMonitor:
+    """Streaming tail monitor: a device ring of the `capacity` most recent per-token acceptance values, their
+    mean and lower 5th percentile taken on the device (spdec_monitor_*)."""
+
+    def __init__(self, capacity: int, device="cuda"):
+        self.capacity = int(capacity)
+        nbytes = int(lib().spdec_monitor_workspace_bytes(self.capacity))
+        if nbytes == 0:
+            raise ValueError("capacity must be in [1, 2^28]")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)   # zero-filled: an empty window
+
+    def reset(self):
+        _check(lib().spdec_monitor_reset(_ptr(self.ws), self.capacity, _stream()), "spdec_monitor_reset")
+
+    def append(self, alpha):
+        if not isinstance(alpha, torch.Tensor) or alpha.dim() != 1:
+            raise ValueError("alpha must be a 1-D tensor")
+        _need(alpha, "alpha", torch.float32, (alpha.shape[0],))
+        _check(lib().spdec_monitor_append(_ptr(self.ws), self.capacity, _ptr(alpha), int(alpha.shape[0]), _stream()),
+               "spdec_monitor_append")
+
+    def stats(self, out=None):
+        if out is None:
+            out = torch.empty(2, dtype=torch.float32, device=self.ws.device)
+        _need(out, "out", torch.float32, (2,))
+        _check(lib().spdec_monitor_stats(_ptr(self.ws), self.capacity, _ptr(out), _stream()), "spdec_monitor_stats")
+        return out
+
+    def count(self) -> int:
+        return int(self.ws[:8].view(torch.int64).item())
 
 
 def tail_stats(alpha, out=None):

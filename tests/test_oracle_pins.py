@@ -330,3 +330,17 @@ def test_tail_stats_matches_numpy(n):
     mean, p5 = O.tail_stats(x)
     assert abs(p5 - np.percentile(x, 5)) < 1e-15
     assert abs(mean - np.mean(x)) < 1e-15
+
+
+def test_monitor_window_hand_worked():
+    """A window of 5 after appending [0.9, 0.8] then [0.7, 0.95, 0.99, 0.5]: the last five values
+    0.8, 0.7, 0.95, 0.99, 0.5; sorted 0.5, 0.7, 0.8, 0.95, 0.99; rank 0.05 * 4 = 0.2 gives
+    0.5 + 0.2 * (0.7 - 0.5) = 0.54; mean 3.94 / 5 = 0.788."""
+    w = O.monitor_window([np.array([0.9, 0.8]), np.array([0.7, 0.95, 0.99, 0.5])], 5)
+    assert w.tolist() == [0.8, 0.7, 0.95, 0.99, 0.5]
+    mean, p5 = O.tail_stats(w)
+    assert abs(mean - 0.788) < 1e-15 and abs(p5 - 0.54) < 1e-15
+    # fewer values than the window holds: all of them; a batch longer than the window: its tail
+    assert O.monitor_window([np.array([0.3])], 5).tolist() == [0.3]
+    assert O.monitor_window([np.arange(10.0)], 3).tolist() == [7.0, 8.0, 9.0]
+    assert O.monitor_window([], 3).shape == (0,)
