@@ -355,6 +355,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(StreamArg
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(c.v_pool);
 
   while (pos < end) {
+    while (s_pre[u + 1] <= pos) ++u;  // units with no entry have no segment
     const int b = u / c.hkv, g = u % c.hkv;
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);
@@ -618,6 +619,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_stream_g8_kernel(Str
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(c.v_pool);
 
   while (pos < end) {
+    while (s_pre[u + 1] <= pos) ++u;  // units with no entry have no segment
     const int b = u / c.hkv, g = u % c.hkv;
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);

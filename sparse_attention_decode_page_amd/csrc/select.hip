@@ -147,6 +147,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
   const S* q = reinterpret_cast<const S*>(qv);
   const S* mm = reinterpret_cast<const S*>(c.kminmax);
   while (pos < end) {
+    while (s_pre[u + 1] <= pos) ++u;  // units with no entry have no segment
     const int b = u / c.hkv, g = u % c.hkv;
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(256) void score_grouped_kernel(CacheView c, const v
   const S* q = reinterpret_cast<const S*>(qv);
   const S* mm = reinterpret_cast<const S*>(c.kminmax);
   while (pos < end) {
+    while (s_pre[u + 1] <= pos) ++u;  // units with no entry have no segment
     int b0, g, members, first;
     if (u < units_sh) {
       b0 = (u / c.hkv) * N;

@@ -135,6 +135,8 @@ void verify_stream_kernel(VerifyArgs a) {
   uint16_t* qs = s_q[wave];
 
   while (pos < end) {
+    while (s_pre[u + 1] <= pos) ++u;  // units with no entry have no segment
+    while (s_pre[u + 1] <= pos) ++u;  // units with no entry have no segment
     const int b = PREFIX ? (u / c.hkv) * a.T : u / c.hkv;  // sequence whose page table the list follows
     const int g = u % c.hkv;
     const int ubase = s_pre[u];
