@@ -795,85 +795,119 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_stream_g8_kernel(Str
   }
 }
 
-// Merge of the stream partials of one (sequence, query head), chunks in order.
-// The first kMergePre chunks' partials (slots below jmax always lie inside the
-// workspace) are requested together with the chunk count, so a unit of up to
-// kMergePre chunks costs one round trip to memory; later chunks are read after.
-constexpr int kMergePre = 8;
+// Merge of the stream partials of one (sequence, query head):
+// o = sum_j w_j acc_j / sum_j w_j l_j with w_j = 2^(m_j - M), M = max_j m_j,
+// and lse = ln2 (M + log2 sum_j w_j l_j). The workgroup's threads split the
+// partials by channel group (four channels, one 16-byte load) and chunk
+// subset (chunks s, s + NS, ...), so all of a unit's chunks are requested at
+// once (up to kMergeBatch per thread, at clamped slots: slots below jmax lie
+// inside the workspace), together with the chunk count and the (m, l) pairs:
+// a unit of up to kMergeBatch * NS chunks costs one round trip to memory.
+// Weights go through LDS; subset sums are added in subset order, so the
+// result is fixed for a given chunking.
+// The launch takes the smallest form (64 threads x 4 loads, 128 x 8 or
+// 256 x 8) whose first batch covers the chunks a unit is expected to have
+// (waves / units + 2, at most jmax); units with more take further batches.
+constexpr int kMaxMergeChunks = 1024;  // stream_plan caps the chunks per unit here
 
-template <int D, bool SPARSE>
-__global__ __launch_bounds__(kWave) void stream_merge_kernel(StreamArgs a) {
-  constexpr int DPL = D / kWave;
+template <int D, int NT, int kMergeBatch, bool SPARSE>
+__global__ __launch_bounds__(NT) void stream_merge_kernel(StreamArgs a) {
+  constexpr int kMergeThreads = NT;
+  constexpr int CG = D / 4;               // channel groups
+  constexpr int NS = kMergeThreads / CG;  // chunk subsets
+  constexpr int NWV = kMergeThreads / kWave;
+  __shared__ float s_w[kMaxMergeChunks];
+  __shared__ float s_red[2][NWV];
+  __shared__ float4 s_o[NS][CG];
   const CacheView& c = a.c;
   const int bh = blockIdx.x;
   const int b = bh / c.hq, h = bh % c.hq;
   const int u = b * c.hkv + h / c.group;
   const int hh = h % c.group;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int cg = tid % CG, sub = tid / CG;
   auto ml_of = [&](int jj) { return a.part_ml + (((int64_t)u * a.jmax + jj) * c.group + hh) * 2; };
-  auto acc_of = [&](int jj) { return a.part_acc + (((int64_t)u * a.jmax + jj) * c.group + hh) * D + lane * DPL; };
-  // Lane jj's chunk (m, l) and the leading chunks' accumulators, at clamped slots.
-  const float* ml0 = ml_of(min(lane, a.jmax - 1));
+  auto acc_of = [&](int jj) {
+    return reinterpret_cast<const float4*>(a.part_acc + (((int64_t)u * a.jmax + jj) * c.group + hh) * D) + cg;
+  };
+  const float* ml0 = ml_of(min(tid, a.jmax - 1));
   const float m0 = ml0[0], l0 = ml0[1];
-  float pre[kMergePre][DPL];
+  float4 pre[kMergeBatch];
 #pragma unroll
-  for (int i = 0; i < kMergePre; ++i) {
-    const float* src = acc_of(min(i, a.jmax - 1));
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) pre[i][e] = src[e];
+  for (int q = 0; q < kMergeBatch; ++q) {
+    pre[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q * NS < a.jmax) pre[q] = *acc_of(min(sub + q * NS, a.jmax - 1));
   }
   const int n = unit_entries<SPARSE>(a, u);
   const int J = n > 0 ? min(max(a.count[u], 0), a.jmax) : 0;
-  float M = lane < J ? m0 : kNegBig;
-  for (int jj = lane + kWave; jj < J; jj += kWave) M = fmaxf(M, ml_of(jj)[0]);
+  float M = tid < J ? m0 : kNegBig;
+  for (int jj = tid + kMergeThreads; jj < J; jj += kMergeThreads) M = fmaxf(M, ml_of(jj)[0]);
   M = group_max<kWave>(M);
-  // Lane jj holds chunk jj's weight; chunks past the wave width (long lists
-  // only) recompute theirs where they are used.
-  float Ls = 0.f, w_own = 0.f;
-  if (lane < J) {
-    w_own = exp2f(m0 - M);
-    Ls += w_own * l0;
+  if (lane == 0) s_red[0][wv] = M;
+  __syncthreads();
+  M = s_red[0][0];
+#pragma unroll
+  for (int i = 1; i < NWV; ++i) M = fmaxf(M, s_red[0][i]);
+  float Ls = 0.f;
+  if (tid < J) {
+    const float w = exp2f(m0 - M);
+    s_w[tid] = w;
+    Ls = w * l0;
   }
-  for (int jj = lane + kWave; jj < J; jj += kWave) {
+  for (int jj = tid + kMergeThreads; jj < J; jj += kMergeThreads) {
     const float* ml = ml_of(jj);
-    Ls += exp2f(ml[0] - M) * ml[1];
+    const float w = exp2f(ml[0] - M);
+    s_w[jj] = w;
+    Ls = fmaf(w, ml[1], Ls);
   }
   Ls = group_sum<kWave>(Ls);
-  float o[DPL];
+  if (lane == 0) s_red[1][wv] = Ls;
+  __syncthreads();  // also publishes s_w
+  Ls = s_red[1][0];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int i = 1; i < NWV; ++i) Ls += s_red[1][i];
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float w, const float4& v) {
+    o.x = fmaf(w, v.x, o.x);
+    o.y = fmaf(w, v.y, o.y);
+    o.z = fmaf(w, v.z, o.z);
+    o.w = fmaf(w, v.w, o.w);
+  };
 #pragma unroll
-  for (int i = 0; i < kMergePre; ++i) {
-    if (i < J) {
-      const float wgt = __shfl(w_own, i);
+  for (int q = 0; q < kMergeBatch; ++q) {
+    const int jj = sub + q * NS;
+    if (jj < J) add(s_w[jj], pre[q]);
+  }
+  // Units of more chunks (long lists over few units): further batches.
+  for (int jb = kMergeBatch * NS; jb < J; jb += kMergeBatch * NS) {
+    float4 v[kMergeBatch];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, pre[i][e], o[e]);
+    for (int q = 0; q < kMergeBatch; ++q) v[q] = *acc_of(min(jb + sub + q * NS, a.jmax - 1));
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+      const int jj = jb + sub + q * NS;
+      if (jj < J) add(s_w[jj], v[q]);
     }
   }
-  // Later chunks (long lists), kMergePre loads in flight at a time, at clamped
-  // slots (unused ones are never summed).
-  for (int jb = kMergePre; jb < J; jb += kMergePre) {
-    float v[kMergePre][DPL];
+  s_o[sub][cg] = o;
+  __syncthreads();
+  if (sub == 0) {
+    float4 t = s_o[0][cg];
 #pragma unroll
-    for (int q = 0; q < kMergePre; ++q) {
-      const float* src = acc_of(min(jb + q, a.jmax - 1));
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) v[q][e] = src[e];
+    for (int i = 1; i < NS; ++i) {
+      t.x += s_o[i][cg].x;
+      t.y += s_o[i][cg].y;
+      t.z += s_o[i][cg].z;
+      t.w += s_o[i][cg].w;
     }
-#pragma unroll
-    for (int q = 0; q < kMergePre; ++q) {
-      const int jj = jb + q;
-      if (jj < J) {
-        const float wgt = jj < kWave ? __shfl(w_own, jj) : exp2f(ml_of(jj)[0] - M);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] = fmaf(wgt, v[q][e], o[e]);
-      }
-    }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    float* dst = a.out + (int64_t)bh * D + 4 * cg;
+    dst[0] = t.x * inv;
+    dst[1] = t.y * inv;
+    dst[2] = t.z * inv;
+    dst[3] = t.w * inv;
   }
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) a.out[(int64_t)bh * D + lane * DPL + e] = o[e] * inv;
-  if (a.lse != nullptr && lane == 0) a.lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  if (a.lse != nullptr && tid == 0) a.lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 // out_h = sum_j 2^{m_j-M} acc_j / sum_j 2^{m_j-M} l_j, lse_h = ln2 (M + log2 sum_j 2^{m_j-M} l_j),
@@ -948,9 +982,10 @@ hipError_t decode_dispatch(const DecodeArgs& a, hipStream_t s) {
 }
 
 
-// The stream kernel for group size G (G = 8: the matrix-core P.V form).
+// The stream kernel for group size G (G = 8: the matrix-core P.V form);
+// `waves` (nullable) receives the waves launched.
 template <int D, int G, bool SPARSE>
-hipError_t stream_kernel_launch(const StreamArgs& a, hipStream_t s) {
+hipError_t stream_kernel_launch(const StreamArgs& a, hipStream_t s, int64_t* waves = nullptr) {
   const int units = a.c.batch * a.c.hkv;
   const size_t lds = (size_t)(units + 1) * sizeof(int);
   const void* fn;
@@ -961,6 +996,7 @@ hipError_t stream_kernel_launch(const StreamArgs& a, hipStream_t s) {
   int grid = 0;
   hipError_t e = persistent_grid(fn, kDecodeThreads, lds, &grid);
   if (e != hipSuccess) return e;
+  if (waves != nullptr) *waves = (int64_t)grid * kDecodeWaves;
   if constexpr (G == 8)
     hipLaunchKernelGGL((decode_stream_g8_kernel<D, SPARSE>), dim3(grid), dim3(kDecodeThreads), lds, s, a);
   else
@@ -976,9 +1012,18 @@ hipError_t stream_partials_impl(const StreamArgs& a, hipStream_t s) {
 
 template <int D, int G, bool SPARSE>
 hipError_t stream_impl(const StreamArgs& a, hipStream_t s) {
-  hipError_t e = stream_kernel_launch<D, G, SPARSE>(a, s);
+  int64_t waves = 0;
+  hipError_t e = stream_kernel_launch<D, G, SPARSE>(a, s, &waves);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((stream_merge_kernel<D, SPARSE>), dim3(a.c.batch * a.c.hq), dim3(kWave), 0, s, a);
+  const int64_t units = (int64_t)a.c.batch * a.c.hkv;
+  const int64_t expect = std::min<int64_t>(a.jmax, (waves + units - 1) / units + 2);
+  const dim3 grid(a.c.batch * a.c.hq);
+  if (expect <= 4 * (64 / (D / 4)))
+    hipLaunchKernelGGL((stream_merge_kernel<D, 64, 4, SPARSE>), grid, dim3(64), 0, s, a);
+  else if (expect <= 8 * (128 / (D / 4)))
+    hipLaunchKernelGGL((stream_merge_kernel<D, 128, 8, SPARSE>), grid, dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL((stream_merge_kernel<D, 256, 8, SPARSE>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1001,7 +1046,7 @@ constexpr int kStreamWaveTarget = 8192;
 }  // namespace
 
 void stream_plan(int64_t units, int list_pages, int* jmax, int* rmin) {
-  *jmax = (int)std::min<int64_t>(std::max<int64_t>((kStreamWaveTarget + units - 1) / units + 2, 3), 1024);
+  *jmax = (int)std::min<int64_t>(std::max<int64_t>((kStreamWaveTarget + units - 1) / units + 2, 3), kMaxMergeChunks);
   *rmin = (list_pages + *jmax - 2) / (*jmax - 1);
 }
 

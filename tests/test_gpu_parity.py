@@ -121,6 +121,12 @@ EDGE = [
     ("bf16", 128, 16, 2, 64, [64, 65, 129, 4100], [2, 2, 3, 30]),
     ("bf16", 128, 8, 1, 8, [9, 800, 4095], [2, 50, 300]),
     ("bf16", 128, 32, 8, 16, [5000, 7777], [1, 600]),
+    # many short sequences: 640 units (15 partial slots per unit) and 300 units (30 slots) take the
+    # merge's 64- and 128-thread forms
+    ("bf16", 128, 32, 8, 16, [int(x) for x in np.random.default_rng(77).integers(1, 1200, 80)],
+     [int(x) for x in np.random.default_rng(78).integers(0, 40, 80)]),
+    ("bf16", 128, 16, 4, 16, [int(x) for x in np.random.default_rng(79).integers(1, 1200, 75)],
+     [int(x) for x in np.random.default_rng(80).integers(0, 40, 75)]),
 ]
 
 
