@@ -8,8 +8,10 @@
 // channel and page instead of 2G. Scoring is a GEMV over 2*D values per page,
 // so it streams the page summaries with 16-byte loads and reduces across lanes.
 // The sum is accumulated in fp64 and rounded once, so each fp32 score is the
-// correctly rounded bound even when products cancel (fp64 FMA issues at the
-// fp32 rate on this chip and the kernel is bound by HBM, not ALU).
+// correctly rounded bound even when products cancel. Vector fp64 FMA runs at
+// half the fp32 rate on this chip (78.6 vs 157.3 TFLOP/s); at 2*D FMAs (one
+// flop per byte) per 4*D-byte bf16 summary, streaming at 8 TB/s takes about a
+// tenth of the fp64 rate, so the pass stays bound by HBM, not ALU.
 //
 // Selection (Top-k pages under a KV budget, Sparrow project page "Control
 // Study 2"; sink/local pages always kept): K = min(max(budget,2), cap, P);
