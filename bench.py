@@ -67,6 +67,8 @@ def parse():
                     help="skip the 131072-token page-size sweep (4 sequences, page sizes 8/16/32/64)")
     ap.add_argument("--no-acceptance-pass", action="store_true",
                     help="skip the 32768-token batch with its acceptance over 64 x 151936 logit pairs")
+    ap.add_argument("--no-gather-ceiling", action="store_true",
+                    help="skip the gather-read ceiling probe (the sparse path's page and summary gathers, no math)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -359,6 +361,65 @@ def make_timers(dev, K):
     return timed_loop, scrubbed, (scrub, scrub_out)
 
 
+def _probe_lib():
+    import ctypes
+    from sparse_attention_decode_page_amd import build as B
+    if not os.path.exists(B.PROBE_LIB_PATH):
+        raise RuntimeError(f"{B.PROBE_LIB_PATH} is not built; run sparse_attention_decode_page_amd.build.build()")
+    L = ctypes.CDLL(B.PROBE_LIB_PATH)
+    L.spdec_probe_gather.restype = ctypes.c_int
+    L.spdec_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    L.spdec_probe_sink_words.restype = ctypes.c_int
+    return L
+
+
+def gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_select=None, t_decode=None):
+    """The gather-read ceiling of the sparse path's two streams on this cache: a kernel with the stream
+    kernels' access pattern and no arithmetic (libspdec_probe.so) reads (a) the kept pages' K and V blocks, in
+    the decode's order, and (b) every page's summary, in the scoring pass's order; each timed like the calls
+    (after a scrub read). The calls' times set against these give the fraction of the reachable rate."""
+    import torch
+    L = _probe_lib()
+    dev = sel_idx.device
+    B, H, cap = sel_idx.shape
+    ps, D = spec.page_size, spec.head_dim
+    pt = cache.page_table.long()
+    keep = torch.arange(cap, device=dev)[None, None, :] < sel_cnt.long()[:, :, None]
+    bi, gi, _ = keep.nonzero(as_tuple=True)                 # unit-major, entries ascending
+    phys = pt[bi, sel_idx[keep].long()]
+    kv_off = ((phys * H + gi) * (ps * D * 2)).contiguous()
+    lens = cache.seq_lens.long()
+    P = torch.clamp((lens + ps - 1) // ps, max=pt.shape[1])
+    allp = (torch.arange(pt.shape[1], device=dev)[None, :] < P[:, None])[:, None, :].expand(B, H, pt.shape[1])
+    bj, gj, pj = allp.nonzero(as_tuple=True)
+    sm_off = ((pt[bj, pj] * H + gj) * (2 * D * 2)).contiguous()
+    sink = torch.zeros(L.spdec_probe_sink_words(), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe(base0, base1, off, nbytes):
+        rc = L.spdec_probe_gather(base0.data_ptr(), None if base1 is None else base1.data_ptr(), off.data_ptr(),
+                                  off.numel(), nbytes, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"spdec_probe_gather failed ({rc})")
+
+    t_kv = scrubbed(lambda i: probe(cache.k_pool, cache.v_pool, kv_off, ps * D * 2))
+    t_sm = scrubbed(lambda i: probe(cache.kminmax, None, sm_off, 2 * D * 2))
+    b_kv = int(kv_off.numel()) * ps * D * 2 * 2
+    b_sm = int(sm_off.numel()) * 2 * D * 2
+    res = {"kv_pages": dict(_row(t_kv, b_kv), blocks=int(kv_off.numel()), block_bytes=ps * D * 2, pools=2),
+           "summaries": dict(_row(t_sm, b_sm), blocks=int(sm_off.numel()), block_bytes=2 * D * 2, pools=1),
+           "probe": "libspdec_probe.so: the stream kernels' walk (per-wave contiguous ranges, 64 offsets per "
+                    "window, 16-byte non-temporal loads) with no arithmetic",
+           "timing": "median of 3 x (K x (1 GiB scrub read, probe) minus K x scrub)"}
+    if t_decode is not None:
+        res["sparse_decode_over_ceiling"] = t_kv / t_decode
+    if t_select is not None:
+        res["select_pages_over_ceiling"] = t_sm / t_select
+    del kv_off, sm_off, sink
+    return res
+
+
 def _row(t, b):
     return {"us": t * 1e6, "bytes": int(b), "GBps": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS}
 
@@ -430,6 +491,9 @@ def layer_rows(args, dev, timers, name, acceptance=False):
         "timing": "sparse calls: median of 3 x (K x (1 GiB scrub read, call) minus K x scrub); dense: K calls back "
                   "to back",
     }
+    if not args.no_gather_ceiling:
+        sel()
+        res["gather_ceiling"] = gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_sel, t_dec)
     if acceptance:
         la = torch.from_numpy(wl.logits_a).to(dev)
         lb = torch.from_numpy(wl.logits_b).to(dev)
@@ -794,6 +858,10 @@ def main():
     sel_t = scrubbed(sel)
     dec_t = scrubbed(dec)
     sp_t_warm = timed_loop(sparse_path)
+    ceiling = None
+    if not args.no_gather_ceiling:
+        sel()
+        ceiling = gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, sel_t, dec_t)
     byt_sp = algorithmic_bytes(spec, lens_sparse, wl.budget_pages, cap, R, V)
     sp_b = byt_sp["select_pages"] + byt_sp["sparse_decode"]
     value = spec.batch / sp_t
@@ -913,6 +981,7 @@ def main():
                    "us_no_scrub": sp_t_warm * 1e6,
                    "select_pages": dict(_row(sel_t, byt_sp["select_pages"]), traffic=traffic_of(sel_kernels)),
                    "sparse_decode": dict(_row(dec_t, byt_sp["sparse_decode"]), traffic=traffic_of(dec_kernels))},
+        "gather_ceiling": ceiling,
         "value_runs": {"tokens_per_s": [spec.batch / t for t in value_runs], "median": value,
                        "timing": "three interleaved regions of K (scrub, sparse path) and K scrubs"},
         "dense": dict(_row(de_t, byt_now["dense_decode"]), tokens_per_s=spec.batch / de_t,

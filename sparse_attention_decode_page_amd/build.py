@@ -1,7 +1,9 @@
-"""Compile libspdec.so (all HIP kernels and the C ABI) for gfx950, in-tree.
+"""Compile libspdec.so (all HIP kernels and the C ABI) for gfx950, in-tree,
+and libspdec_probe.so (the gather-read ceiling probe that bench.py times next
+to the kernels; not part of the library's ABI).
 
 Each source compiles to its own object in parallel (`_build/` beside this
-file), then one link step makes the shared library.
+file), then one link step per library makes the shared libraries.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libspdec.so")
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libspdec_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["abi.hip", "grid.hip", "meta.hip", "select.hip", "decode.hip", "verify.hip", "shared.hip", "speculative.hip",
            "acceptance.hip", "control.hip", "check.hip", "noalloc.hip", "monitor.hip"]
 
@@ -50,16 +54,18 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = list(SOURCES)
+    srcs = list(SOURCES) + list(PROBE_SOURCES)
     objs = [os.path.join(OBJ_DIR, s.replace(".hip", ".o")) for s in srcs]
     cc = hipcc()
     cmds = [[cc, *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o]
             for s, o in zip(srcs, objs)]
     with ThreadPoolExecutor(max_workers=min(len(cmds), max(1, min(os.cpu_count() or 1, 16)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
+    for path, names in ((LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)):
+        tmp = path + ".tmp"
+        lib_objs = [os.path.join(OBJ_DIR, s.replace(".hip", ".o")) for s in names]
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *lib_objs, "-o", tmp], verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -312,3 +312,23 @@ def test_check_inputs_checks(L):
     assert chk(None, None, None, None, 0, 1, None, FAKE, None) == -1
     bad = _desc(batch=4, head_dim=96)
     assert chk(ctypes.byref(bad), None, None, None, 0, 1, None, FAKE, None) == -2
+
+
+def test_probe_library_rejects_bad_arguments():
+    """The gather-ceiling probe (a separate library that bench.py times) loads, exports its two calls and
+    rejects bad arguments before touching the GPU."""
+    from sparse_attention_decode_page_amd import build as B
+    if not os.path.exists(B.PROBE_LIB_PATH):
+        B.build()
+    P = ctypes.CDLL(B.PROBE_LIB_PATH)
+    P.spdec_probe_gather.restype = ctypes.c_int
+    P.spdec_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    P.spdec_probe_sink_words.restype = ctypes.c_int
+    assert P.spdec_probe_sink_words() == 65536
+    assert P.spdec_probe_gather(None, None, FAKE, 4, 4096, FAKE, None) == -1     # no base
+    assert P.spdec_probe_gather(FAKE, None, None, 4, 4096, FAKE, None) == -1     # no offsets
+    assert P.spdec_probe_gather(FAKE, None, FAKE, 4, 4096, None, None) == -1     # no sink
+    assert P.spdec_probe_gather(FAKE, None, FAKE, 0, 4096, FAKE, None) == -1     # empty list
+    assert P.spdec_probe_gather(FAKE, None, FAKE, 4, 3000, FAKE, None) == -1     # block not a power of two
+    assert P.spdec_probe_gather(FAKE, None, FAKE, 4, 256, FAKE, None) == -1      # below 512 bytes
