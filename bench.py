@@ -67,6 +67,9 @@ def parse():
                     help="skip the 131072-token page-size sweep (4 sequences, page sizes 8/16/32/64)")
     ap.add_argument("--no-acceptance-pass", action="store_true",
                     help="skip the 32768-token batch with its acceptance over 64 x 151936 logit pairs")
+    ap.add_argument("--layer", default=None,
+                    help="profiling mode: only the layer rows of these comma-separated workloads (sparse path, its "
+                         "two calls, dense decode, gather ceiling), one JSON line; no headline value")
     ap.add_argument("--no-gather-ceiling", action="store_true",
                     help="skip the gather-read ceiling probe (the sparse path's page and summary gathers, no math)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -94,11 +97,14 @@ def algorithmic_bytes(spec, lens, budget_pages, cap, rows, vocab):
     }
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters_qwen3-8b-ragged.md")
-# The measured kernels (dense and sparse decode, scoring, top-B) and their launch
-# configuration (plans, resident grid); a change to any of these invalidates the
-# recorded counter traffic.
-KERNEL_SOURCES = ("common.h", "decode.hip", "select.hip", "grid.hip")
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_counters_{workload}.md")
+
+
+# The measured kernels (dense and sparse decode, scoring, top-B, acceptance) and
+# their launch configuration (plans, resident grid); a change to any of these
+# invalidates the recorded counter traffic.
+KERNEL_SOURCES = ("common.h", "decode.hip", "select.hip", "grid.hip", "acceptance.hip")
 
 
 def describe_lens(spec) -> str:
@@ -128,16 +134,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """Per-dispatch HBM bytes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
+def counter_traffic(workload: str):
+    """Per-dispatch HBM bytes on `workload` from its committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
 
     Returns {kernel: bytes} or None when the summary is missing or the kernel
     sources changed since the counters were taken.
     """
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     table, src = {}, None
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             parts = line.split()
             if len(parts) == 2 and parts[0] == "source_hash":
@@ -420,6 +427,44 @@ def gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_select=None, t_dec
     return res
 
 
+def call_kernels(spec):
+    """Name patterns (over the counter summaries' kernel names) of the kernels each call launches on a bf16
+    workload of this shape; the merge's form and the Top-B's size class depend on the workload."""
+    D, G = spec.head_dim, spec.group
+    dec = (lambda sp: f"decode_stream_g8_kernel<{D},{sp}>") if G == 8 else \
+        (lambda sp: f"decode_stream_kernel<{D},{G},{sp}>")
+    return {"select_pages": [f"score_stream_kernel<BF16,{D},{G}>", "select_topk_reg_kernel<*>"],
+            "sparse_decode": [dec("true"), f"stream_merge_kernel<{D},*,true>"],
+            "dense_decode": [dec("false"), f"stream_merge_kernel<{D},*,false>"]}
+
+
+def copy_probe(torch, dev):
+    """Three plain 1 GiB device-to-device copies: the known byte count that calibrates the HBM counters."""
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    n = int(x.numel() * 4)
+    del x, y
+    torch.cuda.empty_cache()
+    return n
+
+
+def traffic_sum(traffic, patterns):
+    """Summed bytes per call of the kernels matching `patterns` (each must match exactly one kernel)."""
+    import fnmatch
+    if traffic is None:
+        return None
+    total = 0
+    for pat in patterns:
+        hits = [k for k in traffic if fnmatch.fnmatchcase(k, pat)]
+        if len(hits) != 1:
+            return None
+        total += traffic[hits[0]]
+    return int(total)
+
+
 def _row(t, b):
     return {"us": t * 1e6, "bytes": int(b), "GBps": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS}
 
@@ -491,6 +536,12 @@ def layer_rows(args, dev, timers, name, acceptance=False):
         "timing": "sparse calls: median of 3 x (K x (1 GiB scrub read, call) minus K x scrub); dense: K calls back "
                   "to back",
     }
+    traffic = counter_traffic(spec.name)
+    ck = call_kernels(spec)
+    for call in ("select_pages", "sparse_decode", "dense_decode"):
+        res[call]["traffic"] = traffic_sum(traffic, ck[call])
+    res["sparse_path"]["traffic"] = traffic_sum(traffic, ck["select_pages"] + ck["sparse_decode"])
+    res["kernels"] = ck
     if not args.no_gather_ceiling:
         sel()
         res["gather_ceiling"] = gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_sel, t_dec)
@@ -756,6 +807,23 @@ def main():
     from sparse_attention_decode_page_amd import synth as S
 
     K_steps, W = args.steps, args.warmup
+    if args.layer:
+        if not os.path.exists(spdec.LIB_PATH):
+            from sparse_attention_decode_page_amd import build
+            build.build()
+        spdec.lib()
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        timers = make_timers(dev, K_steps)
+        layers = {}
+        for name in args.layer.split(","):
+            layers[name] = layer_rows(args, dev, timers, name, acceptance=S.SPECS[name].logits is not None)
+            print(f"layer {name} done", file=sys.stderr, flush=True)
+        out = {"mode": "layer", "steps": K_steps, "layers": layers, "env": env_info(torch)}
+        if args.copy_probe:
+            out["copy_probe_bytes"] = copy_probe(torch, dev)
+        print(json.dumps(out), flush=True)
+        return
     t_setup = time.perf_counter()
     wl = S.make_workload(args.workload, seed=args.seed, headroom=5 * K_steps + 2 * W + 2)
     spec = wl.spec
@@ -936,16 +1004,13 @@ def main():
         if not args.no_acceptance_pass else None
 
     # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
-    traffic = counter_traffic() if spec.name == WORKLOAD else None
-    dec_kernels = ["decode_stream_kernel<128,4,true>", "stream_merge_kernel<128,true>"]
-    sel_kernels = ["score_stream_kernel<BF16,128,4>", "select_topk_reg_kernel<8,256>"]
-    dense_kernels = ["decode_stream_kernel<128,4,false>", "stream_merge_kernel<128,false>"]
+    traffic = counter_traffic(spec.name)
+    ck = call_kernels(spec)
+    dec_kernels, sel_kernels, dense_kernels = ck["sparse_decode"], ck["select_pages"], ck["dense_decode"]
     acc_kernels = ["acc_one_read_kernel<true>"]
 
     def traffic_of(names):
-        if traffic is None or any(n not in traffic for n in names):
-            return None
-        return int(sum(traffic[n] for n in names))
+        return traffic_sum(traffic, names)
 
     dec_gbps = byt_sp["sparse_decode"] / dec_t / 1e9
     sparse_gbps = sp_b / sp_t / 1e9
@@ -1009,12 +1074,7 @@ def main():
         "setup_s": t_setup,
     }
     if args.copy_probe:
-        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
-        result["copy_probe_bytes"] = int(x.numel() * 4)
+        result["copy_probe_bytes"] = copy_probe(torch, dev)
     if not args.no_cpu_baseline:
         kn = np.stack([t[0] for t in new_tokens[:1]])[0]
         vn = np.stack([t[1] for t in new_tokens[:1]])[0]
