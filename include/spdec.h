@@ -44,6 +44,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The HIP runtime's stream handle, declared as the HIP headers declare it
+ * (an identical typedef), so this header needs no HIP include and may come
+ * before or after them. NULL is the default stream. */
+typedef struct ihipStream_t* hipStream_t;
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -95,10 +100,22 @@ typedef struct spdec_cache {
 } spdec_cache;
 
 /* Human-readable name of a status code (static string, never NULL). */
-const char* spdec_status_string(int status);
+const char* spdec_status_string(spdec_status status);
 
 /* Version of this ABI: major*10000 + minor*100 + patch. */
 int spdec_version(void);
+
+/*
+ * Default scales (host computation, no GPU work): spdec_default_scale is the
+ * softmax scale 1/sqrt(head_dim) for the decode and verify calls (the pages
+ * leave the scale unstated; the standard attention scale is taken);
+ * spdec_default_score_scale is 1/(G*sqrt(head_dim)), the logit scale of a
+ * page bound in spdec_select_pages_top_p (the bound sums the G query heads'
+ * per-head bounds, each a logit at scale 1/sqrt(head_dim)). Both return 0
+ * for an invalid descriptor.
+ */
+float spdec_default_scale(const spdec_cache* cache);
+float spdec_default_score_scale(const spdec_cache* cache);
 
 /*
  * spdec_append_kv - write the new token's key and value into the paged cache
@@ -117,14 +134,14 @@ int spdec_version(void);
  * falls outside its page table or maps to an out-of-range physical page is
  * left unchanged (no write, no increment).
  */
-spdec_status spdec_append_kv(const spdec_cache* cache, const void* k_new, const void* v_new, void* stream);
+spdec_status spdec_append_kv(const spdec_cache* cache, const void* k_new, const void* v_new, hipStream_t stream);
 
 /*
  * spdec_build_meta - recompute every in-use page's key minimum and maximum
  * from the keys in the cache (bulk form of the upkeep in spdec_append_kv, for
  * a prefilled cache). Only the page's valid tokens t < seq_lens[b] count.
  */
-spdec_status spdec_build_meta(const spdec_cache* cache, void* stream);
+spdec_status spdec_build_meta(const spdec_cache* cache, hipStream_t stream);
 
 /*
  * spdec_select_pages - score every page of every (sequence, KV head) and keep
@@ -152,7 +169,7 @@ spdec_status spdec_build_meta(const spdec_cache* cache, void* stream);
 size_t spdec_select_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
 spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
                                 int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_select_pages_top_p - score-mass (top-p) page selection: the budget
@@ -177,7 +194,7 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
 spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, float top_p, float score_scale,
                                       const int32_t* budget_pages, int max_budget_pages, int32_t* sel_idx,
                                       int32_t* sel_cnt, float* scores_out, void* workspace, size_t workspace_bytes,
-                                      void* stream);
+                                      hipStream_t stream);
 
 /*
  * spdec_select_pages_shared - spdec_select_pages for groups of sequences that
@@ -199,7 +216,7 @@ spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, f
 spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, int group_size,
                                        const int32_t* shared_pages, const int32_t* budget_pages,
                                        int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
-                                       void* workspace, size_t workspace_bytes, void* stream);
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_sparse_decode - block-sparse decode attention over the selected pages
@@ -222,7 +239,7 @@ spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, 
 size_t spdec_decode_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
 spdec_status spdec_sparse_decode(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
                                  const int32_t* sel_cnt, int max_budget_pages, float scale, float* out,
-                                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
+                                 float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_dense_decode - the same attention over every page of the cache: the
@@ -230,7 +247,7 @@ spdec_status spdec_sparse_decode(const spdec_cache* cache, const void* q, const 
  * the complete historical KV cache). Workspace: spdec_decode_workspace_bytes(cache, 0).
  */
 spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float scale, float* out, float* lse,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_dense_decode_shared - spdec_dense_decode for groups of sequences that
@@ -255,7 +272,7 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
 size_t spdec_shared_workspace_bytes(const spdec_cache* cache, int group_size);
 spdec_status spdec_dense_decode_shared(const spdec_cache* cache, const void* q, int group_size,
                                        const int32_t* shared_pages, float scale, float* out, float* lse,
-                                       void* workspace, size_t workspace_bytes, void* stream);
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_verify_decode - dense verification of a sparse draft: causal
@@ -280,7 +297,7 @@ spdec_status spdec_dense_decode_shared(const spdec_cache* cache, const void* q, 
  */
 size_t spdec_verify_workspace_bytes(const spdec_cache* cache, int num_positions);
 spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int num_positions, float scale,
-                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_spec_accept - exact speculative sampling of the drafted tokens (S3R
@@ -314,7 +331,7 @@ size_t spdec_spec_accept_workspace_bytes(int batch, int num_draft, int vocab);
 spdec_status spdec_spec_accept(const float* p_logits, const float* q_logits, int batch, int num_draft, int vocab,
                                int64_t row_stride, const int32_t* draft, const float* u_accept,
                                const float* u_sample, float temperature, int32_t* num_accepted,
-                               int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream);
+                               int32_t* next_token, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_acceptance - per-token sparse-vs-dense acceptance (Sparrow project
@@ -343,7 +360,7 @@ spdec_status spdec_spec_accept(const float* p_logits, const float* q_logits, int
 size_t spdec_acceptance_workspace_bytes(int rows, int vocab);
 spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab,
                               int64_t row_stride, float temperature, float* alpha, void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * spdec_acceptance_noalloc - spdec_acceptance for callers that cannot allocate
@@ -361,7 +378,7 @@ spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int 
  */
 #define SPDEC_NOALLOC_SCRATCH_BYTES (2u << 20)
 spdec_status spdec_acceptance_noalloc(const float* logits_a, const float* logits_b, int rows, int vocab,
-                                      int64_t row_stride, float temperature, float* alpha, void* stream);
+                                      int64_t row_stride, float temperature, float* alpha, hipStream_t stream);
 
 /*
  * spdec_acceptance_ex - spdec_acceptance with its form and wait made explicit
@@ -379,7 +396,7 @@ spdec_status spdec_acceptance_noalloc(const float* logits_a, const float* logits
 spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, int rows, int vocab,
                                  int64_t row_stride, float temperature, float* alpha, void* workspace,
                                  size_t workspace_bytes, int force_path, int spin_limit, int32_t* fallbacks,
-                                 int32_t* path_taken, void* stream);
+                                 int32_t* path_taken, hipStream_t stream);
 
 /*
  * spdec_tail_stats - on-device tail statistics of the per-token acceptance
@@ -394,7 +411,7 @@ spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, i
  * alpha: fp32 [rows] (device); out: fp32 [2] (device). 1 <= rows <= 8192
  * (SPDEC_ERR_UNSUPPORTED above). No workspace.
  */
-spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream);
+spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, hipStream_t stream);
 
 /*
  * spdec_monitor_* - streaming tail monitor of the per-token acceptance over a
@@ -419,9 +436,9 @@ spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* st
  *   gives NaN for both (the controller then keeps its state).
  */
 size_t spdec_monitor_workspace_bytes(int capacity);
-spdec_status spdec_monitor_reset(void* monitor, int capacity, void* stream);
-spdec_status spdec_monitor_append(void* monitor, int capacity, const float* alpha, int n, void* stream);
-spdec_status spdec_monitor_stats(void* monitor, int capacity, float* out, void* stream);
+spdec_status spdec_monitor_reset(void* monitor, int capacity, hipStream_t stream);
+spdec_status spdec_monitor_append(void* monitor, int capacity, const float* alpha, int n, hipStream_t stream);
+spdec_status spdec_monitor_stats(void* monitor, int capacity, float* out, hipStream_t stream);
 
 /*
  * spdec_budget_update - sparsity-schedule controller: one correction of the
@@ -459,7 +476,7 @@ typedef struct spdec_budget_params {
 } spdec_budget_params;
 
 spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t* seq_lens, int batch,
-                                 const spdec_budget_params* params, int32_t* budget_pages, void* stream);
+                                 const spdec_budget_params* params, int32_t* budget_pages, hipStream_t stream);
 
 /*
  * spdec_check_inputs - counts, on the device, violations of the data
@@ -495,7 +512,7 @@ spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t*
 #define SPDEC_CHECK_FIRST 5
 spdec_status spdec_check_inputs(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
                                 const int32_t* sel_cnt, int max_budget_pages, int group_size,
-                                const int32_t* shared_pages, int32_t* report, void* stream);
+                                const int32_t* shared_pages, int32_t* report, hipStream_t stream);
 
 #ifdef __cplusplus
 }

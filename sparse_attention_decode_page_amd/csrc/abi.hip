@@ -60,7 +60,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-const char* spdec_status_string(int status) {
+const char* spdec_status_string(spdec_status status) {
   switch (status) {
     case SPDEC_OK: return "SPDEC_OK";
     case SPDEC_ERR_INVALID: return "SPDEC_ERR_INVALID: invalid argument";
@@ -73,22 +73,34 @@ const char* spdec_status_string(int status) {
 
 int spdec_version(void) { return 100; }
 
-spdec_status spdec_append_kv(const spdec_cache* cache, const void* k_new, const void* v_new, void* stream) {
+float spdec_default_scale(const spdec_cache* cache) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK) return 0.f;
+  return (float)(1.0 / sqrt((double)v.head_dim));  // rounded once
+}
+
+float spdec_default_score_scale(const spdec_cache* cache) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK) return 0.f;
+  return (float)(1.0 / ((double)v.group * sqrt((double)v.head_dim)));  // rounded once
+}
+
+spdec_status spdec_append_kv(const spdec_cache* cache, const void* k_new, const void* v_new, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
   if (!v.k_pool || !v.v_pool || !v.kminmax || !k_new || !v_new) return SPDEC_ERR_INVALID;
   if (!aligned16(v.k_pool) || !aligned16(v.v_pool) || !aligned16(v.kminmax) || !aligned16(k_new) || !aligned16(v_new))
     return SPDEC_ERR_INVALID;
-  return from_hip(spdec::launch_append_kv(v, k_new, v_new, static_cast<hipStream_t>(stream)));
+  return from_hip(spdec::launch_append_kv(v, k_new, v_new, stream));
 }
 
-spdec_status spdec_build_meta(const spdec_cache* cache, void* stream) {
+spdec_status spdec_build_meta(const spdec_cache* cache, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
   if (!v.k_pool || !v.kminmax || !aligned16(v.k_pool) || !aligned16(v.kminmax)) return SPDEC_ERR_INVALID;
-  return from_hip(spdec::launch_build_meta(v, static_cast<hipStream_t>(stream)));
+  return from_hip(spdec::launch_build_meta(v, stream));
 }
 
 size_t spdec_select_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
@@ -99,7 +111,7 @@ size_t spdec_select_workspace_bytes(const spdec_cache* cache, int max_budget_pag
 
 spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
                                 int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
@@ -109,13 +121,13 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
   if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_select(v, q, budget_pages, max_budget_pages, sel_idx, sel_cnt, scores_out, workspace,
-                                       static_cast<hipStream_t>(stream)));
+                                       stream));
 }
 
 spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, float top_p, float score_scale,
                                       const int32_t* budget_pages, int max_budget_pages, int32_t* sel_idx,
                                       int32_t* sel_cnt, float* scores_out, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+                                      hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
@@ -127,13 +139,13 @@ spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, f
   if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_select_top_p(v, q, top_p, score_scale, budget_pages, max_budget_pages, sel_idx,
-                                             sel_cnt, scores_out, workspace, static_cast<hipStream_t>(stream)));
+                                             sel_cnt, scores_out, workspace, stream));
 }
 
 spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, int group_size,
                                        const int32_t* shared_pages, const int32_t* budget_pages,
                                        int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
@@ -145,7 +157,7 @@ spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, 
   if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_select_shared(v, q, budget_pages, max_budget_pages, group_size, shared_pages, sel_idx,
-                                              sel_cnt, scores_out, workspace, static_cast<hipStream_t>(stream)));
+                                              sel_cnt, scores_out, workspace, stream));
 }
 
 size_t spdec_decode_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
@@ -156,7 +168,7 @@ size_t spdec_decode_workspace_bytes(const spdec_cache* cache, int max_budget_pag
 
 static spdec_status decode_common(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
                                   const int32_t* sel_cnt, int max_budget_pages, float scale, float* out, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
@@ -166,19 +178,19 @@ static spdec_status decode_common(const spdec_cache* cache, const void* q, const
   const spdec::DecodePlan plan = spdec::decode_plan(v, max_budget_pages);
   if (workspace == nullptr || workspace_bytes < spdec::decode_workspace_bytes(v, plan)) return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_decode(v, plan, q, sel_idx, sel_cnt, scale, out, lse, workspace,
-                                       static_cast<hipStream_t>(stream)));
+                                       stream));
 }
 
 spdec_status spdec_sparse_decode(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
                                  const int32_t* sel_cnt, int max_budget_pages, float scale, float* out, float* lse,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!sel_idx || !sel_cnt || max_budget_pages < 1) return SPDEC_ERR_INVALID;
   return decode_common(cache, q, sel_idx, sel_cnt, max_budget_pages, scale, out, lse, workspace, workspace_bytes,
                        stream);
 }
 
 spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float scale, float* out, float* lse,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(cache, q, nullptr, nullptr, 0, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -190,7 +202,7 @@ size_t spdec_shared_workspace_bytes(const spdec_cache* cache, int group_size) {
 
 spdec_status spdec_dense_decode_shared(const spdec_cache* cache, const void* q, int group_size,
                                        const int32_t* shared_pages, float scale, float* out, float* lse,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
@@ -202,7 +214,7 @@ spdec_status spdec_dense_decode_shared(const spdec_cache* cache, const void* q, 
   if (workspace == nullptr || workspace_bytes < spdec::shared_workspace_bytes(v, group_size))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_dense_shared(v, q, group_size, shared_pages, scale, out, lse, workspace,
-                                             static_cast<hipStream_t>(stream)));
+                                             stream));
 }
 
 size_t spdec_verify_workspace_bytes(const spdec_cache* cache, int num_positions) {
@@ -212,7 +224,7 @@ size_t spdec_verify_workspace_bytes(const spdec_cache* cache, int num_positions)
 }
 
 spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int num_positions, float scale,
-                                 float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
@@ -224,7 +236,7 @@ spdec_status spdec_verify_decode(const spdec_cache* cache, const void* q, int nu
   if (workspace == nullptr || workspace_bytes < spdec::verify_workspace_bytes(v, num_positions))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_verify(v, q, num_positions, scale, out, lse, workspace,
-                                       static_cast<hipStream_t>(stream)));
+                                       stream));
 }
 
 size_t spdec_spec_accept_workspace_bytes(int batch, int num_draft, int vocab) {
@@ -235,7 +247,7 @@ size_t spdec_spec_accept_workspace_bytes(int batch, int num_draft, int vocab) {
 spdec_status spdec_spec_accept(const float* p_logits, const float* q_logits, int batch, int num_draft, int vocab,
                                int64_t row_stride, const int32_t* draft, const float* u_accept,
                                const float* u_sample, float temperature, int32_t* num_accepted,
-                               int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream) {
+                               int32_t* next_token, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!p_logits || !u_sample || !num_accepted || !next_token) return SPDEC_ERR_INVALID;
   if (num_draft > 0 && (!q_logits || !draft || !u_accept)) return SPDEC_ERR_INVALID;
   if (batch < 1 || num_draft < 0 || vocab < 1 || vocab > (1 << 28) || row_stride < vocab) return SPDEC_ERR_INVALID;
@@ -245,7 +257,7 @@ spdec_status spdec_spec_accept(const float* p_logits, const float* q_logits, int
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_spec_accept(p_logits, num_draft > 0 ? q_logits : p_logits, batch, num_draft, vocab,
                                             row_stride, draft, u_accept, u_sample, temperature, num_accepted,
-                                            next_token, workspace, static_cast<hipStream_t>(stream)));
+                                            next_token, workspace, stream));
 }
 
 size_t spdec_acceptance_workspace_bytes(int rows, int vocab) {
@@ -268,19 +280,19 @@ extern "C" {
 
 spdec_status spdec_acceptance(const float* logits_a, const float* logits_b, int rows, int vocab, int64_t row_stride,
                               float temperature, float* alpha, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              hipStream_t stream) {
   const spdec_status st = spdec::acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
   if (st != SPDEC_OK) return st;
   if (workspace == nullptr || workspace_bytes < spdec::acceptance_workspace_bytes(rows, vocab))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_acceptance(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha, workspace,
-                                           static_cast<hipStream_t>(stream), nullptr));
+                                           stream, nullptr));
 }
 
 spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, int rows, int vocab,
                                  int64_t row_stride, float temperature, float* alpha, void* workspace,
                                  size_t workspace_bytes, int force_path, int spin_limit, int32_t* fallbacks,
-                                 int32_t* path_taken, void* stream) {
+                                 int32_t* path_taken, hipStream_t stream) {
   const spdec_status st = spdec::acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
   if (st != SPDEC_OK) return st;
   if (force_path != -1 && force_path != 1 && force_path != 2) return SPDEC_ERR_INVALID;
@@ -289,13 +301,13 @@ spdec_status spdec_acceptance_ex(const float* logits_a, const float* logits_b, i
     return SPDEC_ERR_WORKSPACE;
   spdec::AcceptanceDiag diag{force_path, spin_limit, fallbacks, path_taken};
   const hipError_t e = spdec::launch_acceptance(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha,
-                                                workspace, static_cast<hipStream_t>(stream), &diag);
+                                                workspace, stream, &diag);
   if (e == hipErrorInvalidValue && force_path == 1) return SPDEC_ERR_UNSUPPORTED;
   return from_hip(e);
 }
 
 spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t* seq_lens, int batch,
-                                 const spdec_budget_params* params, int32_t* budget_pages, void* stream) {
+                                 const spdec_budget_params* params, int32_t* budget_pages, hipStream_t stream) {
   if (!tail || !scale || !seq_lens || !params || !budget_pages) return SPDEC_ERR_INVALID;
   const spdec_budget_params& p = *params;
   auto fin = [](float x) { return isfinite(x); };
@@ -309,12 +321,12 @@ spdec_status spdec_budget_update(const float* tail, float* scale, const int32_t*
   if (p.max_budget_pages < 2 || p.max_budget_pages > 32768) return SPDEC_ERR_INVALID;
   if (batch < 1 || batch > 65536) return SPDEC_ERR_INVALID;
   return from_hip(spdec::launch_budget_update(tail, scale, seq_lens, batch, p, budget_pages,
-                                              static_cast<hipStream_t>(stream)));
+                                              stream));
 }
 
 spdec_status spdec_check_inputs(const spdec_cache* cache, const void* q, const int32_t* sel_idx,
                                 const int32_t* sel_cnt, int max_budget_pages, int group_size,
-                                const int32_t* shared_pages, int32_t* report, void* stream) {
+                                const int32_t* shared_pages, int32_t* report, hipStream_t stream) {
   CacheView v;
   spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
@@ -324,7 +336,7 @@ spdec_status spdec_check_inputs(const spdec_cache* cache, const void* q, const i
   if (shared_pages != nullptr && (group_size < 1 || v.batch % group_size != 0)) return SPDEC_ERR_INVALID;
   return from_hip(spdec::launch_check(v, q, sel_idx, sel_cnt, sel_idx ? max_budget_pages : 0,
                                       shared_pages ? group_size : 1, shared_pages, report,
-                                      static_cast<hipStream_t>(stream)));
+                                      stream));
 }
 
 size_t spdec_monitor_workspace_bytes(int capacity) {
@@ -332,29 +344,29 @@ size_t spdec_monitor_workspace_bytes(int capacity) {
   return spdec::monitor_workspace_bytes(capacity);
 }
 
-spdec_status spdec_monitor_reset(void* monitor, int capacity, void* stream) {
+spdec_status spdec_monitor_reset(void* monitor, int capacity, hipStream_t stream) {
   if (!monitor) return SPDEC_ERR_INVALID;
   if (capacity < 1 || capacity > spdec::kMonitorMaxCapacity) return SPDEC_ERR_INVALID;
-  return from_hip(spdec::launch_monitor_reset(monitor, capacity, static_cast<hipStream_t>(stream)));
+  return from_hip(spdec::launch_monitor_reset(monitor, capacity, stream));
 }
 
-spdec_status spdec_monitor_append(void* monitor, int capacity, const float* alpha, int n, void* stream) {
+spdec_status spdec_monitor_append(void* monitor, int capacity, const float* alpha, int n, hipStream_t stream) {
   if (!monitor || (n > 0 && !alpha) || n < 0) return SPDEC_ERR_INVALID;
   if (capacity < 1 || capacity > spdec::kMonitorMaxCapacity) return SPDEC_ERR_INVALID;
   if (n == 0) return SPDEC_OK;
-  return from_hip(spdec::launch_monitor_append(monitor, capacity, alpha, n, static_cast<hipStream_t>(stream)));
+  return from_hip(spdec::launch_monitor_append(monitor, capacity, alpha, n, stream));
 }
 
-spdec_status spdec_monitor_stats(void* monitor, int capacity, float* out, void* stream) {
+spdec_status spdec_monitor_stats(void* monitor, int capacity, float* out, hipStream_t stream) {
   if (!monitor || !out) return SPDEC_ERR_INVALID;
   if (capacity < 1 || capacity > spdec::kMonitorMaxCapacity) return SPDEC_ERR_INVALID;
-  return from_hip(spdec::launch_monitor_stats(monitor, capacity, out, static_cast<hipStream_t>(stream)));
+  return from_hip(spdec::launch_monitor_stats(monitor, capacity, out, stream));
 }
 
-spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, void* stream) {
+spdec_status spdec_tail_stats(const float* alpha, int rows, float* out, hipStream_t stream) {
   if (!alpha || !out || rows < 1) return SPDEC_ERR_INVALID;
   if (rows > spdec::kTailMaxRows) return SPDEC_ERR_UNSUPPORTED;
-  return from_hip(spdec::launch_tail_stats(alpha, rows, out, static_cast<hipStream_t>(stream)));
+  return from_hip(spdec::launch_tail_stats(alpha, rows, out, stream));
 }
 
 }  // extern "C"

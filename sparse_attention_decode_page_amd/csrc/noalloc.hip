@@ -48,13 +48,13 @@ hipError_t scratch_address(void** out) {
 }  // namespace
 
 extern "C" spdec_status spdec_acceptance_noalloc(const float* logits_a, const float* logits_b, int rows, int vocab,
-                                                 int64_t row_stride, float temperature, float* alpha, void* stream) {
+                                                 int64_t row_stride, float temperature, float* alpha, hipStream_t stream) {
   const spdec_status st = spdec::acceptance_args(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha);
   if (st != SPDEC_OK) return st;
   if (spdec::acceptance_workspace_bytes(rows, vocab) > kScratchBytes) return SPDEC_ERR_UNSUPPORTED;
   void* ws = nullptr;
   if (scratch_address(&ws) != hipSuccess) return SPDEC_ERR_HIP;
   const hipError_t e = spdec::launch_acceptance(logits_a, logits_b, rows, vocab, row_stride, temperature, alpha, ws,
-                                                static_cast<hipStream_t>(stream), nullptr);
+                                                stream, nullptr);
   return e == hipSuccess ? SPDEC_OK : SPDEC_ERR_HIP;
 }

@@ -92,11 +92,11 @@ hipError_t launch(const char* b0, const char* b1, const int64_t* off, int64_t n,
 // base1 at the same offsets. sink: device uint32 [65536], overwritten. Returns
 // 0, -1 for bad arguments (nothing launched), -4 for a launch failure.
 extern "C" int spdec_probe_gather(const void* base0, const void* base1, const int64_t* off, int64_t n,
-                                  int block_bytes, uint32_t* sink, void* stream) {
+                                  int block_bytes, uint32_t* sink, hipStream_t stream) {
   if (base0 == nullptr || off == nullptr || sink == nullptr || n < 1) return -1;
   const char* b0 = static_cast<const char*>(base0);
   const char* b1 = static_cast<const char*>(base1);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
   hipError_t e;
   switch (block_bytes) {
     case 512: e = launch<32>(b0, b1, off, n, sink, s); break;

@@ -9,7 +9,6 @@ shared library is missing or fails to load, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -21,6 +20,7 @@ SPDEC_OK, SPDEC_ERR_INVALID, SPDEC_ERR_UNSUPPORTED, SPDEC_ERR_WORKSPACE, SPDEC_E
 SPDEC_F32, SPDEC_BF16 = 0, 1
 
 ABI_FUNCTIONS = (
+    "spdec_default_scale", "spdec_default_score_scale",
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
     "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_select_pages_shared", "spdec_select_pages_top_p",
     "spdec_decode_workspace_bytes",
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
     sig = {
         "spdec_status_string": (ctypes.c_char_p, [I]),
         "spdec_version": (I, []),
+        "spdec_default_scale": (ctypes.c_float, [D]),
+        "spdec_default_score_scale": (ctypes.c_float, [D]),
         "spdec_append_kv": (I, [D, P, P, P]),
         "spdec_build_meta": (I, [D, P]),
         "spdec_select_workspace_bytes": (SZ, [D, I]),
@@ -130,6 +132,10 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
         raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _default_scale(cache) -> float:
+    return lib().spdec_default_scale(ctypes.byref(cache.desc))
 
 
 def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> torch.Tensor:
@@ -222,7 +228,7 @@ def select_pages_top_p(cache: PagedCache, q, top_p: float, max_budget_pages: int
     if budget_pages is not None:
         _need(budget_pages, "budget_pages", torch.int32, (cache.batch,))
     if score_scale is None:
-        score_scale = 1.0 / ((cache.num_q_heads // cache.num_kv_heads) * math.sqrt(cache.head_dim))
+        score_scale = lib().spdec_default_score_scale(ctypes.byref(cache.desc))
     dev = cache.device
     if sel_idx is None:
         sel_idx = torch.zeros((cache.batch, cache.num_kv_heads, max_budget_pages), dtype=torch.int32, device=dev)
@@ -292,7 +298,7 @@ def sparse_decode(cache: PagedCache, q, sel_idx, sel_cnt, max_budget_pages: int,
     _need(sel_idx, "sel_idx", torch.int32, (cache.batch, cache.num_kv_heads, max_budget_pages))
     _need(sel_cnt, "sel_cnt", torch.int32, (cache.batch, cache.num_kv_heads))
     out, lse = _outs(cache, out, lse)
-    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    scale = _default_scale(cache) if scale is None else float(scale)
     ws = _workspace(decode_workspace_bytes(cache, max_budget_pages), cache.device, workspace)
     _check(lib().spdec_sparse_decode(ctypes.byref(cache.desc), _ptr(q), _ptr(sel_idx), _ptr(sel_cnt),
                                      int(max_budget_pages), scale, _ptr(out), _ptr(lse), _ptr(ws),
@@ -303,7 +309,7 @@ def sparse_decode(cache: PagedCache, q, sel_idx, sel_cnt, max_budget_pages: int,
 def dense_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None, lse=None, workspace=None):
     _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
     out, lse = _outs(cache, out, lse)
-    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    scale = _default_scale(cache) if scale is None else float(scale)
     ws = _workspace(decode_workspace_bytes(cache, 0), cache.device, workspace)
     _check(lib().spdec_dense_decode(ctypes.byref(cache.desc), _ptr(q), scale, _ptr(out), _ptr(lse), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream()), "spdec_dense_decode")
@@ -322,7 +328,7 @@ def dense_decode_shared(cache: PagedCache, q, group_size: int, shared_pages, sca
         raise ValueError("batch must be a multiple of group_size")
     _need(shared_pages, "shared_pages", torch.int32, (cache.batch // int(group_size),))
     out, lse = _outs(cache, out, lse)
-    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    scale = _default_scale(cache) if scale is None else float(scale)
     ws = _workspace(shared_workspace_bytes(cache, group_size), cache.device, workspace)
     _check(lib().spdec_dense_decode_shared(ctypes.byref(cache.desc), _ptr(q), int(group_size), _ptr(shared_pages),
                                            scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
@@ -347,7 +353,7 @@ def verify_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None,
         lse = torch.empty((cache.batch, T, cache.num_q_heads), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, (cache.batch, T, cache.num_q_heads, cache.head_dim))
     _need(lse, "lse", torch.float32, (cache.batch, T, cache.num_q_heads))
-    scale = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    scale = _default_scale(cache) if scale is None else float(scale)
     ws = _workspace(verify_workspace_bytes(cache, T), dev, workspace)
     _check(lib().spdec_verify_decode(ctypes.byref(cache.desc), _ptr(q), T, scale, _ptr(out), _ptr(lse), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream()), "spdec_verify_decode")

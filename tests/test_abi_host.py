@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from sparse_attention_decode_page_amd import spdec as S
@@ -40,7 +41,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 28
+    assert len(names) == len(S.ABI_FUNCTIONS) == 30
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -332,3 +333,18 @@ def test_probe_library_rejects_bad_arguments():
     assert P.spdec_probe_gather(FAKE, None, FAKE, 0, 4096, FAKE, None) == -1     # empty list
     assert P.spdec_probe_gather(FAKE, None, FAKE, 4, 3000, FAKE, None) == -1     # block not a power of two
     assert P.spdec_probe_gather(FAKE, None, FAKE, 4, 256, FAKE, None) == -1      # below 512 bytes
+
+
+def test_default_scales(L):
+    """The library's default softmax scale 1/sqrt(D) and top-p score scale 1/(G sqrt(D)), each the fp32
+    rounding of the fp64 value; 0 for an invalid descriptor."""
+    import math
+    for D, Hq, Hkv in ((128, 8, 2), (64, 32, 4), (128, 8, 8)):
+        d = _desc(head_dim=D, num_q_heads=Hq, num_kv_heads=Hkv)
+        got = L.spdec_default_scale(ctypes.byref(d))
+        assert np.float32(got) == np.float32(1.0 / math.sqrt(D))
+        got = L.spdec_default_score_scale(ctypes.byref(d))
+        assert np.float32(got) == np.float32(1.0 / ((Hq // Hkv) * math.sqrt(D)))
+    bad = _desc(head_dim=96)
+    assert L.spdec_default_scale(ctypes.byref(bad)) == 0.0
+    assert L.spdec_default_score_scale(ctypes.byref(bad)) == 0.0
