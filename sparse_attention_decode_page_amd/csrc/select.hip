@@ -688,17 +688,23 @@ __global__ __launch_bounds__(NT) void select_topp_reg_kernel(CacheView c, const 
     return (unsigned long long)(exp(cs * ((double)s - dm)) * kMassOne + 0.5);
   };
   // Up to 16 keys per thread the masses stay in registers; 32 recompute them
-  // (the same value every time) rather than spill.
+  // (the same value every time) rather than spill. Masses come from the keys
+  // the thread holds (key_score inverts score_key; a zero keeps its mass).
   constexpr bool kKeep = KPT <= 16;
   unsigned long long wf[kKeep ? KPT : 1];
   auto mass_of = [&](int r) -> unsigned long long {
-    if constexpr (kKeep) return wf[r];
-    return i0 + r < M ? fixed_mass(srow[i0 + r + 1]) : 0ull;
+    if constexpr (kKeep) {
+      return wf[r];
+    } else {
+      uint32_t k = key[r];
+      asm volatile("" : "+v"(k));  // computed where it is used, not carried from an earlier loop
+      return i0 + r < M ? fixed_mass(key_score(k)) : 0ull;
+    }
   };
   unsigned long long local = 0;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
-    const unsigned long long m = i0 + r < M ? fixed_mass(srow[i0 + r + 1]) : 0ull;
+    const unsigned long long m = i0 + r < M ? fixed_mass(key_score(key[r])) : 0ull;
     if constexpr (kKeep) wf[r] = m;
     local += m;
   }
