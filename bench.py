@@ -465,6 +465,33 @@ def traffic_sum(traffic, patterns):
     return int(total)
 
 
+def acceptance_ceiling(la, lb, scrubbed, t_call=None):
+    """The read-rate ceiling of the acceptance: the probe streams both logit arrays (contiguous, in 16 KiB
+    blocks) with no arithmetic, after a scrub read like the call."""
+    import torch
+    L = _probe_lib()
+    nbytes = la.numel() * la.element_size()
+    blk = 16384
+    if nbytes % blk or lb.numel() * lb.element_size() != nbytes or not (la.is_contiguous() and lb.is_contiguous()):
+        return None
+    off = torch.arange(nbytes // blk, dtype=torch.int64, device=la.device) * blk
+    sink = torch.zeros(L.spdec_probe_sink_words(), dtype=torch.int32, device=la.device)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe(i=0):
+        rc = L.spdec_probe_gather(la.data_ptr(), lb.data_ptr(), off.data_ptr(), off.numel(), blk, sink.data_ptr(),
+                                  stream)
+        if rc != 0:
+            raise RuntimeError(f"spdec_probe_gather failed ({rc})")
+
+    t = scrubbed(probe)
+    res = dict(_row(t, 2 * nbytes), block_bytes=blk,
+               timing="median of 3 x (K x (1 GiB scrub read, probe) minus K x scrub)")
+    if t_call is not None:
+        res["acceptance_over_ceiling"] = t / t_call
+    return res
+
+
 def _row(t, b):
     return {"us": t * 1e6, "bytes": int(b), "GBps": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBPS}
 
@@ -565,6 +592,8 @@ def layer_rows(args, dev, timers, name, acceptance=False):
                                  mean=float(tail[0]), p5=float(tail[1]),
                                  two_pass_us=t_acc2 * 1e6,
                                  timing="median of 3 x (K x (1 GiB scrub read, call) minus K x scrub)")
+        if not args.no_gather_ceiling:
+            res["acceptance"]["read_ceiling"] = acceptance_ceiling(la, lb, scrubbed, t_acc)
         del la, lb, ws_a
     del cache, q, ws_sel, ws_sp, ws_de, sel_idx, sel_cnt
     torch.cuda.empty_cache()
@@ -970,6 +999,7 @@ def main():
     acc_t = scrubbed(acc)
     acc2_t = scrubbed(lambda i: acc(i, 2))
     acc_warm = timed_loop(acc)
+    acc_ceiling = acceptance_ceiling(la, lb, scrubbed, acc_t) if not args.no_gather_ceiling else None
     # --- the whole step captured once into a HIP graph and replayed K times (each replay appends the same
     # captured token)
     graph = torch.cuda.CUDAGraph()
@@ -1054,6 +1084,7 @@ def main():
                       timing="dense_decode K times back to back, one event pair"),
         "acceptance": dict(_row(acc_t, acc_bytes), traffic=traffic_of(acc_kernels), rows=R, vocab=V,
                            two_pass_us=acc2_t * 1e6, us_no_scrub=acc_warm * 1e6, kernels=" + ".join(acc_kernels),
+                           read_ceiling=acc_ceiling,
                            timing="median of 3 x (K x (1 GiB scrub read, acceptance) minus K x scrub)"),
         "full_step": {"tokens_per_s": spec.batch / full_t, "ms_per_step": full_t * 1e3,
                       "step": "append_kv + select_pages + sparse_decode + dense_decode + acceptance",
