@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--layer", default=None,
                     help="profiling mode: only the layer rows of these comma-separated workloads (sparse path, its "
                          "two calls, dense decode, gather ceiling), one JSON line; no headline value")
+    ap.add_argument("--features", default=None,
+                    help="profiling mode: only these comma-separated next rows (verify, shared, top-p) on their "
+                         "workloads, one JSON line; no headline value")
     ap.add_argument("--no-gather-ceiling", action="store_true",
                     help="skip the gather-read ceiling probe (the sparse path's page and summary gathers, no math)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -325,6 +328,11 @@ def speculative_rows(args, spec, wl, cache, dev, up, timed_loop, lens):
         "verified_tokens_per_s": B * T / t_v,
         "accept_us": t_s * 1e6, "accept_bytes": acc_bytes, "accept_GBps": acc_bytes / t_s / 1e9,
         "mean_kept_drafts": float(kept.mean()),
+        "verify_traffic": traffic_sum(counter_traffic(f"verify_{spec.name}"),
+                                      ["verify_stream_kernel<*,false>", "verify_merge_kernel<*>"]),
+        "accept_traffic": traffic_sum(counter_traffic(f"verify_{spec.name}"),
+                                      ["spec_stats_kernel<*>", "spec_decide_kernel", "spec_chunk_kernel<*>",
+                                       "spec_sample_kernel"]),
         "timing": "each call K times back to back under one event pair",
     }
 
@@ -665,6 +673,7 @@ def shared_prefix_rows(args, dev, timed_loop):
     sum_bytes_s = int((P.sum() - (N - 1) * int(wl.shared_pages.sum())) * per_summary)
     del cache, kmm, q, ws_d, ws_s, ws_sel, ws_sp
     torch.cuda.empty_cache()
+    traffic = counter_traffic(f"shared_{spec.name}")
     return {
         "select_us": t_sel * 1e6, "select_shared_us": t_sel_s * 1e6, "select_speedup": t_sel / t_sel_s,
         "select_summary_bytes": sum_bytes, "select_shared_summary_bytes": sum_bytes_s,
@@ -674,6 +683,10 @@ def shared_prefix_rows(args, dev, timed_loop):
         "shared_us": t_s * 1e6, "shared_bytes": bytes_shared, "shared_GBps": bytes_shared / t_s / 1e9,
         "shared_frac_hbm": bytes_shared / t_s / 1e9 / HBM_PEAK_GBPS, "speedup": t_d / t_s,
         "tokens_per_s": spec.batch / t_s,
+        "dense_traffic": traffic_sum(traffic, ["decode_stream_kernel<128,4,false>", "stream_merge_kernel<128,*,false>"]),
+        "shared_traffic": traffic_sum(traffic, ["verify_stream_kernel<*,true>", "decode_stream_kernel<128,4,false>@suffix",
+                                                "shared_merge_kernel<*>"]),
+        "select_shared_traffic": traffic_sum(traffic, ["score_grouped_kernel<*>", "select_topk_reg_kernel<*>"]),
         "timing": "each call K times back to back under one event pair",
     }
 
@@ -819,6 +832,8 @@ def top_p_rows(spec, cache, q, budget, dev, timed_loop):
                      "max_pages": float(kept.max()), "sparse_path_us": t_path * 1e6}
     del sel_idx, sel_cnt, ws_sel, ws_sp
     torch.cuda.empty_cache()
+    res["select_top_p_traffic"] = traffic_sum(counter_traffic(f"top-p_{spec.name}"),
+                                              ["score_stream_kernel<*>", "select_topp_reg_kernel<*>"])
     res["timing"] = "each call K times back to back under one event pair"
     return res
 
@@ -904,6 +919,22 @@ def main():
     spdec.build_meta(cache)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
+    if args.features:
+        timed_loop, _, _ = make_timers(dev, K_steps)
+        want = set(args.features.split(","))
+        out = {"mode": "features", "steps": K_steps, "env": env_info(torch)}
+        if "verify" in want:
+            out["verify"] = speculative_rows(args, spec, wl, cache, dev, up, timed_loop, wl.lens.astype(np.int64))
+        if "top-p" in want:
+            out["top_p"] = top_p_rows(spec, cache, q, budget, dev, timed_loop)
+        if "shared" in want:
+            del cache, k_pool, v_pool, kminmax
+            torch.cuda.empty_cache()
+            out["shared_prefix"] = shared_prefix_rows(args, dev, timed_loop)
+        if args.copy_probe:
+            out["copy_probe_bytes"] = copy_probe(torch, dev)
+        print(json.dumps(out), flush=True)
+        return
 
     def sel(i=0):
         spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
