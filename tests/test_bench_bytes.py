@@ -50,3 +50,32 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_counter_summaries_parse_and_match_patterns(tmp_path, monkeypatch):
+    """The bench reads a counter summary only while its source hash is current, and a call's kernels are found
+    by name pattern, each pattern matching exactly one kernel."""
+    text = "\n".join([
+        "# header", "```",
+        f"source_hash {bench.kernel_source_hash()}",
+        "traffic_bytes decode_stream_kernel<128,4,true> 1000",
+        "traffic_bytes stream_merge_kernel<128,64,4,true> 20",
+        "traffic_bytes stream_merge_kernel<128,64,4,false> 30",
+        "traffic_bytes decode_stream_kernel<128,4,false>@suffix 7",
+        "```", ""])
+    (tmp_path / "traffic_counters_w.md").write_text(text)
+    (tmp_path / "traffic_counters_stale.md").write_text(text.replace(bench.kernel_source_hash(), "0" * 16))
+    monkeypatch.setattr(bench, "traffic_file", lambda w: str(tmp_path / f"traffic_counters_{w}.md"))
+    t = bench.counter_traffic("w")
+    assert t["decode_stream_kernel<128,4,false>@suffix"] == 7
+    assert bench.traffic_sum(t, ["decode_stream_kernel<128,4,true>", "stream_merge_kernel<128,*,true>"]) == 1020
+    assert bench.traffic_sum(t, ["stream_merge_kernel<128,*>"]) is None          # two kernels match
+    assert bench.traffic_sum(t, ["score_stream_kernel<*>"]) is None              # none matches
+    assert bench.traffic_sum(t, ["decode_stream_kernel<128,4,false>"]) is None   # the suffix pass is apart
+    assert bench.counter_traffic("stale") is None
+    assert bench.counter_traffic("missing") is None
+    spec = S.SPECS["qwen3-1.7b-L16k"]
+    ck = bench.call_kernels(spec)
+    assert ck["sparse_decode"] == ["decode_stream_kernel<128,2,true>", "stream_merge_kernel<128,*,true>"]
+    assert bench.call_kernels(S.custom_spec("g8", num_q_heads=64, num_kv_heads=8, head_dim=128))[
+        "dense_decode"][0] == "decode_stream_g8_kernel<128,false>"
