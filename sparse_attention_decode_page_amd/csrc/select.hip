@@ -24,6 +24,8 @@
 // index order, which is the tie rule.
 #include "common.h"
 #include "launch.h"
+#include "scoring.h"
+#include "topb.h"
 
 namespace spdec {
 
@@ -111,12 +113,6 @@ constexpr int kStreamMinPages = 16;
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const void* __restrict__ qv,
                                                            float* __restrict__ scores) {
-  constexpr int VEC = T::VEC;
-  constexpr int LPT = D / VEC;
-  constexpr int PPI = kWave / LPT;
-  constexpr int BATCH = 4;  // load instructions (pairs) in flight per batch
-  static_assert((BATCH * PPI) <= kWave && kWave % (BATCH * PPI) == 0, "batches tile a page-table window");
-  using S = typename T::storage;
   extern __shared__ int s_pre[];  // units + 1
   __shared__ int s_tmp[256 / kWave];
   const int units = c.batch * c.hkv;
@@ -144,93 +140,12 @@ __global__ __launch_bounds__(256) void score_stream_kernel(CacheView c, const vo
   int pos = (int)(w * R);
   const int end = (int)min<int64_t>(pos + R, total);
   int u = find_unit(s_pre, units, pos);
-  const int sub = lane % LPT;
-  const int d0 = sub * VEC;
-  const S* q = reinterpret_cast<const S*>(qv);
-  const S* mm = reinterpret_cast<const S*>(c.kminmax);
   while (pos < end) {
     while (s_pre[u + 1] <= pos) ++u;  // units with no entry have no segment
-    const int b = u / c.hkv, g = u % c.hkv;
     const int ubase = s_pre[u];
     const int seg_end = min(end, s_pre[u + 1]);
-    float* srow = scores + (int64_t)u * c.max_pages;
-    const int32_t* ptab = c.page_table + (int64_t)b * c.max_pages;
-    // Pages [pb, pe) of this unit's list (pe > pb), in batches of BATCH load
-    // instructions (PPI pages each). Page-table entries come 64 at a time, one
-    // per lane, read at clamped indices so that no load waits on a branch:
-    // win0 holds the current window, win1 the next one (fetched a window ahead).
-    const int pb = pos - ubase, pe = seg_end - ubase;
-    const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
-    auto window_raw = [&](int wi) -> int { return ptab[min(pb + wi * kWave + lane, pe - 1)]; };
-    auto window_of = [&](int wi, int t) -> int {
-      return (pb + wi * kWave + lane < pe && t >= 0 && t < c.num_phys) ? t : -1;
-    };
-    auto fetch_window = [&](int wi) -> int { return window_of(wi, window_raw(wi)); };
-    int raw0 = window_raw(0), raw1 = window_raw(1);
-    // The query group's signed sums (loads in flight with the windows').
-    u32x4 qraw[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) qraw[h] = load16(q + ((int64_t)b * c.hq + g * G + h) * D + d0);
-    hold(raw0);
-    hold(raw1);
-#pragma unroll
-    for (int h = 0; h < G; ++h) hold(qraw[h]);
-    double qpos[VEC], qneg[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) { qpos[e] = 0.0; qneg[e] = 0.0; }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float f[VEC];
-      unpack<T>(qraw[h], f);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        qpos[e] += (double)fmaxf(f[e], 0.f);
-        qneg[e] += (double)fminf(f[e], 0.f);
-      }
-    }
-    int win0 = window_of(0, raw0), win1 = window_of(1, raw1);
-    int cur_win = 0;
-    auto issue = [&](int bt, u32x4* lo, u32x4* hi, int* phys) {
-      const int wi = (bt * BATCH * PPI) / kWave;  // a batch never straddles two windows
-      const int wsrc = wi == cur_win ? win0 : win1;
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int pl = (bt * BATCH + i) * PPI + lane / LPT;  // page offset in the segment
-        phys[i] = __shfl(wsrc, pl & (kWave - 1));
-        const int64_t row = ((int64_t)(phys[i] < 0 ? 0 : phys[i]) * c.hkv + g) * 2 * D + d0;
-        lo[i] = load16_stream(mm + row);
-        hi[i] = load16_stream(mm + row + D);
-      }
-    };
-    u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];
-    int phA[BATCH], phB[BATCH];
-    issue(0, loA, hiA, phA);
-    for (int bt = 0; bt < nbatch; ++bt) {
-      const int wnext = ((bt + 1) * BATCH * PPI) / kWave;
-      if (wnext != cur_win && bt + 1 < nbatch) {  // next batch opens a new window
-        win0 = win1;
-        cur_win = wnext;
-        win1 = fetch_window(wnext + 1);
-      }
-      if (bt + 1 < nbatch) issue(bt + 1, loB, hiB, phB);
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        float fl[VEC], fh[VEC];
-        unpack<T>(loA[i], fl);
-        unpack<T>(hiA[i], fh);
-        double sc = 0.0;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          sc = fma((double)fh[e], qpos[e], sc);
-          sc = fma((double)fl[e], qneg[e], sc);
-        }
-        sc = group_sum<LPT>(sc);
-        const int pl = (bt * BATCH + i) * PPI + lane / LPT;
-        if (sub == 0 && phA[i] >= 0 && pb + pl < pe) srow[pb + pl] = (float)sc;
-      }
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) { loA[i] = loB[i]; hiA[i] = hiB[i]; phA[i] = phB[i]; }
-    }
+    score_segment<T, D, G>(c, qv, u / c.hkv, u % c.hkv, pos - ubase, seg_end - ubase,
+                           scores + (int64_t)u * c.max_pages, lane);
     pos = seg_end;
     ++u;
   }
@@ -463,142 +378,6 @@ __global__ __launch_bounds__(256) void score_grouped_kernel(CacheView c, const v
     }
     pos = seg_end;
     ++u;
-  }
-}
-
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-// Top-B select for P - 2 <= NT * KPT middle pages, one workgroup of NT threads
-// per (sequence, KV head), keys in registers. Thread t holds the keys of
-// middle pages [t*KPT, t*KPT + KPT) (index order, so the compaction emits
-// ascending pages). Radix digits are taken on
-// key - min_key: the span of real scores is a few exponent steps, so the first
-// 8-bit digit already spreads the keys over the histogram and 2-3 passes
-// usually suffice.
-template <int NT>
-struct TopBShared {
-  uint32_t hist[256];
-  uint32_t red[NT / kWave][2];
-  int digit, above;
-  int wave_sums[NT / kWave][2];
-};
-
-// The keys of middle pages 1 .. M (M = P - 2) and their block minimum and
-// significant bit count.
-template <int KPT, int NT>
-__device__ __forceinline__ void load_keys(const float* srow, int M, uint32_t (&key)[KPT], uint32_t& kmin, int& nbits,
-                                          TopBShared<NT>& sh) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int i0 = tid * KPT;
-  kmin = 0xFFFFFFFFu;
-  uint32_t kmax = 0u;
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const int i = i0 + r;
-    key[r] = i < M ? score_key(srow[i + 1]) : 0u;
-    if (i < M) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
-  }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-  }
-  if (lane == 0) { sh.red[wave][0] = kmin; sh.red[wave][1] = kmax; }
-  __syncthreads();
-  kmin = sh.red[0][0];
-  kmax = sh.red[0][1];
-#pragma unroll
-  for (int w = 1; w < NT / kWave; ++w) { kmin = min(kmin, sh.red[w][0]); kmax = max(kmax, sh.red[w][1]); }
-  const uint32_t span = kmax - kmin;
-  nbits = span == 0 ? 0 : 32 - __clz((int)span);
-  __syncthreads();  // red is reused
-}
-
-template <int KPT, int NT>
-__device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M, int need, uint32_t T, int eq_take,
-                                               int32_t* out, TopBShared<NT>& sh);
-
-// Writes the `need` highest keys of the middle pages (equal keys in page
-// order) ascending to out[1 .. need].
-template <int KPT, int NT>
-__device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int need, uint32_t kmin, int nbits,
-                                         int32_t* out, TopBShared<NT>& sh) {
-  const int tid = threadIdx.x;
-  const int i0 = tid * KPT;
-  uint32_t prefix = 0, mask = 0;
-  int remaining = need;
-  for (int hi = nbits; hi > 0; hi -= 8) {
-    const int lo = max(hi - 8, 0);
-    const uint32_t dmask = (1u << (hi - lo)) - 1u;
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const uint32_t off = key[r] - kmin;
-      if (i0 + r < M && (off & mask) == prefix) atomicAdd(&sh.hist[(off >> lo) & dmask], 1u);
-    }
-    __syncthreads();
-    if (tid < kWave) {
-      const int top = 255 - 4 * tid;
-      const int c0 = sh.hist[top], c1 = sh.hist[top - 1], c2 = sh.hist[top - 2], c3 = sh.hist[top - 3];
-      const int tot = c0 + c1 + c2 + c3;
-      const int incl = wave_incl_scan(tot);
-      const int excl = incl - tot;
-      if (excl < remaining && remaining <= incl) {
-        const int rr = remaining - excl;
-        int digit, above;
-        if (rr <= c0) { digit = top; above = excl; }
-        else if (rr <= c0 + c1) { digit = top - 1; above = excl + c0; }
-        else if (rr <= c0 + c1 + c2) { digit = top - 2; above = excl + c0 + c1; }
-        else { digit = top - 3; above = excl + c0 + c1 + c2; }
-        sh.digit = digit;
-        sh.above = above;
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh.digit << lo;
-    mask |= dmask << lo;
-    remaining -= sh.above;
-    __syncthreads();
-  }
-  write_selected<KPT, NT>(key, M, need, kmin + prefix, remaining, out, sh);
-}
-
-// Writes the middle pages with key > T and the first eq_take pages with key
-// == T (page order) ascending to out[1 .. need].
-template <int KPT, int NT>
-__device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M, int need, uint32_t T, int eq_take,
-                                               int32_t* out, TopBShared<NT>& sh) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int i0 = tid * KPT;
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    if (i0 + r < M) { gt += key[r] > T; eq += key[r] == T; }
-  }
-  const int gt_incl = wave_incl_scan(gt);
-  const int eq_incl = wave_incl_scan(eq);
-  if (lane == kWave - 1) { sh.wave_sums[wave][0] = gt_incl; sh.wave_sums[wave][1] = eq_incl; }
-  __syncthreads();
-  int gt_before = gt_incl - gt, eq_before = eq_incl - eq;
-  for (int w = 0; w < wave; ++w) { gt_before += sh.wave_sums[w][0]; eq_before += sh.wave_sums[w][1]; }
-  int pos = 1 + gt_before + min(eq_before, eq_take);
-  int eq_seen = eq_before;
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    if (i0 + r < M) {
-      bool take = key[r] > T;
-      if (key[r] == T) { take = eq_seen < eq_take; ++eq_seen; }
-      if (take && pos <= need) out[pos++] = i0 + r + 1;
-    }
   }
 }
 
