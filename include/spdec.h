@@ -250,6 +250,30 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * spdec_sparse_path - one decode step of the sparse path: spdec_select_pages
+ * then spdec_sparse_decode over the pages it kept (Sparrow project page,
+ * "Control Study 2": score the pages, keep the budgeted Top-k, attend over
+ * the kept KV only).
+ *
+ * Arguments and outputs are those of the two calls: sel_idx, sel_cnt and
+ * scores_out (nullable) as spdec_select_pages writes them, out and lse
+ * (nullable) as spdec_sparse_decode writes them for that selection. For a
+ * bf16 cache with G <= 4, max_pages_per_seq <= 2048, max_budget_pages <=
+ * 2048, batch <= 512 and at least one (sequence, KV head) per compute unit,
+ * the step runs as one kernel, one workgroup per (sequence, KV head), which
+ * keeps scores and the kept list in LDS: the selection is the same (page
+ * indices and scores bit for bit), out and lse differ from the two calls only
+ * by the order in which the kept tokens' partial sums are added (fp32
+ * rounding). Other shapes run the two calls. max_budget_pages >= 2, scale > 0.
+ * Workspace: spdec_sparse_path_workspace_bytes(cache, max_budget_pages).
+ */
+size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
+spdec_status spdec_sparse_path(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
+                               int max_budget_pages, float scale, int32_t* sel_idx, int32_t* sel_cnt,
+                               float* scores_out, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * spdec_dense_decode_shared - spdec_dense_decode for groups of sequences that
  * share their leading pages (a prompt sampled several times; the Sparrow
  * project page's cost model, "Control Study 2", charges the prompt once per

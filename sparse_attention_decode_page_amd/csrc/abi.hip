@@ -194,6 +194,42 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
   return decode_common(cache, q, nullptr, nullptr, 0, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK || max_budget_pages < 2) return 0;
+  return align256(spdec::select_workspace_bytes(v)) +
+         spdec::decode_workspace_bytes(v, spdec::decode_plan(v, max_budget_pages));
+}
+
+spdec_status spdec_sparse_path(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
+                               int max_budget_pages, float scale, int32_t* sel_idx, int32_t* sel_cnt,
+                               float* scores_out, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  CacheView v;
+  spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (!v.k_pool || !v.v_pool || !v.kminmax || !q || !budget_pages || !sel_idx || !sel_cnt || !out)
+    return SPDEC_ERR_INVALID;
+  if (!aligned16(v.k_pool) || !aligned16(v.v_pool) || !aligned16(v.kminmax) || !aligned16(q))
+    return SPDEC_ERR_INVALID;
+  if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return SPDEC_ERR_INVALID;
+  const size_t score_bytes = align256(spdec::select_workspace_bytes(v));
+  const spdec::DecodePlan plan = spdec::decode_plan(v, max_budget_pages);
+  if (workspace == nullptr || workspace_bytes < score_bytes + spdec::decode_workspace_bytes(v, plan))
+    return SPDEC_ERR_WORKSPACE;
+  if (spdec::path_fused_supported(v, max_budget_pages))
+    return from_hip(spdec::launch_sparse_path_fused(v, q, budget_pages, max_budget_pages, scale, sel_idx, sel_cnt,
+                                                    scores_out, out, lse, stream));
+  hipError_t e = spdec::launch_select(v, q, budget_pages, max_budget_pages, sel_idx, sel_cnt, scores_out, workspace,
+                                      stream);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(spdec::launch_decode(v, plan, q, sel_idx, sel_cnt, scale, out, lse,
+                                       static_cast<char*>(workspace) + score_bytes, stream));
+}
+
 size_t spdec_shared_workspace_bytes(const spdec_cache* cache, int group_size) {
   CacheView v;
   if (view_of(cache, &v) != SPDEC_OK || !spdec::shared_supported(v, group_size)) return 0;

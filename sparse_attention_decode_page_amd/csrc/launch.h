@@ -64,6 +64,16 @@ bool select_shared_supported(const CacheView& c, int group_size);
 hipError_t launch_select_shared(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
                                 int group_size, const int32_t* shared_pages, int32_t* sel_idx, int32_t* sel_cnt,
                                 float* scores, void* ws, hipStream_t s);
+// The whole sparse path (scores, Top-B select, attention over the kept pages,
+// merge) in one launch, one workgroup per (sequence, KV head): bf16 caches
+// with G <= 4, at most kPathMaxPages pages per sequence and in the list, at
+// most kPathMaxSeqs sequences, and at least one unit per compute unit.
+constexpr int kPathMaxPages = 2048;
+constexpr int kPathMaxSeqs = 512;
+bool path_fused_supported(const CacheView& c, int max_budget);
+hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
+                                    float scale, int32_t* sel_idx, int32_t* sel_cnt, float* scores, float* out,
+                                    float* lse, hipStream_t s);
 hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float scale, float* out, float* lse, void* ws, hipStream_t s);
 // Dense stream partials over each sequence's pages from first_page[b / group_size]

@@ -1,0 +1,274 @@
+// The sparse path (page scores, Top-B selection, attention over the kept
+// pages, merge) in one kernel, for batches of at least one (sequence, KV head)
+// unit per compute unit.
+//
+// Each workgroup (eight waves) owns one unit and runs every step of it with
+// the intermediate data in LDS: the waves score the unit's pages into LDS
+// (scoring.h), the workgroup selects the Top-B from them (topb.h, ties to the
+// lower index, emitted ascending into an LDS list), the waves split the kept
+// pages and stream them (stream_window.h), and their partials are merged in
+// wave order. No workgroup reads what another wrote, so there is no exchange
+// between workgroups and one launch replaces four. Workgroup i takes the unit
+// of rank i when units are ordered by the bytes they read (largest first,
+// ties to the lower sequence): the dispatcher starts the largest units first
+// and the smaller ones fill the compute units as they free up, and units in
+// different steps keep HBM busy while others are in their latency-bound
+// steps (selection, the first page-table lookups).
+//
+// Scores, selection and the per-chunk softmax arithmetic are those of
+// spdec_select_pages and spdec_sparse_decode; only the split of a unit's
+// kept pages into chunks differs, so outputs agree to rounding.
+#include "common.h"
+#include "launch.h"
+#include "scoring.h"
+#include "stream_window.h"
+#include "topb.h"
+
+namespace spdec {
+
+namespace {
+
+constexpr int kPathThreads = 512;
+constexpr int kPathWaves = kPathThreads / kWave;
+constexpr int kPathKeys = (kPathMaxPages + kPathThreads - 1) / kPathThreads;  // Top-B keys per thread
+
+struct PathArgs {
+  CacheView c;
+  const void* q;
+  const int32_t* budget;
+  int cap;          // max_budget_pages: row stride of sel_idx
+  float qk_scale;   // softmax scale * log2(e)
+  int32_t* sel_idx;
+  int32_t* sel_cnt;
+  float* scores;    // nullable: [batch][Hkv][max_pages]
+  float* out;
+  float* lse;       // nullable
+  int lpt;          // 1: workgroups take units largest first (more units than compute units)
+};
+
+// Pages P and kept pages K of sequence b, and the bytes one of its units
+// reads in units of 4*D bytes (a page summary, or one token's K and V row).
+__device__ __forceinline__ long long path_work(const PathArgs& a, int b, int& P, int& K) {
+  const CacheView& c = a.c;
+  const int L = max(c.seq_lens[b], 0);
+  P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
+  K = min(min(max(a.budget[b], 2), a.cap), P);
+  const bool scored = K < P && K > 2;
+  return (scored ? (long long)P : 0ll) + (long long)min(L, K * c.page_size);
+}
+
+// s_rank[t] = rank of sequence t when sequences are ordered by path_work,
+// largest first, ties to the lower index. The comparisons are split over all
+// threads (parts = kPathThreads / B per sequence) and their counts added in
+// LDS. Ends with a barrier.
+__device__ __forceinline__ void rank_sequences(const PathArgs& a, long long* s_work, int* s_rank) {
+  const int tid = threadIdx.x, B = a.c.batch;
+  for (int t = tid; t < B; t += kPathThreads) {
+    int P, K;
+    s_work[t] = path_work(a, t, P, K);
+    s_rank[t] = 0;
+  }
+  __syncthreads();
+  const int parts = max(1, kPathThreads / B);
+  const int chunk = (B + parts - 1) / parts;
+  for (int i = tid; i < B * parts; i += kPathThreads) {
+    const int t = i % B, part = i / B;
+    const long long wt = s_work[t];
+    const int lo = part * chunk, hi = min(B, lo + chunk);
+    int r = 0;
+#pragma unroll 8
+    for (int t2 = lo; t2 < hi; ++t2) {
+      const long long w2 = s_work[t2];
+      r += (w2 > wt || (w2 == wt && t2 < t)) ? 1 : 0;
+    }
+    if (r != 0) atomicAdd(&s_rank[t], r);
+  }
+  __syncthreads();
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
+  constexpr int NJ = D / 32;
+  constexpr int LPT = D / 8;
+  const CacheView& c = a.c;
+  __shared__ float s_score[kPathMaxPages];
+  __shared__ int s_list[kPathMaxPages];
+  __shared__ int s_ptab[kPathMaxPages];  // the unit's page-table row, when the scoring pass read it
+  __shared__ long long s_work[kPathMaxSeqs];
+  __shared__ int s_rank[kPathMaxSeqs];
+  __shared__ TopBShared<kPathThreads> sh;
+  __shared__ float s_acc[kPathWaves][G][D];
+  __shared__ float s_ml[kPathWaves][G][2];
+  __shared__ int s_seq;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int B = c.batch;
+
+  // The unit: KV head blockIdx % Hkv of the sequence of rank blockIdx / Hkv
+  // (with no more units than compute units every unit starts at once, and the
+  // rank is the sequence index).
+  const int want = blockIdx.x / c.hkv, g = blockIdx.x % c.hkv;
+  if (a.lpt) {
+    rank_sequences(a, s_work, s_rank);
+    for (int t = tid; t < B; t += kPathThreads)
+      if (s_rank[t] == want) s_seq = t;
+  } else if (tid == 0) {
+    s_seq = want;
+  }
+  __syncthreads();
+  const int b = s_seq;
+  const int u = b * c.hkv + g;
+  const int L = max(c.seq_lens[b], 0);
+  int P, K;
+  path_work(a, b, P, K);
+  float* out_rows = a.out + ((int64_t)b * c.hq + g * G) * D;
+  float* lse_rows = a.lse != nullptr ? a.lse + (int64_t)b * c.hq + g * G : nullptr;
+  if (P == 0) {  // no token: no page, zero output, lse = ln 0
+    for (int i = tid; i < G * D; i += kPathThreads) out_rows[i] = 0.f;
+    if (lse_rows != nullptr && tid < G) lse_rows[tid] = -INFINITY;
+    if (tid == 0) a.sel_cnt[u] = 0;
+    return;
+  }
+
+  // Scores of the unit's pages (needed by the select, or asked for).
+  const bool select = K < P && K > 2;
+  if (select || a.scores != nullptr) {
+    const int per = (P + kPathWaves - 1) / kPathWaves;
+    const int p0 = min(P, wave * per), p1 = min(P, p0 + per);
+    if (p0 < p1) score_segment<BF16, D, G>(c, a.q, b, g, p0, p1, s_score, lane, s_ptab);
+  }
+  __syncthreads();
+  if (a.scores != nullptr)
+    for (int i = tid; i < P; i += kPathThreads) a.scores[(int64_t)u * c.max_pages + i] = s_score[i];
+
+  // The kept pages, ascending, into s_list[0 .. K).
+  if (K >= P) {
+    for (int i = tid; i < P; i += kPathThreads) s_list[i] = i;
+  } else {
+    if (tid == 0) {
+      s_list[0] = 0;
+      s_list[K - 1] = P - 1;
+    }
+    if (select) {
+      uint32_t key[kPathKeys], kmin;
+      int nbits;
+      load_keys<kPathKeys, kPathThreads>(s_score, P - 2, key, kmin, nbits, sh);
+      emit_top<kPathKeys, kPathThreads>(key, P - 2, K - 2, kmin, nbits, s_list, sh);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < K; i += kPathThreads) a.sel_idx[(int64_t)u * a.cap + i] = s_list[i];
+  if (tid == 0) a.sel_cnt[u] = K;
+
+  // Attention over the kept pages: wave w streams entries [w*per, (w+1)*per).
+  float m[G], lsum[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegBig;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  const int per = (K + kPathWaves - 1) / kPathWaves;
+  const int e0 = min(K, wave * per), e1 = min(K, e0 + per);
+  if (e0 < e1) {
+    const int r16 = lane % 16, q4 = lane / 16;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
+    u32x4 qa[NJ];  // A operands: row r16 holds query head r16 % G
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+      qa[jj] = load16(qp + ((int64_t)b * c.hq + g * G + r16 % G) * D + 32 * jj + 8 * q4);
+    for (int wb = e0; wb < e1; wb += kWave) {
+      // Window of up to 64 entries: lane i holds entry wb+i's physical page and valid tokens.
+      const int nwin = min(kWave, e1 - wb);
+      const int logical = s_list[min(wb + lane, e1 - 1)];
+      const int ph = select ? s_ptab[logical]
+                            : c.page_table[(int64_t)b * c.max_pages + min(max(logical, 0), c.max_pages - 1)];
+      const bool ok = lane < nwin && logical >= 0 && logical < P && ph >= 0 && ph < c.num_phys;
+      const int phys_w = ok ? ph : 0;
+      const int valid_w = ok ? min(c.page_size, L - logical * c.page_size) : 0;
+      stream_window<D, G>(c, g, nwin, phys_w, valid_w, qa, a.qk_scale, lane, m, lsum, acc);
+    }
+    close_segment<D, G>(lsum, acc);
+  }
+  const int vsub = lane % LPT, vtok = lane / LPT;
+  if (vtok == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * vsub + e] = acc[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_ml[wave][h][0] = m[h];
+      s_ml[wave][h][1] = lsum[h];
+    }
+  }
+  __syncthreads();
+
+  // Merge of the waves' partials in wave order: o = sum_w 2^(m_w - M) acc_w /
+  // sum_w 2^(m_w - M) l_w, lse = ln2 (M + log2 sum_w 2^(m_w - M) l_w).
+  for (int i = tid; i < G * D; i += kPathThreads) {
+    const int h = i / D, d = i % D;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kPathWaves; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    float Ls = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPathWaves; ++w) {
+      const float wt = exp2f(s_ml[w][h][0] - M);
+      Ls = fmaf(wt, s_ml[w][h][1], Ls);
+      o = fmaf(wt, s_acc[w][h][d], o);
+    }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    out_rows[h * D + d] = o * inv;
+    if (lse_rows != nullptr && d == 0) lse_rows[h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t path_launch(const PathArgs& a, hipStream_t s) {
+  const dim3 grid(a.c.batch * a.c.hkv), block(kPathThreads);
+  switch (a.c.group) {
+    case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((sparse_path_kernel<D, 4>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
+}  // namespace
+
+bool path_fused_supported(const CacheView& c, int max_budget) {
+  const int cus = compute_units();
+  return cus > 0 && c.dtype == SPDEC_BF16 && c.group <= 4 && c.max_pages <= kPathMaxPages &&
+         max_budget <= kPathMaxPages && c.batch <= kPathMaxSeqs && (int64_t)c.batch * c.hkv >= cus;
+}
+
+hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
+                                    float scale, int32_t* sel_idx, int32_t* sel_cnt, float* scores, float* out,
+                                    float* lse, hipStream_t s) {
+  PathArgs a;
+  a.c = c;
+  a.q = q;
+  a.budget = budget;
+  a.cap = max_budget;
+  a.qk_scale = scale * kLog2e;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.scores = scores;
+  a.out = out;
+  a.lse = lse;
+  a.lpt = (int64_t)c.batch * c.hkv > compute_units() ? 1 : 0;
+  return c.head_dim == 64 ? path_launch<64>(a, s) : path_launch<128>(a, s);
+}
+
+}  // namespace spdec

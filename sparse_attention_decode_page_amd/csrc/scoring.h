@@ -17,30 +17,34 @@ namespace {
 // One wave scores pages [pb, pe) (pe > pb) of unit (b, g) into srow[pb .. pe)
 // (srow: global or LDS). The summaries are streamed with 16-byte
 // non-temporal loads, PPI pages per load instruction, in batches of BATCH
-// instructions with the next batch in flight; page-table entries come 64 at a
-// time, one per lane, read at clamped indices so that no load waits on a
-// branch, the next window fetched a window ahead and together with the query
-// loads (one wait per segment start).
+// instruction pairs, over windows of 64 pages whose page-table entries come
+// one per lane. Batches alternate between two register sets: the next batch
+// is issued before the current one is used, always (past the segment end the
+// loads read a valid row that is never used), and each window's entries are
+// read two windows ahead, so the loads in flight never sit behind a branch
+// and the wait before a batch covers only that batch's loads. ptab_out
+// (nullable, LDS) receives the segment's page-table entries as read.
 template <typename T, int D, int G>
 __device__ __forceinline__ void score_segment(const CacheView& c, const void* qv, int b, int g, int pb, int pe,
-                                              float* srow, int lane) {
+                                              float* srow, int lane, int* ptab_out = nullptr) {
   constexpr int VEC = T::VEC;
   constexpr int LPT = D / VEC;
   constexpr int PPI = kWave / LPT;
-  constexpr int BATCH = 4;  // load instructions (pairs) in flight per batch
-  static_assert((BATCH * PPI) <= kWave && kWave % (BATCH * PPI) == 0, "batches tile a page-table window");
+  constexpr int BATCH = 4;                  // load instruction pairs per batch
+  constexpr int NBW = kWave / (BATCH * PPI);  // batches per window
+  static_assert(NBW >= 2 && NBW % 2 == 0 && kWave % (BATCH * PPI) == 0, "batches tile a window in pairs");
   using S = typename T::storage;
   const int sub = lane % LPT;
   const int d0 = sub * VEC;
   const S* q = reinterpret_cast<const S*>(qv);
   const S* mm = reinterpret_cast<const S*>(c.kminmax);
   const int32_t* ptab = c.page_table + (int64_t)b * c.max_pages;
-  const int nbatch = (pe - pb + BATCH * PPI - 1) / (BATCH * PPI);
+  const int nwin = (pe - pb + kWave - 1) / kWave;
+  // Page-table entries of window wi, one per lane (index clamped into the segment).
   auto window_raw = [&](int wi) -> int { return ptab[min(pb + wi * kWave + lane, pe - 1)]; };
   auto window_of = [&](int wi, int t) -> int {
     return (pb + wi * kWave + lane < pe && t >= 0 && t < c.num_phys) ? t : -1;
   };
-  auto fetch_window = [&](int wi) -> int { return window_of(wi, window_raw(wi)); };
   int raw0 = window_raw(0), raw1 = window_raw(1);
   // The query group's signed sums (loads in flight with the windows').
   u32x4 qraw[G];
@@ -63,36 +67,23 @@ __device__ __forceinline__ void score_segment(const CacheView& c, const void* qv
       qneg[e] += (double)fminf(f[e], 0.f);
     }
   }
-  int win0 = window_of(0, raw0), win1 = window_of(1, raw1);
-  int cur_win = 0;
-  auto issue = [&](int bt, u32x4* lo, u32x4* hi, int* phys) {
-    const int wi = (bt * BATCH * PPI) / kWave;  // a batch never straddles two windows
-    const int wsrc = wi == cur_win ? win0 : win1;
+  // Batch j of a window: pages (j*BATCH + i)*PPI + lane/LPT of the window, i < BATCH.
+  auto issue = [&](int j, int wv, u32x4* lo, u32x4* hi, int* phys) {
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
-      const int pl = (bt * BATCH + i) * PPI + lane / LPT;  // page offset in the segment
-      phys[i] = __shfl(wsrc, pl & (kWave - 1));
+      phys[i] = __shfl(wv, (j * BATCH + i) * PPI + lane / LPT);
       const int64_t row = ((int64_t)(phys[i] < 0 ? 0 : phys[i]) * c.hkv + g) * 2 * D + d0;
       lo[i] = load16_stream(mm + row);
       hi[i] = load16_stream(mm + row + D);
     }
   };
-  u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];
-  int phA[BATCH], phB[BATCH];
-  issue(0, loA, hiA, phA);
-  for (int bt = 0; bt < nbatch; ++bt) {
-    const int wnext = ((bt + 1) * BATCH * PPI) / kWave;
-    if (wnext != cur_win && bt + 1 < nbatch) {  // next batch opens a new window
-      win0 = win1;
-      cur_win = wnext;
-      win1 = fetch_window(wnext + 1);
-    }
-    if (bt + 1 < nbatch) issue(bt + 1, loB, hiB, phB);
+  auto consume = [&](int wi, int j, const u32x4* lo, const u32x4* hi, const int* phys) {
+    if (pb + wi * kWave + j * BATCH * PPI >= pe) return;  // batch past the segment end
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       float fl[VEC], fh[VEC];
-      unpack<T>(loA[i], fl);
-      unpack<T>(hiA[i], fh);
+      unpack<T>(lo[i], fl);
+      unpack<T>(hi[i], fh);
       double sc = 0.0;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -100,11 +91,32 @@ __device__ __forceinline__ void score_segment(const CacheView& c, const void* qv
         sc = fma((double)fl[e], qneg[e], sc);
       }
       sc = group_sum<LPT>(sc);
-      const int pl = (bt * BATCH + i) * PPI + lane / LPT;
-      if (sub == 0 && phA[i] >= 0 && pb + pl < pe) srow[pb + pl] = (float)sc;
+      const int p = pb + wi * kWave + (j * BATCH + i) * PPI + lane / LPT;
+      if (sub == 0 && phys[i] >= 0 && p < pe) srow[p] = (float)sc;
     }
+  };
+  u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];
+  int phA[BATCH], phB[BATCH];
+  auto keep_window = [&](int wi, int raw) {
+    if (ptab_out != nullptr && pb + wi * kWave + lane < pe) ptab_out[pb + wi * kWave + lane] = raw;
+  };
+  keep_window(0, raw0);
+  int win = window_of(0, raw0);
+  issue(0, win, loA, hiA, phA);
+  for (int wi = 0; wi < nwin; ++wi) {
+    const int raw2 = window_raw(wi + 2);
+    const int win_next = window_of(wi + 1, raw1);  // past the end: no page (-1)
+    keep_window(wi + 1, raw1);
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) { loA[i] = loB[i]; hiA[i] = hiB[i]; phA[i] = phB[i]; }
+    for (int j = 0; j < NBW; j += 2) {
+      issue(j + 1, win, loB, hiB, phB);
+      consume(wi, j, loA, hiA, phA);
+      if (j + 2 < NBW) issue(j + 2, win, loA, hiA, phA);
+      else issue(0, win_next, loA, hiA, phA);
+      consume(wi, j + 1, loB, hiB, phB);
+    }
+    win = win_next;
+    raw1 = raw2;
   }
 }
 

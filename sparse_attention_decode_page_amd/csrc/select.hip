@@ -511,7 +511,8 @@ __global__ __launch_bounds__(NT) void select_topp_reg_kernel(CacheView c, const 
     for (int hi = nbits; hi > 0 && found; hi -= 8) {
       const int lo = max(hi - 8, 0);
       const uint32_t dmask = (1u << (hi - lo)) - 1u;
-      for (int i = tid; i < 256; i += NT) { sh.hist[i] = 0; s_mass[i] = 0ull; }
+      // hist[2]: the Top-B passes below clear it before they use it; load_keys cleared hist[0] for them.
+      for (int i = tid; i < 256; i += NT) { sh.hist[2][i] = 0; s_mass[i] = 0ull; }
       if (tid == 0) s_found = 0;
       __syncthreads();
 #pragma unroll
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(NT) void select_topp_reg_kernel(CacheView c, const 
         const uint32_t off = key[r] - kmin;
         if (i0 + r < M && (off & mask) == prefix) {
           const uint32_t d = (off >> lo) & dmask;
-          atomicAdd(&sh.hist[d], 1u);
+          atomicAdd(&sh.hist[2][d], 1u);
           atomicAdd(&s_mass[d], mass_of(r));
         }
       }
@@ -535,8 +536,8 @@ __global__ __launch_bounds__(NT) void select_topp_reg_kernel(CacheView c, const 
           if (lane >= off) incl += y;
         }
         const unsigned long long excl = incl - tot;
-        const int c0 = sh.hist[top], c1 = sh.hist[top - 1], c2 = sh.hist[top - 2];
-        const int ctot = c0 + c1 + c2 + sh.hist[top - 3];
+        const int c0 = sh.hist[2][top], c1 = sh.hist[2][top - 1], c2 = sh.hist[2][top - 2];
+        const int ctot = c0 + c1 + c2 + sh.hist[2][top - 3];
         const int cincl = wave_incl_scan(ctot);
         const int cexcl = cincl - ctot;
         if (excl < rem && rem <= incl) {

@@ -30,7 +30,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // usually suffice.
 template <int NT>
 struct TopBShared {
-  uint32_t hist[256];
+  uint32_t hist[3][256];  // radix pass p counts into hist[p % 3]
   uint32_t red[NT / kWave][2];
   int digit, above;
   int wave_sums[NT / kWave][2];
@@ -57,6 +57,7 @@ __device__ __forceinline__ void load_keys(const float* srow, int M, uint32_t (&k
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
   }
   if (lane == 0) { sh.red[wave][0] = kmin; sh.red[wave][1] = kmax; }
+  for (int i = tid; i < 256; i += NT) sh.hist[0][i] = 0;  // the first radix pass's counts
   __syncthreads();
   kmin = sh.red[0][0];
   kmax = sh.red[0][1];
@@ -73,48 +74,68 @@ __device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M
 
 // Writes the `need` highest keys of the middle pages (equal keys in page
 // order) ascending to out[1 .. need].
+//
+// One barrier per radix pass: pass p counts into hist[p % 3] while clearing
+// hist[(p + 1) % 3] (last read by pass p - 2's scans, which every wave
+// finished before the barrier of pass p - 1), and after the barrier every
+// wave scans the 256 counts itself, so the cut digit needs no broadcast. The
+// passes stop early once every key left under the resolved prefix is taken.
 template <int KPT, int NT>
 __device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int need, uint32_t kmin, int nbits,
                                          int32_t* out, TopBShared<NT>& sh) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave;
   const int i0 = tid * KPT;
   uint32_t prefix = 0, mask = 0;
   int remaining = need;
-  for (int hi = nbits; hi > 0; hi -= 8) {
+  uint32_t T = kmin;  // cut key: all keys above it are taken, then eq_take keys equal to it
+  int eq_take = 0;
+  int p = 0;
+  for (int hi = nbits; hi > 0; hi -= 8, ++p) {
     const int lo = max(hi - 8, 0);
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-    __syncthreads();
+    uint32_t* H = sh.hist[p % 3];
+    for (int i = tid; i < 256; i += NT) sh.hist[(p + 1) % 3][i] = 0;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const uint32_t off = key[r] - kmin;
-      if (i0 + r < M && (off & mask) == prefix) atomicAdd(&sh.hist[(off >> lo) & dmask], 1u);
+      if (i0 + r < M && (off & mask) == prefix) atomicAdd(&H[(off >> lo) & dmask], 1u);
     }
     __syncthreads();
-    if (tid < kWave) {
-      const int top = 255 - 4 * tid;
-      const int c0 = sh.hist[top], c1 = sh.hist[top - 1], c2 = sh.hist[top - 2], c3 = sh.hist[top - 3];
-      const int tot = c0 + c1 + c2 + c3;
-      const int incl = wave_incl_scan(tot);
-      const int excl = incl - tot;
-      if (excl < remaining && remaining <= incl) {
-        const int rr = remaining - excl;
-        int digit, above;
-        if (rr <= c0) { digit = top; above = excl; }
-        else if (rr <= c0 + c1) { digit = top - 1; above = excl + c0; }
-        else if (rr <= c0 + c1 + c2) { digit = top - 2; above = excl + c0 + c1; }
-        else { digit = top - 3; above = excl + c0 + c1 + c2; }
-        sh.digit = digit;
-        sh.above = above;
-      }
+    // Lane l of every wave holds digits 255-4l .. 252-4l; the cut is the digit
+    // at which the count of higher keys first reaches `remaining`.
+    const int top = 255 - 4 * lane;
+    const int c0 = H[top], c1 = H[top - 1], c2 = H[top - 2], c3 = H[top - 3];
+    const int tot = c0 + c1 + c2 + c3;
+    const int incl = wave_incl_scan(tot);
+    const int excl = incl - tot;
+    const bool mine = excl < remaining && remaining <= incl;
+    int digit = 0, above = 0, cnt = 0;
+    if (mine) {
+      const int rr = remaining - excl;
+      if (rr <= c0) { digit = top; above = excl; cnt = c0; }
+      else if (rr <= c0 + c1) { digit = top - 1; above = excl + c0; cnt = c1; }
+      else if (rr <= c0 + c1 + c2) { digit = top - 2; above = excl + c0 + c1; cnt = c2; }
+      else { digit = top - 3; above = excl + c0 + c1 + c2; cnt = c3; }
     }
-    __syncthreads();
-    prefix |= (uint32_t)sh.digit << lo;
+    const int src = __builtin_ctzll(__ballot(mine));  // exactly one lane: 0 < remaining <= total
+    digit = __shfl(digit, src);
+    above = __shfl(above, src);
+    cnt = __shfl(cnt, src);
+    prefix |= (uint32_t)digit << lo;
     mask |= dmask << lo;
-    remaining -= sh.above;
-    __syncthreads();
+    remaining -= above;
+    if (cnt == remaining && prefix != 0) {
+      // Every key under the prefix is taken: keys >= kmin + prefix, none by tie.
+      T = kmin + prefix - 1u;
+      eq_take = 0;
+      remaining = 0;
+      break;
+    }
+    T = kmin + prefix;
+    eq_take = remaining;
   }
-  write_selected<KPT, NT>(key, M, need, kmin + prefix, remaining, out, sh);
+  if (nbits == 0) eq_take = remaining;  // every key equal: take the first `need` in page order
+  write_selected<KPT, NT>(key, M, need, T, eq_take, out, sh);
 }
 
 // Writes the middle pages with key > T and the first eq_take pages with key

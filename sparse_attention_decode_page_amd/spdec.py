@@ -24,7 +24,8 @@ ABI_FUNCTIONS = (
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
     "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_select_pages_shared", "spdec_select_pages_top_p",
     "spdec_decode_workspace_bytes",
-    "spdec_sparse_decode", "spdec_dense_decode", "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
+    "spdec_sparse_decode", "spdec_sparse_path_workspace_bytes", "spdec_sparse_path", "spdec_dense_decode",
+    "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
     "spdec_spec_accept_workspace_bytes", "spdec_spec_accept", "spdec_acceptance_workspace_bytes",
     "spdec_acceptance", "spdec_acceptance_ex", "spdec_acceptance_noalloc", "spdec_tail_stats",
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         "spdec_select_pages_top_p": (I, [D, P, F, F, P, I, P, P, P, P, SZ, P]),
         "spdec_decode_workspace_bytes": (SZ, [D, I]),
         "spdec_sparse_decode": (I, [D, P, P, P, I, F, P, P, P, SZ, P]),
+        "spdec_sparse_path_workspace_bytes": (SZ, [D, I]),
+        "spdec_sparse_path": (I, [D, P, P, I, F, P, P, P, P, P, P, SZ, P]),
         "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
         "spdec_shared_workspace_bytes": (SZ, [D, I]),
         "spdec_dense_decode_shared": (I, [D, P, I, P, F, P, P, P, SZ, P]),
@@ -304,6 +307,34 @@ def sparse_decode(cache: PagedCache, q, sel_idx, sel_cnt, max_budget_pages: int,
                                      int(max_budget_pages), scale, _ptr(out), _ptr(lse), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream()), "spdec_sparse_decode")
     return out, lse
+
+
+def sparse_path_workspace_bytes(cache: PagedCache, max_budget_pages: int) -> int:
+    return int(lib().spdec_sparse_path_workspace_bytes(ctypes.byref(cache.desc), int(max_budget_pages)))
+
+
+def sparse_path(cache: PagedCache, q, budget_pages, max_budget_pages: int, scale: Optional[float] = None,
+                sel_idx=None, sel_cnt=None, scores_out=None, out=None, lse=None, workspace=None):
+    """One sparse decode step (select_pages, then sparse_decode over the kept pages) through spdec_sparse_path.
+    Returns (out, lse, sel_idx, sel_cnt)."""
+    _need(q, "q", cache.dtype, (cache.batch, cache.num_q_heads, cache.head_dim))
+    _need(budget_pages, "budget_pages", torch.int32, (cache.batch,))
+    dev = cache.device
+    if sel_idx is None:
+        sel_idx = torch.zeros((cache.batch, cache.num_kv_heads, max_budget_pages), dtype=torch.int32, device=dev)
+    if sel_cnt is None:
+        sel_cnt = torch.zeros((cache.batch, cache.num_kv_heads), dtype=torch.int32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, (cache.batch, cache.num_kv_heads, max_budget_pages))
+    _need(sel_cnt, "sel_cnt", torch.int32, (cache.batch, cache.num_kv_heads))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.float32, (cache.batch, cache.num_kv_heads, cache.max_pages))
+    out, lse = _outs(cache, out, lse)
+    scale = _default_scale(cache) if scale is None else float(scale)
+    ws = _workspace(sparse_path_workspace_bytes(cache, max_budget_pages), dev, workspace)
+    _check(lib().spdec_sparse_path(ctypes.byref(cache.desc), _ptr(q), _ptr(budget_pages), int(max_budget_pages),
+                                   scale, _ptr(sel_idx), _ptr(sel_cnt), _ptr(scores_out), _ptr(out), _ptr(lse),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream()), "spdec_sparse_path")
+    return out, lse, sel_idx, sel_cnt
 
 
 def dense_decode(cache: PagedCache, q, scale: Optional[float] = None, out=None, lse=None, workspace=None):

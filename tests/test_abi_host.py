@@ -41,7 +41,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 30
+    assert len(names) == len(S.ABI_FUNCTIONS) == 32
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -113,6 +113,32 @@ def test_budget_scale_and_workspace_checks(L):
     assert L.spdec_dense_decode(ctypes.byref(d), FAKE, 0.1, FAKE, None, FAKE, dw - 1, None) == -3
     assert L.spdec_sparse_decode(ctypes.byref(d), FAKE, FAKE, FAKE, 16, 0.1, FAKE, None, FAKE, sw - 1, None) == -3
     assert L.spdec_sparse_decode(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 0.1, FAKE, None, FAKE, sw, None) == -1
+
+
+def test_sparse_path_checks(L):
+    d = _desc()
+    sp = L.spdec_sparse_path
+    need = L.spdec_sparse_path_workspace_bytes(ctypes.byref(d), 16)
+    # scores (rounded up to 256 bytes) ahead of the decode's workspace: what the two calls it stands for need
+    sel = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
+    assert need == (sel + 255) // 256 * 256 + L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
+    assert L.spdec_sparse_path_workspace_bytes(ctypes.byref(d), 1) == 0
+    assert L.spdec_sparse_path_workspace_bytes(None, 16) == 0
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("desc", ctypes.byref(d)), ("q", FAKE), ("budget", FAKE), ("cap", 16), ("scale", 0.1), ("idx", FAKE),
+        ("cnt", FAKE), ("scores", None), ("out", FAKE), ("lse", None), ("ws", FAKE), ("wsb", need), ("s", None))]
+    assert sp(*args(cap=1)) == -1
+    assert sp(*args(scale=0.0)) == -1
+    assert sp(*args(scale=float("inf"))) == -1
+    assert sp(*args(budget=None)) == -1
+    assert sp(*args(idx=None)) == -1
+    assert sp(*args(out=None)) == -1
+    assert sp(*args(q=FAKE + 4)) == -1
+    assert sp(*args(wsb=need - 1)) == -3
+    assert sp(*args(ws=None)) == -3
+    assert sp(*args(desc=None)) == -1
+    bad = _desc(head_dim=96)
+    assert sp(*args(desc=ctypes.byref(bad))) == S.SPDEC_ERR_UNSUPPORTED
 
 
 def test_acceptance_checks(L):

@@ -1,0 +1,220 @@
+"""GPU: spdec_sparse_path (one decode step: page selection, then attention over the kept pages) against the two
+calls it stands for and against the CPU oracle.
+
+Batches with at least one (sequence, KV head) per compute unit run the step as one kernel; the selection it writes
+(sel_idx, sel_cnt, scores) must equal spdec_select_pages' bit for bit, and out / lse must agree with
+spdec_sparse_decode over that selection to fp32 rounding of a different summation order (3e-6 max-abs; both are
+within the oracle's bf16 bar of 1e-2, checked per unit). Smaller batches run the two calls, so every output is
+bitwise equal.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_decode_page_amd import spdec
+from sparse_attention_decode_page_amd import synth as S
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import gpu_support as GS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+# Bar between the one-kernel step and the two calls: both accumulate the same fp32 terms (p_t v_t, e^{z_t}) per
+# token; only the grouping of the per-chunk sums differs. Outputs are convex combinations of bf16 values ~N(0,1)
+# (|v| < 6), so a few ulps of 6 plus the relative error of the normaliser bound the difference.
+TOL_SPLIT = 3e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(spdec.LIB_PATH):
+        from sparse_attention_decode_page_amd import build
+        build.build()
+    spdec.lib()
+    assert torch.cuda.is_available()
+
+
+def _fused(dw) -> bool:
+    """The documented rule under which spdec_sparse_path runs as one kernel."""
+    c = dw.cache
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (c.dtype == torch.bfloat16 and c.num_q_heads // c.num_kv_heads <= 4 and c.max_pages <= 2048
+            and dw.max_budget <= 2048 and c.batch <= 512 and c.batch * c.num_kv_heads >= cus)
+
+
+def _run(wl, units, max_budget=None, expect_fused=None):
+    spec = wl.spec
+    dw = GS.DeviceWorkload(wl)
+    if max_budget is not None:
+        dw.max_budget = max_budget
+    c = dw.cache
+    spdec.build_meta(c)
+    fused = _fused(dw)
+    if expect_fused is not None:
+        assert fused == expect_fused
+    # the two calls
+    scores_a = torch.zeros((c.batch, c.num_kv_heads, c.max_pages), dtype=torch.float32, device=c.device)
+    idx_a, cnt_a = spdec.select_pages(c, dw.q, dw.budget, dw.max_budget, scores_out=scores_a)
+    out_a, lse_a = spdec.sparse_decode(c, dw.q, idx_a, cnt_a, dw.max_budget)
+    # the step; output buffers poisoned so that a missed write shows
+    scores_b = torch.full_like(scores_a, float("nan"))
+    idx_b = torch.full_like(idx_a, -7)
+    cnt_b = torch.full_like(cnt_a, -7)
+    out_b = torch.full_like(out_a, float("nan"))
+    lse_b = torch.full_like(lse_a, float("nan"))
+    spdec.sparse_path(c, dw.q, dw.budget, dw.max_budget, sel_idx=idx_b, sel_cnt=cnt_b, scores_out=scores_b,
+                      out=out_b, lse=lse_b)
+    torch.cuda.synchronize()
+    cnt_a_h, cnt_b_h = cnt_a.cpu().numpy(), cnt_b.cpu().numpy()
+    idx_a_h, idx_b_h = idx_a.cpu().numpy(), idx_b.cpu().numpy()
+    sa, sb = scores_a.cpu().numpy(), scores_b.cpu().numpy()
+    assert np.array_equal(cnt_a_h, cnt_b_h)
+    for b in range(spec.batch):
+        P = wl.pages(b)
+        assert np.array_equal(sa[b, :, :P].view(np.uint32), sb[b, :, :P].view(np.uint32)), b
+        for g in range(spec.num_kv_heads):
+            k = int(cnt_a_h[b, g])
+            assert np.array_equal(idx_a_h[b, g, :k], idx_b_h[b, g, :k]), (b, g)
+    oa, ob = out_a.cpu().numpy(), out_b.cpu().numpy()
+    la, lb = lse_a.cpu().numpy(), lse_b.cpu().numpy()
+    assert np.all(np.isfinite(ob))
+    live = wl.lens > 0
+    assert np.array_equal(np.isneginf(la), np.isneginf(lb))
+    assert np.all(np.isneginf(lb[~live])) and np.all(ob[~live] == 0)
+    d_out = float(np.abs(oa - ob).max())
+    d_lse = float(np.abs(la[live] - lb[live]).max()) if live.any() else 0.0
+    if fused:
+        assert d_out <= TOL_SPLIT and d_lse <= TOL_SPLIT, (d_out, d_lse)
+    else:
+        assert d_out == 0.0 and d_lse == 0.0, (d_out, d_lse)
+    # the oracle, unit by unit, over the step's own selection
+    tol = GS.TOL_OUT[spec.dtype]
+    scale = GS.default_scale(wl)
+    G = spec.group
+    worst = 0.0
+    for (b, g) in units:
+        P = wl.pages(b)
+        K64, V64 = GS.unit_kv_f64(wl, b, g)
+        s64 = GS.oracle_scores(wl, b, g, K64)
+        k = int(cnt_b_h[b, g])
+        GS.check_selection(idx_b_h[b, g], k, s64, int(wl.budget_pages[b]), dw.max_budget)
+        o, lse = O.decode_unit(GS.q_group_f64(wl, b, g), K64, V64, idx_b_h[b, g, :k], spec.page_size, scale)
+        e = float(np.abs(ob[b, g * G:(g + 1) * G] - o).max())
+        el = float(np.abs(lb[b, g * G:(g + 1) * G] - lse).max()) if P else 0.0
+        assert e <= tol and el <= tol, (b, g, e, el)
+        worst = max(worst, e, el)
+    say(f"  {spec.name}: fused={fused} step vs calls out {d_out:.2e} lse {d_lse:.2e}; "
+        f"{len(units)} units vs oracle, worst {worst:.2e}")
+    return dw
+
+
+def _lens(seed, n, lo, hi, zeros=0):
+    r = np.random.default_rng(seed)
+    lens = [int(x) for x in r.integers(lo, hi + 1, n)]
+    for i in range(zeros):
+        lens[(7 * i + 3) % n] = 0
+    return lens
+
+
+# dtype D, Hq, Hkv, ps, batch, (lo, hi) tokens, budget pages (lo, hi), zero-length sequences
+CASES = [
+    ("D128 G4 ps16", 128, 32, 8, 16, 40, (1, 6000), (0, 90), 3),
+    ("D128 G2 ps32", 128, 16, 8, 32, 36, (1, 9000), (0, 60), 2),
+    ("D64 G1 ps8", 64, 8, 8, 8, 34, (1, 16384), (0, 300), 2),
+    ("D64 G4 ps64", 64, 16, 4, 64, 70, (1, 20000), (0, 40), 4),
+    ("D128 G1 ps16", 128, 8, 8, 16, 33, (2000, 32768), (100, 400), 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_step_matches_calls_and_oracle(case):
+    name, D, Hq, Hkv, ps, B, (lo, hi), (blo, bhi), zeros = CASES[case]
+    lens = _lens(case, B, lo, hi, zeros)
+    bud = [int(x) for x in np.random.default_rng(100 + case).integers(blo, bhi + 1, B)]
+    say(f"case path {name}: batch {B}, lens {lo}..{hi} ({zeros} empty), budget pages {blo}..{bhi}")
+    spec = S.custom_spec(f"path-{case}", batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                         dtype="bf16", lens=("list", lens), budget=("pages", bud), outlier_channels=4)
+    wl = S.make_workload(spec, seed=case)
+    _run(wl, GS.sample_units(wl, 40, seed=case), expect_fused=True)
+
+
+def test_step_longest_lists():
+    """2048 pages per sequence (the one-kernel form's limit): budgets that keep every page, all but one (the
+    Top-B over 2046 middle pages), two (sink and local only) and a list capacity of 2048."""
+    B = 32
+    bud = [2048, 2047, 2, 1000] * (B // 4)
+    say("case path longest lists: 32 x 8 units of 2048 pages, capacity 2048")
+    spec = S.custom_spec("path-longest", batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("fixed", 32768), budget=("pages", bud), outlier_channels=4)
+    wl = S.make_workload(spec, seed=21)
+    assert wl.page_table.shape[1] == 2048
+    _run(wl, [(0, 0), (1, 3), (2, 5), (3, 7), (29, 1), (31, 6)], expect_fused=True)
+
+
+def test_step_capacity_two():
+    """A list capacity of 2: every unit keeps its sink and local pages only (no select)."""
+    B = 40
+    say("case path capacity 2")
+    spec = S.custom_spec("path-cap2", batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("list", _lens(9, B, 1, 3000, 2)), budget=("pages", [50] * B),
+                         outlier_channels=4)
+    wl = S.make_workload(spec, seed=9)
+    _run(wl, GS.sample_units(wl, 20, seed=9), max_budget=2, expect_fused=True)
+
+
+@pytest.mark.parametrize("what", ["few units", "f32", "G8", "long tables"])
+def test_step_runs_the_two_calls_elsewhere(what):
+    """Shapes outside the one-kernel form: the step is the two calls, bit for bit."""
+    kw = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype="bf16",
+              lens=("uniform", 100, 5000), budget=("pages", [3, 20, 40, 80]), outlier_channels=4)
+    if what == "f32":
+        kw.update(batch=40, dtype="f32", outlier_channels=0, budget=("pages", [20] * 40))
+    elif what == "G8":
+        kw.update(batch=40, num_q_heads=64, budget=("pages", [20] * 40))
+    elif what == "long tables":
+        kw.update(batch=40, lens=("uniform", 30000, 40000), budget=("pages", [100] * 40))
+    say(f"case path fallback: {what}")
+    wl = S.make_workload(S.custom_spec(f"path-fb-{what}", **kw), seed=5)
+    _run(wl, GS.sample_units(wl, 8, seed=5), expect_fused=False)
+
+
+FULL = ["qwen3-8b-ragged", "qwen3-1.7b-L16k", "qwen3-8b-L32k-acceptance"]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", FULL)
+def test_step_full_size(name):
+    """The full-size workloads that take the one-kernel form: every unit against the two calls, sampled units
+    against the oracle."""
+    say(f"case path full-size {name}: generating")
+    wl = S.make_workload(name, seed=0, build_pool=True)
+    _run(wl, GS.sample_units(wl, 24, seed=3), expect_fused=True)
+    torch.cuda.empty_cache()
+
+
+def test_step_repeat_is_bitwise():
+    """Two steps on the same inputs write the same bits (no atomics, fixed orders)."""
+    B = 40
+    spec = S.custom_spec("path-repeat", batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("list", _lens(31, B, 1, 8000, 1)),
+                         budget=("pages", [int(x) for x in np.random.default_rng(32).integers(0, 200, B)]),
+                         outlier_channels=4)
+    wl = S.make_workload(spec, seed=31)
+    dw = GS.DeviceWorkload(wl)
+    spdec.build_meta(dw.cache)
+    say("case path repeat")
+    r1 = [t.clone() for t in spdec.sparse_path(dw.cache, dw.q, dw.budget, dw.max_budget)]
+    r2 = spdec.sparse_path(dw.cache, dw.q, dw.budget, dw.max_budget)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
