@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: query-aware page-sparse decode attention on one GPU.
 
-The timed step is the sparse path of one decode layer: select_pages (Quest-style
-page bounds over the page summaries, Top-B with sink and local pages) then
-sparse_decode (split-KV attention over the kept pages, LSE merge), on a batch
+The timed step is the sparse path of one decode layer, spdec_sparse_path: page
+scores (Quest-style bounds over the page summaries), Top-B with sink and local
+pages, attention over the kept pages with an LSE merge (one kernel on this
+workload; select_pages then sparse_decode where that form does not apply), on a batch
 shaped like a Qwen3-8B decode layer with ragged 8K-32K contexts (64 sequences,
 32 query / 8 KV heads, head dim 128, page size 16, budgets 1024-4096 tokens
 linear in length). Inputs are seeded synthetic data, resident in HBM before
@@ -14,9 +15,10 @@ the path's time, each of K runs after a 1 GiB scrub read (so neither L2 nor
 the last-level cache holds the previous run's pages) with the K scrubs' own
 time subtracted, the median of three interleaved regions. `sparse` gives its
 effective KV GB/s (selected K/V plus every page summary, valid tokens only)
-and fraction of 8 TB/s, and its two calls apart; `roofline` is for the
-dominant kernel, the sparse_decode call. `full_step` times the whole hot path
-(append_kv, select_pages, sparse_decode, dense_decode, acceptance over 64 x
+and fraction of 8 TB/s, and the same step as the two calls select_pages and
+sparse_decode, each also apart; `roofline` is for the dominant kernel, the
+step's one kernel. `full_step` times the whole hot path
+(append_kv, sparse_path, dense_decode, acceptance over 64 x
 151936 logit rows) back to back, with a per-row breakdown and HIP-graph
 replay. `dense` and `acceptance` time those calls alone; `qwen3_1_7b`,
 `long_context` (4 sequences of 131072 tokens at page sizes 8/16/32/64) and
@@ -91,10 +93,12 @@ def algorithmic_bytes(spec, lens, budget_pages, cap, rows, vocab):
     sel_tokens = np.where(K >= P, L, (K - 1) * ps + last)
     kv_tok = 2 * D * elt                      # K + V row of one token, one KV head
     meta_page = 2 * D * elt                   # kmin + kmax of one page, one KV head
+    scored = (K < P) & (K > 2)                # the step scores only units whose selection is not fixed
     return {
         "append_kv": int(spec.batch * Hkv * (kv_tok + 2 * meta_page)),
         "select_pages": int(Hkv * (P * meta_page).sum()),
         "sparse_decode": int(Hkv * (sel_tokens * kv_tok).sum()),
+        "sparse_path": int(Hkv * (np.where(scored, P * meta_page, 0) + sel_tokens * kv_tok).sum()),
         "dense_decode": int(Hkv * (L * kv_tok).sum()),
         "acceptance": int(2 * rows * vocab * 4),
     }
@@ -107,7 +111,8 @@ def traffic_file(workload: str) -> str:
 # The measured kernels (dense and sparse decode, scoring, top-B, acceptance) and
 # their launch configuration (plans, resident grid); a change to any of these
 # invalidates the recorded counter traffic.
-KERNEL_SOURCES = ("common.h", "decode.hip", "select.hip", "grid.hip", "acceptance.hip")
+KERNEL_SOURCES = ("common.h", "decode.hip", "select.hip", "grid.hip", "acceptance.hip", "path.hip", "scoring.h",
+                  "topb.h", "stream_window.h")
 
 
 def describe_lens(spec) -> str:
@@ -389,7 +394,7 @@ def _probe_lib():
     return L
 
 
-def gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_select=None, t_decode=None):
+def gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_select=None, t_decode=None, t_path=None):
     """The gather-read ceiling of the sparse path's two streams on this cache: a kernel with the stream
     kernels' access pattern and no arithmetic (libspdec_probe.so) reads (a) the kept pages' K and V blocks, in
     the decode's order, and (b) every page's summary, in the scoring pass's order; each timed like the calls
@@ -431,19 +436,25 @@ def gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_select=None, t_dec
         res["sparse_decode_over_ceiling"] = t_kv / t_decode
     if t_select is not None:
         res["select_pages_over_ceiling"] = t_sm / t_select
+    if t_path is not None:
+        res["sparse_path_over_ceiling"] = (t_kv + t_sm) / t_path
     del kv_off, sm_off, sink
     return res
 
 
-def call_kernels(spec):
+def call_kernels(spec, fused=True):
     """Name patterns (over the counter summaries' kernel names) of the kernels each call launches on a bf16
-    workload of this shape; the merge's form and the Top-B's size class depend on the workload."""
+    workload of this shape; the merge's form and the Top-B's size class depend on the workload, the step's
+    form (one kernel or the two calls) on the batch."""
     D, G = spec.head_dim, spec.group
     dec = (lambda sp: f"decode_stream_g8_kernel<{D},{sp}>") if G == 8 else \
         (lambda sp: f"decode_stream_kernel<{D},{G},{sp}>")
-    return {"select_pages": [f"score_stream_kernel<BF16,{D},{G}>", "select_topk_reg_kernel<*>"],
-            "sparse_decode": [dec("true"), f"stream_merge_kernel<{D},*,true>"],
-            "dense_decode": [dec("false"), f"stream_merge_kernel<{D},*,false>"]}
+    calls = {"select_pages": [f"score_stream_kernel<BF16,{D},{G}>", "select_topk_reg_kernel<*>"],
+             "sparse_decode": [dec("true"), f"stream_merge_kernel<{D},*,true>"],
+             "dense_decode": [dec("false"), f"stream_merge_kernel<{D},*,false>"]}
+    calls["sparse_path"] = [f"sparse_path_kernel<{D},{G},*>"] if fused else \
+        calls["select_pages"] + calls["sparse_decode"]
+    return calls
 
 
 def copy_probe(torch, dev):
@@ -537,8 +548,13 @@ def layer_rows(args, dev, timers, name, acceptance=False):
     ws_sel = torch.zeros(spdec.select_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
     ws_sp = torch.zeros(spdec.decode_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
     ws_de = torch.zeros(spdec.decode_workspace_bytes(cache, 0), dtype=torch.uint8, device=dev)
+    ws_path = torch.zeros(spdec.sparse_path_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
     o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
+    fused = spdec.sparse_path_fused(cache, cap)
+
+    def path(i=0):
+        spdec.sparse_path(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, out=o, lse=lse, workspace=ws_path)
 
     def sel(i=0):
         spdec.select_pages(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
@@ -550,20 +566,24 @@ def layer_rows(args, dev, timers, name, acceptance=False):
         spdec.dense_decode(cache, q, out=o, lse=lse, workspace=ws_de)
 
     for _ in range(3):
+        path()
         sel()
         dec()
         dense()
-    t_path = scrubbed(lambda i: (sel(), dec()))
+    t_path = scrubbed(path)
+    t_two = scrubbed(lambda i: (sel(), dec()))
     t_sel = scrubbed(sel)
     t_dec = scrubbed(dec)
     t_dense = timed_loop(dense)
     byt = algorithmic_bytes(spec, wl.lens, wl.budget_pages, cap, 0, 0)
-    b_path = byt["select_pages"] + byt["sparse_decode"]
+    b_path = byt["sparse_path"]
     res = {
         "workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads, "kv_heads": spec.num_kv_heads,
         "head_dim": spec.head_dim, "page_size": spec.page_size, "context": describe_lens(spec),
         "budget": describe_budget(spec),
-        "sparse_path": dict(_row(t_path, b_path), tokens_per_s=spec.batch / t_path),
+        "sparse_path": dict(_row(t_path, b_path), tokens_per_s=spec.batch / t_path,
+                            form="one kernel" if fused else "select_pages + sparse_decode"),
+        "two_calls": dict(_row(t_two, b_path), tokens_per_s=spec.batch / t_two),
         "select_pages": _row(t_sel, byt["select_pages"]),
         "sparse_decode": _row(t_dec, byt["sparse_decode"]),
         "dense_decode": dict(_row(t_dense, byt["dense_decode"]), tokens_per_s=spec.batch / t_dense),
@@ -572,14 +592,14 @@ def layer_rows(args, dev, timers, name, acceptance=False):
                   "to back",
     }
     traffic = counter_traffic(spec.name)
-    ck = call_kernels(spec)
-    for call in ("select_pages", "sparse_decode", "dense_decode"):
+    ck = call_kernels(spec, fused)
+    for call in ("sparse_path", "select_pages", "sparse_decode", "dense_decode"):
         res[call]["traffic"] = traffic_sum(traffic, ck[call])
-    res["sparse_path"]["traffic"] = traffic_sum(traffic, ck["select_pages"] + ck["sparse_decode"])
+    res["two_calls"]["traffic"] = traffic_sum(traffic, ck["select_pages"] + ck["sparse_decode"])
     res["kernels"] = ck
     if not args.no_gather_ceiling:
         sel()
-        res["gather_ceiling"] = gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_sel, t_dec)
+        res["gather_ceiling"] = gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_sel, t_dec, t_path)
     if acceptance:
         la = torch.from_numpy(wl.logits_a).to(dev)
         lb = torch.from_numpy(wl.logits_b).to(dev)
@@ -603,7 +623,7 @@ def layer_rows(args, dev, timers, name, acceptance=False):
         if not args.no_gather_ceiling:
             res["acceptance"]["read_ceiling"] = acceptance_ceiling(la, lb, scrubbed, t_acc)
         del la, lb, ws_a
-    del cache, q, ws_sel, ws_sp, ws_de, sel_idx, sel_cnt
+    del cache, q, ws_sel, ws_sp, ws_de, ws_path, sel_idx, sel_cnt
     torch.cuda.empty_cache()
     return res
 
@@ -691,7 +711,7 @@ def shared_prefix_rows(args, dev, timed_loop):
     }
 
 
-def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap, timed_loop):
+def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_path, cap, timed_loop):
     """Closed loop of the sparsity-schedule controller on the device: budgets -> selection -> sparse decode ->
     a seeded random LM head (the plant stand-in: no model weights) -> acceptance against the dense output's
     logits -> streaming tail monitor over the last steps' tokens -> controller -> budgets, with no host round
@@ -722,8 +742,7 @@ def budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_
     def control_step(k):
         spdec.budget_update(tails[k], scale, cache.seq_lens, prm, budget_pages=bud)
         buds[k].copy_(bud)
-        spdec.select_pages(cache, q, bud, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, workspace=ws_sel)
-        spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
+        spdec.sparse_path(cache, q, bud, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, out=o_s, lse=l_s, workspace=ws_path)
         torch.matmul(o_s.reshape(B, H), w_lm, out=logit_s)
         spdec.acceptance(logit_s, logit_d, 1.0, alpha=al, workspace=ws_a)
         mon.append(al)
@@ -911,6 +930,7 @@ def main():
     ws_sel = torch.zeros(spdec.select_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
     ws_sp = torch.zeros(spdec.decode_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
     ws_de = torch.zeros(spdec.decode_workspace_bytes(cache, 0), dtype=torch.uint8, device=dev)
+    ws_path = torch.zeros(spdec.sparse_path_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
     ws_acc = torch.zeros(spdec.acceptance_workspace_bytes(R, V), dtype=torch.uint8, device=dev)
     o_s = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
     l_s = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
@@ -942,7 +962,13 @@ def main():
     def dec(i=0):
         spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
 
+    fused = spdec.sparse_path_fused(cache, cap)
+
     def sparse_path(i=0):
+        spdec.sparse_path(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, out=o_s, lse=l_s,
+                          workspace=ws_path)
+
+    def two_calls(i=0):
         sel()
         dec()
 
@@ -952,7 +978,7 @@ def main():
     def acc(i=0, path=-1):
         spdec.acceptance_ex(la, lb, spec.temperature, alpha=alpha, workspace=ws_acc, force_path=path)
 
-    rows = ["append_kv", "select_pages", "sparse_decode", "dense_decode", "acceptance"]
+    rows = ["append_kv", "sparse_path", "dense_decode", "acceptance"]
     row_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)] for _ in range(K_steps)]
 
     def step(i, events=None):
@@ -960,14 +986,12 @@ def main():
         rec(0)
         spdec.append_kv(cache, k_new[i], v_new[i])
         rec(1)
-        sel()
+        sparse_path()
         rec(2)
-        dec()
-        rec(3)
         dense()
-        rec(4)
+        rec(3)
         spdec.acceptance(la, lb, spec.temperature, alpha=alpha, workspace=ws_acc)
-        rec(5)
+        rec(4)
 
     for i in range(W):
         step(i)
@@ -976,22 +1000,24 @@ def main():
     timers = make_timers(dev, K_steps)
     timed_loop, scrubbed, _ = timers
 
-    # --- value: the sparse path (select_pages + sparse_decode) on the cache as it stands, each of K runs after a
-    # 1 GiB scrub read, the K scrubs' own time subtracted; three interleaved regions, median.
+    # --- value: the sparse path (spdec_sparse_path) on the cache as it stands, each of K runs after a 1 GiB scrub
+    # read, the K scrubs' own time subtracted; three interleaved regions, median. Then the same step as its two
+    # calls, and each call apart.
     lens_sparse = wl.lens.astype(np.int64) + appended
     t0 = time.perf_counter()
     value_runs = []
     sp_t = scrubbed(sparse_path, reps=3, runs=value_runs)
     wall = time.perf_counter() - t0
+    two_t = scrubbed(two_calls)
     sel_t = scrubbed(sel)
     dec_t = scrubbed(dec)
     sp_t_warm = timed_loop(sparse_path)
     ceiling = None
     if not args.no_gather_ceiling:
         sel()
-        ceiling = gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, sel_t, dec_t)
+        ceiling = gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, sel_t, dec_t, sp_t)
     byt_sp = algorithmic_bytes(spec, lens_sparse, wl.budget_pages, cap, R, V)
-    sp_b = byt_sp["select_pages"] + byt_sp["sparse_decode"]
+    sp_b = byt_sp["sparse_path"]
     value = spec.batch / sp_t
 
     # --- the whole hot path (all five rows) back to back, K steps under one event pair; then K steps with an
@@ -1052,9 +1078,9 @@ def main():
         if not args.no_verify else None
     topp = top_p_rows(spec, cache, q, budget, dev, timed_loop) if not args.no_top_p else None
     monitor = monitor_rows(args, dev, timed_loop) if not args.no_control else None
-    control = budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_sel, ws_sp, cap,
+    control = budget_control_rows(args, spec, cache, q, dev, sel_idx, sel_cnt, ws_path, cap,
                                   timed_loop) if not args.no_control else None
-    del cache, k_pool, v_pool, kminmax, k_new, v_new, ws_sp, ws_de, ws_sel
+    del cache, k_pool, v_pool, kminmax, k_new, v_new, ws_sp, ws_de, ws_sel, ws_path
     torch.cuda.empty_cache()
     shared = shared_prefix_rows(args, dev, timed_loop) if not args.no_shared else None
     shape2 = layer_rows(args, dev, timers, "qwen3-1.7b-L16k") if not args.no_second_shape else None
@@ -1066,8 +1092,9 @@ def main():
 
     # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
     traffic = counter_traffic(spec.name)
-    ck = call_kernels(spec)
+    ck = call_kernels(spec, fused)
     dec_kernels, sel_kernels, dense_kernels = ck["sparse_decode"], ck["select_pages"], ck["dense_decode"]
+    path_kernels = ck["sparse_path"]
     acc_kernels = ["acc_one_read_kernel<true>"]
 
     def traffic_of(names):
@@ -1075,6 +1102,19 @@ def main():
 
     dec_gbps = byt_sp["sparse_decode"] / dec_t / 1e9
     sparse_gbps = sp_b / sp_t / 1e9
+    if fused:
+        # the step is one kernel: it is the dominant (only) kernel of the path
+        roofline = {"bound": "hbm", "achieved": sparse_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": sparse_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(path_kernels),
+                    "kernel": "spdec_sparse_path: " + " + ".join(path_kernels),
+                    "bytes_per_launch": int(sp_b), "us_per_launch": sp_t * 1e6,
+                    "timing": "median of 3 x (K x (1 GiB scrub read, sparse_path) minus K x scrub)"}
+    else:
+        roofline = {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(dec_kernels),
+                    "kernel": "sparse_decode call: " + " + ".join(dec_kernels),
+                    "bytes_per_launch": int(byt_sp["sparse_decode"]), "us_per_launch": dec_t * 1e6,
+                    "timing": "median of 3 x (K x (1 GiB scrub read, sparse_decode) minus K x scrub)"}
     acc_bytes = 2 * R * V * 4
     result = {
         "metric": METRIC,
@@ -1092,19 +1132,21 @@ def main():
         "config": {"workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads,
                    "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "context": describe_lens(spec), "budget": describe_budget(spec), "accumulate": "fp32",
-                   "step": "select_pages + sparse_decode (the sparse path: page scores, Top-B, split-KV attention "
-                           "over the kept pages, LSE merge), each step after a 1 GiB scrub read",
+                   "step": "spdec_sparse_path (page scores, Top-B, attention over the kept pages, LSE merge; "
+                           + ("one kernel" if fused else "select_pages + sparse_decode")
+                           + "), each step after a 1 GiB scrub read",
                    "tokens_per_step": spec.batch},
-        "roofline": {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(dec_kernels),
-                     "kernel": "sparse_decode call: " + " + ".join(dec_kernels),
-                     "bytes_per_launch": int(byt_sp["sparse_decode"]), "us_per_launch": dec_t * 1e6,
-                     "timing": "median of 3 x (K x (1 GiB scrub read, sparse_decode) minus K x scrub)"},
+        "roofline": roofline,
         "sparse": {"tokens_per_s": value, "us": sp_t * 1e6, "bytes": int(sp_b), "eff_GBps": sparse_gbps,
-                   "frac_hbm": sparse_gbps / HBM_PEAK_GBPS,
-                   "traffic": traffic_of(sel_kernels + dec_kernels), "kernels": " + ".join(sel_kernels + dec_kernels),
-                   "timing": "median of 3 x (K x (1 GiB scrub read, select_pages, sparse_decode) minus K x scrub)",
+                   "frac_hbm": sparse_gbps / HBM_PEAK_GBPS, "form": "one kernel" if fused else "two calls",
+                   "traffic": traffic_of(path_kernels), "kernels": " + ".join(path_kernels),
+                   "timing": "median of 3 x (K x (1 GiB scrub read, sparse_path) minus K x scrub)",
                    "us_no_scrub": sp_t_warm * 1e6,
+                   "two_calls": dict(_row(two_t, sp_b), tokens_per_s=spec.batch / two_t,
+                                     traffic=traffic_of(sel_kernels + dec_kernels),
+                                     kernels=" + ".join(sel_kernels + dec_kernels),
+                                     timing="median of 3 x (K x (1 GiB scrub read, select_pages, sparse_decode) "
+                                            "minus K x scrub)"),
                    "select_pages": dict(_row(sel_t, byt_sp["select_pages"]), traffic=traffic_of(sel_kernels)),
                    "sparse_decode": dict(_row(dec_t, byt_sp["sparse_decode"]), traffic=traffic_of(dec_kernels))},
         "gather_ceiling": ceiling,
@@ -1118,7 +1160,7 @@ def main():
                            read_ceiling=acc_ceiling,
                            timing="median of 3 x (K x (1 GiB scrub read, acceptance) minus K x scrub)"),
         "full_step": {"tokens_per_s": spec.batch / full_t, "ms_per_step": full_t * 1e3,
-                      "step": "append_kv + select_pages + sparse_decode + dense_decode + acceptance",
+                      "step": "append_kv + sparse_path + dense_decode + acceptance",
                       "timing": "K steps back to back, one event pair", "rows": rows_out,
                       "graph_ms_per_step": gr_t * 1e3,
                       "graph_timing": "the step captured once in a HIP graph, replayed K times, one event pair"},

@@ -258,8 +258,8 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
  * Arguments and outputs are those of the two calls: sel_idx, sel_cnt and
  * scores_out (nullable) as spdec_select_pages writes them, out and lse
  * (nullable) as spdec_sparse_decode writes them for that selection. For a
- * bf16 cache with G <= 4, max_pages_per_seq <= 2048, max_budget_pages <=
- * 2048, batch <= 512 and at least one (sequence, KV head) per compute unit,
+ * bf16 cache with G <= 4, max_pages_per_seq <= 4096, max_budget_pages <=
+ * 4096, batch <= 512 and at least one (sequence, KV head) per compute unit,
  * the step runs as one kernel, one workgroup per (sequence, KV head), which
  * keeps scores and the kept list in LDS: the selection is the same (page
  * indices and scores bit for bit), out and lse differ from the two calls only
@@ -268,6 +268,10 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
  * Workspace: spdec_sparse_path_workspace_bytes(cache, max_budget_pages).
  */
 size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
+/* 1 if spdec_sparse_path runs this cache shape as one kernel on the current
+ * device, 0 if it runs the two calls, a negative spdec_status for an invalid
+ * descriptor or max_budget_pages < 2. Queries the current device. */
+int spdec_sparse_path_fused(const spdec_cache* cache, int max_budget_pages);
 spdec_status spdec_sparse_path(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
                                int max_budget_pages, float scale, int32_t* sel_idx, int32_t* sel_cnt,
                                float* scores_out, float* out, float* lse, void* workspace, size_t workspace_bytes,

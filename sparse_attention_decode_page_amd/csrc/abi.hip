@@ -203,6 +203,14 @@ size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budge
          spdec::decode_workspace_bytes(v, spdec::decode_plan(v, max_budget_pages));
 }
 
+int spdec_sparse_path_fused(const spdec_cache* cache, int max_budget_pages) {
+  CacheView v;
+  const spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
+  return spdec::path_fused_supported(v, max_budget_pages) ? 1 : 0;
+}
+
 spdec_status spdec_sparse_path(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
                                int max_budget_pages, float scale, int32_t* sel_idx, int32_t* sel_cnt,
                                float* scores_out, float* out, float* lse, void* workspace, size_t workspace_bytes,

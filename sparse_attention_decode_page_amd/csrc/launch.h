@@ -68,7 +68,7 @@ hipError_t launch_select_shared(const CacheView& c, const void* q, const int32_t
 // merge) in one launch, one workgroup per (sequence, KV head): bf16 caches
 // with G <= 4, at most kPathMaxPages pages per sequence and in the list, at
 // most kPathMaxSeqs sequences, and at least one unit per compute unit.
-constexpr int kPathMaxPages = 2048;
+constexpr int kPathMaxPages = 4096;
 constexpr int kPathMaxSeqs = 512;
 bool path_fused_supported(const CacheView& c, int max_budget);
 hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int32_t* budget, int max_budget,

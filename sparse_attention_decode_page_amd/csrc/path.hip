@@ -30,7 +30,11 @@ namespace {
 
 constexpr int kPathThreads = 512;
 constexpr int kPathWaves = kPathThreads / kWave;
-constexpr int kPathKeys = (kPathMaxPages + kPathThreads - 1) / kPathThreads;  // Top-B keys per thread
+// Top-B keys per thread: KPT * kPathThreads middle pages; two forms, for
+// page tables up to 2050 and up to kPathMaxPages pages.
+constexpr int kPathKeysSmall = 4;
+constexpr int kPathKeysLarge = (kPathMaxPages + kPathThreads - 1) / kPathThreads;
+static_assert(kPathKeysLarge * kPathThreads + 2 >= kPathMaxPages, "the large form holds every page");
 
 struct PathArgs {
   CacheView c;
@@ -86,14 +90,15 @@ __device__ __forceinline__ void rank_sequences(const PathArgs& a, long long* s_w
   __syncthreads();
 }
 
-template <int D, int G>
+template <int D, int G, int KPT>
 __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
+  constexpr int MAXP = KPT * kPathThreads + 2;  // pages of a unit this form holds
   constexpr int NJ = D / 32;
   constexpr int LPT = D / 8;
   const CacheView& c = a.c;
-  __shared__ float s_score[kPathMaxPages];
-  __shared__ int s_list[kPathMaxPages];
-  __shared__ int s_ptab[kPathMaxPages];  // the unit's page-table row, when the scoring pass read it
+  __shared__ float s_score[MAXP];
+  __shared__ int s_list[MAXP];
+  __shared__ int s_ptab[MAXP];  // the unit's page-table row, when the scoring pass read it
   __shared__ long long s_work[kPathMaxSeqs];
   __shared__ int s_rank[kPathMaxSeqs];
   __shared__ TopBShared<kPathThreads> sh;
@@ -149,10 +154,10 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
       s_list[K - 1] = P - 1;
     }
     if (select) {
-      uint32_t key[kPathKeys], kmin;
+      uint32_t key[KPT], kmin;
       int nbits;
-      load_keys<kPathKeys, kPathThreads>(s_score, P - 2, key, kmin, nbits, sh);
-      emit_top<kPathKeys, kPathThreads>(key, P - 2, K - 2, kmin, nbits, s_list, sh);
+      load_keys<KPT, kPathThreads>(s_score, P - 2, key, kmin, nbits, sh);
+      emit_top<KPT, kPathThreads>(key, P - 2, K - 2, kmin, nbits, s_list, sh);
     }
   }
   __syncthreads();
@@ -226,15 +231,22 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   }
 }
 
-template <int D>
+template <int D, int KPT>
 hipError_t path_launch(const PathArgs& a, hipStream_t s) {
   const dim3 grid(a.c.batch * a.c.hkv), block(kPathThreads);
   switch (a.c.group) {
-    case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((sparse_path_kernel<D, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1, KPT>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2, KPT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((sparse_path_kernel<D, 4, KPT>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t path_launch(const PathArgs& a, hipStream_t s) {
+  // the form whose LDS arrays hold the page table's width
+  return a.c.max_pages <= kPathKeysSmall * kPathThreads + 2 ? path_launch<D, kPathKeysSmall>(a, s)
+                                                             : path_launch<D, kPathKeysLarge>(a, s);
 }
 
 int compute_units() {

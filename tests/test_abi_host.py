@@ -41,7 +41,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 32
+    assert len(names) == len(S.ABI_FUNCTIONS) == 33
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -139,6 +139,10 @@ def test_sparse_path_checks(L):
     assert sp(*args(desc=None)) == -1
     bad = _desc(head_dim=96)
     assert sp(*args(desc=ctypes.byref(bad))) == S.SPDEC_ERR_UNSUPPORTED
+    # the form query rejects what the call rejects, before it looks at the device
+    assert L.spdec_sparse_path_fused(ctypes.byref(bad), 16) == S.SPDEC_ERR_UNSUPPORTED
+    assert L.spdec_sparse_path_fused(ctypes.byref(d), 1) == S.SPDEC_ERR_INVALID
+    assert L.spdec_sparse_path_fused(None, 16) == S.SPDEC_ERR_INVALID
 
 
 def test_acceptance_checks(L):

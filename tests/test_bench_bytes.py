@@ -2,7 +2,9 @@
 
 Every valid token's K and V row once for the dense decode; the valid tokens of the pages the oracle's
 Top-B selection keeps for the sparse decode (whatever the scores, since the kept pages other than the
-last are always full); kmin + kmax of every page for the selection; both logit rows for the acceptance.
+last are always full); kmin + kmax of every page for the selection (and, for the one-call step, of the pages
+of units whose selection the scores decide: fewer pages kept than there are, more than the two forced ones);
+both logit rows for the acceptance.
 """
 import numpy as np
 import pytest
@@ -23,7 +25,7 @@ def test_algorithmic_bytes_brute_force(dtype, D, ps):
     cap, rows, vocab = 9, 3, 1000
     elt = 2 if dtype == "bf16" else 4
     got = bench.algorithmic_bytes(spec, lens, budget, cap, rows, vocab)
-    sparse = dense = meta = 0
+    sparse = dense = meta = meta_step = 0
     for b in range(B):
         L = int(lens[b])
         P = (L + ps - 1) // ps
@@ -33,9 +35,12 @@ def test_algorithmic_bytes_brute_force(dtype, D, ps):
             sparse += sum(valid[p] for p in keep) * 2 * D * elt
             dense += L * 2 * D * elt
             meta += P * 2 * D * elt
+            if 2 < len(keep) < P:
+                meta_step += P * 2 * D * elt
     assert got["sparse_decode"] == sparse
     assert got["dense_decode"] == dense
     assert got["select_pages"] == meta
+    assert got["sparse_path"] == sparse + meta_step
     assert got["acceptance"] == 2 * rows * vocab * 4
     assert got["append_kv"] == B * Hkv * (2 * D * elt + 2 * 2 * D * elt)
 
@@ -77,5 +82,7 @@ def test_counter_summaries_parse_and_match_patterns(tmp_path, monkeypatch):
     spec = S.SPECS["qwen3-1.7b-L16k"]
     ck = bench.call_kernels(spec)
     assert ck["sparse_decode"] == ["decode_stream_kernel<128,2,true>", "stream_merge_kernel<128,*,true>"]
+    assert ck["sparse_path"] == ["sparse_path_kernel<128,2,*>"]
+    assert bench.call_kernels(spec, fused=False)["sparse_path"] == ck["select_pages"] + ck["sparse_decode"]
     assert bench.call_kernels(S.custom_spec("g8", num_q_heads=64, num_kv_heads=8, head_dim=128))[
         "dense_decode"][0] == "decode_stream_g8_kernel<128,false>"

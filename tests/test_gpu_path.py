@@ -43,11 +43,14 @@ def _lib():
 
 
 def _fused(dw) -> bool:
-    """The documented rule under which spdec_sparse_path runs as one kernel."""
+    """The documented rule under which spdec_sparse_path runs as one kernel, checked against the library's
+    own answer."""
     c = dw.cache
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return (c.dtype == torch.bfloat16 and c.num_q_heads // c.num_kv_heads <= 4 and c.max_pages <= 2048
-            and dw.max_budget <= 2048 and c.batch <= 512 and c.batch * c.num_kv_heads >= cus)
+    rule = (c.dtype == torch.bfloat16 and c.num_q_heads // c.num_kv_heads <= 4 and c.max_pages <= 4096
+            and dw.max_budget <= 4096 and c.batch <= 512 and c.batch * c.num_kv_heads >= cus)
+    assert spdec.sparse_path_fused(c, dw.max_budget) == rule
+    return rule
 
 
 def _run(wl, units, max_budget=None, expect_fused=None):
@@ -127,7 +130,7 @@ def _lens(seed, n, lo, hi, zeros=0):
 # dtype D, Hq, Hkv, ps, batch, (lo, hi) tokens, budget pages (lo, hi), zero-length sequences
 CASES = [
     ("D128 G4 ps16", 128, 32, 8, 16, 40, (1, 6000), (0, 90), 3),
-    ("D128 G2 ps32", 128, 16, 8, 32, 36, (1, 9000), (0, 60), 2),
+    ("D128 G2 ps32", 128, 16, 8, 32, 32, (1, 9000), (0, 60), 2),   # 256 units: no ordering by size
     ("D64 G1 ps8", 64, 8, 8, 8, 34, (1, 16384), (0, 300), 2),
     ("D64 G4 ps64", 64, 16, 4, 64, 70, (1, 20000), (0, 40), 4),
     ("D128 G1 ps16", 128, 8, 8, 16, 33, (2000, 32768), (100, 400), 0),
@@ -146,17 +149,22 @@ def test_step_matches_calls_and_oracle(case):
     _run(wl, GS.sample_units(wl, 40, seed=case), expect_fused=True)
 
 
-def test_step_longest_lists():
-    """2048 pages per sequence (the one-kernel form's limit): budgets that keep every page, all but one (the
-    Top-B over 2046 middle pages), two (sink and local only) and a list capacity of 2048."""
+@pytest.mark.parametrize("pages", [2050, 4096])
+def test_step_longest_lists(pages):
+    """The widest page tables of the one-kernel form's two sizes (2050 pages: 2048 middle pages, four keys per
+    thread; 4096: eight), on two long sequences among short ones: budgets that keep every page, all but one (the
+    Top-B over every middle page), two (sink and local only) and a list capacity of `pages`."""
     B = 32
-    bud = [2048, 2047, 2, 1000] * (B // 4)
-    say("case path longest lists: 32 x 8 units of 2048 pages, capacity 2048")
-    spec = S.custom_spec("path-longest", batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
-                         dtype="bf16", lens=("fixed", 32768), budget=("pages", bud), outlier_channels=4)
+    r = np.random.default_rng(pages)
+    lens = [pages * 16, pages * 16 - 5] + [int(x) for x in r.integers(1, 2000, B - 2)]
+    bud = [pages, pages - 1] + [2, 40] * ((B - 2) // 2)
+    bud[5] = pages  # a short sequence with a budget above its page count
+    say(f"case path longest lists: page table of {pages} pages, capacity {pages}")
+    spec = S.custom_spec(f"path-longest{pages}", batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         page_size=16, dtype="bf16", lens=("list", lens), budget=("pages", bud), outlier_channels=4)
     wl = S.make_workload(spec, seed=21)
-    assert wl.page_table.shape[1] == 2048
-    _run(wl, [(0, 0), (1, 3), (2, 5), (3, 7), (29, 1), (31, 6)], expect_fused=True)
+    assert wl.page_table.shape[1] == pages
+    _run(wl, [(0, 0), (0, 5), (1, 3), (1, 7), (2, 1), (5, 6), (31, 2)], expect_fused=True)
 
 
 def test_step_capacity_two():
@@ -180,7 +188,7 @@ def test_step_runs_the_two_calls_elsewhere(what):
     elif what == "G8":
         kw.update(batch=40, num_q_heads=64, budget=("pages", [20] * 40))
     elif what == "long tables":
-        kw.update(batch=40, lens=("uniform", 30000, 40000), budget=("pages", [100] * 40))
+        kw.update(batch=40, lens=("list", [70000] + [300] * 39), budget=("pages", [100] * 40))
     say(f"case path fallback: {what}")
     wl = S.make_workload(S.custom_spec(f"path-fb-{what}", **kw), seed=5)
     _run(wl, GS.sample_units(wl, 8, seed=5), expect_fused=False)
