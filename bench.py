@@ -452,7 +452,7 @@ def call_kernels(spec, fused=True):
     calls = {"select_pages": [f"score_stream_kernel<BF16,{D},{G}>", "select_topk_reg_kernel<*>"],
              "sparse_decode": [dec("true"), f"stream_merge_kernel<{D},*,true>"],
              "dense_decode": [dec("false"), f"stream_merge_kernel<{D},*,false>"]}
-    calls["sparse_path"] = [f"sparse_path_kernel<{D},{G},*>"] if fused else \
+    calls["sparse_path"] = [f"sparse_path_kernel<{D},{G}>"] if fused else \
         calls["select_pages"] + calls["sparse_decode"]
     return calls
 

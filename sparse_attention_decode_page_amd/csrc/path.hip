@@ -30,11 +30,25 @@ namespace {
 
 constexpr int kPathThreads = 512;
 constexpr int kPathWaves = kPathThreads / kWave;
-// Top-B keys per thread: KPT * kPathThreads middle pages; two forms, for
-// page tables up to 2050 and up to kPathMaxPages pages.
-constexpr int kPathKeysSmall = 4;
-constexpr int kPathKeysLarge = (kPathMaxPages + kPathThreads - 1) / kPathThreads;
-static_assert(kPathKeysLarge * kPathThreads + 2 >= kPathMaxPages, "the large form holds every page");
+// Top-B keys per thread: a unit spreads its P - 2 middle pages over all
+// threads, ceil((P - 2) / kPathThreads) each, in registers sized for up to
+// 2048 middle pages or for kPathMaxPages pages (the smaller size has the
+// shorter loops).
+constexpr int kPathKeysShort = 4;
+constexpr int kPathKeys = (kPathMaxPages + kPathThreads - 1) / kPathThreads;
+static_assert(kPathKeys * kPathThreads + 2 >= kPathMaxPages, "the key registers hold every middle page");
+
+// The need highest of the M = P - 2 middle pages' scores in s_score[1 .. P-1]
+// into out[1 .. need], ascending (ties to the lower page).
+template <int KPT>
+__device__ __forceinline__ void path_top(const float* s_score, int M, int need, int32_t* out,
+                                         TopBShared<kPathThreads>& sh) {
+  uint32_t key[KPT], kmin;
+  int nbits;
+  const int kpt = (M + kPathThreads - 1) / kPathThreads;
+  load_keys<KPT, kPathThreads>(s_score, M, key, kmin, nbits, sh, kpt);
+  emit_top<KPT, kPathThreads>(key, M, need, kmin, nbits, out, sh, kpt);
+}
 
 struct PathArgs {
   CacheView c;
@@ -90,9 +104,9 @@ __device__ __forceinline__ void rank_sequences(const PathArgs& a, long long* s_w
   __syncthreads();
 }
 
-template <int D, int G, int KPT>
+template <int D, int G>
 __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
-  constexpr int MAXP = KPT * kPathThreads + 2;  // pages of a unit this form holds
+  constexpr int MAXP = kPathMaxPages;
   constexpr int NJ = D / 32;
   constexpr int LPT = D / 8;
   const CacheView& c = a.c;
@@ -154,10 +168,10 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
       s_list[K - 1] = P - 1;
     }
     if (select) {
-      uint32_t key[KPT], kmin;
-      int nbits;
-      load_keys<KPT, kPathThreads>(s_score, P - 2, key, kmin, nbits, sh);
-      emit_top<KPT, kPathThreads>(key, P - 2, K - 2, kmin, nbits, s_list, sh);
+      if (P - 2 <= kPathKeysShort * kPathThreads)
+        path_top<kPathKeysShort>(s_score, P - 2, K - 2, s_list, sh);
+      else
+        path_top<kPathKeys>(s_score, P - 2, K - 2, s_list, sh);
     }
   }
   __syncthreads();
@@ -231,22 +245,15 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   }
 }
 
-template <int D, int KPT>
+template <int D>
 hipError_t path_launch(const PathArgs& a, hipStream_t s) {
   const dim3 grid(a.c.batch * a.c.hkv), block(kPathThreads);
   switch (a.c.group) {
-    case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1, KPT>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2, KPT>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((sparse_path_kernel<D, 4, KPT>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((sparse_path_kernel<D, 4>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
-}
-
-template <int D>
-hipError_t path_launch(const PathArgs& a, hipStream_t s) {
-  // the form whose LDS arrays hold the page table's width
-  return a.c.max_pages <= kPathKeysSmall * kPathThreads + 2 ? path_launch<D, kPathKeysSmall>(a, s)
-                                                             : path_launch<D, kPathKeysLarge>(a, s);
 }
 
 int compute_units() {

@@ -21,13 +21,21 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Top-B select for P - 2 <= NT * KPT middle pages, one workgroup of NT threads
-// per (sequence, KV head), keys in registers. Thread t holds the keys of
-// middle pages [t*KPT, t*KPT + KPT) (index order, so the compaction emits
-// ascending pages). Radix digits are taken on
+// Top-B select for P - 2 <= NT * kpt middle pages, one workgroup of NT threads
+// per (sequence, KV head), keys in registers (up to KPT per thread). Thread t
+// holds the keys of middle pages [t*kpt, t*kpt + kpt) (index order, so the
+// compaction emits ascending pages); kpt <= KPT may be chosen per unit so that
+// a register array sized for the longest list spreads a shorter one over all
+// threads. Radix digits are taken on
 // key - min_key: the span of real scores is a few exponent steps, so the first
 // 8-bit digit already spreads the keys over the histogram and 2-3 passes
 // usually suffice.
+// Keys this thread holds: middle pages tid*kpt .. of M, at most kpt.
+template <int KPT>
+__device__ __forceinline__ int held_keys(int M, int kpt) {
+  return min(max(M - (int)threadIdx.x * kpt, 0), min(kpt, KPT));
+}
+
 template <int NT>
 struct TopBShared {
   uint32_t hist[3][256];  // radix pass p counts into hist[p % 3]
@@ -40,16 +48,15 @@ struct TopBShared {
 // significant bit count.
 template <int KPT, int NT>
 __device__ __forceinline__ void load_keys(const float* srow, int M, uint32_t (&key)[KPT], uint32_t& kmin, int& nbits,
-                                          TopBShared<NT>& sh) {
+                                          TopBShared<NT>& sh, int kpt = KPT) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int i0 = tid * KPT;
+  const int i0 = tid * kpt, nv = held_keys<KPT>(M, kpt);
   kmin = 0xFFFFFFFFu;
   uint32_t kmax = 0u;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
-    const int i = i0 + r;
-    key[r] = i < M ? score_key(srow[i + 1]) : 0u;
-    if (i < M) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
+    key[r] = r < nv ? score_key(srow[i0 + r + 1]) : 0u;
+    if (r < nv) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
   }
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -70,7 +77,7 @@ __device__ __forceinline__ void load_keys(const float* srow, int M, uint32_t (&k
 
 template <int KPT, int NT>
 __device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M, int need, uint32_t T, int eq_take,
-                                               int32_t* out, TopBShared<NT>& sh);
+                                               int32_t* out, TopBShared<NT>& sh, int kpt = KPT);
 
 // Writes the `need` highest keys of the middle pages (equal keys in page
 // order) ascending to out[1 .. need].
@@ -82,9 +89,9 @@ __device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M
 // passes stop early once every key left under the resolved prefix is taken.
 template <int KPT, int NT>
 __device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int need, uint32_t kmin, int nbits,
-                                         int32_t* out, TopBShared<NT>& sh) {
+                                         int32_t* out, TopBShared<NT>& sh, int kpt = KPT) {
   const int tid = threadIdx.x, lane = tid % kWave;
-  const int i0 = tid * KPT;
+  const int nv = held_keys<KPT>(M, kpt);
   uint32_t prefix = 0, mask = 0;
   int remaining = need;
   uint32_t T = kmin;  // cut key: all keys above it are taken, then eq_take keys equal to it
@@ -98,7 +105,7 @@ __device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int 
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const uint32_t off = key[r] - kmin;
-      if (i0 + r < M && (off & mask) == prefix) atomicAdd(&H[(off >> lo) & dmask], 1u);
+      if (r < nv && (off & mask) == prefix) atomicAdd(&H[(off >> lo) & dmask], 1u);
     }
     __syncthreads();
     // Lane l of every wave holds digits 255-4l .. 252-4l; the cut is the digit
@@ -135,20 +142,20 @@ __device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int 
     eq_take = remaining;
   }
   if (nbits == 0) eq_take = remaining;  // every key equal: take the first `need` in page order
-  write_selected<KPT, NT>(key, M, need, T, eq_take, out, sh);
+  write_selected<KPT, NT>(key, M, need, T, eq_take, out, sh, kpt);
 }
 
 // Writes the middle pages with key > T and the first eq_take pages with key
 // == T (page order) ascending to out[1 .. need].
 template <int KPT, int NT>
 __device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M, int need, uint32_t T, int eq_take,
-                                               int32_t* out, TopBShared<NT>& sh) {
+                                               int32_t* out, TopBShared<NT>& sh, int kpt) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int i0 = tid * KPT;
+  const int i0 = tid * kpt, nv = held_keys<KPT>(M, kpt);
   int gt = 0, eq = 0;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
-    if (i0 + r < M) { gt += key[r] > T; eq += key[r] == T; }
+    if (r < nv) { gt += key[r] > T; eq += key[r] == T; }
   }
   const int gt_incl = wave_incl_scan(gt);
   const int eq_incl = wave_incl_scan(eq);
@@ -160,7 +167,7 @@ __device__ __forceinline__ void write_selected(const uint32_t (&key)[KPT], int M
   int eq_seen = eq_before;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
-    if (i0 + r < M) {
+    if (r < nv) {
       bool take = key[r] > T;
       if (key[r] == T) { take = eq_seen < eq_take; ++eq_seen; }
       if (take && pos <= need) out[pos++] = i0 + r + 1;
