@@ -213,3 +213,61 @@ def test_side_streams_and_concurrent_calls_match_the_default_stream():
     for r, o in zip(ref, outs):
         for a, b in zip(r, o):
             assert torch.equal(a, b)
+
+
+def test_one_kernel_step_graph_replay_matches_eager():
+    """append_kv -> sparse_path on a batch that takes the one-kernel form (32 sequences x 8 KV heads), captured
+    once: every replay equals the eager step bit for bit (selection, scores, outputs)."""
+    steps = 4
+    spec = S.custom_spec("graph-path", batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("uniform", 200, 3000), budget=("pages", [24] * 32), outlier_channels=2)
+    wl = S.make_workload(spec, seed=6, headroom=steps + 1)
+    print("graph replay: one-kernel sparse step", flush=True)
+
+    class Step:
+        def __init__(self):
+            self.dw = GS.DeviceWorkload(wl)
+            spdec.build_meta(self.dw.cache)
+            c, dev = self.dw.cache, "cuda"
+            self.si = torch.zeros((spec.batch, spec.num_kv_heads, 24), dtype=torch.int32, device=dev)
+            self.sc = torch.zeros((spec.batch, spec.num_kv_heads), dtype=torch.int32, device=dev)
+            self.scores = torch.zeros((spec.batch, spec.num_kv_heads, c.max_pages), dtype=torch.float32, device=dev)
+            self.ws = torch.zeros(spdec.sparse_path_workspace_bytes(c, 24), dtype=torch.uint8, device=dev)
+            self.o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
+
+        def run(self, k_new, v_new):
+            c = self.dw.cache
+            spdec.append_kv(c, k_new, v_new)
+            spdec.sparse_path(c, self.dw.q, self.dw.budget, 24, sel_idx=self.si, sel_cnt=self.sc,
+                              scores_out=self.scores, out=self.o, lse=self.lse, workspace=self.ws)
+
+        def snapshot(self):
+            return {n: t.clone() for n, t in (("si", self.si), ("sc", self.sc), ("scores", self.scores),
+                                                ("o", self.o), ("lse", self.lse), ("lens", self.dw.seq_lens))}
+
+    eager, graphed = Step(), Step()
+    assert spdec.sparse_path_fused(graphed.dw.cache, 24) == (
+        spec.batch * spec.num_kv_heads >= torch.cuda.get_device_properties(0).multi_processor_count)
+    tokens = [S.append_tokens(wl, i) for i in range(steps)]
+    k_static = GS.to_device_storage(tokens[0][0], "bf16")
+    v_static = GS.to_device_storage(tokens[0][1], "bf16")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run(k_static, v_static)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        k_i = GS.to_device_storage(tokens[i][0], "bf16")
+        v_i = GS.to_device_storage(tokens[i][1], "bf16")
+        eager.run(k_i, v_i)
+        torch.cuda.synchronize()
+        k_static.copy_(k_i)
+        v_static.copy_(v_i)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = eager.snapshot(), graphed.snapshot()
+        for name in a:
+            assert torch.equal(a[name].view(torch.int32) if a[name].dtype == torch.float32 else a[name],
+                               b[name].view(torch.int32) if b[name].dtype == torch.float32 else b[name]), (i, name)
+        graphed.o.fill_(float("nan"))

@@ -134,6 +134,10 @@ CASES = [
     ("D64 G1 ps8", 64, 8, 8, 8, 34, (1, 16384), (0, 300), 2),
     ("D64 G4 ps64", 64, 16, 4, 64, 70, (1, 20000), (0, 40), 4),
     ("D128 G1 ps16", 128, 8, 8, 16, 33, (2000, 32768), (100, 400), 0),
+    # 512 sequences of one KV head (the most the form takes): ranks of 512 sequences, one comparison loop each
+    ("D64 G4 ps16 B512", 64, 4, 1, 16, 512, (1, 3000), (0, 60), 5),
+    # equal lengths and budgets: every unit reads the same bytes, the order falls back to the sequence index
+    ("D128 G2 ps16 equal", 128, 2, 1, 16, 300, (1000, 1000), (20, 20), 0),
 ]
 
 
