@@ -442,18 +442,21 @@ def gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_select=None, t_dec
     return res
 
 
-def call_kernels(spec, fused=True):
+def call_kernels(spec, form="one kernel"):
     """Name patterns (over the counter summaries' kernel names) of the kernels each call launches on a bf16
     workload of this shape; the merge's form and the Top-B's size class depend on the workload, the step's
-    form (one kernel or the two calls) on the batch."""
+    form (one kernel, sliced or the two calls) on the batch."""
     D, G = spec.head_dim, spec.group
     dec = (lambda sp: f"decode_stream_g8_kernel<{D},{sp}>") if G == 8 else \
         (lambda sp: f"decode_stream_kernel<{D},{G},{sp}>")
     calls = {"select_pages": [f"score_stream_kernel<BF16,{D},{G}>", "select_topk_reg_kernel<*>"],
              "sparse_decode": [dec("true"), f"stream_merge_kernel<{D},*,true>"],
              "dense_decode": [dec("false"), f"stream_merge_kernel<{D},*,false>"]}
-    calls["sparse_path"] = [f"sparse_path_kernel<{D},{G}>"] if fused else \
-        calls["select_pages"] + calls["sparse_decode"]
+    calls["sparse_path"] = {
+        "one kernel": [f"sparse_path_kernel<{D},{G}>"],
+        "sliced": [f"slice_score_kernel<{D},{G}>", f"slice_select_kernel<{D},{G},true>",
+                   f"stream_merge_kernel<{D},64,4,true>"],
+    }.get(form, calls["select_pages"] + calls["sparse_decode"])
     return calls
 
 
@@ -551,7 +554,7 @@ def layer_rows(args, dev, timers, name, acceptance=False):
     ws_path = torch.zeros(spdec.sparse_path_workspace_bytes(cache, cap), dtype=torch.uint8, device=dev)
     o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
-    fused = spdec.sparse_path_fused(cache, cap)
+    form = spdec.sparse_path_form(cache, cap)
 
     def path(i=0):
         spdec.sparse_path(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, out=o, lse=lse, workspace=ws_path)
@@ -581,8 +584,7 @@ def layer_rows(args, dev, timers, name, acceptance=False):
         "workload": spec.name, "batch": spec.batch, "q_heads": spec.num_q_heads, "kv_heads": spec.num_kv_heads,
         "head_dim": spec.head_dim, "page_size": spec.page_size, "context": describe_lens(spec),
         "budget": describe_budget(spec),
-        "sparse_path": dict(_row(t_path, b_path), tokens_per_s=spec.batch / t_path,
-                            form="one kernel" if fused else "select_pages + sparse_decode"),
+        "sparse_path": dict(_row(t_path, b_path), tokens_per_s=spec.batch / t_path, form=form),
         "two_calls": dict(_row(t_two, b_path), tokens_per_s=spec.batch / t_two),
         "select_pages": _row(t_sel, byt["select_pages"]),
         "sparse_decode": _row(t_dec, byt["sparse_decode"]),
@@ -592,7 +594,7 @@ def layer_rows(args, dev, timers, name, acceptance=False):
                   "to back",
     }
     traffic = counter_traffic(spec.name)
-    ck = call_kernels(spec, fused)
+    ck = call_kernels(spec, form)
     for call in ("sparse_path", "select_pages", "sparse_decode", "dense_decode"):
         res[call]["traffic"] = traffic_sum(traffic, ck[call])
     res["two_calls"]["traffic"] = traffic_sum(traffic, ck["select_pages"] + ck["sparse_decode"])
@@ -962,7 +964,7 @@ def main():
     def dec(i=0):
         spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
 
-    fused = spdec.sparse_path_fused(cache, cap)
+    form = spdec.sparse_path_form(cache, cap)
 
     def sparse_path(i=0):
         spdec.sparse_path(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, out=o_s, lse=l_s,
@@ -1092,7 +1094,7 @@ def main():
 
     # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
     traffic = counter_traffic(spec.name)
-    ck = call_kernels(spec, fused)
+    ck = call_kernels(spec, form)
     dec_kernels, sel_kernels, dense_kernels = ck["sparse_decode"], ck["select_pages"], ck["dense_decode"]
     path_kernels = ck["sparse_path"]
     acc_kernels = ["acc_one_read_kernel<true>"]
@@ -1102,7 +1104,7 @@ def main():
 
     dec_gbps = byt_sp["sparse_decode"] / dec_t / 1e9
     sparse_gbps = sp_b / sp_t / 1e9
-    if fused:
+    if form == "one kernel":
         # the step is one kernel: it is the dominant (only) kernel of the path
         roofline = {"bound": "hbm", "achieved": sparse_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": sparse_gbps / HBM_PEAK_GBPS, "traffic": traffic_of(path_kernels),
@@ -1133,12 +1135,12 @@ def main():
                    "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "context": describe_lens(spec), "budget": describe_budget(spec), "accumulate": "fp32",
                    "step": "spdec_sparse_path (page scores, Top-B, attention over the kept pages, LSE merge; "
-                           + ("one kernel" if fused else "select_pages + sparse_decode")
+                           + form
                            + "), each step after a 1 GiB scrub read",
                    "tokens_per_step": spec.batch},
         "roofline": roofline,
         "sparse": {"tokens_per_s": value, "us": sp_t * 1e6, "bytes": int(sp_b), "eff_GBps": sparse_gbps,
-                   "frac_hbm": sparse_gbps / HBM_PEAK_GBPS, "form": "one kernel" if fused else "two calls",
+                   "frac_hbm": sparse_gbps / HBM_PEAK_GBPS, "form": form,
                    "traffic": traffic_of(path_kernels), "kernels": " + ".join(path_kernels),
                    "timing": "median of 3 x (K x (1 GiB scrub read, sparse_path) minus K x scrub)",
                    "us_no_scrub": sp_t_warm * 1e6,

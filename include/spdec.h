@@ -257,21 +257,36 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
  *
  * Arguments and outputs are those of the two calls: sel_idx, sel_cnt and
  * scores_out (nullable) as spdec_select_pages writes them, out and lse
- * (nullable) as spdec_sparse_decode writes them for that selection. For a
- * bf16 cache with G <= 4, max_pages_per_seq <= 4096, max_budget_pages <=
- * 4096, batch <= 512 and at least one (sequence, KV head) per compute unit,
- * the step runs as one kernel, one workgroup per (sequence, KV head), which
- * keeps scores and the kept list in LDS: the selection is the same (page
- * indices and scores bit for bit), out and lse differ from the two calls only
- * by the order in which the kept tokens' partial sums are added (fp32
- * rounding). Other shapes run the two calls. max_budget_pages >= 2, scale > 0.
- * Workspace: spdec_sparse_path_workspace_bytes(cache, max_budget_pages).
+ * (nullable) as spdec_sparse_decode writes them for that selection. The
+ * selection is always the same, page indices and scores bit for bit; out and
+ * lse may differ from the two calls by the order in which the kept tokens'
+ * partial sums are added (fp32 rounding). Forms, by shape (bf16 cache and
+ * G <= 4 for both fused forms), on the current device:
+ *   SPDEC_PATH_ONE_KERNEL: at least one (sequence, KV head) per compute unit,
+ *     max_pages_per_seq and max_budget_pages <= 4096, batch <= 512: one
+ *     kernel, one workgroup per (sequence, KV head) with scores, kept list
+ *     and page-table row in LDS;
+ *   SPDEC_PATH_SLICED: at most half as many (sequence, KV head) as compute
+ *     units (and at most 128), max_budget_pages <= 4096: each unit's pages cut
+ *     into S slices (S = compute units / units, at most 16, raised until a
+ *     slice holds at most 4096 pages), S * (max_budget_pages - 2) <= 4096:
+ *     each slice's own Top-k candidates, the unit's Top-k from them, the kept
+ *     pages streamed by the S workgroups and their partials merged (three
+ *     kernels);
+ *   SPDEC_PATH_TWO_CALLS: any other shape.
+ * max_budget_pages >= 2, scale > 0. Workspace:
+ * spdec_sparse_path_workspace_bytes(cache, max_budget_pages) (enough for any
+ * form; no part of it needs to be cleared). Calls that share a workspace must
+ * not overlap.
  */
+#define SPDEC_PATH_TWO_CALLS 0
+#define SPDEC_PATH_ONE_KERNEL 1
+#define SPDEC_PATH_SLICED 2
 size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
-/* 1 if spdec_sparse_path runs this cache shape as one kernel on the current
- * device, 0 if it runs the two calls, a negative spdec_status for an invalid
- * descriptor or max_budget_pages < 2. Queries the current device. */
-int spdec_sparse_path_fused(const spdec_cache* cache, int max_budget_pages);
+/* The form (SPDEC_PATH_*) spdec_sparse_path takes for this cache shape on the
+ * current device, or a negative spdec_status for an invalid descriptor or
+ * max_budget_pages < 2. Queries the current device. */
+int spdec_sparse_path_form(const spdec_cache* cache, int max_budget_pages);
 spdec_status spdec_sparse_path(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
                                int max_budget_pages, float scale, int32_t* sel_idx, int32_t* sel_cnt,
                                float* scores_out, float* out, float* lse, void* workspace, size_t workspace_bytes,

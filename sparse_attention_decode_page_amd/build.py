@@ -21,7 +21,7 @@ OBJ_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libspdec.so")
 PROBE_LIB_PATH = os.path.join(PKG_DIR, "libspdec_probe.so")
 PROBE_SOURCES = ["probe.hip"]
-SOURCES = ["abi.hip", "grid.hip", "meta.hip", "select.hip", "decode.hip", "path.hip", "verify.hip", "shared.hip", "speculative.hip",
+SOURCES = ["abi.hip", "grid.hip", "meta.hip", "select.hip", "decode.hip", "path.hip", "slice.hip", "verify.hip", "shared.hip", "speculative.hip",
            "acceptance.hip", "control.hip", "check.hip", "noalloc.hip", "monitor.hip"]
 
 # Packed-FP32 VALU instructions are switched off for all device code.

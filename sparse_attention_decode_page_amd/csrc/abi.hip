@@ -196,19 +196,34 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
-  CacheView v;
-  if (view_of(cache, &v) != SPDEC_OK || max_budget_pages < 2) return 0;
+// The form spdec_sparse_path takes for a validated shape on the current device.
+static int path_form(const CacheView& v, int max_budget_pages, int* slices) {
+  *slices = 0;
+  if (spdec::path_fused_supported(v, max_budget_pages)) return SPDEC_PATH_ONE_KERNEL;
+  *slices = spdec::slice_count(v, max_budget_pages, spdec::device_compute_units());
+  return *slices > 0 ? SPDEC_PATH_SLICED : SPDEC_PATH_TWO_CALLS;
+}
+
+static size_t two_call_bytes(const CacheView& v, int max_budget_pages) {
   return align256(spdec::select_workspace_bytes(v)) +
          spdec::decode_workspace_bytes(v, spdec::decode_plan(v, max_budget_pages));
 }
 
-int spdec_sparse_path_fused(const spdec_cache* cache, int max_budget_pages) {
+size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
+  CacheView v;
+  if (view_of(cache, &v) != SPDEC_OK || max_budget_pages < 2) return 0;
+  const size_t two = two_call_bytes(v, max_budget_pages);
+  const size_t sliced = spdec::slice_workspace_bytes(v, max_budget_pages);
+  return two > sliced ? two : sliced;
+}
+
+int spdec_sparse_path_form(const spdec_cache* cache, int max_budget_pages) {
   CacheView v;
   const spdec_status st = view_of(cache, &v);
   if (st != SPDEC_OK) return st;
   if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
-  return spdec::path_fused_supported(v, max_budget_pages) ? 1 : 0;
+  int slices;
+  return path_form(v, max_budget_pages, &slices);
 }
 
 spdec_status spdec_sparse_path(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
@@ -224,18 +239,22 @@ spdec_status spdec_sparse_path(const spdec_cache* cache, const void* q, const in
     return SPDEC_ERR_INVALID;
   if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return SPDEC_ERR_INVALID;
-  const size_t score_bytes = align256(spdec::select_workspace_bytes(v));
-  const spdec::DecodePlan plan = spdec::decode_plan(v, max_budget_pages);
-  if (workspace == nullptr || workspace_bytes < score_bytes + spdec::decode_workspace_bytes(v, plan))
+  if (workspace == nullptr || workspace_bytes < spdec_sparse_path_workspace_bytes(cache, max_budget_pages))
     return SPDEC_ERR_WORKSPACE;
-  if (spdec::path_fused_supported(v, max_budget_pages))
+  int slices;
+  const int form = path_form(v, max_budget_pages, &slices);
+  if (form == SPDEC_PATH_ONE_KERNEL)
     return from_hip(spdec::launch_sparse_path_fused(v, q, budget_pages, max_budget_pages, scale, sel_idx, sel_cnt,
                                                     scores_out, out, lse, stream));
-  hipError_t e = spdec::launch_select(v, q, budget_pages, max_budget_pages, sel_idx, sel_cnt, scores_out, workspace,
-                                      stream);
+  if (form == SPDEC_PATH_SLICED)
+    return from_hip(spdec::launch_slice_path(v, q, budget_pages, max_budget_pages, slices, scale, sel_idx, sel_cnt,
+                                             scores_out, out, lse, workspace, stream));
+  char* ws = static_cast<char*>(workspace);
+  const size_t score_bytes = align256(spdec::select_workspace_bytes(v));
+  hipError_t e = spdec::launch_select(v, q, budget_pages, max_budget_pages, sel_idx, sel_cnt, scores_out, ws, stream);
   if (e != hipSuccess) return from_hip(e);
-  return from_hip(spdec::launch_decode(v, plan, q, sel_idx, sel_cnt, scale, out, lse,
-                                       static_cast<char*>(workspace) + score_bytes, stream));
+  return from_hip(spdec::launch_decode(v, spdec::decode_plan(v, max_budget_pages), q, sel_idx, sel_cnt, scale, out,
+                                       lse, ws + score_bytes, stream));
 }
 
 size_t spdec_shared_workspace_bytes(const spdec_cache* cache, int group_size) {

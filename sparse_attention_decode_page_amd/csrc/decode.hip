@@ -1001,6 +1001,37 @@ hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q,
   return sparse ? decode_dispatch<true>(a, s) : decode_dispatch<false>(a, s);
 }
 
+hipError_t launch_stream_merge(const CacheView& c, const int32_t* sel_cnt, int list_cap, int jmax,
+                               const float* part_acc, const float* part_ml, const int* count, float* out, float* lse,
+                               hipStream_t s) {
+  StreamArgs a;
+  a.c = c;
+  a.q = nullptr;
+  a.sel_idx = nullptr;
+  a.sel_cnt = sel_cnt;
+  a.list_cap = list_cap;
+  a.jmax = jmax;
+  a.rmin = 1;
+  a.qk_scale = 0.f;
+  a.part_acc = const_cast<float*>(part_acc);
+  a.part_ml = const_cast<float*>(part_ml);
+  a.count = const_cast<int*>(count);
+  a.out = out;
+  a.lse = lse;
+  a.first_page = nullptr;
+  a.group_size = 1;
+  const dim3 grid(c.batch * c.hq);
+  const int D = c.head_dim;
+  if (jmax <= 4 * (64 / (D / 4))) {
+    if (D == 64) hipLaunchKernelGGL((stream_merge_kernel<64, 64, 4, true>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((stream_merge_kernel<128, 64, 4, true>), grid, dim3(64), 0, s, a);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((stream_merge_kernel<64, 128, 8, true>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((stream_merge_kernel<128, 128, 8, true>), grid, dim3(128), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_dense_stream_partials(const CacheView& c, const DecodePlan& p, const void* q,
                                         const int32_t* first_page, int group_size, float scale, float* part_acc,
                                         float* part_ml, int* count, hipStream_t s) {

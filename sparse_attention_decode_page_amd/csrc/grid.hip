@@ -14,4 +14,12 @@ hipError_t persistent_grid(const void* kernel, int block, size_t dyn_lds, int* g
   return hipSuccess;
 }
 
+int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
 }  // namespace spdec

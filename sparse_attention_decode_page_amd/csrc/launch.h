@@ -44,6 +44,8 @@ constexpr int kMaxStreamUnits = 8192;
 // Workgroups that fill the current device once for `kernel` (resident blocks
 // per compute unit x compute units).
 hipError_t persistent_grid(const void* kernel, int block, size_t dyn_lds, int* grid);
+// Compute units of the current device (0 if the runtime cannot say).
+int device_compute_units();
 size_t decode_workspace_bytes(const CacheView& c, const DecodePlan& p);
 size_t select_workspace_bytes(const CacheView& c);
 size_t acceptance_workspace_bytes(int rows, int vocab);
@@ -71,6 +73,29 @@ hipError_t launch_select_shared(const CacheView& c, const void* q, const int32_t
 constexpr int kPathMaxPages = 4096;
 constexpr int kPathMaxSeqs = 512;
 bool path_fused_supported(const CacheView& c, int max_budget);
+// The sliced sparse path for batches of few units: each unit's pages cut into
+// S slices scored by S workgroups (slice candidates, then the unit's Top-B
+// from them) and its kept list streamed by the same S workgroups, partials
+// merged by the stream merge. slice_count gives S for this shape on a device
+// of `cus` compute units, 0 where the form does not apply (bf16, G <= 4, at
+// least two slices per unit, at most kSliceMaxUnits units and kSliceMaxPages pages per slice,
+// S * (max_budget - 2) <= kSliceMaxCand candidates, max_budget <= kSliceMaxList).
+constexpr int kSliceMaxS = 16;
+constexpr int kSliceMaxUnits = 128;
+constexpr int kSliceMaxPages = 4096;
+constexpr int kSliceMaxCand = 4096;
+constexpr int kSliceMaxList = 4096;
+int slice_count(const CacheView& c, int max_budget, int cus);
+size_t slice_workspace_bytes(const CacheView& c, int max_budget);
+// out == nullptr: the selection only (sel_idx, sel_cnt, scores).
+hipError_t launch_slice_path(const CacheView& c, const void* q, const int32_t* budget, int max_budget, int S,
+                             float scale, int32_t* sel_idx, int32_t* sel_cnt, float* scores, float* out, float* lse,
+                             void* ws, hipStream_t s);
+// The stream merge alone over partials in the decode's layout ([units][jmax]
+// slots, count[u] of them written); units with sel_cnt 0 get zeros, lse -inf.
+hipError_t launch_stream_merge(const CacheView& c, const int32_t* sel_cnt, int list_cap, int jmax,
+                               const float* part_acc, const float* part_ml, const int* count, float* out, float* lse,
+                               hipStream_t s);
 hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
                                     float scale, int32_t* sel_idx, int32_t* sel_cnt, float* scores, float* out,
                                     float* lse, hipStream_t s);

@@ -21,8 +21,8 @@
 #include "common.h"
 #include "launch.h"
 #include "scoring.h"
-#include "stream_window.h"
 #include "topb.h"
+#include "unit_stream.h"
 
 namespace spdec {
 
@@ -107,8 +107,6 @@ __device__ __forceinline__ void rank_sequences(const PathArgs& a, long long* s_w
 template <int D, int G>
 __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   constexpr int MAXP = kPathMaxPages;
-  constexpr int NJ = D / 32;
-  constexpr int LPT = D / 8;
   const CacheView& c = a.c;
   __shared__ float s_score[MAXP];
   __shared__ int s_list[MAXP];
@@ -116,8 +114,7 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   __shared__ long long s_work[kPathMaxSeqs];
   __shared__ int s_rank[kPathMaxSeqs];
   __shared__ TopBShared<kPathThreads> sh;
-  __shared__ float s_acc[kPathWaves][G][D];
-  __shared__ float s_ml[kPathWaves][G][2];
+  __shared__ WaveParts<D, G, kPathWaves> s_parts;
   __shared__ int s_seq;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int B = c.batch;
@@ -180,65 +177,19 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
 
   // Attention over the kept pages: wave w streams entries [w*per, (w+1)*per).
   float m[G], lsum[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    lsum[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
   const int per = (K + kPathWaves - 1) / kPathWaves;
   const int e0 = min(K, wave * per), e1 = min(K, e0 + per);
-  if (e0 < e1) {
-    const int r16 = lane % 16, q4 = lane / 16;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
-    u32x4 qa[NJ];  // A operands: row r16 holds query head r16 % G
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-      qa[jj] = load16(qp + ((int64_t)b * c.hq + g * G + r16 % G) * D + 32 * jj + 8 * q4);
-    for (int wb = e0; wb < e1; wb += kWave) {
-      // Window of up to 64 entries: lane i holds entry wb+i's physical page and valid tokens.
-      const int nwin = min(kWave, e1 - wb);
-      const int logical = s_list[min(wb + lane, e1 - 1)];
-      const int ph = select ? s_ptab[logical]
-                            : c.page_table[(int64_t)b * c.max_pages + min(max(logical, 0), c.max_pages - 1)];
-      const bool ok = lane < nwin && logical >= 0 && logical < P && ph >= 0 && ph < c.num_phys;
-      const int phys_w = ok ? ph : 0;
-      const int valid_w = ok ? min(c.page_size, L - logical * c.page_size) : 0;
-      stream_window<D, G>(c, g, nwin, phys_w, valid_w, qa, a.qk_scale, lane, m, lsum, acc);
-    }
-    close_segment<D, G>(lsum, acc);
-  }
-  const int vsub = lane % LPT, vtok = lane / LPT;
-  if (vtok == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * vsub + e] = acc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_ml[wave][h][0] = m[h];
-      s_ml[wave][h][1] = lsum[h];
-    }
-  }
+  stream_list_range<D, G>(c, a.q, a.qk_scale, b, g, L, P, s_list, select ? s_ptab : nullptr, e0, e1, lane, m, lsum,
+                          acc);
+  store_wave_part<D, G, kPathWaves>(s_parts, wave, lane, m, lsum, acc);
   __syncthreads();
 
   // Merge of the waves' partials in wave order: o = sum_w 2^(m_w - M) acc_w /
   // sum_w 2^(m_w - M) l_w, lse = ln2 (M + log2 sum_w 2^(m_w - M) l_w).
   for (int i = tid; i < G * D; i += kPathThreads) {
     const int h = i / D, d = i % D;
-    float M = kNegBig;
-#pragma unroll
-    for (int w = 0; w < kPathWaves; ++w) M = fmaxf(M, s_ml[w][h][0]);
-    float Ls = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPathWaves; ++w) {
-      const float wt = exp2f(s_ml[w][h][0] - M);
-      Ls = fmaf(wt, s_ml[w][h][1], Ls);
-      o = fmaf(wt, s_acc[w][h][d], o);
-    }
+    float M, Ls, o;
+    fold_wave_parts<D, G, kPathWaves>(s_parts, h, d, M, Ls, o);
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
     out_rows[h * D + d] = o * inv;
     if (lse_rows != nullptr && d == 0) lse_rows[h] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
@@ -256,18 +207,10 @@ hipError_t path_launch(const PathArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int compute_units() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return cus;
-}
-
 }  // namespace
 
 bool path_fused_supported(const CacheView& c, int max_budget) {
-  const int cus = compute_units();
+  const int cus = device_compute_units();
   return cus > 0 && c.dtype == SPDEC_BF16 && c.group <= 4 && c.max_pages <= kPathMaxPages &&
          max_budget <= kPathMaxPages && c.batch <= kPathMaxSeqs && (int64_t)c.batch * c.hkv >= cus;
 }
@@ -286,7 +229,7 @@ hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int
   a.scores = scores;
   a.out = out;
   a.lse = lse;
-  a.lpt = (int64_t)c.batch * c.hkv > compute_units() ? 1 : 0;
+  a.lpt = (int64_t)c.batch * c.hkv > device_compute_units() ? 1 : 0;
   return c.head_dim == 64 ? path_launch<64>(a, s) : path_launch<128>(a, s);
 }
 

@@ -23,10 +23,11 @@ namespace {
 // loads read a valid row that is never used), and each window's entries are
 // read two windows ahead, so the loads in flight never sit behind a branch
 // and the wait before a batch covers only that batch's loads. ptab_out
-// (nullable, LDS) receives the segment's page-table entries as read.
+// (nullable, LDS) receives the segment's page-table entries as read. Page p's
+// score goes to srow[p - srow_base].
 template <typename T, int D, int G>
 __device__ __forceinline__ void score_segment(const CacheView& c, const void* qv, int b, int g, int pb, int pe,
-                                              float* srow, int lane, int* ptab_out = nullptr) {
+                                              float* srow, int lane, int* ptab_out = nullptr, int srow_base = 0) {
   constexpr int VEC = T::VEC;
   constexpr int LPT = D / VEC;
   constexpr int PPI = kWave / LPT;
@@ -92,7 +93,7 @@ __device__ __forceinline__ void score_segment(const CacheView& c, const void* qv
       }
       sc = group_sum<LPT>(sc);
       const int p = pb + wi * kWave + (j * BATCH + i) * PPI + lane / LPT;
-      if (sub == 0 && phys[i] >= 0 && p < pe) srow[p] = (float)sc;
+      if (sub == 0 && phys[i] >= 0 && p < pe) srow[p - srow_base] = (float)sc;
     }
   };
   u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];

@@ -24,7 +24,7 @@ ABI_FUNCTIONS = (
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
     "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_select_pages_shared", "spdec_select_pages_top_p",
     "spdec_decode_workspace_bytes",
-    "spdec_sparse_decode", "spdec_sparse_path_workspace_bytes", "spdec_sparse_path_fused", "spdec_sparse_path",
+    "spdec_sparse_decode", "spdec_sparse_path_workspace_bytes", "spdec_sparse_path_form", "spdec_sparse_path",
     "spdec_dense_decode",
     "spdec_shared_workspace_bytes", "spdec_dense_decode_shared",
     "spdec_verify_workspace_bytes", "spdec_verify_decode",
@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
         "spdec_decode_workspace_bytes": (SZ, [D, I]),
         "spdec_sparse_decode": (I, [D, P, P, P, I, F, P, P, P, SZ, P]),
         "spdec_sparse_path_workspace_bytes": (SZ, [D, I]),
-        "spdec_sparse_path_fused": (I, [D, I]),
+        "spdec_sparse_path_form": (I, [D, I]),
         "spdec_sparse_path": (I, [D, P, P, I, F, P, P, P, P, P, P, SZ, P]),
         "spdec_dense_decode": (I, [D, P, F, P, P, P, SZ, P]),
         "spdec_shared_workspace_bytes": (SZ, [D, I]),
@@ -315,11 +315,15 @@ def sparse_path_workspace_bytes(cache: PagedCache, max_budget_pages: int) -> int
     return int(lib().spdec_sparse_path_workspace_bytes(ctypes.byref(cache.desc), int(max_budget_pages)))
 
 
-def sparse_path_fused(cache: PagedCache, max_budget_pages: int) -> bool:
-    """Whether sparse_path runs this cache shape as one kernel on the current device."""
-    r = int(lib().spdec_sparse_path_fused(ctypes.byref(cache.desc), int(max_budget_pages)))
-    _check(min(r, 0), "spdec_sparse_path_fused")
-    return r == 1
+PATH_FORMS = {0: "two calls", 1: "one kernel", 2: "sliced"}
+
+
+def sparse_path_form(cache: PagedCache, max_budget_pages: int) -> str:
+    """The form sparse_path takes for this cache shape on the current device: "one kernel", "sliced" or
+    "two calls"."""
+    r = int(lib().spdec_sparse_path_form(ctypes.byref(cache.desc), int(max_budget_pages)))
+    _check(min(r, 0), "spdec_sparse_path_form")
+    return PATH_FORMS[r]
 
 
 def sparse_path(cache: PagedCache, q, budget_pages, max_budget_pages: int, scale: Optional[float] = None,

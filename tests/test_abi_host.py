@@ -119,9 +119,14 @@ def test_sparse_path_checks(L):
     d = _desc()
     sp = L.spdec_sparse_path
     need = L.spdec_sparse_path_workspace_bytes(ctypes.byref(d), 16)
-    # scores (rounded up to 256 bytes) ahead of the decode's workspace: what the two calls it stands for need
+    # the two calls' needs (scores rounded up to 256 bytes, then the decode's workspace) or the sliced form's
+    # (every unit's candidates: 4096 page-score pairs, 16 slices' counts and partials), whichever is larger
     sel = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
-    assert need == (sel + 255) // 256 * 256 + L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
+    two = (sel + 255) // 256 * 256 + L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
+    r = lambda x: (x + 255) // 256 * 256
+    units, G, D = 4, 4, 128
+    sliced = r(units * 4096 * 4) * 2 + r(units * 16 * 4) + r(units * 16 * G * D * 4) + r(units * 16 * G * 2 * 4) + r(units * 4)
+    assert need == max(two, sliced)
     assert L.spdec_sparse_path_workspace_bytes(ctypes.byref(d), 1) == 0
     assert L.spdec_sparse_path_workspace_bytes(None, 16) == 0
     args = lambda **kw: [kw.get(k, v) for k, v in (
@@ -140,9 +145,9 @@ def test_sparse_path_checks(L):
     bad = _desc(head_dim=96)
     assert sp(*args(desc=ctypes.byref(bad))) == S.SPDEC_ERR_UNSUPPORTED
     # the form query rejects what the call rejects, before it looks at the device
-    assert L.spdec_sparse_path_fused(ctypes.byref(bad), 16) == S.SPDEC_ERR_UNSUPPORTED
-    assert L.spdec_sparse_path_fused(ctypes.byref(d), 1) == S.SPDEC_ERR_INVALID
-    assert L.spdec_sparse_path_fused(None, 16) == S.SPDEC_ERR_INVALID
+    assert L.spdec_sparse_path_form(ctypes.byref(bad), 16) == S.SPDEC_ERR_UNSUPPORTED
+    assert L.spdec_sparse_path_form(ctypes.byref(d), 1) == S.SPDEC_ERR_INVALID
+    assert L.spdec_sparse_path_form(None, 16) == S.SPDEC_ERR_INVALID
 
 
 def test_acceptance_checks(L):

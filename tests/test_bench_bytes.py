@@ -83,6 +83,7 @@ def test_counter_summaries_parse_and_match_patterns(tmp_path, monkeypatch):
     ck = bench.call_kernels(spec)
     assert ck["sparse_decode"] == ["decode_stream_kernel<128,2,true>", "stream_merge_kernel<128,*,true>"]
     assert ck["sparse_path"] == ["sparse_path_kernel<128,2>"]
-    assert bench.call_kernels(spec, fused=False)["sparse_path"] == ck["select_pages"] + ck["sparse_decode"]
+    assert bench.call_kernels(spec, "two calls")["sparse_path"] == ck["select_pages"] + ck["sparse_decode"]
+    assert bench.call_kernels(spec, "sliced")["sparse_path"][0] == "slice_score_kernel<128,2>"
     assert bench.call_kernels(S.custom_spec("g8", num_q_heads=64, num_kv_heads=8, head_dim=128))[
         "dense_decode"][0] == "decode_stream_g8_kernel<128,false>"

@@ -247,8 +247,8 @@ def test_one_kernel_step_graph_replay_matches_eager():
                                                 ("o", self.o), ("lse", self.lse), ("lens", self.dw.seq_lens))}
 
     eager, graphed = Step(), Step()
-    assert spdec.sparse_path_fused(graphed.dw.cache, 24) == (
-        spec.batch * spec.num_kv_heads >= torch.cuda.get_device_properties(0).multi_processor_count)
+    assert spdec.sparse_path_form(graphed.dw.cache, 24) == ("one kernel" if spec.batch * spec.num_kv_heads >= (
+        torch.cuda.get_device_properties(0).multi_processor_count) else "two calls")
     tokens = [S.append_tokens(wl, i) for i in range(steps)]
     k_static = GS.to_device_storage(tokens[0][0], "bf16")
     v_static = GS.to_device_storage(tokens[0][1], "bf16")

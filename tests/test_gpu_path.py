@@ -1,11 +1,11 @@
 """GPU: spdec_sparse_path (one decode step: page selection, then attention over the kept pages) against the two
 calls it stands for and against the CPU oracle.
 
-Batches with at least one (sequence, KV head) per compute unit run the step as one kernel; the selection it writes
-(sel_idx, sel_cnt, scores) must equal spdec_select_pages' bit for bit, and out / lse must agree with
-spdec_sparse_decode over that selection to fp32 rounding of a different summation order (3e-6 max-abs; both are
-within the oracle's bf16 bar of 1e-2, checked per unit). Smaller batches run the two calls, so every output is
-bitwise equal.
+Batches with at least one (sequence, KV head) per compute unit run the step as one kernel, batches of at most half
+as many in the sliced form (each unit's pages cut over several workgroups); in both the selection (sel_idx,
+sel_cnt, scores) must equal spdec_select_pages' bit for bit, and out / lse must agree with spdec_sparse_decode over
+that selection to fp32 rounding of a different summation order (3e-6 max-abs; both are within the oracle's bf16
+bar of 1e-2, checked per unit). Other shapes run the two calls, so every output is bitwise equal.
 """
 import os
 import sys
@@ -42,27 +42,36 @@ def _lib():
     assert torch.cuda.is_available()
 
 
-def _fused(dw) -> bool:
-    """The documented rule under which spdec_sparse_path runs as one kernel, checked against the library's
-    own answer."""
+def _form(dw) -> str:
+    """The documented rule for the form spdec_sparse_path takes, checked against the library's own answer."""
     c = dw.cache
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    rule = (c.dtype == torch.bfloat16 and c.num_q_heads // c.num_kv_heads <= 4 and c.max_pages <= 4096
-            and dw.max_budget <= 4096 and c.batch <= 512 and c.batch * c.num_kv_heads >= cus)
-    assert spdec.sparse_path_fused(c, dw.max_budget) == rule
-    return rule
+    units = c.batch * c.num_kv_heads
+    cap = dw.max_budget
+    base = c.dtype == torch.bfloat16 and c.num_q_heads // c.num_kv_heads <= 4
+    form = "two calls"
+    if base and c.max_pages <= 4096 and cap <= 4096 and c.batch <= 512 and units >= cus:
+        form = "one kernel"
+    elif base and units <= 128 and cap <= 4096:
+        S = min(16, cus // units)
+        while 2 <= S <= 16 and -(-c.max_pages // S) > 4096:
+            S += 1
+        if 2 <= S <= 16 and S * (cap - 2) <= 4096:
+            form = "sliced"
+    assert spdec.sparse_path_form(c, cap) == form, (form, spdec.sparse_path_form(c, cap))
+    return form
 
 
-def _run(wl, units, max_budget=None, expect_fused=None):
+def _run(wl, units, max_budget=None, expect_form=None):
     spec = wl.spec
     dw = GS.DeviceWorkload(wl)
     if max_budget is not None:
         dw.max_budget = max_budget
     c = dw.cache
     spdec.build_meta(c)
-    fused = _fused(dw)
-    if expect_fused is not None:
-        assert fused == expect_fused
+    form = _form(dw)
+    if expect_form is not None:
+        assert form == expect_form, form
     # the two calls
     scores_a = torch.zeros((c.batch, c.num_kv_heads, c.max_pages), dtype=torch.float32, device=c.device)
     idx_a, cnt_a = spdec.select_pages(c, dw.q, dw.budget, dw.max_budget, scores_out=scores_a)
@@ -94,7 +103,7 @@ def _run(wl, units, max_budget=None, expect_fused=None):
     assert np.all(np.isneginf(lb[~live])) and np.all(ob[~live] == 0)
     d_out = float(np.abs(oa - ob).max())
     d_lse = float(np.abs(la[live] - lb[live]).max()) if live.any() else 0.0
-    if fused:
+    if form != "two calls":
         assert d_out <= TOL_SPLIT and d_lse <= TOL_SPLIT, (d_out, d_lse)
     else:
         assert d_out == 0.0 and d_lse == 0.0, (d_out, d_lse)
@@ -114,7 +123,7 @@ def _run(wl, units, max_budget=None, expect_fused=None):
         el = float(np.abs(lb[b, g * G:(g + 1) * G] - lse).max()) if P else 0.0
         assert e <= tol and el <= tol, (b, g, e, el)
         worst = max(worst, e, el)
-    say(f"  {spec.name}: fused={fused} step vs calls out {d_out:.2e} lse {d_lse:.2e}; "
+    say(f"  {spec.name}: {form}: step vs calls out {d_out:.2e} lse {d_lse:.2e}; "
         f"{len(units)} units vs oracle, worst {worst:.2e}")
     return dw
 
@@ -150,7 +159,7 @@ def test_step_matches_calls_and_oracle(case):
     spec = S.custom_spec(f"path-{case}", batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
                          dtype="bf16", lens=("list", lens), budget=("pages", bud), outlier_channels=4)
     wl = S.make_workload(spec, seed=case)
-    _run(wl, GS.sample_units(wl, 40, seed=case), expect_fused=True)
+    _run(wl, GS.sample_units(wl, 40, seed=case), expect_form="one kernel")
 
 
 @pytest.mark.parametrize("pages", [2050, 4096])
@@ -168,7 +177,7 @@ def test_step_longest_lists(pages):
                          page_size=16, dtype="bf16", lens=("list", lens), budget=("pages", bud), outlier_channels=4)
     wl = S.make_workload(spec, seed=21)
     assert wl.page_table.shape[1] == pages
-    _run(wl, [(0, 0), (0, 5), (1, 3), (1, 7), (2, 1), (5, 6), (31, 2)], expect_fused=True)
+    _run(wl, [(0, 0), (0, 5), (1, 3), (1, 7), (2, 1), (5, 6), (31, 2)], expect_form="one kernel")
 
 
 def test_step_capacity_two():
@@ -179,23 +188,102 @@ def test_step_capacity_two():
                          dtype="bf16", lens=("list", _lens(9, B, 1, 3000, 2)), budget=("pages", [50] * B),
                          outlier_channels=4)
     wl = S.make_workload(spec, seed=9)
-    _run(wl, GS.sample_units(wl, 20, seed=9), max_budget=2, expect_fused=True)
+    _run(wl, GS.sample_units(wl, 20, seed=9), max_budget=2, expect_form="one kernel")
 
 
-@pytest.mark.parametrize("what", ["few units", "f32", "G8", "long tables"])
+@pytest.mark.parametrize("what", ["between the forms", "f32", "G8", "long tables"])
 def test_step_runs_the_two_calls_elsewhere(what):
-    """Shapes outside the one-kernel form: the step is the two calls, bit for bit."""
-    kw = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype="bf16",
-              lens=("uniform", 100, 5000), budget=("pages", [3, 20, 40, 80]), outlier_channels=4)
+    """Shapes outside both fused forms: the step is the two calls, bit for bit."""
+    kw = dict(batch=20, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype="bf16",
+              lens=("uniform", 100, 5000), budget=("pages", [3, 20, 40, 80] * 5), outlier_channels=4)
     if what == "f32":
         kw.update(batch=40, dtype="f32", outlier_channels=0, budget=("pages", [20] * 40))
     elif what == "G8":
         kw.update(batch=40, num_q_heads=64, budget=("pages", [20] * 40))
     elif what == "long tables":
         kw.update(batch=40, lens=("list", [70000] + [300] * 39), budget=("pages", [100] * 40))
+    elif what == "between the forms":
+        assert 128 < 20 * 8 < 256
     say(f"case path fallback: {what}")
     wl = S.make_workload(S.custom_spec(f"path-fb-{what}", **kw), seed=5)
-    _run(wl, GS.sample_units(wl, 8, seed=5), expect_fused=False)
+    _run(wl, GS.sample_units(wl, 8, seed=5), expect_form="two calls")
+
+
+# The sliced form: dtype D, Hq, Hkv, ps, batch, (lo, hi) tokens, budget pages, empty sequences
+SLICED = [
+    ("D128 G4 ps16", 128, 32, 8, 16, 4, (20000, 40000), [3, 40, 200, 400], 0),
+    ("D128 G2 ps32", 128, 16, 8, 32, 6, (1, 60000), [2, 100, 800, 120, 0, 60], 1),
+    ("D64 G1 ps8", 64, 4, 4, 8, 8, (30000, 70000), [500, 2, 7, 256, 511, 100, 300, 1], 0),
+    ("D64 G4 ps64", 64, 16, 4, 64, 3, (100, 200000), [30, 10, 60], 0),
+    ("D128 G4 ps16 one unit", 128, 4, 1, 16, 1, (65536, 65536), [250], 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SLICED)))
+def test_sliced_step_matches_calls_and_oracle(case):
+    """Few units (at most half the compute units): each unit's pages cut into slices scored by separate
+    workgroups, the unit's Top-B taken from the slices' candidates, the kept pages streamed by the slices and
+    merged: selection bit for bit as the two calls, outputs within fp32 reordering, sampled units against the
+    oracle. Budgets below 2, equal to and above the page count, empty sequences."""
+    name, D, Hq, Hkv, ps, B, (lo, hi), bud, zeros = SLICED[case]
+    lens = _lens(500 + case, B, lo, hi, zeros)
+    say(f"case sliced {name}: batch {B}, lens {lens}, budget pages {bud}")
+    spec = S.custom_spec(f"sliced-{case}", batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                         dtype="bf16", lens=("list", lens), budget=("pages", bud), outlier_channels=4)
+    wl = S.make_workload(spec, seed=500 + case)
+    _run(wl, GS.sample_units(wl, 12, seed=case), expect_form="sliced")
+
+
+def test_sliced_workspace_shared_across_calls_and_shapes():
+    """One workspace (never cleared between calls) through sliced calls of two shapes, a one-kernel call and a
+    two-call shape: every result equals a fresh workspace's bit for bit."""
+    def wl_of(name, B, Hkv, lens, bud, seed):
+        spec = S.custom_spec(name, batch=B, num_q_heads=4 * Hkv, num_kv_heads=Hkv, head_dim=128, page_size=16,
+                             dtype="bf16", lens=("list", lens), budget=("pages", bud), outlier_channels=4)
+        return S.make_workload(spec, seed=seed)
+    shapes = [wl_of("ws-a", 4, 8, [20000, 9000, 30000, 100], [300, 40, 200, 2], 1),
+              wl_of("ws-b", 2, 4, [50000, 7000], [120, 60], 2),
+              wl_of("ws-c", 40, 8, _lens(3, 40, 1, 3000, 1), [30] * 40, 3),
+              wl_of("ws-d", 20, 8, _lens(4, 20, 1, 3000, 1), [30] * 20, 4)]
+    devs = [GS.DeviceWorkload(w) for w in shapes]
+    for dw in devs:
+        spdec.build_meta(dw.cache)
+    need = max(spdec.sparse_path_workspace_bytes(dw.cache, dw.max_budget) for dw in devs)
+    shared = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")  # not cleared: nothing may rely on zeros
+    say("case sliced workspace shared: forms " + ", ".join(spdec.sparse_path_form(dw.cache, dw.max_budget)
+                                                           for dw in devs))
+    for rep in range(2):
+        for dw in devs:
+            got = spdec.sparse_path(dw.cache, dw.q, dw.budget, dw.max_budget, workspace=shared)
+            want = spdec.sparse_path(dw.cache, dw.q, dw.budget, dw.max_budget)
+            torch.cuda.synchronize()
+            for x, y in zip(got, want):
+                if x.dtype == torch.float32:
+                    x, y = x.view(torch.int32), y.view(torch.int32)
+                assert torch.equal(x, y), (rep, dw.wl.spec.name)
+
+
+LONG = ["long-131k-ps8", "long-131k-ps16", "long-131k-ps32", "long-131k-ps64"]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", LONG)
+def test_sliced_step_full_size(name):
+    """The 131K-token cache at every page size (4 sequences, 32 units): the sliced form, every unit against the
+    two calls, sampled units against the oracle, and the planted block kept."""
+    say(f"case sliced full-size {name}: generating")
+    wl = S.make_workload(name, seed=0, build_pool=True)
+    dw = _run(wl, GS.sample_units(wl, 6, seed=4), expect_form="sliced")
+    sel_idx, sel_cnt = spdec.select_pages(dw.cache, dw.q, dw.budget, dw.max_budget)
+    si, sc = sel_idx.cpu().numpy(), sel_cnt.cpu().numpy()
+    ps = wl.spec.page_size
+    for b in range(wl.spec.batch):
+        for g in range(wl.spec.num_kv_heads):
+            s0 = int(wl.plant_start[b, g])
+            pages = set(range(s0 // ps, (s0 + wl.spec.planted_block - 1) // ps + 1))
+            assert pages <= set(si[b, g, :sc[b, g]].tolist()), (b, g)
+    torch.cuda.empty_cache()
 
 
 FULL = ["qwen3-8b-ragged", "qwen3-1.7b-L16k", "qwen3-8b-L32k-acceptance"]
@@ -209,7 +297,7 @@ def test_step_full_size(name):
     against the oracle."""
     say(f"case path full-size {name}: generating")
     wl = S.make_workload(name, seed=0, build_pool=True)
-    _run(wl, GS.sample_units(wl, 24, seed=3), expect_fused=True)
+    _run(wl, GS.sample_units(wl, 24, seed=3), expect_form="one kernel")
     torch.cuda.empty_cache()
 
 
