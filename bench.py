@@ -111,8 +111,9 @@ def traffic_file(workload: str) -> str:
 # The measured kernels (dense and sparse decode, scoring, top-B, acceptance) and
 # their launch configuration (plans, resident grid); a change to any of these
 # invalidates the recorded counter traffic.
-KERNEL_SOURCES = ("common.h", "decode.hip", "select.hip", "grid.hip", "acceptance.hip", "path.hip", "scoring.h",
-                  "topb.h", "stream_window.h")
+# Every device source of the library: a change to any of them voids the committed counter traffic.
+KERNEL_SOURCES = tuple(sorted(f for f in os.listdir(os.path.join(ROOT, "sparse_attention_decode_page_amd", "csrc"))
+                              if f.endswith((".hip", ".h"))))
 
 
 def describe_lens(spec) -> str:
