@@ -11,14 +11,40 @@
 namespace spdec {
 namespace {
 
+// Inclusive prefix sum over the wave on DPP (no LDS traffic): Hillis-Steele
+// shifts inside each 16-lane row, then row 0's total into row 1 and row 2's
+// into row 3 (row_bcast:15), then rows 0-1's total into rows 2 and 3
+// (row_bcast:31). Lanes a step does not write take the `old` operand, 0.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return x;
+}
+
+// Minimum and maximum over the wave, returned wave-uniform: butterflies
+// inside each 16-lane row on DPP, then the four rows' results read out.
+__device__ __forceinline__ void wave_min_max(uint32_t& lo, uint32_t& hi) {
+  auto step = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    lo = min(lo, (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, C, 0xF, 0xF, false));
+    hi = max(hi, (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, C, 0xF, 0xF, false));
+  };
+  step(std::integral_constant<int, kQuadSwap1>{});
+  step(std::integral_constant<int, kQuadSwap2>{});
+  step(std::integral_constant<int, kRowHalfMirror>{});
+  step(std::integral_constant<int, kRowMirror>{});
+  uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)lo, 0), h = (uint32_t)__builtin_amdgcn_readlane((int)hi, 0);
+#pragma unroll
+  for (int r = 16; r < kWave; r += 16) {
+    l = min(l, (uint32_t)__builtin_amdgcn_readlane((int)lo, r));
+    h = max(h, (uint32_t)__builtin_amdgcn_readlane((int)hi, r));
+  }
+  lo = l;
+  hi = h;
 }
 
 // Top-B select for P - 2 <= NT * kpt middle pages, one workgroup of NT threads
@@ -58,11 +84,7 @@ __device__ __forceinline__ void load_keys(const float* srow, int M, uint32_t (&k
     key[r] = r < nv ? score_key(srow[i0 + r + 1]) : 0u;
     if (r < nv) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
   }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-  }
+  wave_min_max(kmin, kmax);
   if (lane == 0) { sh.red[wave][0] = kmin; sh.red[wave][1] = kmax; }
   for (int i = tid; i < 256; i += NT) sh.hist[0][i] = 0;  // the first radix pass's counts
   __syncthreads();
@@ -125,9 +147,9 @@ __device__ __forceinline__ void emit_top(const uint32_t (&key)[KPT], int M, int 
       else { digit = top - 3; above = excl + c0 + c1 + c2; cnt = c3; }
     }
     const int src = __builtin_ctzll(__ballot(mine));  // exactly one lane: 0 < remaining <= total
-    digit = __shfl(digit, src);
-    above = __shfl(above, src);
-    cnt = __shfl(cnt, src);
+    digit = __builtin_amdgcn_readlane(digit, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    cnt = __builtin_amdgcn_readlane(cnt, src);
     prefix |= (uint32_t)digit << lo;
     mask |= dmask << lo;
     remaining -= above;
