@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   float m[G], lsum[G], acc[G][8];
   const int per = (K + kPathWaves - 1) / kPathWaves;
   const int e0 = min(K, wave * per), e1 = min(K, e0 + per);
-  stream_list_range<D, G>(c, a.q, a.qk_scale, b, g, L, P, s_list, select ? s_ptab : nullptr, e0, e1, lane, m, lsum,
+  stream_list_range<D, G>(c, a.q, a.qk_scale, b, g, L, P, s_list, nullptr, select ? s_ptab : nullptr, e0, e1, lane, m, lsum,
                           acc);
   store_wave_part<D, G, kPathWaves>(s_parts, wave, lane, m, lsum, acc);
   __syncthreads();

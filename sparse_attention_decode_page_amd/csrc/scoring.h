@@ -22,9 +22,9 @@ namespace {
 // is issued before the current one is used, always (past the segment end the
 // loads read a valid row that is never used), and each window's entries are
 // read two windows ahead, so the loads in flight never sit behind a branch
-// and the wait before a batch covers only that batch's loads. ptab_out
-// (nullable, LDS) receives the segment's page-table entries as read. Page p's
-// score goes to srow[p - srow_base].
+// and the wait before a batch covers only that batch's loads. Page p's score
+// goes to srow[p - srow_base] and, when ptab_out (LDS) is given, its
+// page-table entry as read to ptab_out[p - srow_base].
 template <typename T, int D, int G>
 __device__ __forceinline__ void score_segment(const CacheView& c, const void* qv, int b, int g, int pb, int pe,
                                               float* srow, int lane, int* ptab_out = nullptr, int srow_base = 0) {
@@ -99,7 +99,7 @@ __device__ __forceinline__ void score_segment(const CacheView& c, const void* qv
   u32x4 loA[BATCH], hiA[BATCH], loB[BATCH], hiB[BATCH];
   int phA[BATCH], phB[BATCH];
   auto keep_window = [&](int wi, int raw) {
-    if (ptab_out != nullptr && pb + wi * kWave + lane < pe) ptab_out[pb + wi * kWave + lane] = raw;
+    if (ptab_out != nullptr && pb + wi * kWave + lane < pe) ptab_out[pb + wi * kWave + lane - srow_base] = raw;
   };
   keep_window(0, raw0);
   int win = window_of(0, raw0);

@@ -53,6 +53,7 @@ struct SliceArgs {
   float qk_scale;     // softmax scale * log2(e)
   int32_t* cand_page; // [units][S][cstride]
   float* cand_score;  // [units][S][cstride]
+  int32_t* cand_phys; // [units][S][cstride]: the candidate's page-table entry
   int32_t* cand_cnt;  // [units][S]
   int32_t* sel_idx;
   int32_t* sel_cnt;
@@ -87,6 +88,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kSliceThreads) void slice_score_kernel(SliceArgs a) {
   const CacheView& c = a.c;
   __shared__ float s_buf[kSliceMaxPages + 1];  // s_buf[1 + p - p0]: page p's score
+  __shared__ int s_ph[kSliceMaxPages];          // s_ph[p - p0]: page p's page-table entry
   __shared__ int s_pos[kSliceMaxPages + 1];
   __shared__ TopBShared<kSliceThreads> sh;
   float* s_score = s_buf + 1;
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(kSliceThreads) void slice_score_kernel(SliceArgs a)
   }
   const int wper = (p1 - p0 + kSliceWaves - 1) / kSliceWaves;
   const int w0 = min(p1, p0 + wave * wper), w1 = min(p1, w0 + wper);
-  if (w0 < w1) score_segment<BF16, D, G>(c, a.q, b, g, w0, w1, s_score, lane, nullptr, p0);
+  if (w0 < w1) score_segment<BF16, D, G>(c, a.q, b, g, w0, w1, s_score, lane, s_ph, p0);
   __syncthreads();
   if (a.scores != nullptr)
     for (int p = p0 + tid; p < p1; p += kSliceThreads) a.scores[(int64_t)u * c.max_pages + p] = s_score[p - p0];
@@ -119,10 +121,12 @@ __global__ __launch_bounds__(kSliceThreads) void slice_score_kernel(SliceArgs a)
   const int n = min(need, M);
   int32_t* cp = a.cand_page + ((int64_t)u * a.S + s) * a.cstride;
   float* cs = a.cand_score + ((int64_t)u * a.S + s) * a.cstride;
+  int32_t* cph = a.cand_phys + ((int64_t)u * a.S + s) * a.cstride;
   if (n == M) {
     for (int i = tid; i < M; i += kSliceThreads) {
       cp[i] = m0 + i;
       cs[i] = s_score[m0 + i - p0];
+      cph[i] = s_ph[m0 + i - p0];
     }
   } else {
     // srow[1 + i] = score of middle page m0 + i
@@ -136,6 +140,7 @@ __global__ __launch_bounds__(kSliceThreads) void slice_score_kernel(SliceArgs a)
       const int page = m0 + s_pos[i + 1] - 1;
       cp[i] = page;
       cs[i] = s_score[page - p0];
+      cph[i] = s_ph[page - p0];
     }
   }
   if (tid == 0) *cnt_out = n;
@@ -146,7 +151,9 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(SliceArgs a
   const CacheView& c = a.c;
   __shared__ float s_cs[kSliceMaxCand + 1];  // s_cs[1 + i]: candidate i's score
   __shared__ int s_cp[kSliceMaxCand + 1];    // s_cp[1 + i]: candidate i's page
+  __shared__ int s_cph[kSliceMaxCand + 1];   // s_cph[1 + i]: candidate i's page-table entry
   __shared__ int s_list[kSliceMaxList];
+  __shared__ int s_lph[kSliceMaxList];       // page-table entry of each s_list page
   __shared__ int s_pre[kSliceMaxS + 1];
   __shared__ TopBShared<kSliceThreads> sh;
   __shared__ WaveParts<D, G, kSliceWaves> s_parts;
@@ -163,64 +170,53 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(SliceArgs a
     return;
   }
   const bool select = K < P && K > 2;
-  // The kept pages, ascending, into s_list[0 .. K).
+  // The kept pages, ascending, into s_list[0 .. K), with their page-table
+  // entries in s_lph when K < P (the candidates carry theirs from scoring).
   if (K >= P) {
     for (int i = tid; i < P; i += kSliceThreads) s_list[i] = i;
   } else {
     if (tid == 0) {
+      const int32_t* prow = c.page_table + (int64_t)b * c.max_pages;
       s_list[0] = 0;
       s_list[K - 1] = P - 1;
+      s_lph[0] = prow[0];
+      s_lph[K - 1] = prow[P - 1];
     }
     if (select) {
       // Every slot of the unit's slices is requested together with the slices'
-      // counts (one round trip); the counted ones are packed in slice order.
+      // counts (one round trip), then the counted ones are packed in slice
+      // order straight from the registers.
       const int nslot = a.S * a.cstride;
-      int cnt_j = 0;
-      if (tid < a.S) cnt_j = a.cand_cnt[(int64_t)u * a.S + tid];
-      const int32_t* cp = a.cand_page + (int64_t)u * a.S * a.cstride;
-      const float* cs = a.cand_score + (int64_t)u * a.S * a.cstride;
-      for (int i = tid; i < nslot; i += kSliceThreads) {
-        s_cp[1 + i] = cp[i];
-        s_cs[1 + i] = cs[i];
-      }
-      if (tid < a.S) s_pre[tid] = cnt_j;
-      __syncthreads();
-      if (tid == 0) {
-        int t = 0;
-        for (int j = 0; j < a.S; ++j) {
-          const int n = s_pre[j];
-          s_pre[j] = t;
-          t += n;
-        }
-        s_pre[a.S] = t;
-      }
-      __syncthreads();
-      const int Mc = s_pre[a.S];
-      // pack slot j*cstride + k (k < count_j) to position s_pre[j] + k, in place
-      // through registers: every thread reads its slots before any writes
+      if (tid < a.S) s_pre[tid] = a.cand_cnt[(int64_t)u * a.S + tid];
+      const int64_t ubase = (int64_t)u * a.S * a.cstride;
       constexpr int kSlotsPerThread = (kSliceMaxCand + kSliceThreads - 1) / kSliceThreads;
-      int pk[kSlotsPerThread];
+      int pk[kSlotsPerThread], ph[kSlotsPerThread];
       float sk[kSlotsPerThread];
-      int dst[kSlotsPerThread];
 #pragma unroll
       for (int r = 0; r < kSlotsPerThread; ++r) {
         const int i = tid + r * kSliceThreads;
-        dst[r] = -1;
         if (i < nslot) {
-          const int j = i / a.cstride, k = i % a.cstride;
-          if (k < s_pre[j + 1] - s_pre[j]) {
-            dst[r] = s_pre[j] + k;
-            pk[r] = s_cp[1 + i];
-            sk[r] = s_cs[1 + i];
-          }
+          pk[r] = a.cand_page[ubase + i];
+          sk[r] = a.cand_score[ubase + i];
+          ph[r] = a.cand_phys[ubase + i];
         }
       }
       __syncthreads();
+      // Lane j of every wave: slice j's count and the counts before it.
+      const int cj = lane < a.S ? s_pre[lane] : 0;
+      const int incl = wave_incl_scan(cj);
+      const int Mc = __builtin_amdgcn_readlane(incl, a.S - 1);
 #pragma unroll
       for (int r = 0; r < kSlotsPerThread; ++r) {
-        if (dst[r] >= 0) {
-          s_cp[1 + dst[r]] = pk[r];
-          s_cs[1 + dst[r]] = sk[r];
+        const int i = tid + r * kSliceThreads;
+        const int j = min(i / a.cstride, a.S - 1);
+        const int before = __shfl(incl - cj, j);
+        const int cnt = __shfl(cj, j);
+        const int k = i - j * a.cstride;
+        if (i < nslot && k < cnt) {
+          s_cp[1 + before + k] = pk[r];
+          s_cs[1 + before + k] = sk[r];
+          s_cph[1 + before + k] = ph[r];
         }
       }
       __syncthreads();
@@ -229,7 +225,11 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(SliceArgs a
       else
         slice_top<kSliceKeys>(s_cs, Mc, K - 2, s_list, sh);
       __syncthreads();
-      for (int i = 1 + tid; i < K - 1; i += kSliceThreads) s_list[i] = s_cp[s_list[i]];
+      for (int i = 1 + tid; i < K - 1; i += kSliceThreads) {
+        const int ci = s_list[i];
+        s_list[i] = s_cp[ci];
+        s_lph[i] = s_cph[ci];
+      }
     }
   }
   __syncthreads();
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(SliceArgs a
     const int wper = (s1 - s0 + kSliceWaves - 1) / kSliceWaves;
     const int e0 = min(s1, s0 + wave * wper), e1 = min(s1, e0 + wper);
     float m[G], lsum[G], acc[G][8];
-    stream_list_range<D, G>(c, a.q, a.qk_scale, b, g, L, P, s_list, nullptr, e0, e1, lane, m, lsum, acc);
+    stream_list_range<D, G>(c, a.q, a.qk_scale, b, g, L, P, s_list, K < P ? s_lph : nullptr, nullptr, e0, e1, lane, m,
+                            lsum, acc);
     store_wave_part<D, G, kSliceWaves>(s_parts, wave, lane, m, lsum, acc);
     __syncthreads();
     const int64_t slot = (int64_t)u * a.S + s;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(SliceArgs a
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct SliceLayout {
-  size_t cand_page, cand_score, cand_cnt, part_acc, part_ml, count, total;
+  size_t cand_page, cand_score, cand_phys, cand_cnt, part_acc, part_ml, count, total;
 };
 
 // Workspace regions, each sized for any S the form takes: S * (max_budget - 2)
@@ -280,6 +281,8 @@ SliceLayout slice_layout(const CacheView& c) {
   off += align256(units * kSliceMaxCand * sizeof(int32_t));
   l.cand_score = off;
   off += align256(units * kSliceMaxCand * sizeof(float));
+  l.cand_phys = off;
+  off += align256(units * kSliceMaxCand * sizeof(int32_t));
   l.cand_cnt = off;
   off += align256(units * kSliceMaxS * sizeof(int32_t));
   l.part_acc = off;
@@ -353,6 +356,7 @@ hipError_t launch_slice_path(const CacheView& c, const void* q, const int32_t* b
   a.qk_scale = scale * kLog2e;
   a.cand_page = reinterpret_cast<int32_t*>(base + l.cand_page);
   a.cand_score = reinterpret_cast<float*>(base + l.cand_score);
+  a.cand_phys = reinterpret_cast<int32_t*>(base + l.cand_phys);
   a.cand_cnt = reinterpret_cast<int32_t*>(base + l.cand_cnt);
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;

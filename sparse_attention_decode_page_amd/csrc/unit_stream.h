@@ -22,13 +22,16 @@ struct WaveParts {
 };
 
 // One wave's partial over entries [e0, e1) of `list` (logical pages, LDS) of
-// unit (b, g) with L tokens in P pages. ptab (nullable, LDS) holds the unit's
-// page-table row; otherwise entries are looked up in the page table. Leaves
-// the closed partial in m, lsum, acc (m = kNegBig, zeros for an empty range).
+// unit (b, g) with L tokens in P pages. An entry's physical page comes from
+// lphys (nullable, LDS: the page-table entry of each list entry), else from
+// ptab (nullable, LDS: the unit's page-table row), else from the page table.
+// Leaves the closed partial in m, lsum, acc (m = kNegBig, zeros for an empty
+// range).
 template <int D, int G>
 __device__ __forceinline__ void stream_list_range(const CacheView& c, const void* q, float qk_scale, int b, int g,
-                                                  int L, int P, const int* list, const int* ptab, int e0, int e1,
-                                                  int lane, float (&m)[G], float (&lsum)[G], float (&acc)[G][8]) {
+                                                  int L, int P, const int* list, const int* lphys, const int* ptab,
+                                                  int e0, int e1, int lane, float (&m)[G], float (&lsum)[G],
+                                                  float (&acc)[G][8]) {
   constexpr int NJ = D / 32;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -47,8 +50,10 @@ __device__ __forceinline__ void stream_list_range(const CacheView& c, const void
   for (int wb = e0; wb < e1; wb += kWave) {
     // Window of up to 64 entries: lane i holds entry wb+i's physical page and valid tokens.
     const int nwin = min(kWave, e1 - wb);
-    const int logical = list[min(wb + lane, e1 - 1)];
-    const int ph = ptab != nullptr
+    const int ei = min(wb + lane, e1 - 1);
+    const int logical = list[ei];
+    const int ph = lphys != nullptr ? lphys[ei]
+                   : ptab != nullptr
                        ? ptab[min(max(logical, 0), P - 1)]
                        : c.page_table[(int64_t)b * c.max_pages + min(max(logical, 0), c.max_pages - 1)];
     const bool ok = lane < nwin && logical >= 0 && logical < P && ph >= 0 && ph < c.num_phys;

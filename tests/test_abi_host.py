@@ -120,12 +120,13 @@ def test_sparse_path_checks(L):
     sp = L.spdec_sparse_path
     need = L.spdec_sparse_path_workspace_bytes(ctypes.byref(d), 16)
     # the two calls' needs (scores rounded up to 256 bytes, then the decode's workspace) or the sliced form's
-    # (every unit's candidates: 4096 page-score pairs, 16 slices' counts and partials), whichever is larger
+    # (every unit's candidates: 4096 page, score and page-table triples, 16 slices' counts and partials), whichever
+    # is larger
     sel = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
     two = (sel + 255) // 256 * 256 + L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
     r = lambda x: (x + 255) // 256 * 256
     units, G, D = 4, 4, 128
-    sliced = r(units * 4096 * 4) * 2 + r(units * 16 * 4) + r(units * 16 * G * D * 4) + r(units * 16 * G * 2 * 4) + r(units * 4)
+    sliced = r(units * 4096 * 4) * 3 + r(units * 16 * 4) + r(units * 16 * G * D * 4) + r(units * 16 * G * 2 * 4) + r(units * 4)
     assert need == max(two, sliced)
     assert L.spdec_sparse_path_workspace_bytes(ctypes.byref(d), 1) == 0
     assert L.spdec_sparse_path_workspace_bytes(None, 16) == 0
