@@ -64,11 +64,12 @@ struct PathArgs {
   int lpt;          // 1: workgroups take units largest first (more units than compute units)
 };
 
-// Pages P and kept pages K of sequence b, and the bytes one of its units
-// reads in units of 4*D bytes (a page summary, or one token's K and V row).
-__device__ __forceinline__ long long path_work(const PathArgs& a, int b, int& P, int& K) {
+// Tokens L, pages P and kept pages K of sequence b, and the bytes one of its
+// units reads in units of 4*D bytes (a page summary, or one token's K and V
+// row).
+__device__ __forceinline__ long long path_work(const PathArgs& a, int b, int& L, int& P, int& K) {
   const CacheView& c = a.c;
-  const int L = max(c.seq_lens[b], 0);
+  L = max(c.seq_lens[b], 0);
   P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
   K = min(min(max(a.budget[b], 2), a.cap), P);
   const bool scored = K < P && K > 2;
@@ -78,13 +79,14 @@ __device__ __forceinline__ long long path_work(const PathArgs& a, int b, int& P,
 // s_rank[t] = rank of sequence t when sequences are ordered by path_work,
 // largest first, ties to the lower index. The comparisons are split over all
 // threads (parts = kPathThreads / B per sequence) and their counts added in
-// LDS. Ends with a barrier.
-__device__ __forceinline__ void rank_sequences(const PathArgs& a, long long* s_work, int* s_rank) {
+// LDS. Thread t < B (B <= kPathThreads) returns sequence t's L, P, K. Ends
+// with a barrier.
+__device__ __forceinline__ void rank_sequences(const PathArgs& a, long long* s_work, int* s_rank, int& L, int& P,
+                                               int& K) {
   const int tid = threadIdx.x, B = a.c.batch;
-  for (int t = tid; t < B; t += kPathThreads) {
-    int P, K;
-    s_work[t] = path_work(a, t, P, K);
-    s_rank[t] = 0;
+  if (tid < B) {
+    s_work[tid] = path_work(a, tid, L, P, K);
+    s_rank[tid] = 0;
   }
   __syncthreads();
   const int parts = max(1, kPathThreads / B);
@@ -115,27 +117,36 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   __shared__ int s_rank[kPathMaxSeqs];
   __shared__ TopBShared<kPathThreads> sh;
   __shared__ WaveParts<D, G, kPathWaves> s_parts;
-  __shared__ int s_seq;
+  __shared__ int s_seq, s_L, s_P, s_K;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int B = c.batch;
 
   // The unit: KV head blockIdx % Hkv of the sequence of rank blockIdx / Hkv
   // (with no more units than compute units every unit starts at once, and the
   // rank is the sequence index).
+  // The thread that found the unit's sequence passes its shape on in LDS.
   const int want = blockIdx.x / c.hkv, g = blockIdx.x % c.hkv;
   if (a.lpt) {
-    rank_sequences(a, s_work, s_rank);
-    for (int t = tid; t < B; t += kPathThreads)
-      if (s_rank[t] == want) s_seq = t;
+    int tL = 0, tP = 0, tK = 0;
+    rank_sequences(a, s_work, s_rank, tL, tP, tK);
+    if (tid < B && s_rank[tid] == want) {
+      s_seq = tid;
+      s_L = tL;
+      s_P = tP;
+      s_K = tK;
+    }
   } else if (tid == 0) {
+    int tL, tP, tK;
+    path_work(a, want, tL, tP, tK);
     s_seq = want;
+    s_L = tL;
+    s_P = tP;
+    s_K = tK;
   }
   __syncthreads();
   const int b = s_seq;
   const int u = b * c.hkv + g;
-  const int L = max(c.seq_lens[b], 0);
-  int P, K;
-  path_work(a, b, P, K);
+  const int L = s_L, P = s_P, K = s_K;
   float* out_rows = a.out + ((int64_t)b * c.hq + g * G) * D;
   float* lse_rows = a.lse != nullptr ? a.lse + (int64_t)b * c.hq + g * G : nullptr;
   if (P == 0) {  // no token: no page, zero output, lse = ln 0
