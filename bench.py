@@ -108,9 +108,6 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_counters_{workload}.md")
 
 
-# The measured kernels (dense and sparse decode, scoring, top-B, acceptance) and
-# their launch configuration (plans, resident grid); a change to any of these
-# invalidates the recorded counter traffic.
 # Every device source of the library: a change to any of them voids the committed counter traffic.
 KERNEL_SOURCES = tuple(sorted(f for f in os.listdir(os.path.join(ROOT, "sparse_attention_decode_page_amd", "csrc"))
                               if f.endswith((".hip", ".h"))))
@@ -443,14 +440,17 @@ def gather_ceiling(cache, spec, sel_idx, sel_cnt, scrubbed, t_select=None, t_dec
     return res
 
 
-def call_kernels(spec, form="one kernel"):
+def call_kernels(spec, form="one kernel", select_form="two calls"):
     """Name patterns (over the counter summaries' kernel names) of the kernels each call launches on a bf16
-    workload of this shape; the merge's form and the Top-B's size class depend on the workload, the step's
-    form (one kernel, sliced or the two calls) on the batch."""
+    workload of this shape; the merge's form and the Top-B's size class depend on the workload, the step's and
+    the selection's forms (one kernel, sliced, or two calls / two kernels) on the batch."""
     D, G = spec.head_dim, spec.group
     dec = (lambda sp: f"decode_stream_g8_kernel<{D},{sp}>") if G == 8 else \
         (lambda sp: f"decode_stream_kernel<{D},{G},{sp}>")
-    calls = {"select_pages": [f"score_stream_kernel<BF16,{D},{G}>", "select_topk_reg_kernel<*>"],
+    select = {"one kernel": [f"select_path_kernel<{D},{G}>"],
+              "sliced": [f"slice_score_kernel<{D},{G}>", f"slice_select_kernel<{D},{G},false>"]}.get(
+        select_form, [f"score_stream_kernel<BF16,{D},{G}>", "select_topk_reg_kernel<*>"])
+    calls = {"select_pages": select,
              "sparse_decode": [dec("true"), f"stream_merge_kernel<{D},*,true>"],
              "dense_decode": [dec("false"), f"stream_merge_kernel<{D},*,false>"]}
     calls["sparse_path"] = {
@@ -556,6 +556,7 @@ def layer_rows(args, dev, timers, name, acceptance=False):
     o = torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device=dev)
     form = spdec.sparse_path_form(cache, cap)
+    select_form = spdec.select_pages_form(cache, cap)
 
     def path(i=0):
         spdec.sparse_path(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, out=o, lse=lse, workspace=ws_path)
@@ -587,7 +588,7 @@ def layer_rows(args, dev, timers, name, acceptance=False):
         "budget": describe_budget(spec),
         "sparse_path": dict(_row(t_path, b_path), tokens_per_s=spec.batch / t_path, form=form),
         "two_calls": dict(_row(t_two, b_path), tokens_per_s=spec.batch / t_two),
-        "select_pages": _row(t_sel, byt["select_pages"]),
+        "select_pages": dict(_row(t_sel, byt["select_pages"]), form=select_form),
         "sparse_decode": _row(t_dec, byt["sparse_decode"]),
         "dense_decode": dict(_row(t_dense, byt["dense_decode"]), tokens_per_s=spec.batch / t_dense),
         "sparse_over_dense": t_dense / t_path,
@@ -595,7 +596,7 @@ def layer_rows(args, dev, timers, name, acceptance=False):
                   "to back",
     }
     traffic = counter_traffic(spec.name)
-    ck = call_kernels(spec, form)
+    ck = call_kernels(spec, form, select_form)
     for call in ("sparse_path", "select_pages", "sparse_decode", "dense_decode"):
         res[call]["traffic"] = traffic_sum(traffic, ck[call])
     res["two_calls"]["traffic"] = traffic_sum(traffic, ck["select_pages"] + ck["sparse_decode"])
@@ -966,6 +967,7 @@ def main():
         spdec.sparse_decode(cache, q, sel_idx, sel_cnt, cap, out=o_s, lse=l_s, workspace=ws_sp)
 
     form = spdec.sparse_path_form(cache, cap)
+    select_form = spdec.select_pages_form(cache, cap)
 
     def sparse_path(i=0):
         spdec.sparse_path(cache, q, budget, cap, sel_idx=sel_idx, sel_cnt=sel_cnt, out=o_s, lse=l_s,
@@ -1095,7 +1097,7 @@ def main():
 
     # HBM traffic measured by rocprofv3 counters for these kernels (bytes per call), if still current
     traffic = counter_traffic(spec.name)
-    ck = call_kernels(spec, form)
+    ck = call_kernels(spec, form, select_form)
     dec_kernels, sel_kernels, dense_kernels = ck["sparse_decode"], ck["select_pages"], ck["dense_decode"]
     path_kernels = ck["sparse_path"]
     acc_kernels = ["acc_one_read_kernel<true>"]
@@ -1150,7 +1152,8 @@ def main():
                                      kernels=" + ".join(sel_kernels + dec_kernels),
                                      timing="median of 3 x (K x (1 GiB scrub read, select_pages, sparse_decode) "
                                             "minus K x scrub)"),
-                   "select_pages": dict(_row(sel_t, byt_sp["select_pages"]), traffic=traffic_of(sel_kernels)),
+                   "select_pages": dict(_row(sel_t, byt_sp["select_pages"]), traffic=traffic_of(sel_kernels),
+                                        form=select_form, kernels=" + ".join(sel_kernels)),
                    "sparse_decode": dict(_row(dec_t, byt_sp["sparse_decode"]), traffic=traffic_of(dec_kernels))},
         "gather_ceiling": ceiling,
         "value_runs": {"tokens_per_s": [spec.batch / t for t in value_runs], "median": value,

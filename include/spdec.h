@@ -164,9 +164,28 @@ spdec_status spdec_build_meta(const spdec_cache* cache, hipStream_t stream);
  *               ascending; entries past sel_cnt are left untouched
  * sel_cnt:      int32 [batch][Hkv] out: K
  * scores_out:   nullable fp32 [batch][Hkv][max_pages_per_seq] out: s_p for p < P
- * max_budget_pages >= 2. Workspace: spdec_select_workspace_bytes().
+ * Forms (SPDEC_PATH_* below; the same scores and cut in each, so the same
+ * selection), bf16 cache and G <= 4 for the fused ones, on the current device:
+ *   SPDEC_PATH_ONE_KERNEL: the shapes of spdec_sparse_path's one-kernel form:
+ *     one workgroup per (sequence, KV head) scores its pages into LDS and
+ *     takes the Top-k there (no workspace used);
+ *   SPDEC_PATH_SLICED: the shapes of spdec_sparse_path's sliced form, when
+ *     the workspace holds spdec_select_workspace_bytes(): each slice's own
+ *     Top-k candidates, then the unit's Top-k from them (two kernels);
+ *   SPDEC_PATH_TWO_CALLS: otherwise: a scoring kernel writes every score to
+ *     scores_out or the workspace, a Top-k kernel reads them.
+ * max_budget_pages >= 2. Workspace: spdec_select_workspace_bytes() (enough
+ * for every form; may be null when scores_out is given, which rules out the
+ * sliced form). No part of it needs to be cleared.
  */
+#define SPDEC_PATH_TWO_CALLS 0
+#define SPDEC_PATH_ONE_KERNEL 1
+#define SPDEC_PATH_SLICED 2
 size_t spdec_select_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
+/* The form (SPDEC_PATH_*) spdec_select_pages takes for this cache shape on the
+ * current device with the full workspace, or a negative spdec_status for an
+ * invalid descriptor or max_budget_pages < 2. */
+int spdec_select_pages_form(const spdec_cache* cache, int max_budget_pages);
 spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
                                 int max_budget_pages, int32_t* sel_idx, int32_t* sel_cnt, float* scores_out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -279,9 +298,6 @@ spdec_status spdec_dense_decode(const spdec_cache* cache, const void* q, float s
  * form; no part of it needs to be cleared). Calls that share a workspace must
  * not overlap.
  */
-#define SPDEC_PATH_TWO_CALLS 0
-#define SPDEC_PATH_ONE_KERNEL 1
-#define SPDEC_PATH_SLICED 2
 size_t spdec_sparse_path_workspace_bytes(const spdec_cache* cache, int max_budget_pages);
 /* The form (SPDEC_PATH_*) spdec_sparse_path takes for this cache shape on the
  * current device, or a negative spdec_status for an invalid descriptor or

@@ -106,7 +106,33 @@ spdec_status spdec_build_meta(const spdec_cache* cache, hipStream_t stream) {
 size_t spdec_select_workspace_bytes(const spdec_cache* cache, int max_budget_pages) {
   CacheView v;
   if (view_of(cache, &v) != SPDEC_OK || max_budget_pages < 2) return 0;
-  return spdec::select_workspace_bytes(v);
+  const size_t scores = spdec::select_workspace_bytes(v);
+  const size_t sliced = spdec::slice_workspace_bytes(v, max_budget_pages);
+  return scores > sliced ? scores : sliced;
+}
+
+// The form spdec_select_pages takes for a validated shape on the current
+// device, given workspace_bytes of workspace: the one-kernel selection needs
+// none, the sliced one its candidate slots, the two kernels the scores
+// (unless they go to scores_out).
+static int select_form(const CacheView& v, int max_budget_pages, size_t workspace_bytes, int* slices) {
+  *slices = 0;
+  if (spdec::path_fused_supported(v, max_budget_pages)) return SPDEC_PATH_ONE_KERNEL;
+  const int S = spdec::slice_count(v, max_budget_pages, spdec::device_compute_units());
+  if (S > 0 && workspace_bytes >= spdec::slice_workspace_bytes(v, max_budget_pages)) {
+    *slices = S;
+    return SPDEC_PATH_SLICED;
+  }
+  return SPDEC_PATH_TWO_CALLS;
+}
+
+int spdec_select_pages_form(const spdec_cache* cache, int max_budget_pages) {
+  CacheView v;
+  const spdec_status st = view_of(cache, &v);
+  if (st != SPDEC_OK) return st;
+  if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
+  int slices;
+  return select_form(v, max_budget_pages, spdec_select_workspace_bytes(cache, max_budget_pages), &slices);
 }
 
 spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const int32_t* budget_pages,
@@ -118,8 +144,17 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
   if (!v.kminmax || !q || !budget_pages || !sel_idx || !sel_cnt) return SPDEC_ERR_INVALID;
   if (!aligned16(v.kminmax) || !aligned16(q)) return SPDEC_ERR_INVALID;
   if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
-  if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
+  if (scores_out == nullptr &&
+      (workspace == nullptr || workspace_bytes < spdec_select_workspace_bytes(cache, max_budget_pages)))
     return SPDEC_ERR_WORKSPACE;
+  int slices;
+  const int form = select_form(v, max_budget_pages, workspace == nullptr ? 0 : workspace_bytes, &slices);
+  if (form == SPDEC_PATH_ONE_KERNEL)
+    return from_hip(spdec::launch_sparse_path_fused(v, q, budget_pages, max_budget_pages, 1.f, sel_idx, sel_cnt,
+                                                    scores_out, nullptr, nullptr, stream));
+  if (form == SPDEC_PATH_SLICED)
+    return from_hip(spdec::launch_slice_path(v, q, budget_pages, max_budget_pages, slices, 1.f, sel_idx, sel_cnt,
+                                             scores_out, nullptr, nullptr, workspace, stream));
   return from_hip(spdec::launch_select(v, q, budget_pages, max_budget_pages, sel_idx, sel_cnt, scores_out, workspace,
                                        stream));
 }
@@ -136,7 +171,8 @@ spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, f
   if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
   if (!isfinite(top_p) || !(top_p > 0.f) || !(top_p <= 1.f)) return SPDEC_ERR_INVALID;
   if (!isfinite(score_scale) || !(score_scale >= 0.f)) return SPDEC_ERR_INVALID;
-  if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
+  if (scores_out == nullptr &&
+      (workspace == nullptr || workspace_bytes < spdec_select_workspace_bytes(cache, max_budget_pages)))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_select_top_p(v, q, top_p, score_scale, budget_pages, max_budget_pages, sel_idx,
                                              sel_cnt, scores_out, workspace, stream));
@@ -154,7 +190,8 @@ spdec_status spdec_select_pages_shared(const spdec_cache* cache, const void* q, 
   if (max_budget_pages < 2) return SPDEC_ERR_INVALID;
   if (group_size < 1 || v.batch % group_size != 0) return SPDEC_ERR_INVALID;
   if (!spdec::select_shared_supported(v, group_size)) return SPDEC_ERR_UNSUPPORTED;
-  if (scores_out == nullptr && (workspace == nullptr || workspace_bytes < spdec::select_workspace_bytes(v)))
+  if (scores_out == nullptr &&
+      (workspace == nullptr || workspace_bytes < spdec_select_workspace_bytes(cache, max_budget_pages)))
     return SPDEC_ERR_WORKSPACE;
   return from_hip(spdec::launch_select_shared(v, q, budget_pages, max_budget_pages, group_size, shared_pages, sel_idx,
                                               sel_cnt, scores_out, workspace, stream));

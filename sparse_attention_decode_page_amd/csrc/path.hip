@@ -62,18 +62,19 @@ struct PathArgs {
   float* out;
   float* lse;       // nullable
   int lpt;          // 1: workgroups take units largest first (more units than compute units)
+  int stream;       // 1: the whole step; 0: the selection only (no attention)
 };
 
 // Tokens L, pages P and kept pages K of sequence b, and the bytes one of its
 // units reads in units of 4*D bytes (a page summary, or one token's K and V
-// row).
+// row; the summaries only for the selection alone).
 __device__ __forceinline__ long long path_work(const PathArgs& a, int b, int& L, int& P, int& K) {
   const CacheView& c = a.c;
   L = max(c.seq_lens[b], 0);
   P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
   K = min(min(max(a.budget[b], 2), a.cap), P);
   const bool scored = K < P && K > 2;
-  return (scored ? (long long)P : 0ll) + (long long)min(L, K * c.page_size);
+  return (scored ? (long long)P : 0ll) + (a.stream ? (long long)min(L, K * c.page_size) : 0ll);
 }
 
 // s_rank[t] = rank of sequence t when sequences are ordered by path_work,
@@ -106,54 +107,58 @@ __device__ __forceinline__ void rank_sequences(const PathArgs& a, long long* s_w
   __syncthreads();
 }
 
+// LDS of the per-unit selection.
+struct UnitSelectShared {
+  float score[kPathMaxPages];
+  int list[kPathMaxPages];
+  long long work[kPathMaxSeqs];
+  int rank[kPathMaxSeqs];
+  TopBShared<kPathThreads> sh;
+  int seq, L, P, K;
+};
+
+// The workgroup's unit (b, g) with its L tokens in P pages, and its kept pages
+// (K, ascending) in sm.list, also written to sel_idx / sel_cnt. ptab
+// (nullable, LDS) receives the unit's page-table row when the pages are
+// scored. Returns false, after writing sel_cnt = 0, for a unit with no token.
 template <int D, int G>
-__global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
-  constexpr int MAXP = kPathMaxPages;
+__device__ __forceinline__ bool unit_selection(const PathArgs& a, UnitSelectShared& sm, int* ptab, int& b, int& g,
+                                               int& L, int& P, int& K) {
   const CacheView& c = a.c;
-  __shared__ float s_score[MAXP];
-  __shared__ int s_list[MAXP];
-  __shared__ int s_ptab[MAXP];  // the unit's page-table row, when the scoring pass read it
-  __shared__ long long s_work[kPathMaxSeqs];
-  __shared__ int s_rank[kPathMaxSeqs];
-  __shared__ TopBShared<kPathThreads> sh;
-  __shared__ WaveParts<D, G, kPathWaves> s_parts;
-  __shared__ int s_seq, s_L, s_P, s_K;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int B = c.batch;
-
   // The unit: KV head blockIdx % Hkv of the sequence of rank blockIdx / Hkv
   // (with no more units than compute units every unit starts at once, and the
-  // rank is the sequence index).
-  // The thread that found the unit's sequence passes its shape on in LDS.
-  const int want = blockIdx.x / c.hkv, g = blockIdx.x % c.hkv;
+  // rank is the sequence index). The thread that found the unit's sequence
+  // passes its shape on in LDS.
+  const int want = blockIdx.x / c.hkv;
+  g = blockIdx.x % c.hkv;
   if (a.lpt) {
     int tL = 0, tP = 0, tK = 0;
-    rank_sequences(a, s_work, s_rank, tL, tP, tK);
-    if (tid < B && s_rank[tid] == want) {
-      s_seq = tid;
-      s_L = tL;
-      s_P = tP;
-      s_K = tK;
+    rank_sequences(a, sm.work, sm.rank, tL, tP, tK);
+    if (tid < B && sm.rank[tid] == want) {
+      sm.seq = tid;
+      sm.L = tL;
+      sm.P = tP;
+      sm.K = tK;
     }
   } else if (tid == 0) {
     int tL, tP, tK;
     path_work(a, want, tL, tP, tK);
-    s_seq = want;
-    s_L = tL;
-    s_P = tP;
-    s_K = tK;
+    sm.seq = want;
+    sm.L = tL;
+    sm.P = tP;
+    sm.K = tK;
   }
   __syncthreads();
-  const int b = s_seq;
+  b = sm.seq;
+  L = sm.L;
+  P = sm.P;
+  K = sm.K;
   const int u = b * c.hkv + g;
-  const int L = s_L, P = s_P, K = s_K;
-  float* out_rows = a.out + ((int64_t)b * c.hq + g * G) * D;
-  float* lse_rows = a.lse != nullptr ? a.lse + (int64_t)b * c.hq + g * G : nullptr;
-  if (P == 0) {  // no token: no page, zero output, lse = ln 0
-    for (int i = tid; i < G * D; i += kPathThreads) out_rows[i] = 0.f;
-    if (lse_rows != nullptr && tid < G) lse_rows[tid] = -INFINITY;
+  if (P == 0) {
     if (tid == 0) a.sel_cnt[u] = 0;
-    return;
+    return false;
   }
 
   // Scores of the unit's pages (needed by the select, or asked for).
@@ -161,30 +166,51 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   if (select || a.scores != nullptr) {
     const int per = (P + kPathWaves - 1) / kPathWaves;
     const int p0 = min(P, wave * per), p1 = min(P, p0 + per);
-    if (p0 < p1) score_segment<BF16, D, G>(c, a.q, b, g, p0, p1, s_score, lane, s_ptab);
+    if (p0 < p1) score_segment<BF16, D, G>(c, a.q, b, g, p0, p1, sm.score, lane, ptab);
   }
   __syncthreads();
   if (a.scores != nullptr)
-    for (int i = tid; i < P; i += kPathThreads) a.scores[(int64_t)u * c.max_pages + i] = s_score[i];
+    for (int i = tid; i < P; i += kPathThreads) a.scores[(int64_t)u * c.max_pages + i] = sm.score[i];
 
-  // The kept pages, ascending, into s_list[0 .. K).
+  // The kept pages, ascending, into list[0 .. K).
   if (K >= P) {
-    for (int i = tid; i < P; i += kPathThreads) s_list[i] = i;
+    for (int i = tid; i < P; i += kPathThreads) sm.list[i] = i;
   } else {
     if (tid == 0) {
-      s_list[0] = 0;
-      s_list[K - 1] = P - 1;
+      sm.list[0] = 0;
+      sm.list[K - 1] = P - 1;
     }
     if (select) {
       if (P - 2 <= kPathKeysShort * kPathThreads)
-        path_top<kPathKeysShort>(s_score, P - 2, K - 2, s_list, sh);
+        path_top<kPathKeysShort>(sm.score, P - 2, K - 2, sm.list, sm.sh);
       else
-        path_top<kPathKeys>(s_score, P - 2, K - 2, s_list, sh);
+        path_top<kPathKeys>(sm.score, P - 2, K - 2, sm.list, sm.sh);
     }
   }
   __syncthreads();
-  for (int i = tid; i < K; i += kPathThreads) a.sel_idx[(int64_t)u * a.cap + i] = s_list[i];
+  for (int i = tid; i < K; i += kPathThreads) a.sel_idx[(int64_t)u * a.cap + i] = sm.list[i];
   if (tid == 0) a.sel_cnt[u] = K;
+  return true;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
+  const CacheView& c = a.c;
+  __shared__ UnitSelectShared sm;
+  __shared__ int s_ptab[kPathMaxPages];  // the unit's page-table row, when the scoring pass read it
+  __shared__ WaveParts<D, G, kPathWaves> s_parts;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  int b, g, L, P, K;
+  const bool any = unit_selection<D, G>(a, sm, s_ptab, b, g, L, P, K);
+  float* out_rows = a.out + ((int64_t)b * c.hq + g * G) * D;
+  float* lse_rows = a.lse != nullptr ? a.lse + (int64_t)b * c.hq + g * G : nullptr;
+  if (!any) {  // no token: no page, zero output, lse = ln 0
+    for (int i = tid; i < G * D; i += kPathThreads) out_rows[i] = 0.f;
+    if (lse_rows != nullptr && tid < G) lse_rows[tid] = -INFINITY;
+    return;
+  }
+  const bool select = K < P && K > 2;
+  const int* s_list = sm.list;
 
   // Attention over the kept pages: wave w streams entries [w*per, (w+1)*per).
   float m[G], lsum[G], acc[G][8];
@@ -207,13 +233,31 @@ __global__ __launch_bounds__(kPathThreads) void sparse_path_kernel(PathArgs a) {
   }
 }
 
+// The selection alone (spdec_select_pages) in one kernel: each workgroup
+// scores its unit's pages into LDS and takes the Top-B there, so the scores
+// never go through HBM (unless asked for) and one launch replaces two.
+template <int D, int G>
+__global__ __launch_bounds__(kPathThreads) void select_path_kernel(PathArgs a) {
+  __shared__ UnitSelectShared sm;
+  int b, g, L, P, K;
+  unit_selection<D, G>(a, sm, nullptr, b, g, L, P, K);
+}
+
 template <int D>
 hipError_t path_launch(const PathArgs& a, hipStream_t s) {
   const dim3 grid(a.c.batch * a.c.hkv), block(kPathThreads);
-  switch (a.c.group) {
-    case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((sparse_path_kernel<D, 4>), grid, block, 0, s, a); break;
+  if (a.stream) {
+    switch (a.c.group) {
+      case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((sparse_path_kernel<D, 4>), grid, block, 0, s, a); break;
+    }
+  } else {
+    switch (a.c.group) {
+      case 1: hipLaunchKernelGGL((select_path_kernel<D, 1>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((select_path_kernel<D, 2>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((select_path_kernel<D, 4>), grid, block, 0, s, a); break;
+    }
   }
   return hipGetLastError();
 }
@@ -241,6 +285,7 @@ hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int
   a.out = out;
   a.lse = lse;
   a.lpt = (int64_t)c.batch * c.hkv > device_compute_units() ? 1 : 0;
+  a.stream = out != nullptr ? 1 : 0;
   return c.head_dim == 64 ? path_launch<64>(a, s) : path_launch<128>(a, s);
 }
 

@@ -22,7 +22,7 @@ SPDEC_F32, SPDEC_BF16 = 0, 1
 ABI_FUNCTIONS = (
     "spdec_default_scale", "spdec_default_score_scale",
     "spdec_status_string", "spdec_version", "spdec_append_kv", "spdec_build_meta",
-    "spdec_select_workspace_bytes", "spdec_select_pages", "spdec_select_pages_shared", "spdec_select_pages_top_p",
+    "spdec_select_workspace_bytes", "spdec_select_pages_form", "spdec_select_pages", "spdec_select_pages_shared", "spdec_select_pages_top_p",
     "spdec_decode_workspace_bytes",
     "spdec_sparse_decode", "spdec_sparse_path_workspace_bytes", "spdec_sparse_path_form", "spdec_sparse_path",
     "spdec_dense_decode",
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "spdec_append_kv": (I, [D, P, P, P]),
         "spdec_build_meta": (I, [D, P]),
         "spdec_select_workspace_bytes": (SZ, [D, I]),
+        "spdec_select_pages_form": (I, [D, I]),
         "spdec_select_pages": (I, [D, P, P, I, P, P, P, P, SZ, P]),
         "spdec_select_pages_shared": (I, [D, P, I, P, P, I, P, P, P, P, SZ, P]),
         "spdec_select_pages_top_p": (I, [D, P, F, F, P, I, P, P, P, P, SZ, P]),
@@ -200,6 +201,14 @@ def build_meta(cache: PagedCache):
 
 def select_workspace_bytes(cache: PagedCache, max_budget_pages: int) -> int:
     return int(lib().spdec_select_workspace_bytes(ctypes.byref(cache.desc), int(max_budget_pages)))
+
+
+def select_pages_form(cache: PagedCache, max_budget_pages: int) -> str:
+    """Which form select_pages takes for this shape on the current device with the full workspace:
+    "one kernel", "sliced" or "two calls" (a scoring and a Top-k kernel)."""
+    r = int(lib().spdec_select_pages_form(ctypes.byref(cache.desc), int(max_budget_pages)))
+    _check(min(r, 0), "spdec_select_pages_form")
+    return PATH_FORMS[r]
 
 
 def select_pages(cache: PagedCache, q, budget_pages, max_budget_pages: int, sel_idx=None, sel_cnt=None,

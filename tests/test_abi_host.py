@@ -41,7 +41,7 @@ def _declared():
 
 def test_every_declared_function_is_exported(L):
     names = _declared()
-    assert len(names) == len(S.ABI_FUNCTIONS) == 33
+    assert len(names) == len(S.ABI_FUNCTIONS) == 34
     assert set(names) == set(S.ABI_FUNCTIONS)
     for n in names:
         assert hasattr(L, n), n
@@ -55,6 +55,14 @@ def test_status_strings_and_version(L):
 
 
 FAKE = 0x7F0000000000  # 4 KiB-aligned address that is never dereferenced by a rejected call
+
+
+def _sliced_bytes(units, G, D):
+    """The sliced forms' workspace: every unit's 4096 candidate slots (page, score, page-table entry), 16 slices'
+    counts and partials (acc, then (m, l)), one partial count per unit; regions rounded up to 256 bytes."""
+    r = lambda x: (x + 255) // 256 * 256
+    return (r(units * 4096 * 4) * 3 + r(units * 16 * 4) + r(units * 16 * G * D * 4) + r(units * 16 * G * 2 * 4)
+            + r(units * 4))
 
 
 def _desc(**kw):
@@ -99,11 +107,19 @@ def test_budget_scale_and_workspace_checks(L):
     d = _desc()
     # max_budget_pages below 2
     assert L.spdec_select_pages(ctypes.byref(d), FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1 << 30, None) == -1
-    # select workspace: needed unless scores_out is given
+    # select workspace, needed unless scores_out is given: the scores, or for a shape the sliced form takes
+    # (bf16, G <= 4, at most 128 units, max_budget_pages <= 4096) the candidate slots, whichever is larger
     need = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
-    assert need == 2 * 2 * 64 * 4
+    assert need == _sliced_bytes(units=4, G=4, D=128)
+    d32 = _desc(dtype=S.SPDEC_F32)
+    assert L.spdec_select_workspace_bytes(ctypes.byref(d32), 16) == 2 * 2 * 64 * 4
+    assert L.spdec_select_workspace_bytes(ctypes.byref(d), 5000) == 2 * 2 * 64 * 4
+    assert L.spdec_select_workspace_bytes(ctypes.byref(d), 1) == 0
     assert L.spdec_select_pages(ctypes.byref(d), FAKE, FAKE, 16, FAKE, FAKE, None, FAKE, need - 1, None) == -3
     assert L.spdec_select_pages(ctypes.byref(d), FAKE, FAKE, 16, FAKE, FAKE, None, None, 0, None) == -3
+    assert L.spdec_select_pages_form(ctypes.byref(_desc(head_dim=96)), 16) == S.SPDEC_ERR_UNSUPPORTED
+    assert L.spdec_select_pages_form(ctypes.byref(d), 1) == S.SPDEC_ERR_INVALID
+    assert L.spdec_select_pages_form(None, 16) == S.SPDEC_ERR_INVALID
     # decode: bad scale, then short workspace
     dw = L.spdec_decode_workspace_bytes(ctypes.byref(d), 0)
     sw = L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
@@ -122,12 +138,9 @@ def test_sparse_path_checks(L):
     # the two calls' needs (scores rounded up to 256 bytes, then the decode's workspace) or the sliced form's
     # (every unit's candidates: 4096 page, score and page-table triples, 16 slices' counts and partials), whichever
     # is larger
-    sel = L.spdec_select_workspace_bytes(ctypes.byref(d), 16)
-    two = (sel + 255) // 256 * 256 + L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
-    r = lambda x: (x + 255) // 256 * 256
-    units, G, D = 4, 4, 128
-    sliced = r(units * 4096 * 4) * 3 + r(units * 16 * 4) + r(units * 16 * G * D * 4) + r(units * 16 * G * 2 * 4) + r(units * 4)
-    assert need == max(two, sliced)
+    scores = 2 * 2 * 64 * 4
+    two = (scores + 255) // 256 * 256 + L.spdec_decode_workspace_bytes(ctypes.byref(d), 16)
+    assert need == max(two, _sliced_bytes(units=4, G=4, D=128))
     assert L.spdec_sparse_path_workspace_bytes(ctypes.byref(d), 1) == 0
     assert L.spdec_sparse_path_workspace_bytes(None, 16) == 0
     args = lambda **kw: [kw.get(k, v) for k, v in (

@@ -85,5 +85,10 @@ def test_counter_summaries_parse_and_match_patterns(tmp_path, monkeypatch):
     assert ck["sparse_path"] == ["sparse_path_kernel<128,2>"]
     assert bench.call_kernels(spec, "two calls")["sparse_path"] == ck["select_pages"] + ck["sparse_decode"]
     assert bench.call_kernels(spec, "sliced")["sparse_path"][0] == "slice_score_kernel<128,2>"
+    assert ck["select_pages"] == ["score_stream_kernel<BF16,128,2>", "select_topk_reg_kernel<*>"]
+    assert bench.call_kernels(spec, "one kernel", "one kernel")["select_pages"] == ["select_path_kernel<128,2>"]
+    assert bench.call_kernels(spec, "sliced", "sliced")["select_pages"] == [
+        "slice_score_kernel<128,2>", "slice_select_kernel<128,2,false>"]
+    assert bench.call_kernels(spec, "two calls", "one kernel")["sparse_path"][0] == "select_path_kernel<128,2>"
     assert bench.call_kernels(S.custom_spec("g8", num_q_heads=64, num_kv_heads=8, head_dim=128))[
         "dense_decode"][0] == "decode_stream_g8_kernel<128,false>"

@@ -263,6 +263,81 @@ def test_sliced_workspace_shared_across_calls_and_shapes():
                 assert torch.equal(x, y), (rep, dw.wl.spec.name)
 
 
+def _sub_cache(c, n):
+    """The first n sequences of a cache as a batch of their own (leading rows of the page table and lengths)."""
+    return spdec.PagedCache(c.k_pool, c.v_pool, c.kminmax, c.page_table[:n], c.seq_lens[:n], c.num_q_heads)
+
+
+def _check_select_forms(wl, units, n_sub):
+    """spdec_select_pages in the form its shape takes (the step's rule, full workspace) against the two kernels
+    (scores to scores_out, no workspace: a scoring and a Top-k kernel for every shape the one-kernel form does not
+    take; for one-kernel shapes, the first n_sub sequences as a batch of their own): sel_cnt, sel_idx and scores
+    bit for bit; sampled units against the oracle's scores and the Top-B rule."""
+    dw = GS.DeviceWorkload(wl)
+    c = dw.cache
+    spdec.build_meta(c)
+    form = _form(dw)
+    assert spdec.select_pages_form(c, dw.max_budget) == form
+    ws = torch.full((spdec.select_workspace_bytes(c, dw.max_budget),), 0xA5, dtype=torch.uint8, device=c.device)
+    shape = (c.batch, c.num_kv_heads, c.max_pages)
+    sc_a = torch.full(shape, float("nan"), dtype=torch.float32, device=c.device)
+    idx_a, cnt_a = spdec.select_pages(c, dw.q, dw.budget, dw.max_budget, scores_out=sc_a, workspace=ws)
+    idx_b, cnt_b = spdec.select_pages(c, dw.q, dw.budget, dw.max_budget, workspace=ws)
+    sc_c = torch.full(shape, float("nan"), dtype=torch.float32, device=c.device)
+    if form == "one kernel":
+        sub = _sub_cache(c, n_sub)
+        assert spdec.select_pages_form(sub, dw.max_budget) != "one kernel"
+        idx_c, cnt_c = spdec.select_pages(sub, dw.q[:n_sub], dw.budget[:n_sub], dw.max_budget,
+                                          scores_out=sc_c[:n_sub])
+        nb = n_sub
+    else:
+        idx_c, cnt_c = spdec.select_pages(c, dw.q, dw.budget, dw.max_budget, scores_out=sc_c)
+        nb = c.batch
+    torch.cuda.synchronize()
+    ca, cb, cc = cnt_a.cpu().numpy(), cnt_b.cpu().numpy(), cnt_c.cpu().numpy()
+    ia, ib, ic = idx_a.cpu().numpy(), idx_b.cpu().numpy(), idx_c.cpu().numpy()
+    sa, scc = sc_a.cpu().numpy(), sc_c.cpu().numpy()
+    assert np.array_equal(ca, cb) and np.array_equal(ca[:nb], cc)
+    for b in range(c.batch):
+        P = wl.pages(b)
+        if b < nb:
+            assert np.array_equal(sa[b, :, :P].view(np.uint32), scc[b, :, :P].view(np.uint32)), b
+        for g in range(c.num_kv_heads):
+            k = int(ca[b, g])
+            assert np.array_equal(ia[b, g, :k], ib[b, g, :k]), (b, g)
+            if b < nb:
+                assert np.array_equal(ia[b, g, :k], ic[b, g, :k]), (b, g)
+    for (b, g) in units:
+        K64, _ = GS.unit_kv_f64(wl, b, g)
+        s64 = GS.oracle_scores(wl, b, g, K64)
+        GS.check_selection(ia[b, g], int(ca[b, g]), s64, int(wl.budget_pages[b]), dw.max_budget)
+    say(f"  {wl.spec.name}: select {form}: equal to the two kernels on {nb} of {c.batch} sequences; "
+        f"{len(units)} units vs oracle")
+
+
+@pytest.mark.parametrize("case", [("one kernel", i) for i in range(len(CASES))] +
+                         [("sliced", i) for i in range(len(SLICED))])
+def test_select_forms_match_two_kernels_and_oracle(case):
+    """spdec_select_pages in its fused forms (one kernel for batches of at least one unit per compute unit,
+    sliced for few units) selects and scores exactly as its scoring and Top-k kernels do."""
+    kind, i = case
+    if kind == "one kernel":
+        name, D, Hq, Hkv, ps, B, (lo, hi), (blo, bhi), zeros = CASES[i]
+        lens = _lens(i, B, lo, hi, zeros)
+        bud = [int(x) for x in np.random.default_rng(100 + i).integers(blo, bhi + 1, B)]
+        seed = i
+    else:
+        name, D, Hq, Hkv, ps, B, (lo, hi), bud, zeros = SLICED[i]
+        lens = _lens(500 + i, B, lo, hi, zeros)
+        seed = 500 + i
+    say(f"case select forms {kind} {name}: batch {B}")
+    spec = S.custom_spec(f"select-{kind[0]}{i}", batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                         page_size=ps, dtype="bf16", lens=("list", lens), budget=("pages", bud), outlier_channels=4)
+    wl = S.make_workload(spec, seed=seed)
+    # a sub-batch of at most 128 units runs the two kernels when its scores go to scores_out
+    _check_select_forms(wl, GS.sample_units(wl, 12, seed=seed), n_sub=max(1, min(B, 120 // Hkv)))
+
+
 LONG = ["long-131k-ps8", "long-131k-ps16", "long-131k-ps32", "long-131k-ps64"]
 
 
