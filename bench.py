@@ -855,8 +855,13 @@ def top_p_rows(spec, cache, q, budget, dev, timed_loop):
                      "max_pages": float(kept.max()), "sparse_path_us": t_path * 1e6}
     del sel_idx, sel_cnt, ws_sel, ws_sp
     torch.cuda.empty_cache()
-    res["select_top_p_traffic"] = traffic_sum(counter_traffic(f"top-p_{spec.name}"),
-                                              ["score_stream_kernel<*>", "select_topp_reg_kernel<*>"])
+    # the top-p selection takes one kernel where the Top-B selection does, else the scoring and top-p kernels
+    one = spdec.select_pages_form(cache, cap) == "one kernel"
+    topp_kernels = [f"select_topp_path_kernel<{spec.head_dim},{spec.group}>"] if one else \
+        ["score_stream_kernel<*>", "select_topp_reg_kernel<*>"]
+    res["select_top_p_form"] = "one kernel" if one else "two kernels"
+    res["select_top_p_kernels"] = " + ".join(topp_kernels)
+    res["select_top_p_traffic"] = traffic_sum(counter_traffic(f"top-p_{spec.name}"), topp_kernels)
     res["timing"] = "each call K times back to back under one event pair"
     return res
 

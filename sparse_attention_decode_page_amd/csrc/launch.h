@@ -99,6 +99,11 @@ hipError_t launch_stream_merge(const CacheView& c, const int32_t* sel_cnt, int l
 hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int32_t* budget, int max_budget,
                                     float scale, int32_t* sel_idx, int32_t* sel_cnt, float* scores, float* out,
                                     float* lse, hipStream_t s);
+// spdec_select_pages_top_p in one kernel (the shapes path_fused_supported takes):
+// scores in LDS, the top-p cut there.
+hipError_t launch_select_topp_fused(const CacheView& c, const void* q, float top_p, float score_scale,
+                                    const int32_t* budget, int max_budget, int32_t* sel_idx, int32_t* sel_cnt,
+                                    float* scores, hipStream_t s);
 hipError_t launch_decode(const CacheView& c, const DecodePlan& p, const void* q, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float scale, float* out, float* lse, void* ws, hipStream_t s);
 // Dense stream partials over each sequence's pages from first_page[b / group_size]

@@ -22,6 +22,7 @@
 #include "launch.h"
 #include "scoring.h"
 #include "topb.h"
+#include "topp.h"
 #include "unit_stream.h"
 
 namespace spdec {
@@ -63,6 +64,8 @@ struct PathArgs {
   float* lse;       // nullable
   int lpt;          // 1: workgroups take units largest first (more units than compute units)
   int stream;       // 1: the whole step; 0: the selection only (no attention)
+  int topp;         // 1: the score-mass (top-p) selection only; budget then nullable (caps)
+  float top_p, score_scale;
 };
 
 // Tokens L, pages P and kept pages K of sequence b, and the bytes one of its
@@ -72,7 +75,8 @@ __device__ __forceinline__ long long path_work(const PathArgs& a, int b, int& L,
   const CacheView& c = a.c;
   L = max(c.seq_lens[b], 0);
   P = min((L + c.page_size - 1) >> c.ps_log2, c.max_pages);
-  K = min(min(max(a.budget[b], 2), a.cap), P);
+  K = min(min(a.budget != nullptr ? max(a.budget[b], 2) : a.cap, a.cap), P);
+  if (a.topp) return P > 2 ? (long long)P : 0ll;  // the masses need every page's score
   const bool scored = K < P && K > 2;
   return (scored ? (long long)P : 0ll) + (a.stream ? (long long)min(L, K * c.page_size) : 0ll);
 }
@@ -121,11 +125,12 @@ struct UnitSelectShared {
 // (K, ascending) in sm.list, also written to sel_idx / sel_cnt. ptab
 // (nullable, LDS) receives the unit's page-table row when the pages are
 // scored. Returns false, after writing sel_cnt = 0, for a unit with no token.
-template <int D, int G>
-__device__ __forceinline__ bool unit_selection(const PathArgs& a, UnitSelectShared& sm, int* ptab, int& b, int& g,
-                                               int& L, int& P, int& K) {
+// The workgroup's unit: sequence b, KV head g, with L tokens in P pages and K
+// (the Top-B count, or the cap for the top-p selection).
+__device__ __forceinline__ void unit_resolve(const PathArgs& a, UnitSelectShared& sm, int& b, int& g, int& L, int& P,
+                                             int& K) {
   const CacheView& c = a.c;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x;
   const int B = c.batch;
   // The unit: KV head blockIdx % Hkv of the sequence of rank blockIdx / Hkv
   // (with no more units than compute units every unit starts at once, and the
@@ -155,6 +160,32 @@ __device__ __forceinline__ bool unit_selection(const PathArgs& a, UnitSelectShar
   L = sm.L;
   P = sm.P;
   K = sm.K;
+}
+
+// The scores of pages [0, P) of unit (b, g) into sm.score, the eight waves
+// taking a contiguous share each (ptab, nullable LDS, receives the unit's
+// page-table row); written to a.scores too when asked for. Ends with a barrier.
+template <int D, int G>
+__device__ __forceinline__ void unit_scores(const PathArgs& a, UnitSelectShared& sm, int* ptab, int b, int g, int P,
+                                            bool needed) {
+  const CacheView& c = a.c;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  if (needed || a.scores != nullptr) {
+    const int per = (P + kPathWaves - 1) / kPathWaves;
+    const int p0 = min(P, wave * per), p1 = min(P, p0 + per);
+    if (p0 < p1) score_segment<BF16, D, G>(c, a.q, b, g, p0, p1, sm.score, lane, ptab);
+  }
+  __syncthreads();
+  if (a.scores != nullptr)
+    for (int i = tid; i < P; i += kPathThreads) a.scores[((int64_t)b * c.hkv + g) * c.max_pages + i] = sm.score[i];
+}
+
+template <int D, int G>
+__device__ __forceinline__ bool unit_selection(const PathArgs& a, UnitSelectShared& sm, int* ptab, int& b, int& g,
+                                               int& L, int& P, int& K) {
+  const CacheView& c = a.c;
+  const int tid = threadIdx.x;
+  unit_resolve(a, sm, b, g, L, P, K);
   const int u = b * c.hkv + g;
   if (P == 0) {
     if (tid == 0) a.sel_cnt[u] = 0;
@@ -163,14 +194,7 @@ __device__ __forceinline__ bool unit_selection(const PathArgs& a, UnitSelectShar
 
   // Scores of the unit's pages (needed by the select, or asked for).
   const bool select = K < P && K > 2;
-  if (select || a.scores != nullptr) {
-    const int per = (P + kPathWaves - 1) / kPathWaves;
-    const int p0 = min(P, wave * per), p1 = min(P, p0 + per);
-    if (p0 < p1) score_segment<BF16, D, G>(c, a.q, b, g, p0, p1, sm.score, lane, ptab);
-  }
-  __syncthreads();
-  if (a.scores != nullptr)
-    for (int i = tid; i < P; i += kPathThreads) a.scores[(int64_t)u * c.max_pages + i] = sm.score[i];
+  unit_scores<D, G>(a, sm, ptab, b, g, P, select);
 
   // The kept pages, ascending, into list[0 .. K).
   if (K >= P) {
@@ -243,10 +267,37 @@ __global__ __launch_bounds__(kPathThreads) void select_path_kernel(PathArgs a) {
   unit_selection<D, G>(a, sm, nullptr, b, g, L, P, K);
 }
 
+// The score-mass (top-p) selection (spdec_select_pages_top_p) in one kernel:
+// each workgroup scores its unit's pages into LDS and takes the top-p cut
+// there.
+template <int D, int G>
+__global__ __launch_bounds__(kPathThreads) void select_topp_path_kernel(PathArgs a) {
+  __shared__ UnitSelectShared sm;
+  __shared__ ToppShared<kPathThreads> ts;
+  int b, g, L, P, K;
+  unit_resolve(a, sm, b, g, L, P, K);
+  unit_scores<D, G>(a, sm, nullptr, b, g, P, P > 2);
+  const int64_t u = (int64_t)b * a.c.hkv + g;
+  // keys spread over every thread: ceil((P - 2) / 512) each, in registers for up to 2048 or 4094 middle pages
+  const int kpt = max(1, (P - 2 + kPathThreads - 1) / kPathThreads);
+  if (P - 2 <= kPathKeysShort * kPathThreads)
+    topp_cut<kPathKeysShort, kPathThreads>(sm.score, P, K, a.top_p, a.score_scale, a.sel_idx + u * a.cap,
+                                           a.sel_cnt + u, ts, kpt);
+  else
+    topp_cut<kPathKeys, kPathThreads>(sm.score, P, K, a.top_p, a.score_scale, a.sel_idx + u * a.cap,
+                                      a.sel_cnt + u, ts, kpt);
+}
+
 template <int D>
 hipError_t path_launch(const PathArgs& a, hipStream_t s) {
   const dim3 grid(a.c.batch * a.c.hkv), block(kPathThreads);
-  if (a.stream) {
+  if (a.topp) {
+    switch (a.c.group) {
+      case 1: hipLaunchKernelGGL((select_topp_path_kernel<D, 1>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((select_topp_path_kernel<D, 2>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((select_topp_path_kernel<D, 4>), grid, block, 0, s, a); break;
+    }
+  } else if (a.stream) {
     switch (a.c.group) {
       case 1: hipLaunchKernelGGL((sparse_path_kernel<D, 1>), grid, block, 0, s, a); break;
       case 2: hipLaunchKernelGGL((sparse_path_kernel<D, 2>), grid, block, 0, s, a); break;
@@ -286,6 +337,30 @@ hipError_t launch_sparse_path_fused(const CacheView& c, const void* q, const int
   a.lse = lse;
   a.lpt = (int64_t)c.batch * c.hkv > device_compute_units() ? 1 : 0;
   a.stream = out != nullptr ? 1 : 0;
+  a.topp = 0;
+  a.top_p = a.score_scale = 0.f;
+  return c.head_dim == 64 ? path_launch<64>(a, s) : path_launch<128>(a, s);
+}
+
+hipError_t launch_select_topp_fused(const CacheView& c, const void* q, float top_p, float score_scale,
+                                    const int32_t* budget, int max_budget, int32_t* sel_idx, int32_t* sel_cnt,
+                                    float* scores, hipStream_t s) {
+  PathArgs a;
+  a.c = c;
+  a.q = q;
+  a.budget = budget;
+  a.cap = max_budget;
+  a.qk_scale = 0.f;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.scores = scores;
+  a.out = nullptr;
+  a.lse = nullptr;
+  a.lpt = (int64_t)c.batch * c.hkv > device_compute_units() ? 1 : 0;
+  a.stream = 0;
+  a.topp = 1;
+  a.top_p = top_p;
+  a.score_scale = score_scale;
   return c.head_dim == 64 ? path_launch<64>(a, s) : path_launch<128>(a, s);
 }
 

@@ -26,6 +26,7 @@
 #include "launch.h"
 #include "scoring.h"
 #include "topb.h"
+#include "topp.h"
 
 namespace spdec {
 
@@ -411,190 +412,22 @@ __global__ __launch_bounds__(NT) void select_topk_reg_kernel(CacheView c, const 
   emit_top<KPT, NT>(key, P - 2, K - 2, kmin, nbits, out, sh);
 }
 
-// Score-mass (top-p) selection over the same keys. The page masses
-// w = exp(c (s - max s)) (fp64, so w <= 1) are summed as 2^-48 fixed-point
-// integers: integer sums do not depend on their order, which keeps the
-// histograms deterministic under LDS atomics. MSB-first radix passes on the
-// keys find the smallest count of middle pages, in the Top-B order, whose
-// mass with the two forced pages reaches ceil(top_p * total); the count is
-// capped, and emit_top writes that many pages exactly as the Top-B select
-// would.
-constexpr double kMassOne = 281474976710656.0;  // 2^48
-
+// Score-mass (top-p) selection over the same keys (topp.h), one workgroup
+// per unit reading the unit's scores.
 template <int KPT, int NT>
 __global__ __launch_bounds__(NT) void select_topp_reg_kernel(CacheView c, const float* __restrict__ scores,
                                                            float top_p, float score_scale,
                                                            const int32_t* __restrict__ budget, int cap,
                                                            int32_t* __restrict__ sel_idx,
                                                            int32_t* __restrict__ sel_cnt) {
-  __shared__ TopBShared<NT> sh;
-  __shared__ unsigned long long s_mass[256];
-  __shared__ unsigned long long s_msum[NT / kWave];
-  __shared__ float s_fmax[NT / kWave];
-  __shared__ unsigned long long s_mabove, s_wtie;
-  __shared__ int s_cabove, s_found;
+  __shared__ ToppShared<NT> ts;
   const int unit = blockIdx.x;
   const int b = unit / c.hkv;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int L = c.seq_lens[b];
   const int P = min((max(L, 0) + c.page_size - 1) >> c.ps_log2, c.max_pages);
-  int32_t* out = sel_idx + (int64_t)unit * cap;
-  if (P <= 2) {
-    if (tid < P) out[tid] = tid;
-    if (tid == 0) sel_cnt[unit] = P;
-    return;
-  }
   const int kcap = min(min(budget != nullptr ? max(budget[b], 2) : cap, cap), P);
-  const float* srow = scores + (int64_t)unit * c.max_pages;
-  const int M = P - 2;
-  const int i0 = tid * KPT;
-  uint32_t key[KPT], kmin;
-  int nbits;
-  load_keys<KPT, NT>(srow, M, key, kmin, nbits, sh);
-
-  // Masses: the largest score, then fixed-point w for the middle pages.
-  float mx = -INFINITY;
-  for (int i = tid; i < P; i += NT) mx = fmaxf(mx, srow[i]);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) s_fmax[wave] = mx;
-  __syncthreads();
-  mx = s_fmax[0];
-#pragma unroll
-  for (int w = 1; w < NT / kWave; ++w) mx = fmaxf(mx, s_fmax[w]);
-  const double cs = (double)score_scale, dm = (double)mx;
-  auto fixed_mass = [&](float s) {
-    return (unsigned long long)(exp(cs * ((double)s - dm)) * kMassOne + 0.5);
-  };
-  // Up to 16 keys per thread the masses stay in registers; 32 recompute them
-  // (the same value every time) rather than spill. Masses come from the keys
-  // the thread holds (key_score inverts score_key; a zero keeps its mass).
-  constexpr bool kKeep = KPT <= 16;
-  unsigned long long wf[kKeep ? KPT : 1];
-  auto mass_of = [&](int r) -> unsigned long long {
-    if constexpr (kKeep) {
-      return wf[r];
-    } else {
-      uint32_t k = key[r];
-      asm volatile("" : "+v"(k));  // computed where it is used, not carried from an earlier loop
-      return i0 + r < M ? fixed_mass(key_score(k)) : 0ull;
-    }
-  };
-  unsigned long long local = 0;
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const unsigned long long m = i0 + r < M ? fixed_mass(key_score(key[r])) : 0ull;
-    if constexpr (kKeep) wf[r] = m;
-    local += m;
-  }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) local += __shfl_xor(local, off);
-  if (lane == 0) s_msum[wave] = local;
-  __syncthreads();
-  unsigned long long middle = 0;
-#pragma unroll
-  for (int w = 0; w < NT / kWave; ++w) middle += s_msum[w];
-  const unsigned long long forced = fixed_mass(srow[0]) + fixed_mass(srow[P - 1]);
-  const double tgt = ceil((double)top_p * (double)(forced + middle));
-  int k_mass;
-  uint32_t T_mass = 0;
-  int eq_mass = 0;
-  if ((double)forced >= tgt) {
-    k_mass = 0;
-  } else {
-    // Mass still needed from the middle pages (the crossing exists unless
-    // rounding put the target above the whole mass: then every page is kept).
-    unsigned long long rem = (unsigned long long)tgt - forced;
-    uint32_t prefix = 0, mask = 0;
-    int cnt_above = 0;
-    bool found = rem <= middle;
-    for (int hi = nbits; hi > 0 && found; hi -= 8) {
-      const int lo = max(hi - 8, 0);
-      const uint32_t dmask = (1u << (hi - lo)) - 1u;
-      // hist[2]: the Top-B passes below clear it before they use it; load_keys cleared hist[0] for them.
-      for (int i = tid; i < 256; i += NT) { sh.hist[2][i] = 0; s_mass[i] = 0ull; }
-      if (tid == 0) s_found = 0;
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        const uint32_t off = key[r] - kmin;
-        if (i0 + r < M && (off & mask) == prefix) {
-          const uint32_t d = (off >> lo) & dmask;
-          atomicAdd(&sh.hist[2][d], 1u);
-          atomicAdd(&s_mass[d], mass_of(r));
-        }
-      }
-      __syncthreads();
-      if (tid < kWave) {
-        const int top = 255 - 4 * tid;
-        const unsigned long long m0 = s_mass[top], m1 = s_mass[top - 1], m2 = s_mass[top - 2], m3 = s_mass[top - 3];
-        const unsigned long long tot = m0 + m1 + m2 + m3;
-        unsigned long long incl = tot;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const unsigned long long y = __shfl_up(incl, off);
-          if (lane >= off) incl += y;
-        }
-        const unsigned long long excl = incl - tot;
-        const int c0 = sh.hist[2][top], c1 = sh.hist[2][top - 1], c2 = sh.hist[2][top - 2];
-        const int ctot = c0 + c1 + c2 + sh.hist[2][top - 3];
-        const int cincl = wave_incl_scan(ctot);
-        const int cexcl = cincl - ctot;
-        if (excl < rem && rem <= incl) {
-          const unsigned long long rr = rem - excl;
-          int digit;
-          unsigned long long above;
-          int cab;
-          if (rr <= m0) { digit = top; above = excl; cab = cexcl; }
-          else if (rr <= m0 + m1) { digit = top - 1; above = excl + m0; cab = cexcl + c0; }
-          else if (rr <= m0 + m1 + m2) { digit = top - 2; above = excl + m0 + m1; cab = cexcl + c0 + c1; }
-          else { digit = top - 3; above = excl + m0 + m1 + m2; cab = cexcl + c0 + c1 + c2; }
-          sh.digit = digit;
-          s_mabove = above;
-          s_cabove = cab;
-          s_found = 1;
-        }
-      }
-      __syncthreads();
-      found = s_found != 0;
-      if (found) {
-        prefix |= (uint32_t)sh.digit << lo;
-        mask |= dmask << lo;
-        rem -= s_mabove;
-        cnt_above += s_cabove;
-      }
-      __syncthreads();
-    }
-    if (found) {
-      // Pages with the threshold key share one score, hence one mass.
-      const uint32_t T = kmin + prefix;
-#pragma unroll
-      for (int r = 0; r < KPT; ++r)
-        if (i0 + r < M && key[r] == T) s_wtie = mass_of(r);
-      __syncthreads();
-      const unsigned long long wt = s_wtie;
-      eq_mass = wt > 0 ? (int)((rem + wt - 1) / wt) : M;
-      k_mass = cnt_above + eq_mass;
-      T_mass = T;
-    } else {
-      k_mass = M;
-    }
-  }
-  const int need = min(min(k_mass, M), kcap - 2);
-  const int K = need + 2;
-  if (tid == 0) {
-    out[0] = 0;
-    out[K - 1] = P - 1;
-    sel_cnt[unit] = K;
-  }
-  if (need == 0) return;
-  if (need == k_mass && k_mass < M) {
-    // The mass decided the count: its threshold key and tie share are the
-    // Top-B order's cut for exactly this many pages.
-    write_selected<KPT, NT>(key, M, need, T_mass, eq_mass, out, sh);
-  } else {
-    emit_top<KPT, NT>(key, M, need, kmin, nbits, out, sh);
-  }
+  topp_cut<KPT, NT>(scores + (int64_t)unit * c.max_pages, P, kcap, top_p, score_scale, sel_idx + (int64_t)unit * cap,
+                    sel_cnt + unit, ts);
 }
 
 template <typename T, int D, int G>
@@ -672,6 +505,8 @@ hipError_t launch_select(const CacheView& c, const void* q, const int32_t* budge
 hipError_t launch_select_top_p(const CacheView& c, const void* q, float top_p, float score_scale,
                                const int32_t* budget, int max_budget, int32_t* sel_idx, int32_t* sel_cnt,
                                float* scores_out, void* ws, hipStream_t s) {
+  if (path_fused_supported(c, max_budget))
+    return launch_select_topp_fused(c, q, top_p, score_scale, budget, max_budget, sel_idx, sel_cnt, scores_out, s);
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
   hipError_t e = launch_score(c, q, scores, s);
   if (e != hipSuccess) return e;

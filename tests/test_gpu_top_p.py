@@ -165,3 +165,45 @@ def test_top_p_qwen3_8b_ragged_sampled():
 def test_top_p_long_context_8190_middle_pages():
     wl = S.make_workload("long-131k-ps16", seed=0)
     _check(wl, 0.95, GS.sample_units(wl, 3, seed=2), use_budget=False)
+
+
+@pytest.mark.parametrize("use_budget", [True, False])
+def test_top_p_one_kernel_form(use_budget):
+    """A batch of at least one (sequence, KV head) per compute unit takes the one-kernel form (scores in LDS, the
+    same cut): kept pages, counts and scores bit for bit as the scoring and top-p kernels give them on the first
+    sequences as a batch of their own, and sampled units against the oracle."""
+    spec = S.custom_spec("topp-one", batch=40, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                         dtype="bf16", lens=("uniform", 1, 6000), budget=("tokens", 1024), outlier_channels=2)
+    wl = S.make_workload(spec, seed=61)
+    dw = GS.DeviceWorkload(wl)
+    cache = dw.cache
+    spdec.build_meta(cache)
+    assert spdec.select_pages_form(cache, dw.max_budget) == "one kernel"
+    c32 = float(np.float32(1.0 / (spec.group * math.sqrt(spec.head_dim))))
+    cap = dw.max_budget if use_budget else int(wl.page_table.shape[1])
+    budget = dw.budget if use_budget else None
+    shape = (spec.batch, spec.num_kv_heads, cache.max_pages)
+    sc_a = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    idx_a, cnt_a = spdec.select_pages_top_p(cache, dw.q, 0.9, cap, score_scale=c32, budget_pages=budget,
+                                            scores_out=sc_a)
+    n = 12   # 96 units: the scoring and top-p kernels
+    sub = spdec.PagedCache(cache.k_pool, cache.v_pool, cache.kminmax, cache.page_table[:n], cache.seq_lens[:n],
+                           cache.num_q_heads)
+    assert spdec.select_pages_form(sub, dw.max_budget) != "one kernel"
+    sc_b = torch.full((n,) + shape[1:], float("nan"), dtype=torch.float32, device="cuda")
+    idx_b, cnt_b = spdec.select_pages_top_p(sub, dw.q[:n], 0.9, cap, score_scale=c32,
+                                            budget_pages=budget[:n] if budget is not None else None, scores_out=sc_b)
+    torch.cuda.synchronize()
+    ca, cb = cnt_a.cpu().numpy(), cnt_b.cpu().numpy()
+    ia, ib = idx_a.cpu().numpy(), idx_b.cpu().numpy()
+    sa, sb = sc_a.cpu().numpy(), sc_b.cpu().numpy()
+    assert np.array_equal(ca[:n], cb)
+    for b in range(n):
+        P = wl.pages(b)
+        assert np.array_equal(sa[b, :, :P].view(np.uint32), sb[b, :, :P].view(np.uint32)), b
+        for g in range(spec.num_kv_heads):
+            k = int(ca[b, g])
+            assert np.array_equal(ia[b, g, :k], ib[b, g, :k]), (b, g)
+    print(f"  top-p one kernel (budget {use_budget}): {n} of {spec.batch} sequences equal to the two kernels",
+          flush=True)
+    _check(wl, 0.9, GS.sample_units(wl, 10, seed=62), use_budget=use_budget)
