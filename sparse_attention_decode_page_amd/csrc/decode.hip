@@ -433,9 +433,10 @@ __global__ __launch_bounds__(kDecodeThreads, (D == 64 && G <= 2) ? 4 : 1) void d
 // For the B operand each lane loads, for its own four tokens, the chunk of
 // DPC = D/16 channels starting at DPC (l % 16): column n of block jb then
 // stands for channel DPC n + jb (no transpose). Each fp32 weight enters P.V
-// as the sum of three bf16 values (hi + mid + lo, each the rounded remainder
-// of the previous), which carries all 24 bits of its significand, so the
-// products and fp32 sums match the VALU form up to summation order.
+// as the sum of three bf16 values that add up to it exactly (hi: the weight
+// with its low 16 bits cleared; mid: the same of the exact remainder; lo: the
+// rest, at most 8 significant bits), so the products and fp32 sums match the
+// VALU form up to summation order.
 template <int DPC> struct VChunk;
 template <> struct VChunk<8> { using type = u32x4; };
 template <> struct VChunk<4> { typedef uint32_t type __attribute__((ext_vector_type(2))); };
@@ -445,11 +446,6 @@ __device__ __forceinline__ VChunk<4>::type load_vchunk(const uint16_t* p, VChunk
   return __builtin_nontemporal_load(reinterpret_cast<const VChunk<4>::type*>(p));
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs of either sign).
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16) & 0xFFFFu;
-}
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -628,13 +624,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_stream_g8_kernel(Str
         for (int e = 0; e < 4; ++e) {
           const float pe = fast_exp2(sv[e] - m);
           lsum += pe;
-          const uint32_t h1 = bf16_rne(pe);
-          const float r1 = pe - __uint_as_float(h1 << 16);
-          const uint32_t h2 = bf16_rne(r1);
-          const float r2 = r1 - __uint_as_float(h2 << 16);
-          p1[e] = (short)h1;
-          p2[e] = (short)h2;
-          p3[e] = (short)bf16_rne(r2);
+          const uint32_t u1 = __float_as_uint(pe) & 0xFFFF0000u;
+          const float r1 = pe - __uint_as_float(u1);
+          const uint32_t u2 = __float_as_uint(r1) & 0xFFFF0000u;
+          const float r2 = r1 - __uint_as_float(u2);
+          p1[e] = (short)(u1 >> 16);
+          p2[e] = (short)(u2 >> 16);
+          p3[e] = (short)(__float_as_uint(r2) >> 16);
         }
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {

@@ -47,10 +47,19 @@ typedef float vf32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ vbf16x8_t vas_bf16x8(const u32x4& v) { return __builtin_bit_cast(vbf16x8_t, v); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite and >= 0 here).
-__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// A non-negative finite fp32 weight as three bf16 terms that sum to it
+// exactly: hi is the weight with its low 16 bits cleared, mid the same of
+// the remainder (w - hi has at most 16 significant bits, and the subtraction
+// is exact), lo the remainder after that (at most 8 significant bits, so it
+// is a bf16 value).
+__device__ __forceinline__ void split3_bf16(float w, short& hi, short& mid, short& lo) {
+  const uint32_t u1 = __float_as_uint(w) & 0xFFFF0000u;
+  const float r1 = w - __uint_as_float(u1);
+  const uint32_t u2 = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(u2);
+  hi = (short)(u1 >> 16);
+  mid = (short)(u2 >> 16);
+  lo = (short)(__float_as_uint(r2) >> 16);
 }
 
 // A lane's V chunk of one token: DPC bf16 channels (16 bytes for D = 128,
@@ -308,22 +317,19 @@ void verify_stream_kernel(VerifyArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) o[st][jb][r] *= ar[r];
           }
-          // Each fp32 weight enters P.V as three bf16 terms (hi + mid + lo,
-          // each the rounded remainder of the previous): all 24 bits of its
-          // significand, so the products match fp32 weights and the result
-          // matches the single-query dense decode up to summation order.
+          // Each fp32 weight enters P.V as three bf16 terms that sum to it
+          // exactly (split3_bf16): the products match fp32 weights and the
+          // result matches the single-query dense decode up to summation order.
           vs16x4_t p1, p2, p3;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float pe = fast_exp2(s[e] - m[st]);
             lsum[st] += pe;
-            const uint32_t h1 = bf16_bits_rne(pe);
-            const float r1 = pe - __uint_as_float(h1 << 16);
-            const uint32_t h2 = bf16_bits_rne(r1);
-            const float r2 = r1 - __uint_as_float(h2 << 16);
-            p1[e] = (short)h1;
-            p2[e] = (short)h2;
-            p3[e] = (short)bf16_bits_rne(r2);
+            short hi, mid, lo;
+            split3_bf16(pe, hi, mid, lo);
+            p1[e] = hi;
+            p2[e] = mid;
+            p3[e] = lo;
           }
 #pragma unroll
           for (int jb = 0; jb < NB; ++jb) {
