@@ -208,7 +208,9 @@ spdec_status spdec_select_pages(const spdec_cache* cache, const void* q, const i
  *
  * 0 < top_p <= 1, score_scale >= 0 (finite; 1/(G*sqrt(D)) reads the bound,
  * which sums the G query heads, as a per-head logit). Outputs and workspace
- * as spdec_select_pages.
+ * as spdec_select_pages. Forms: in the shapes of spdec_select_pages'
+ * SPDEC_PATH_ONE_KERNEL form, one kernel (scores in LDS, the same cut);
+ * otherwise a scoring kernel and a top-p kernel (no sliced form).
  */
 spdec_status spdec_select_pages_top_p(const spdec_cache* cache, const void* q, float top_p, float score_scale,
                                       const int32_t* budget_pages, int max_budget_pages, int32_t* sel_idx,
