@@ -216,6 +216,9 @@ SLICED = [
     ("D64 G1 ps8", 64, 4, 4, 8, 8, (30000, 70000), [500, 2, 7, 256, 511, 100, 300, 1], 0),
     ("D64 G4 ps64", 64, 16, 4, 64, 3, (100, 200000), [30, 10, 60], 0),
     ("D128 G4 ps16 one unit", 128, 4, 1, 16, 1, (65536, 65536), [250], 0),
+    # 128 units, the most the form takes: two slices per unit
+    ("D128 G4 ps16 128 units", 128, 32, 8, 16, 16, (1, 30000), [2, 9, 64, 300, 130, 0, 45, 1000, 17, 250, 80,
+                                                                    3, 500, 120, 33, 700], 1),
 ]
 
 
